@@ -1,0 +1,155 @@
+"""The library's byte layout of the packed cache, restated for comparison.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The pages fix no byte layout: they only say that codes, scales and
+zero-points are stored (scale storage eats part of the saving, "KV Cache
+Quantization Analysis", sec. 2 granularity bullet) and that the recent
+window stays in full precision (sec. 3).  The layout below is the one the
+library documents in ``include/kvq.h``; this module writes it out
+independently so that tests can compare the library's planes byte for byte.
+
+Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
+
+* K codes   [B][Hkv][NB*32][D*b/8]  token-major; channel c of a token sits at
+  bit (c*b mod 8) of byte floor(c*b/8) (LSB first).  FP8: one byte per code.
+* V codes   [B][Hkv][NB][32*D*b/8]  one block of 32 tokens is 64 "records"
+  of D*b/16 bytes.  Record l = 16*qd + r holds channels {16*m + r} for
+  m = 0 .. D/16-1 and the eight tokens T = (4qd, 4qd+1, 4qd+2, 4qd+3,
+  16+4qd, 16+4qd+1, 16+4qd+2, 16+4qd+3) of the block, laid out per format:
+    INT4  word m: nibble j (bits 4j..4j+3) = code(T[j], 16m + r)
+    INT8, FP8  bytes 8m .. 8m+7 = codes of T[0], T[4], T[1], T[5], T[2],
+          T[6], T[3], T[7] for channel 16m + r
+    INT2  word p (channels 16*(2p) + r = "A" and 16*(2p+1) + r = "B"):
+          byte 0 = A's T[0..3], byte 1 = B's T[0..3], byte 2 = A's T[4..7],
+          byte 3 = B's T[4..7], two bits per code, LSB first.
+* K meta    [B][Hkv][NB][2][D]        fp32: s[D] then z[D] of the block's group
+* V meta    [B][Hkv][NB][2][D/G_v][32] fp32: s then z, [channel group][token]
+* K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+
+
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack the last axis of ``codes`` LSB-first: element i at bit i*b."""
+    codes = np.asarray(codes, np.uint8)
+    if bits == 8:
+        return codes.copy()
+    per = 8 // bits
+    n = codes.shape[-1]
+    assert n % per == 0
+    c = codes.reshape(codes.shape[:-1] + (n // per, per)).astype(np.uint16)
+    shifts = (np.arange(per) * bits).astype(np.uint16)
+    return np.bitwise_or.reduce(c << shifts, axis=-1).astype(np.uint8)
+
+
+def unpack_bits(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Inverse of :func:`pack_bits` (``n`` codes along the last axis)."""
+    packed = np.asarray(packed, np.uint8)
+    if bits == 8:
+        return packed[..., :n].copy()
+    per = 8 // bits
+    shifts = (np.arange(per) * bits).astype(np.uint8)
+    c = (packed[..., :, None] >> shifts) & ((1 << bits) - 1)
+    return c.reshape(packed.shape[:-1] + (-1,))[..., :n].astype(np.uint8)
+
+
+def _record_tokens(qd: int):
+    return [4 * qd + j for j in range(4)] + [16 + 4 * qd + j for j in range(4)]
+
+
+def v_block_stream_order(fmt: str, d: int):
+    """(token, channel) of every code of a V block in packed-stream order."""
+    if d % 32:
+        raise ValueError("head_dim must be a multiple of 32")
+    tok, ch = [], []
+    sigma = [0, 4, 1, 5, 2, 6, 3, 7]
+    for lane in range(64):
+        qd, r = divmod(lane, 16)
+        t = _record_tokens(qd)
+        if fmt == "int4":
+            for m in range(d // 16):
+                for j in range(8):
+                    tok.append(t[j]); ch.append(16 * m + r)
+        elif fmt in ("int8", "fp8"):
+            for m in range(d // 16):
+                for k in range(8):
+                    tok.append(t[sigma[k]]); ch.append(16 * m + r)
+        elif fmt == "int2":
+            for p in range(d // 32):
+                for tile, half in ((2 * p, 0), (2 * p + 1, 0), (2 * p, 4), (2 * p + 1, 4)):
+                    for j in range(4):
+                        tok.append(t[half + j]); ch.append(16 * tile + r)
+        else:
+            raise ValueError(fmt)
+    return np.array(tok), np.array(ch)
+
+
+def _bits(fmt: str) -> int:
+    return {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}[fmt]
+
+
+def pack_k_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """[..., N, D] codes -> [..., N, D*b/8] bytes (token-major, LSB first)."""
+    return pack_bits(codes, _bits(fmt))
+
+
+def unpack_k_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
+    return unpack_bits(packed, _bits(fmt), d)
+
+
+def pack_v_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """[..., NB*32, D] codes -> [..., NB, 32*D*b/8] swizzled block bytes."""
+    codes = np.asarray(codes, np.uint8)
+    n, d = codes.shape[-2:]
+    assert n % BLOCK == 0
+    nb = n // BLOCK
+    blk = codes.reshape(codes.shape[:-2] + (nb, BLOCK, d))
+    tok, ch = v_block_stream_order(fmt, d)
+    stream = blk[..., tok, ch]                      # [..., NB, 32*D]
+    return pack_bits(stream, _bits(fmt))
+
+
+def unpack_v_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
+    """Inverse of :func:`pack_v_codes`: [..., NB, bytes] -> [..., NB*32, D]."""
+    packed = np.asarray(packed, np.uint8)
+    nb = packed.shape[-2]
+    stream = unpack_bits(packed, _bits(fmt), BLOCK * d)
+    tok, ch = v_block_stream_order(fmt, d)
+    out = np.zeros(packed.shape[:-1] + (BLOCK, d), np.uint8)
+    out[..., tok, ch] = stream
+    return out.reshape(packed.shape[:-2] + (nb * BLOCK, d))
+
+
+def pack_k_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """s, z [..., NB, D] -> [..., NB, 2, D] fp32."""
+    return np.stack([np.asarray(s, np.float32), np.asarray(z, np.float32)], axis=-2)
+
+
+def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """s, z [..., NB*32, Gn] -> [..., NB, 2, Gn, 32] fp32."""
+    s = np.asarray(s, np.float32)
+    z = np.asarray(z, np.float32)
+    n, gn = s.shape[-2:]
+    nb = n // BLOCK
+    sb = np.swapaxes(s.reshape(s.shape[:-2] + (nb, BLOCK, gn)), -1, -2)
+    zb = np.swapaxes(z.reshape(z.shape[:-2] + (nb, BLOCK, gn)), -1, -2)
+    return np.stack([sb, zb], axis=-3)
+
+
+def unpack_k_meta(m: np.ndarray):
+    m = np.asarray(m, np.float32)
+    return m[..., 0, :].copy(), m[..., 1, :].copy()
+
+
+def unpack_v_meta(m: np.ndarray):
+    """[..., NB, 2, Gn, 32] -> s, z [..., NB*32, Gn]."""
+    m = np.asarray(m, np.float32)
+    nb, _, gn, blk = m.shape[-4:]
+    s = np.swapaxes(m[..., 0, :, :], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
+    z = np.swapaxes(m[..., 1, :, :], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
+    return s.copy(), z.copy()

@@ -1,0 +1,224 @@
+"""Quantization codecs of the KV cache, written out in numpy.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Integer formats (INT8 / INT4 / INT2)
+------------------------------------
+"KV Cache Quantization Analysis", sec. 2 (quantization basics) gives uniform
+affine quantization: a real x maps to the integer q = round(x/s + z) and back
+to x_hat = s * (q - z), with s the scale and z the zero-point; an asymmetric
+z (non-zero) is preferred when the data is not centred on zero; per-channel /
+per-token granularity stores one (s, z) pair per row or column.
+
+Readings taken where the page is silent (each also listed in the design doc):
+
+* range estimator: s and z map the group minimum to code 0 and the group
+  maximum to code 2^b - 1 (plain min/max, no clipping);
+* every step is one IEEE fp32 operation with round-to-nearest-even, in the
+  order the formula is written: s = (max - min) / (2^b - 1), z = (-min) / s,
+  q = clamp(rint(x / s + z), 0, 2^b - 1); true division, no fused
+  multiply-add;
+* z is kept real-valued (fp32), not rounded to an integer;
+* a constant group (max == min) gets s = 1, so every code is 0 and the
+  dequantized value equals the constant exactly;
+* the group minimum is normalised with ``+ 0.0`` so that a zero minimum is
+  always +0 (then z is -0.0, bit pattern 0x80000000);
+* dequantization x_hat = s * (q - z) is evaluated in fp64 from the stored
+  fp32 s and z.
+
+FP8 E4M3
+--------
+Sec. 4 of the same page (FP8 / INT8) names the OCP E4M3 format (4 exponent
+bits, 3 mantissa bits) used with an fp32 scale.  The page prints a +-240
+range, which is the maximum of the "fnuz" E4M3 variant; the OCP format the
+page names has maximum finite magnitude 448 (exponent bias 7, no infinities,
+S.1111.111 is NaN).  This oracle uses OCP E4M3 with max 448 and restates the
+codec from the format definition: the encoder rounds to nearest, ties to the
+even code, after an explicit clamp to [-448, 448]; the sign of zero is kept.
+The scale is symmetric and per tensor: v = x / s in fp32, code = E4M3(v),
+x_hat = s * decode(code).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+# --------------------------------------------------------------------------
+# Integer affine quantization
+# --------------------------------------------------------------------------
+
+
+def int_qmax(bits: int) -> int:
+    """Largest code of a b-bit unsigned code (2^b - 1)."""
+    if bits not in (2, 4, 8):
+        raise ValueError(f"unsupported bit width {bits}")
+    return (1 << bits) - 1
+
+
+def int_group_params(x: np.ndarray, bits: int, axis):
+    """Scale and zero-point of each group of ``x`` reduced over ``axis``.
+
+    ``x`` must be float32 (exact upcast of the fp16 cache input).  Returns
+    (s, z) as float32 arrays with ``axis`` removed.  Follows the affine
+    formula of "KV Cache Quantization Analysis", sec. 2, with the min/max
+    range reading stated in the module docstring.
+    """
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("int_group_params expects float32 input")
+    qmax = F32(int_qmax(bits))
+    mn = x.min(axis=axis) + F32(0.0)          # -0 -> +0
+    mx = x.max(axis=axis)
+    s = (mx - mn) / qmax                       # fp32 true division, RNE
+    s = np.where(s == F32(0.0), F32(1.0), s).astype(F32)
+    z = (-mn) / s                              # fp32, real-valued zero-point
+    return s.astype(F32), z.astype(F32)
+
+
+def int_encode(x: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int) -> np.ndarray:
+    """q = clamp(rint(x / s + z), 0, 2^b - 1) in fp32 steps; returns uint8.
+
+    ``s`` and ``z`` must broadcast against ``x``.
+    """
+    x = np.asarray(x, dtype=F32)
+    s = np.asarray(s, dtype=F32)
+    z = np.asarray(z, dtype=F32)
+    v = (x / s) + z                            # two separately rounded fp32 ops
+    q = np.rint(v)                             # round half to even
+    q = np.clip(q, F32(0.0), F32(int_qmax(bits)))
+    return q.astype(np.uint8)
+
+
+def int_decode(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """x_hat = s * (q - z), evaluated in fp64 from the stored fp32 s, z."""
+    return np.asarray(s, np.float64) * (np.asarray(q, np.float64) - np.asarray(z, np.float64))
+
+
+def quantize_k_group(kg: np.ndarray, bits: int):
+    """Key group of shape [..., G_k tokens, D]: per-channel (s, z) over tokens.
+
+    "KV Cache Quantization Analysis", sec. 3: a few fixed Key channels hold
+    large values, so each channel gets its own scale (per-channel Keys).
+    Returns codes [..., G_k, D] uint8 and s, z [..., D] float32.
+    """
+    x = np.asarray(kg, np.float16).astype(F32)
+    s, z = int_group_params(x, bits, axis=-2)
+    q = int_encode(x, s[..., None, :], z[..., None, :], bits)
+    return q, s, z
+
+
+def quantize_v_tokens(v: np.ndarray, bits: int, g_v: int):
+    """Values of shape [..., T, D]: per-token (s, z) over groups of g_v channels.
+
+    "KV Cache Quantization Analysis", sec. 3: the attention output mixes
+    Value rows, so errors are confined per token (per-token Values).
+    Returns codes [..., T, D] uint8 and s, z [..., T, D // g_v] float32.
+    """
+    x = np.asarray(v, np.float16).astype(F32)
+    d = x.shape[-1]
+    if d % g_v:
+        raise ValueError("head_dim must be a multiple of the V channel group")
+    xg = x.reshape(x.shape[:-1] + (d // g_v, g_v))
+    s, z = int_group_params(xg, bits, axis=-1)
+    q = int_encode(xg, s[..., None], z[..., None], bits)
+    return q.reshape(x.shape), s, z
+
+
+def dequantize_k_group(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`quantize_k_group` in fp64."""
+    return int_decode(q, s[..., None, :], z[..., None, :])
+
+
+def dequantize_v_tokens(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`quantize_v_tokens` in fp64."""
+    d = q.shape[-1]
+    g = s.shape[-1]
+    qg = q.reshape(q.shape[:-1] + (g, d // g))
+    return int_decode(qg, s[..., None], z[..., None]).reshape(q.shape)
+
+
+# --------------------------------------------------------------------------
+# OCP FP8 E4M3
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+E4M3_NAN_CODES = (0x7F, 0xFF)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """Value of every one of the 256 E4M3 codes (fp64; NaN for 0x7F/0xFF).
+
+    Bit layout S EEEE MMM, exponent bias 7.  E == 0 is subnormal:
+    (-1)^S * 2^-6 * M/8; otherwise (-1)^S * 2^(E-7) * (1 + M/8).  E == 15 with
+    M == 7 is NaN; there are no infinities.
+    """
+    out = np.empty(256, np.float64)
+    for c in range(256):
+        sgn = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            out[c] = np.nan
+        elif e == 0:
+            out[c] = sgn * (2.0 ** -6) * (m / 8.0)
+        else:
+            out[c] = sgn * (2.0 ** (e - 7)) * (1.0 + m / 8.0)
+    return out
+
+
+_E4M3 = e4m3_decode_table()
+_E4M3_POS = _E4M3[:0x7F]          # codes 0x00..0x7E, strictly increasing, 0 .. 448
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round finite values with |v| <= 448 to the nearest E4M3 code.
+
+    Ties go to the code with an even mantissa (even code).  The sign bit is
+    taken from the input, so -0.0 encodes to 0x80.  Values outside
+    [-448, 448] raise: callers clamp first.
+    """
+    v = np.asarray(v, np.float64)
+    if not np.all(np.isfinite(v)) or np.any(np.abs(v) > E4M3_MAX):
+        raise ValueError("e4m3_encode needs finite values within +-448")
+    a = np.abs(v)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")       # table[hi-1] < a <= table[hi]
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]                                 # exact in fp64
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == _E4M3_POS[hi], hi, code).astype(np.uint8)
+    neg = np.signbit(v)
+    return (code | np.where(neg, 0x80, 0x00)).astype(np.uint8)
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """E4M3 code -> value (fp64)."""
+    return _E4M3[np.asarray(code, np.uint8)]
+
+
+def fp8_scale(x_prefill: np.ndarray) -> np.float32:
+    """Per-tensor scale used by the tests: amax(|x|) / 448 in fp32 (1 if all 0).
+
+    Sec. 5 of the analysis page says calibrated scales improve FP8 quality;
+    the scale is a fixed input of the cache once set.  This recipe is the
+    plainest calibration: map the largest magnitude seen at prefill to 448.
+    """
+    a = F32(np.max(np.abs(np.asarray(x_prefill, np.float16).astype(F32))))
+    if a == F32(0.0):
+        return F32(1.0)
+    return F32(a / F32(E4M3_MAX))
+
+
+def fp8_encode(x: np.ndarray, s) -> np.ndarray:
+    """code = E4M3_RNE(clamp(x / s, -448, 448)), with x / s one fp32 division."""
+    v = np.asarray(x, np.float16).astype(F32) / F32(s)
+    v = np.clip(v, F32(-E4M3_MAX), F32(E4M3_MAX))
+    return e4m3_encode(v)
+
+
+def fp8_decode(code: np.ndarray, s) -> np.ndarray:
+    """x_hat = s * decode(code) in fp64."""
+    return np.float64(F32(s)) * e4m3_decode(code)

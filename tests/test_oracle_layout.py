@@ -1,0 +1,75 @@
+"""Pins of the oracle's restatement of the library's byte layout.
+
+The forward formulas below locate each code from the plain-language layout
+rules (record, word, nibble) one element at a time; the oracle builds the
+layout from a stream order.  Agreement pins the stream order.
+"""
+import numpy as np
+import pytest
+
+from oracle import layout
+
+
+def _tok(qd, j):
+    return 4 * qd + j if j < 4 else 16 + 4 * qd + (j - 4)
+
+
+@pytest.mark.parametrize("fmt,bits", [("int4", 4), ("int8", 8), ("fp8", 8), ("int2", 2)])
+def test_v_block_layout_rules(fmt, bits):
+    rng = np.random.default_rng(bits)
+    d = 128
+    codes = rng.integers(0, 1 << bits, size=(2, 32, d), dtype=np.uint8)
+    if fmt == "fp8":
+        codes = rng.integers(0, 256, size=(2, 32, d), dtype=np.uint8)
+    packed = layout.pack_v_codes(codes.reshape(64, d), fmt)          # [2 blocks][bytes]
+    assert packed.shape == (2, 32 * d * bits // 8)
+    rec = d * bits // 16
+    sigma = [0, 4, 1, 5, 2, 6, 3, 7]
+    for blk in range(2):
+        for lane in range(64):
+            qd, r = divmod(lane, 16)
+            base = lane * rec
+            for m in range(d // 16):
+                ch = 16 * m + r
+                for j in range(8):
+                    t = _tok(qd, j)
+                    c = codes[blk, t, ch]
+                    if fmt == "int4":
+                        word = int.from_bytes(packed[blk, base + 4 * m: base + 4 * m + 4].tobytes(), "little")
+                        assert (word >> (4 * j)) & 0xF == c
+                    elif bits == 8:
+                        k = sigma.index(j)
+                        assert packed[blk, base + 8 * m + k] == c
+                    else:
+                        p, tile_b = divmod(m, 2)
+                        byte = (2 if j >= 4 else 0) + tile_b
+                        jj = j % 4
+                        assert (packed[blk, base + 4 * p + byte] >> (2 * jj)) & 3 == c
+    assert np.array_equal(layout.unpack_v_codes(packed, fmt, d), codes.reshape(64, d))
+
+
+@pytest.mark.parametrize("bits,fmt", [(2, "int2"), (4, "int4"), (8, "int8")])
+def test_k_codes_are_lsb_first_token_major(bits, fmt):
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 1 << bits, size=(3, 5, 128), dtype=np.uint8)
+    packed = layout.pack_k_codes(codes, fmt)
+    assert packed.shape == (3, 5, 128 * bits // 8)
+    for c in range(128):
+        byte, bit = divmod(c * bits, 8)
+        assert np.array_equal((packed[..., byte] >> bit) & ((1 << bits) - 1), codes[..., c])
+    assert np.array_equal(layout.unpack_k_codes(packed, fmt, 128), codes)
+
+
+def test_meta_layouts():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((2, 3, 128)).astype(np.float32)
+    z = rng.standard_normal((2, 3, 128)).astype(np.float32)
+    m = layout.pack_k_meta(s, z)
+    assert m.shape == (2, 3, 2, 128) and np.array_equal(m[:, :, 1], z)
+    sv = rng.standard_normal((2, 64, 4)).astype(np.float32)
+    zv = rng.standard_normal((2, 64, 4)).astype(np.float32)
+    mv = layout.pack_v_meta(sv, zv)
+    assert mv.shape == (2, 2, 2, 4, 32)
+    assert mv[1, 1, 0, 3, 7] == sv[1, 32 + 7, 3] and mv[0, 0, 1, 2, 31] == zv[0, 31, 2]
+    s2, z2 = layout.unpack_v_meta(mv)
+    assert np.array_equal(s2, sv) and np.array_equal(z2, zv)
