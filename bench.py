@@ -1,0 +1,267 @@
+"""Decode-step benchmark of the quantized KV cache on one MI355X.
+
+One step = for every layer of the model: append one new token's K / V to
+that layer's packed cache (quantize-on-append) and run fused-dequant decode
+attention for all query heads (split-K kernel + reduce).  Inputs are
+synthetic and already resident in HBM when the timed region starts.  Each
+layer owns its own cache buffer, so the timed loop streams every layer's
+packed cache from HBM (one layer's cache is larger than the 256 MB
+last-level cache, and the 32 layers together are ~10 GB).
+
+Default workload: the Llama-3-8B layer shape (32 query / 8 KV heads,
+head_dim 128) at batch 16 and 8192 cached tokens, 32 layers, with the cache
+quantized to INT8 (headline) and to FP8 E4M3.  The single JSON line on
+stdout carries the INT8 numbers as "value" and the FP8 numbers under "fp8".
+
+Reported: effective KV GB/s = algorithmic attention bytes of the timed steps
+/ their wall time (appends included), tokens/s = batch / step time, and a
+roofline entry for the decode-attention call measured with HIP events on
+the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attention effective KV GB/s (% of HBM peak) + tokens/s, batch16 seq8192"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "llama3_8b_kivi2", "llama3_70b", "long_ctx"])
+    ap.add_argument("--formats", default=None, help="comma list overriding the workload's formats")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count")
+    ap.add_argument("--blocks-per-wave", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def copy_bandwidth(torch) -> float:
+    """GB/s of a plain device-to-device copy of 2 GiB (read + write bytes)."""
+    n = 2 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del x, y
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
+    """Time the decode step with the given per-layer formats; returns a result dict."""
+    layers = len(fmt_list)
+    b, hkv, hq, d, n0 = w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.seq_len
+    total_steps = args.warmup + args.steps
+    max_tokens = n0 + total_steps + 32
+    log(f"generating synthetic prefill ({b}x{n0}x{hkv}x{d} fp16 K/V)")
+    kp, vp = synth.prefill(w)
+    kd = torch.from_numpy(kp).cuda()
+    vd = torch.from_numpy(vp).cuda()
+    del kp, vp
+    # FP8 calibration: amax / 448 of the prefill, per tensor (a caller input)
+    k_scale = float(kd.abs().max().float().item()) / 448.0
+    v_scale = float(vd.abs().max().float().item()) / 448.0
+    caches = []
+    for li, fmt in enumerate(fmt_list):
+        lay = kvq.make_layout(b, hkv, hq, d, max_tokens, fmt, residual_tokens=w.residual_tokens,
+                              sink_tokens=w.sink_tokens, k_scale=np.float32(k_scale), v_scale=np.float32(v_scale))
+        c = kvq.Cache.create(lay)
+        c.append(kd, vd)
+        caches.append(c)
+    torch.cuda.synchronize()
+    del kd, vd
+    log(f"{layers} layer caches prefilled ({sum(c.buf.numel() for c in caches) / 2**30:.2f} GiB)")
+    steps_k, steps_v = [], []
+    for j in range(total_steps):
+        ks, vs = synth.append_step(w, j)
+        steps_k.append(torch.from_numpy(ks).cuda())
+        steps_v.append(torch.from_numpy(vs).cuda())
+    q = torch.from_numpy(synth.queries(w)).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty(max(c.workspace_bytes(args.blocks_per_wave) for c in caches) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+
+    def step(j, ev=None):
+        for li, c in enumerate(caches):
+            c.append(steps_k[j], steps_v[j])
+            if ev is not None:
+                ev[li][0].record()
+            c.attention(q, out, ws, args.blocks_per_wave)
+            if ev is not None:
+                ev[li][1].record()
+
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
+           for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    attn_ms = [evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps) for li in range(layers)]
+    nbytes = 0
+    for s in range(args.steps):
+        n = n0 + args.warmup + s + 1
+        for fmt in fmt_list:
+            nbytes += accounting.attention_bytes(b, hkv, hq, d, n, fmt, w.sink_tokens, w.residual_tokens)
+    per_call_bytes = nbytes / (args.steps * layers)
+    ms_step = total_ms / args.steps
+    attn_avg_ms = float(np.mean(attn_ms))
+    res = {
+        "formats": sorted(set(fmt_list)),
+        "layers": layers,
+        "ms_per_step": ms_step,
+        "effective_gbps": nbytes / (total_ms * 1e-3) / 1e9,
+        "tokens_per_s": b / (ms_step * 1e-3),
+        "attn_call_us": attn_avg_ms * 1e3,
+        "attn_gbps": per_call_bytes / (attn_avg_ms * 1e-3) / 1e9,
+        "append_us_per_layer": (ms_step - attn_avg_ms * layers) * 1e3 / layers,
+        "bytes_per_attn_call": per_call_bytes,
+    }
+    res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
+    log(f"{'/'.join(res['formats'])}: {ms_step:.3f} ms/step, {res['tokens_per_s']:.0f} tok/s, "
+        f"effective {res['effective_gbps']:.0f} GB/s, attention call {res['attn_call_us']:.1f} us "
+        f"= {res['attn_gbps']:.0f} GB/s")
+    del caches, steps_k, steps_v, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, fmt, seconds):
+    """The CPU oracle's decode attention on a time-bounded sample of (sequence, KV head) pairs."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    from oracle import nbytes as obytes
+    from quantized_kv_cache_quant_amd import synth
+
+    nrep = w.num_q_heads // w.num_kv_heads
+    n = w.seq_len + 1
+    k, v = synth.kv_tokens(w, 1000 + w.index, 2000 + w.index, 1, n, 1, w.head_dim)
+    q = synth.queries(w, 1, nrep, w.head_dim)
+    from oracle import quant
+    lay = ocache.Layout(1, 1, nrep, w.head_dim, n, fmt, residual_tokens=w.residual_tokens,
+                        sink_tokens=w.sink_tokens, k_scale=float(quant.fp8_scale(k)),
+                        v_scale=float(quant.fp8_scale(v)))
+    st = ocache.build_cache(k, v, lay)           # set-up, not timed
+    per_head = obytes.step_bytes(lay, n)["total"]
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            kh, vh = ocache.dequantize(st)
+            oattn.attention(q, kh, vh)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": per_head * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} x one (sequence, KV head) decode step of {fmt} ({n} tokens, {nrep} query heads): "
+                      f"fp64 dequantize + attention, {dt:.1f} s, single thread",
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              "(the decode-attention path shards by KV head / token range without exchange, "
+              "see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from quantized_kv_cache_quant_amd import accounting, kvq, synth
+    kvq.lib()
+    w = synth.WORKLOADS[args.workload]
+    if args.formats:
+        variants = [f.strip() for f in args.formats.split(",")]
+    elif args.workload == "long_ctx":
+        variants = ["mixed"]
+    else:
+        variants = list(w.formats)
+    if args.workload == "llama3_8b" and not args.formats:
+        variants = ["int8", "fp8"]                   # INT8 is the headline line
+    nl = args.layers or w.layers
+    results = {}
+    for var in variants:
+        if var == "mixed":
+            fl = list(w.formats)[:nl] if nl <= len(w.formats) else (list(w.formats) * nl)[:nl]
+        else:
+            fl = [var] * nl
+        results[var] = run_format(torch, kvq, synth, accounting, w, fl, args)
+    copy_gbps = copy_bandwidth(torch)
+    log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
+    head = results[variants[0]]
+    line = {
+        "metric": METRIC,
+        "value": round(head["effective_gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{variants[0]} KV codes, f16 MFMA operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.notes}", "batch": w.batch, "seq_len": w.seq_len,
+                   "layers": head["layers"], "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "residual_tokens": w.residual_tokens,
+                   "sink_tokens": w.sink_tokens, "kv_format": variants[0]},
+        "tokens_per_s": round(head["tokens_per_s"], 1),
+        "pct_of_hbm_peak": round(head["pct_of_hbm_peak"], 2),
+        "attn_call_us": round(head["attn_call_us"], 2),
+        "append_us_per_layer": round(head["append_us_per_layer"], 2),
+        "copy_gbps_measured": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(head["attn_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "attn_kernel + reduce_kernel (one kv_decode_attention call)",
+                     "bytes_per_launch": head["bytes_per_attn_call"]},
+    }
+    for var in variants[1:]:
+        r = results[var]
+        line[var] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+    if not args.no_cpu_baseline:
+        fmt0 = variants[0] if variants[0] != "mixed" else "int4"
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(w, fmt0, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * kvq.h -- quantized KV cache for MI355X (gfx950): C ABI.
+ *
+ * Two hot calls, as the method describes its integration ("KV Cache
+ * Quantization Analysis", sec. 5, system integration): quantize the new
+ * token's K and V right after they are produced and store them
+ * (kv_quant_append), and dequantize inside attention (kv_decode_attention).
+ * Everything else here is sizing, validation and set-up.
+ *
+ * Conventions (every entry point):
+ *  - Return value: KVQ_OK (0) or a negative kvq_status.  No exceptions, no
+ *    aborts, no device allocation, no host<->device synchronisation.
+ *  - Memory: the caller owns every buffer.  Device pointers are plain HIP
+ *    device addresses; "stream" is a hipStream_t passed as void* (NULL =
+ *    the default stream).  All device work is enqueued on that stream.
+ *  - Validation happens on the host before anything is enqueued.  A call
+ *    that returns a validation error (NULL, LAYOUT, UNSUPPORTED, CAPACITY,
+ *    ALIGN, WORKSPACE, EMPTY) has changed nothing.  KVQ_ERR_HIP means a
+ *    kernel launch failed; the cache contents are then undefined.
+ *  - A cache must not be used from two streams at once; the host struct is
+ *    not thread-safe.
+ *  - Inputs must be finite (no NaN / Inf); this is not checked.
+ *
+ * Cache layout (one cache per layer; all sequences of the batch hold the
+ * same number of tokens n).  Readings of the pages, fixed here:
+ *  - the first S tokens are attention sinks kept in fp16 ("W4A16 + KV cache
+ *    quantization: combined accuracy", layer-sensitivity section);
+ *  - the other tokens ("body", index u = t - S) are quantized 32 at a time,
+ *    keeping at least R recent body tokens in fp16 ("KV Cache Quantization
+ *    Analysis", sec. 3, full-precision recent window): after n tokens,
+ *    n_q = 32 * floor(max(0, n - S - R) / 32) body tokens are quantized and
+ *    r = n - S - n_q stay in an fp16 ring of R + 32 slots (token u in slot
+ *    u mod (R + 32));
+ *  - INT formats: Keys per channel over each block of 32 tokens, Values per
+ *    token over groups of 32 channels (same page, sec. 3 and sec. 4, KIVI);
+ *    q = clamp(rint(x / s + z), 0, 2^b - 1), s = (max - min) / (2^b - 1)
+ *    (s = 1 for a constant group), z = -min / s, each a single fp32 IEEE
+ *    operation (same page, sec. 2, affine quantization);
+ *  - FP8: OCP E4M3 (max 448) of clamp(x / s, -448, 448) with one fp32 scale
+ *    for K and one for V per layer (same page, sec. 4, FP8 / INT8).
+ *
+ * Planes inside the caller's device buffer (offsets from kvq_cache_plane;
+ * NB = max(0, max_tokens - S - R) / 32 blocks, D = head_dim, b = bits):
+ *   K codes  [B][Hkv][NB*32][D*b/8] token-major; channel c at bit (c*b mod 8)
+ *            of byte floor(c*b/8).  FP8: one E4M3 byte per channel.
+ *   V codes  [B][Hkv][NB][32*D*b/8] per 32-token block: 64 records of
+ *            D*b/16 bytes.  Record l = 16*qd + r holds channels 16*m + r
+ *            (m = 0 .. D/16-1) of the tokens T = (4qd .. 4qd+3,
+ *            16+4qd .. 16+4qd+3):
+ *              INT4       word m, nibble j = code(T[j], 16m + r)
+ *              INT8, FP8  bytes 8m..8m+7 = T[0],T[4],T[1],T[5],T[2],T[6],T[3],T[7]
+ *              INT2       word p: byte 0 / 1 = channel 32p + r / 32p + 16 + r
+ *                         of T[0..3], byte 2 / 3 = the same channels of T[4..7]
+ *            (the order in which the attention kernel's matrix-core operands
+ *            are loaded).
+ *   K meta   [B][Hkv][NB][2][D] fp32: s then z per channel (INT only)
+ *   V meta   [B][Hkv][NB][2][D/32][32] fp32: s then z, [group][token] (INT)
+ *   K ring, V ring  [B][Hkv][R+32][D] fp16
+ *   K sink, V sink  [B][Hkv][S][D] fp16
+ * Each plane starts on a 256-byte boundary.
+ *
+ * Limits of this version (KVQ_ERR_UNSUPPORTED otherwise): head_dim == 128,
+ * k_group_tokens == 32, v_group_channels == 32, num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,         /* a required pointer is NULL */
+  KVQ_ERR_LAYOUT = -2,       /* inconsistent sizes (e.g. Hq % Hkv != 0, T < 0) */
+  KVQ_ERR_UNSUPPORTED = -3,  /* valid but not implemented (see limits above) */
+  KVQ_ERR_CAPACITY = -4,     /* append past max_tokens, or buffer too small */
+  KVQ_ERR_ALIGN = -5,        /* buffer not aligned (base: 256 B, tensors: 16 B) */
+  KVQ_ERR_WORKSPACE = -6,    /* workspace NULL or smaller than required */
+  KVQ_ERR_HIP = -7,          /* a kernel launch failed */
+  KVQ_ERR_EMPTY = -8         /* attention over an empty cache */
+} kvq_status;
+
+typedef enum { KVQ_INT8 = 0, KVQ_INT4 = 1, KVQ_INT2 = 2, KVQ_FP8_E4M3 = 3 } kvq_format;
+
+/* One layer's cache geometry.  Per-layer formats (e.g. INT8 on the first and
+ * last layers, INT4 in between) use one layout and one cache per layer. */
+typedef struct {
+  int32_t batch;             /* B >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t num_q_heads;       /* Hq, a multiple of Hkv (GQA: q head h reads KV head h / (Hq/Hkv)) */
+  int32_t head_dim;          /* D (128) */
+  int32_t max_tokens;        /* capacity in tokens per sequence */
+  int32_t format;            /* kvq_format */
+  int32_t k_group_tokens;    /* tokens per Key scale group (32) */
+  int32_t v_group_channels;  /* channels per Value scale group (32) */
+  int32_t residual_tokens;   /* R >= 0: recent body tokens always kept in fp16 */
+  int32_t sink_tokens;       /* S >= 0: first tokens always kept in fp16 */
+  float k_scale;             /* FP8 only: Key scale, finite and > 0 */
+  float v_scale;             /* FP8 only: Value scale, finite and > 0 */
+} kvq_layout;
+
+enum {
+  KVQ_PLANE_K_CODES = 0, KVQ_PLANE_V_CODES, KVQ_PLANE_K_META, KVQ_PLANE_V_META,
+  KVQ_PLANE_K_RING, KVQ_PLANE_V_RING, KVQ_PLANE_K_SINK, KVQ_PLANE_V_SINK,
+  KVQ_NUM_PLANES
+};
+
+/* Host-side handle of one cache.  Plain data owned by the caller; filled by
+ * kvq_cache_init; n_tokens is advanced by kv_quant_append only after its
+ * kernels were enqueued successfully.  Copying the struct together with the
+ * device buffer's bytes saves and restores the cache. */
+typedef struct {
+  kvq_layout layout;
+  void* base;                          /* device buffer */
+  uint64_t bytes;                      /* its size */
+  int64_t n_tokens;                    /* tokens per sequence currently cached */
+  int32_t n_blocks_cap;                /* NB */
+  int32_t ring_slots;                  /* R + 32 */
+  uint64_t plane_off[KVQ_NUM_PLANES];  /* byte offsets from base */
+  uint64_t plane_bytes[KVQ_NUM_PLANES];
+} kvq_cache;
+
+/* Static string naming a status code. */
+const char* kvq_status_string(int32_t status);
+
+/* Check a layout.  Returns KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_LAYOUT or
+ * KVQ_ERR_UNSUPPORTED. */
+int32_t kvq_layout_validate(const kvq_layout* layout);
+
+/* Device bytes needed for one cache with this layout (*bytes, host memory). */
+int32_t kvq_cache_bytes(const kvq_layout* layout, uint64_t* bytes);
+
+/* Bind a caller-allocated device buffer (256-B aligned, >= kvq_cache_bytes)
+ * to *cache and set it empty (n_tokens = 0).  Enqueues nothing: plane
+ * contents are undefined until written by kv_quant_append. */
+int32_t kvq_cache_init(kvq_cache* cache, const kvq_layout* layout, void* dev_base, uint64_t bytes);
+
+/* Byte offset and size of one plane (KVQ_PLANE_*) inside the buffer. */
+int32_t kvq_cache_plane(const kvq_cache* cache, int32_t plane, uint64_t* offset, uint64_t* bytes);
+
+/* Current routing: sinks held, quantized body tokens, fp16 residual tokens. */
+int32_t kvq_cache_window(const kvq_cache* cache, int64_t* n_sink, int64_t* n_q, int64_t* n_residual);
+
+/* Quantize-on-append ("KV Cache Quantization Analysis", sec. 5: quantize
+ * the new K, V right after they are computed, then store).
+ * K, V: device fp16 [B][T][Hkv][D], contiguous, 16-B aligned, read only.
+ * Appends T >= 0 tokens to every sequence: sinks and residual tokens are
+ * copied to their fp16 planes; every block of 32 body tokens that leaves the
+ * residual window is quantized (from the ring or directly from K, V) and its
+ * codes and scale/zero planes written.  Errors: KVQ_ERR_CAPACITY if
+ * n_tokens + T > max_tokens (nothing enqueued). */
+int32_t kv_quant_append(kvq_cache* cache, const void* K, const void* V, int32_t T, void* stream);
+
+/* Workspace bytes kv_decode_attention_split needs for any n_tokens up to
+ * max_tokens with the given blocks_per_wave (0 = the library's choice, which
+ * needs no more than blocks_per_wave = 1). */
+int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_wave, uint64_t* bytes);
+
+/* Fused-dequant decode attention ("KV Cache Quantization Analysis", sec. 4
+ * and sec. 5: dequantization fused into the attention matmuls; "W4A16 + KV
+ * cache quantization: combined accuracy", softmax(Q K^T / sqrt(d)) with GQA).
+ * q: device fp16 [B][Hq][D]; out: device fp16 [B][Hq][D]; both 16-B aligned.
+ * For every sequence b and query head h:
+ *   out[b][h] = sum_t softmax_t(q[b][h] . k_hat[b][g][t] / sqrt(D)) v_hat[b][g][t]
+ * over all n_tokens cached tokens, g = h / (Hq/Hkv), with k_hat, v_hat the
+ * dequantized (or fp16) cache entries.  Split-K: a first kernel writes one
+ * partial (max, sum, unnormalised output) per token range into ws, a second
+ * combines them.  ws: device scratch of >= kvq_workspace_bytes(cache, 0)
+ * bytes, overwritten.  Errors: KVQ_ERR_EMPTY if n_tokens == 0. */
+int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
+                            uint64_t ws_bytes, void* stream);
+
+/* kv_decode_attention with an explicit token range per split:
+ * blocks_per_wave in [1, 16] blocks of 32 quantized tokens per wavefront
+ * (four wavefronts per split).  Results agree with every other choice up to
+ * fp32 rounding.  0 selects the library's choice. */
+int32_t kv_decode_attention_split(const kvq_cache* cache, const void* q, void* out, void* ws,
+                                  uint64_t ws_bytes, int32_t blocks_per_wave, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,273 @@
+// Quantize-on-append kernels for gfx950.
+//
+// "KV Cache Quantization Analysis", sec. 5 (system integration): the new
+// token's K and V are quantized right after they are computed and stored in
+// the cache.  Sec. 3 / sec. 4 (KIVI): Keys per channel, Values per token,
+// the most recent tokens kept in full precision.  Sec. 2: affine
+// quantization q = round(x / s + z), x_hat = s * (q - z).  Sec. 4 (FP8 /
+// INT8): OCP E4M3 with an fp32 scale.
+//
+// Two kernels, enqueued in this order on one stream:
+//  flush_kernel  one workgroup per (32-token block leaving the residual
+//                window, KV head, sequence): gathers the block's fp16 K / V
+//                from the ring or the new input, computes the per-channel K
+//                and per-token V scale / zero-point, encodes and writes the
+//                packed codes in the documented plane layouts.
+//  copy_kernel   copies new sink tokens and new residual tokens into their
+//                fp16 planes (ring slot u mod (R + 32)).  It runs after the
+//                flush because it may overwrite ring slots the flush read.
+//
+// Bit-exactness: every quantization step is one IEEE fp32 operation in the
+// order of the formula (true division, no contraction: this file is built
+// with -ffp-contract=off and correctly rounded fp32 division), rint is
+// round-half-even, exactly like the CPU oracle.
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t encode_int(float x, float s, float z) {
+  constexpr float kQmax = (float)((1 << BITS) - 1);
+  float v = x / s;
+  v = v + z;
+  v = __builtin_rintf(v);
+  v = fminf(fmaxf(v, 0.0f), kQmax);
+  return (uint32_t)v;
+}
+
+// Two fp32 values -> two OCP E4M3 bytes (low 16 bits of the result), after
+// the explicit clamp to +-448; the hardware conversion rounds to nearest even.
+__device__ __forceinline__ uint32_t encode_fp8_pair(float a, float b, float s) {
+  float va = fminf(fmaxf(a / s, -448.0f), 448.0f);
+  float vb = fminf(fmaxf(b / s, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
+}
+
+// Token index (0..31 inside a block) of slot j (0..7) of V record quarter qd.
+__device__ __forceinline__ int record_token(int qd, int j) {
+  return (j < 4) ? (4 * qd + j) : (16 + 4 * qd + (j - 4));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
+  constexpr bool kFp8 = FMT == KVQ_FP8_E4M3;
+  constexpr int kBits = FMT == KVQ_INT4 ? 4 : (FMT == KVQ_INT2 ? 2 : 8);
+  constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
+  constexpr float kQmax = (float)((1 << kBits) - 1);
+
+  __shared__ float ks[kBlock][kHeadDim + 1];
+  __shared__ float vs[kBlock][kHeadDim + 1];
+  __shared__ float sk[kHeadDim], zk[kHeadDim];
+  __shared__ float sv[kBlock][kVGroups], zv[kBlock][kVGroups];
+
+  const int tid = threadIdx.x;
+  const int64_t blk = (int64_t)p.first_block + blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t bh = (int64_t)b * p.hkv + h;
+
+  // 1) gather the block's 32 tokens (16-byte chunks, 16 per token row)
+  for (int e = tid; e < kBlock * 16; e += 256) {
+    const int t = e >> 4;
+    const int c8 = (e & 15) * 8;
+    const int64_t u = blk * kBlock + t;               // body index
+    const uint16_t* ksrc;
+    const uint16_t* vsrc;
+    if (u < p.n_body_old) {                           // still in the residual ring
+      const int64_t off = (bh * p.ring_slots + (u % p.ring_slots)) * kHeadDim + c8;
+      ksrc = p.k_ring + off;
+      vsrc = p.v_ring + off;
+    } else {                                          // arrives with this append
+      const int64_t i = u + p.sink - p.n_old;
+      const int64_t off = (((int64_t)b * p.T + i) * p.hkv + h) * kHeadDim + c8;
+      ksrc = p.k_in + off;
+      vsrc = p.v_in + off;
+    }
+    const uint4 kk = *reinterpret_cast<const uint4*>(ksrc);
+    const uint4 vv = *reinterpret_cast<const uint4*>(vsrc);
+    const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ks[t][c8 + 2 * j] = half_bits_to_float(kw[j] & 0xFFFFu);
+      ks[t][c8 + 2 * j + 1] = half_bits_to_float(kw[j] >> 16);
+      vs[t][c8 + 2 * j] = half_bits_to_float(vw[j] & 0xFFFFu);
+      vs[t][c8 + 2 * j + 1] = half_bits_to_float(vw[j] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // 2) scale / zero-point: K per channel over the 32 tokens, V per token
+  //    over each group of 32 channels
+  if constexpr (!kFp8) {
+    if (tid < kHeadDim) {
+      const int c = tid;
+      float mn = ks[0][c], mx = ks[0][c];
+      for (int t = 1; t < kBlock; ++t) {
+        mn = fminf(mn, ks[t][c]);
+        mx = fmaxf(mx, ks[t][c]);
+      }
+      mn = mn + 0.0f;                                 // a zero minimum is +0
+      float s = (mx - mn) / kQmax;
+      if (s == 0.0f) s = 1.0f;
+      const float z = (-mn) / s;
+      sk[c] = s;
+      zk[c] = z;
+      float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);
+      km[c] = s;
+      km[kHeadDim + c] = z;
+    } else {
+      const int e = tid - kHeadDim;
+      const int t = e >> 2, g = e & 3;
+      float mn = vs[t][kVGroup * g], mx = mn;
+      for (int c = 1; c < kVGroup; ++c) {
+        mn = fminf(mn, vs[t][kVGroup * g + c]);
+        mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+      }
+      mn = mn + 0.0f;
+      float s = (mx - mn) / kQmax;
+      if (s == 0.0f) s = 1.0f;
+      const float z = (-mn) / s;
+      sv[t][g] = s;
+      zv[t][g] = z;
+      float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);
+      vm[g * kBlock + t] = s;
+      vm[kVGroups * kBlock + g * kBlock + t] = z;
+    }
+    __syncthreads();
+  }
+
+  // 3) K codes: token-major rows, channel c at bit (c * bits) (LSB first)
+  {
+    constexpr int kWordsPerRow = kRowBytes / 4;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
+    for (int w = tid; w < kBlock * kWordsPerRow; w += 256) {
+      const int t = w / kWordsPerRow;
+      const int wi = w % kWordsPerRow;
+      uint32_t word = 0;
+      if constexpr (kFp8) {
+        const int c = wi * 4;
+        word = encode_fp8_pair(ks[t][c], ks[t][c + 1], p.k_scale) |
+               (encode_fp8_pair(ks[t][c + 2], ks[t][c + 3], p.k_scale) << 16);
+      } else {
+        constexpr int kPer = 32 / kBits;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int c = wi * kPer + j;
+          word |= encode_int<kBits>(ks[t][c], sk[c], zk[c]) << (j * kBits);
+        }
+      }
+      dst[w] = word;
+    }
+  }
+
+  // 4) V codes: 64 records per block in the attention kernel's operand order
+  {
+    constexpr int kRecWords = kHeadDim * kBits / 16 / 4;   // words per record
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
+    for (int w = tid; w < 64 * kRecWords; w += 256) {
+      const int lane = w / kRecWords;
+      const int wi = w % kRecWords;
+      const int qd = lane >> 4, r = lane & 15;
+      uint32_t word = 0;
+      if constexpr (kBits == 4) {                 // word m: nibble j = T[j], channel 16m + r
+        const int ch = 16 * wi + r;
+        const int g = ch / kVGroup;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = record_token(qd, j);
+          word |= encode_int<4>(vs[t][ch], sv[t][g], zv[t][g]) << (4 * j);
+        }
+      } else if constexpr (kBits == 8) {          // bytes 8m..8m+7 = T0 T4 T1 T5 T2 T6 T3 T7
+        const int ch = 16 * (wi >> 1) + r;
+        const int g = ch / kVGroup;
+        // slot k of the 8 bytes holds record token (k >> 1) + 4 * (k & 1)
+        const int base = 4 * (wi & 1);
+        auto sel = [](int k) { return (k >> 1) + 4 * (k & 1); };
+        if constexpr (kFp8) {
+          const float x0 = vs[record_token(qd, sel(base + 0))][ch];
+          const float x1 = vs[record_token(qd, sel(base + 1))][ch];
+          const float x2 = vs[record_token(qd, sel(base + 2))][ch];
+          const float x3 = vs[record_token(qd, sel(base + 3))][ch];
+          word = encode_fp8_pair(x0, x1, p.v_scale) | (encode_fp8_pair(x2, x3, p.v_scale) << 16);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int t = record_token(qd, sel(base + k));
+            word |= encode_int<8>(vs[t][ch], sv[t][g], zv[t][g]) << (8 * k);
+          }
+        }
+      } else {                                    // INT2 word p: A = 32p + r, B = 32p + 16 + r
+        const int cha = 32 * wi + r, chb = cha + 16;
+        const int ga = cha / kVGroup, gb = chb / kVGroup;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t0 = record_token(qd, j), t1 = record_token(qd, 4 + j);
+          word |= encode_int<2>(vs[t0][cha], sv[t0][ga], zv[t0][ga]) << (2 * j);
+          word |= encode_int<2>(vs[t0][chb], sv[t0][gb], zv[t0][gb]) << (8 + 2 * j);
+          word |= encode_int<2>(vs[t1][cha], sv[t1][ga], zv[t1][ga]) << (16 + 2 * j);
+          word |= encode_int<2>(vs[t1][chb], sv[t1][gb], zv[t1][gb]) << (24 + 2 * j);
+        }
+      }
+      dst[w] = word;
+    }
+  }
+}
+
+// One thread per 16-byte chunk of one token row of K or V.
+__global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t total = (int64_t)p.T * p.hkv * 2 * 16;
+  if (e >= total) return;
+  const int chunk = (int)(e & 15);
+  int64_t rest = e >> 4;
+  const int kv = (int)(rest & 1);
+  rest >>= 1;
+  const int h = (int)(rest % p.hkv);
+  const int64_t i = rest / p.hkv;                  // input token
+  const int64_t t = p.n_old + i;                   // absolute token
+  uint16_t* dst;
+  if (t < p.sink) {
+    uint16_t* plane = kv ? p.v_sink : p.k_sink;
+    dst = plane + (((int64_t)b * p.hkv + h) * p.sink + t) * kHeadDim + chunk * 8;
+  } else {
+    const int64_t u = t - p.sink;
+    if (u < p.n_q_new) return;                     // quantized straight from the input
+    uint16_t* plane = kv ? p.v_ring : p.k_ring;
+    dst = plane + (((int64_t)b * p.hkv + h) * p.ring_slots + (u % p.ring_slots)) * kHeadDim + chunk * 8;
+  }
+  const uint16_t* src = (kv ? p.v_in : p.k_in) + (((int64_t)b * p.T + i) * p.hkv + h) * kHeadDim + chunk * 8;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
+}  // namespace
+
+hipError_t launch_flush(int fmt, const FlushParams& p, int n_blocks, int batch, hipStream_t s) {
+  const dim3 grid(n_blocks, p.hkv, batch), block(256);
+  switch (fmt) {
+    case KVQ_INT8: hipLaunchKernelGGL(flush_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
+    case KVQ_INT4: hipLaunchKernelGGL(flush_kernel<KVQ_INT4>, grid, block, 0, s, p); break;
+    case KVQ_INT2: hipLaunchKernelGGL(flush_kernel<KVQ_INT2>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E4M3: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E4M3>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s) {
+  const int64_t total = (int64_t)p.T * p.hkv * 2 * 16;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks, batch), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

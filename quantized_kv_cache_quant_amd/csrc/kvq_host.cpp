@@ -1,0 +1,309 @@
+// Host side of the C ABI in include/kvq.h: layout validation, byte sizing,
+// plane placement, token routing and launch configuration.  Nothing here
+// touches device memory; kernels are enqueued on the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr uint64_t kPlaneAlign = 256;
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Window {
+  int64_t n_sink, n_q, r;
+};
+
+// Routing after n tokens: S sinks, n_q quantized body tokens (a multiple of
+// 32, leaving at least R body tokens in fp16), r residual tokens.
+Window window(const kvq_layout& L, int64_t n) {
+  Window w;
+  w.n_sink = n < L.sink_tokens ? n : L.sink_tokens;
+  int64_t body = n - w.n_sink;
+  int64_t over = body - L.residual_tokens;
+  w.n_q = over > 0 ? (over / kBlock) * kBlock : 0;
+  w.r = body - w.n_q;
+  return w;
+}
+
+int32_t nb_cap(const kvq_layout& L) {
+  int64_t over = (int64_t)L.max_tokens - L.sink_tokens - L.residual_tokens;
+  return over > 0 ? (int32_t)(over / kBlock) : 0;
+}
+
+// Plane sizes in bytes for a validated layout.
+void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
+  const uint64_t bh = (uint64_t)L.batch * L.num_kv_heads;
+  const uint64_t nb = (uint64_t)nb_cap(L);
+  const uint64_t bits = (uint64_t)format_bits(L.format);
+  const uint64_t d = (uint64_t)L.head_dim;
+  const bool fp8 = L.format == KVQ_FP8_E4M3;
+  sz[KVQ_PLANE_K_CODES] = bh * nb * kBlock * d * bits / 8;
+  sz[KVQ_PLANE_V_CODES] = sz[KVQ_PLANE_K_CODES];
+  sz[KVQ_PLANE_K_META] = fp8 ? 0 : bh * nb * 2 * d * sizeof(float);
+  sz[KVQ_PLANE_V_META] = fp8 ? 0 : bh * nb * 2 * (d / L.v_group_channels) * kBlock * sizeof(float);
+  sz[KVQ_PLANE_K_RING] = bh * (uint64_t)(L.residual_tokens + kBlock) * d * 2;
+  sz[KVQ_PLANE_V_RING] = sz[KVQ_PLANE_K_RING];
+  sz[KVQ_PLANE_K_SINK] = bh * (uint64_t)L.sink_tokens * d * 2;
+  sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
+}
+
+int32_t choose_blocks_per_wave(const kvq_cache& c, int64_t nblk) {
+  // Aim for about 2048 body workgroups (8 per CU on 256 CUs): enough to fill
+  // the chip several times over while keeping the split-K partials small.
+  const int64_t total = (int64_t)c.layout.batch * c.layout.num_kv_heads * nblk;
+  int64_t bpw = (total + (int64_t)kWavesPerSplit * 2048 - 1) / ((int64_t)kWavesPerSplit * 2048);
+  if (bpw < 1) bpw = 1;
+  if (bpw > 16) bpw = 16;
+  return (int32_t)bpw;
+}
+
+int32_t body_splits(int64_t nblk, int32_t bpw) {
+  const int64_t per = (int64_t)bpw * kWavesPerSplit;
+  return (int32_t)((nblk + per - 1) / per);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int32_t s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_NULL: return "KVQ_ERR_NULL: a required pointer is NULL";
+    case KVQ_ERR_LAYOUT: return "KVQ_ERR_LAYOUT: inconsistent sizes";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: valid but not implemented";
+    case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY: capacity exceeded or buffer too small";
+    case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN: misaligned buffer";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: workspace missing or too small";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: kernel launch failed";
+    case KVQ_ERR_EMPTY: return "KVQ_ERR_EMPTY: attention over an empty cache";
+    default: return "unknown kvq status";
+  }
+}
+
+int32_t kvq_layout_validate(const kvq_layout* L) {
+  if (!L) return KVQ_ERR_NULL;
+  if (L->batch < 1 || L->num_kv_heads < 1 || L->num_q_heads < 1 || L->head_dim < 1 ||
+      L->max_tokens < 1 || L->residual_tokens < 0 || L->sink_tokens < 0 ||
+      L->k_group_tokens < 1 || L->v_group_channels < 1)
+    return KVQ_ERR_LAYOUT;
+  if (L->num_q_heads % L->num_kv_heads) return KVQ_ERR_LAYOUT;
+  if (L->head_dim % L->v_group_channels) return KVQ_ERR_LAYOUT;
+  if (L->format < KVQ_INT8 || L->format > KVQ_FP8_E4M3) return KVQ_ERR_LAYOUT;
+  if (L->format == KVQ_FP8_E4M3) {
+    if (!std::isfinite(L->k_scale) || !std::isfinite(L->v_scale) || !(L->k_scale > 0.f) ||
+        !(L->v_scale > 0.f))
+      return KVQ_ERR_LAYOUT;
+  }
+  if (L->sink_tokens > L->max_tokens) return KVQ_ERR_LAYOUT;
+  if (L->head_dim != kHeadDim || L->k_group_tokens != kBlock || L->v_group_channels != kVGroup)
+    return KVQ_ERR_UNSUPPORTED;
+  const int nrep = L->num_q_heads / L->num_kv_heads;
+  if (nrep != 1 && nrep != 2 && nrep != 4 && nrep != 8) return KVQ_ERR_UNSUPPORTED;
+  // grid.y = Hkv and grid.z = B must fit the launch limits
+  if (L->num_kv_heads > 65535 || L->batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)L->residual_tokens + kBlock > (int64_t)1 << 30) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int32_t kvq_cache_bytes(const kvq_layout* L, uint64_t* bytes) {
+  if (!L || !bytes) return KVQ_ERR_NULL;
+  int32_t st = kvq_layout_validate(L);
+  if (st != KVQ_OK) return st;
+  uint64_t sz[KVQ_NUM_PLANES];
+  plane_sizes(*L, sz);
+  uint64_t total = 0;
+  for (int i = 0; i < KVQ_NUM_PLANES; ++i) total = align_up(total, kPlaneAlign) + sz[i];
+  *bytes = align_up(total, kPlaneAlign);
+  return KVQ_OK;
+}
+
+int32_t kvq_cache_init(kvq_cache* c, const kvq_layout* L, void* base, uint64_t bytes) {
+  if (!c || !L || !base) return KVQ_ERR_NULL;
+  uint64_t need = 0;
+  int32_t st = kvq_cache_bytes(L, &need);
+  if (st != KVQ_OK) return st;
+  if (!aligned(base, kPlaneAlign)) return KVQ_ERR_ALIGN;
+  if (bytes < need) return KVQ_ERR_CAPACITY;
+  std::memset(c, 0, sizeof(*c));
+  c->layout = *L;
+  c->base = base;
+  c->bytes = bytes;
+  c->n_tokens = 0;
+  c->n_blocks_cap = nb_cap(*L);
+  c->ring_slots = L->residual_tokens + kBlock;
+  uint64_t sz[KVQ_NUM_PLANES];
+  plane_sizes(*L, sz);
+  uint64_t off = 0;
+  for (int i = 0; i < KVQ_NUM_PLANES; ++i) {
+    off = align_up(off, kPlaneAlign);
+    c->plane_off[i] = off;
+    c->plane_bytes[i] = sz[i];
+    off += sz[i];
+  }
+  return KVQ_OK;
+}
+
+int32_t kvq_cache_plane(const kvq_cache* c, int32_t plane, uint64_t* offset, uint64_t* bytes) {
+  if (!c || !offset || !bytes) return KVQ_ERR_NULL;
+  if (plane < 0 || plane >= KVQ_NUM_PLANES) return KVQ_ERR_LAYOUT;
+  *offset = c->plane_off[plane];
+  *bytes = c->plane_bytes[plane];
+  return KVQ_OK;
+}
+
+int32_t kvq_cache_window(const kvq_cache* c, int64_t* n_sink, int64_t* n_q, int64_t* n_res) {
+  if (!c || !n_sink || !n_q || !n_res) return KVQ_ERR_NULL;
+  Window w = window(c->layout, c->n_tokens);
+  *n_sink = w.n_sink;
+  *n_q = w.n_q;
+  *n_res = w.r;
+  return KVQ_OK;
+}
+
+int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, void* stream) {
+  if (!c || !c->base) return KVQ_ERR_NULL;
+  const kvq_layout& L = c->layout;
+  int32_t st = kvq_layout_validate(&L);
+  if (st != KVQ_OK) return st;
+  if (T < 0) return KVQ_ERR_LAYOUT;
+  if (T == 0) return KVQ_OK;
+  if (!K || !V) return KVQ_ERR_NULL;
+  if (!aligned(K, 16) || !aligned(V, 16)) return KVQ_ERR_ALIGN;
+  if (c->n_tokens + (int64_t)T > (int64_t)L.max_tokens) return KVQ_ERR_CAPACITY;
+  const int64_t n_old = c->n_tokens;
+  const int64_t n_new = n_old + T;
+  const Window w0 = window(L, n_old);
+  const Window w1 = window(L, n_new);
+  if (w1.n_q / kBlock > c->n_blocks_cap) return KVQ_ERR_CAPACITY;  // cannot happen for valid caches
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(c->base);
+  auto plane = [&](int i) { return base + c->plane_off[i]; };
+
+  // 1) quantize the blocks that leave the residual window (reads ring slots
+  //    of old tokens, so it runs before the copy below overwrites any slot)
+  const int64_t n_flush = (w1.n_q - w0.n_q) / kBlock;
+  if (n_flush > 0) {
+    FlushParams p{};
+    p.k_in = static_cast<const uint16_t*>(K);
+    p.v_in = static_cast<const uint16_t*>(V);
+    p.k_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_RING));
+    p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
+    p.k_codes = reinterpret_cast<uint8_t*>(plane(KVQ_PLANE_K_CODES));
+    p.v_codes = reinterpret_cast<uint8_t*>(plane(KVQ_PLANE_V_CODES));
+    p.k_meta = reinterpret_cast<float*>(plane(KVQ_PLANE_K_META));
+    p.v_meta = reinterpret_cast<float*>(plane(KVQ_PLANE_V_META));
+    p.n_old = n_old;
+    p.T = T;
+    p.hkv = L.num_kv_heads;
+    p.sink = L.sink_tokens;
+    p.ring_slots = c->ring_slots;
+    p.nb_cap = c->n_blocks_cap;
+    p.first_block = (int32_t)(w0.n_q / kBlock);
+    p.n_body_old = n_old - w0.n_sink;
+    p.k_scale = L.k_scale;
+    p.v_scale = L.v_scale;
+    if (n_flush > 0x7fffffff) return KVQ_ERR_UNSUPPORTED;
+    if (launch_flush(L.format, p, (int)n_flush, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  }
+  // 2) copy new sink tokens and new residual tokens to their fp16 planes
+  CopyParams cp{};
+  cp.k_in = static_cast<const uint16_t*>(K);
+  cp.v_in = static_cast<const uint16_t*>(V);
+  cp.k_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_RING));
+  cp.v_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_RING));
+  cp.k_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_SINK));
+  cp.v_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_SINK));
+  cp.n_old = n_old;
+  cp.n_q_new = w1.n_q;
+  cp.T = T;
+  cp.hkv = L.num_kv_heads;
+  cp.sink = L.sink_tokens;
+  cp.ring_slots = c->ring_slots;
+  if (launch_copy(cp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  c->n_tokens = n_new;
+  return KVQ_OK;
+}
+
+int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpw, uint64_t* bytes) {
+  if (!c || !bytes) return KVQ_ERR_NULL;
+  if (bpw < 0 || bpw > 16) return KVQ_ERR_LAYOUT;
+  const kvq_layout& L = c->layout;
+  // the library's own choice never uses fewer blocks per wave than 1
+  const int32_t b = bpw == 0 ? 1 : bpw;
+  const uint64_t nsplit = 1 + (uint64_t)body_splits(c->n_blocks_cap, b);
+  *bytes = (uint64_t)L.batch * L.num_kv_heads * nsplit * (L.num_q_heads / L.num_kv_heads) *
+           kPartStride * sizeof(float);
+  return KVQ_OK;
+}
+
+int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, void* ws,
+                                  uint64_t ws_bytes, int32_t bpw, void* stream) {
+  if (!c || !c->base || !q || !out) return KVQ_ERR_NULL;
+  const kvq_layout& L = c->layout;
+  int32_t st = kvq_layout_validate(&L);
+  if (st != KVQ_OK) return st;
+  if (bpw < 0 || bpw > 16) return KVQ_ERR_LAYOUT;
+  if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  if (c->n_tokens == 0) return KVQ_ERR_EMPTY;
+  const Window w = window(L, c->n_tokens);
+  const int64_t nblk = w.n_q / kBlock;
+  const int32_t b = bpw == 0 ? choose_blocks_per_wave(*c, nblk) : bpw;
+  const int32_t nsplit = 1 + body_splits(nblk, b);
+  const uint64_t need = (uint64_t)L.batch * L.num_kv_heads * nsplit *
+                        (L.num_q_heads / L.num_kv_heads) * kPartStride * sizeof(float);
+  if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (nsplit > 0x7fff) return KVQ_ERR_UNSUPPORTED;
+
+  char* base = static_cast<char*>(c->base);
+  auto plane = [&](int i) { return base + c->plane_off[i]; };
+  AttnParams p{};
+  p.k_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_K_CODES));
+  p.v_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_V_CODES));
+  p.k_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_K_META));
+  p.v_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_V_META));
+  p.k_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_RING));
+  p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
+  p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));
+  p.v_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_SINK));
+  p.q = static_cast<const uint16_t*>(q);
+  p.part = static_cast<float*>(ws);
+  p.hkv = L.num_kv_heads;
+  p.nrep = L.num_q_heads / L.num_kv_heads;
+  p.nb_cap = c->n_blocks_cap;
+  p.nblk = (int32_t)nblk;
+  p.ring_slots = c->ring_slots;
+  p.sink_cap = L.sink_tokens;
+  p.n_sink = (int32_t)w.n_sink;
+  p.n_res = (int32_t)w.r;
+  p.ring_first = (int32_t)(w.n_q % c->ring_slots);
+  p.blocks_per_wave = b;
+  p.nsplit = nsplit;
+  p.k_scale = L.k_scale;
+  p.v_scale = L.v_scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (launch_attention(L.format, p, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  ReduceParams rp{};
+  rp.part = p.part;
+  rp.out = static_cast<uint16_t*>(out);
+  rp.hkv = p.hkv;
+  rp.nrep = p.nrep;
+  rp.nsplit = nsplit;
+  if (launch_reduce(rp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
+int32_t kv_decode_attention(const kvq_cache* c, const void* q, void* out, void* ws,
+                            uint64_t ws_bytes, void* stream) {
+  return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+"""ctypes binding of ``libkvq.so`` (the C ABI declared in ``include/kvq.h``).
+
+Argument marshalling only: every step of quantization and attention runs in
+the library's HIP kernels.  torch tensors supply device memory and the
+current HIP stream.  Importing this module without a built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_OK = 0
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_LAYOUT", -3: "KVQ_ERR_UNSUPPORTED",
+          -4: "KVQ_ERR_CAPACITY", -5: "KVQ_ERR_ALIGN", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP",
+          -8: "KVQ_ERR_EMPTY"}
+FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3}
+PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink")
+EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
+           "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
+           "kv_decode_attention", "kv_decode_attention_split")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("k_group_tokens", ctypes.c_int32), ("v_group_channels", ctypes.c_int32),
+                ("residual_tokens", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("layout", Layout), ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
+                ("n_tokens", ctypes.c_int64), ("n_blocks_cap", ctypes.c_int32),
+                ("ring_slots", ctypes.c_int32), ("plane_off", ctypes.c_uint64 * len(PLANES)),
+                ("plane_bytes", ctypes.c_uint64 * len(PLANES))]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run quantized_kv_cache_quant_amd.build first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, U64, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_int64
+        LP, CP = ctypes.POINTER(Layout), ctypes.POINTER(CacheStruct)
+        sig = {
+            "kvq_status_string": (ctypes.c_char_p, [I32]),
+            "kvq_layout_validate": (I32, [LP]),
+            "kvq_cache_bytes": (I32, [LP, ctypes.POINTER(U64)]),
+            "kvq_cache_init": (I32, [CP, LP, P, U64]),
+            "kvq_cache_plane": (I32, [CP, I32, ctypes.POINTER(U64), ctypes.POINTER(U64)]),
+            "kvq_cache_window": (I32, [CP, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+            "kv_quant_append": (I32, [CP, P, P, I32, P]),
+            "kvq_workspace_bytes": (I32, [CP, I32, ctypes.POINTER(U64)]),
+            "kv_decode_attention": (I32, [CP, P, P, P, U64, P]),
+            "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def make_layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, fmt, *, k_group_tokens=32,
+                v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0) -> Layout:
+    return Layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, FORMATS[fmt], k_group_tokens,
+                  v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale))
+
+
+def cache_bytes(layout: Layout) -> int:
+    n = ctypes.c_uint64()
+    check(lib().kvq_cache_bytes(ctypes.byref(layout), ctypes.byref(n)), "kvq_cache_bytes")
+    return n.value
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Cache:
+    """One layer's packed cache: a device byte tensor plus the host handle."""
+    layout: Layout
+    buf: "object"          # torch.uint8 device tensor (keeps the memory alive)
+    handle: CacheStruct
+
+    @classmethod
+    def create(cls, layout: Layout, device="cuda") -> "Cache":
+        import torch
+        nbytes = cache_bytes(layout)
+        # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        h = CacheStruct()
+        check(lib().kvq_cache_init(ctypes.byref(h), ctypes.byref(layout), ctypes.c_void_p(buf.data_ptr()),
+                                   nbytes), "kvq_cache_init")
+        return cls(layout, buf, h)
+
+    @property
+    def n_tokens(self) -> int:
+        return self.handle.n_tokens
+
+    def window(self):
+        a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        check(lib().kvq_cache_window(ctypes.byref(self.handle), ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c)), "kvq_cache_window")
+        return a.value, b.value, c.value
+
+    def plane(self, name: str):
+        """A uint8 view of one plane of the device buffer."""
+        off, nb = ctypes.c_uint64(), ctypes.c_uint64()
+        check(lib().kvq_cache_plane(ctypes.byref(self.handle), PLANES.index(name), ctypes.byref(off),
+                                    ctypes.byref(nb)), "kvq_cache_plane")
+        return self.buf[off.value:off.value + nb.value]
+
+    def append(self, k, v, stream=None) -> None:
+        """k, v: contiguous fp16 device tensors [B][T][Hkv][D]."""
+        _check_tensor(k, "K")
+        _check_tensor(v, "V")
+        t = k.shape[1]
+        check(lib().kv_quant_append(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
+                                    ctypes.c_void_p(v.data_ptr()), int(t), _stream(stream)), "kv_quant_append")
+
+    def workspace_bytes(self, blocks_per_wave: int = 0) -> int:
+        n = ctypes.c_uint64()
+        check(lib().kvq_workspace_bytes(ctypes.byref(self.handle), int(blocks_per_wave), ctypes.byref(n)),
+              "kvq_workspace_bytes")
+        return n.value
+
+    def attention(self, q, out, ws, blocks_per_wave: int = 0, stream=None) -> None:
+        """q, out: contiguous fp16 device tensors [B][Hq][D]; ws: device scratch tensor."""
+        _check_tensor(q, "q")
+        _check_tensor(out, "out")
+        check(lib().kv_decode_attention_split(ctypes.byref(self.handle), ctypes.c_void_p(q.data_ptr()),
+                                              ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                              ws.numel() * ws.element_size(), int(blocks_per_wave),
+                                              _stream(stream)), "kv_decode_attention")
+
+
+def _check_tensor(t, name: str) -> None:
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.float16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float16 tensor")

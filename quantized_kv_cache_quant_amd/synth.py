@@ -108,11 +108,14 @@ def prefill(w: Workload, batch: int | None = None, tokens: int | None = None,
 
 def append_step(w: Workload, step: int, batch: int | None = None,
                 num_kv_heads: int | None = None, head_dim: int | None = None,
-                first_token: int = 0):
-    """K, V of the single token appended at decode step ``step`` (seed 5000+100i+j)."""
+                first_token: int | None = None):
+    """K, V of the single token appended at decode step ``step`` (seed 5000+100i+j).
+
+    The token's absolute position defaults to seq_len + step (after the prompt).
+    """
     s = 5000 + 100 * w.index + step
-    return kv_tokens(w, s, s + 50, batch or w.batch, 1, num_kv_heads, head_dim,
-                     first_token=first_token)
+    pos = w.seq_len + step if first_token is None else first_token
+    return kv_tokens(w, s, s + 50, batch or w.batch, 1, num_kv_heads, head_dim, first_token=pos)
 
 
 def queries(w: Workload, batch: int | None = None, num_q_heads: int | None = None,

@@ -1,0 +1,141 @@
+"""Helpers shared by the GPU parity tests: drive the library, read its planes back.
+
+Reading back uses the oracle's restatement of the documented byte layout
+(``oracle.layout``) to turn the library's raw planes into logical codes,
+scales and zero-points; the oracle's own quantization of the same inputs is
+computed by ``oracle.cache.build_cache``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import cache as ocache
+from oracle import layout as olayout
+from quantized_kv_cache_quant_amd import kvq
+
+BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    kvq.lib()                      # raises if libkvq.so is missing
+
+
+def olayout_of(lay_kw: dict) -> ocache.Layout:
+    k = dict(lay_kw)
+    return ocache.Layout(k["batch"], k["num_kv_heads"], k["num_q_heads"], 128, k["max_tokens"], k["fmt"],
+                         residual_tokens=k.get("residual_tokens", 128), sink_tokens=k.get("sink_tokens", 0),
+                         k_scale=k.get("k_scale", 1.0), v_scale=k.get("v_scale", 1.0))
+
+
+def make_cache(lay_kw: dict) -> kvq.Cache:
+    k = dict(lay_kw)
+    lay = kvq.make_layout(k.pop("batch"), k.pop("num_kv_heads"), k.pop("num_q_heads"), 128,
+                          k.pop("max_tokens"), k.pop("fmt"), **k)
+    return kvq.Cache.create(lay)
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def append_chunks(c: kvq.Cache, k: np.ndarray, v: np.ndarray, chunks) -> None:
+    """Append k, v [B][n][Hkv][D] in the given chunk sizes."""
+    t0 = 0
+    for t in chunks:
+        c.append(to_dev(k[:, t0:t0 + t]), to_dev(v[:, t0:t0 + t]))
+        t0 += t
+    assert t0 == k.shape[1]
+    torch.cuda.synchronize()
+
+
+def plane_np(c: kvq.Cache, name: str) -> np.ndarray:
+    return c.plane(name).cpu().numpy()
+
+
+def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
+    """The library's cache contents as a logical oracle.CacheState."""
+    b, hkv, d = olay.batch, olay.num_kv_heads, 128
+    bits = BITS[olay.fmt]
+    nb_cap = c.handle.n_blocks_cap
+    rs = c.handle.ring_slots
+    n = c.n_tokens
+    n_sink, n_q, r = c.window()
+    nb = n_q // 32
+    row = d * bits // 8
+
+    def pl(name, dtype, shape):
+        return plane_np(c, name).view(dtype).reshape(shape)
+
+    kc = pl("k_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
+    vc = pl("v_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
+    codes_k = olayout.unpack_k_codes(kc.reshape(b, hkv, nb * 32, row), olay.fmt, d)
+    codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
+    s_k = z_k = s_v = z_v = None
+    if olay.fmt != "fp8":
+        km = pl("k_meta", np.float32, (b, hkv, nb_cap, 2, d))[:, :, :nb]
+        vm = pl("v_meta", np.float32, (b, hkv, nb_cap, 2, 4, 32))[:, :, :nb]
+        s_k, z_k = olayout.unpack_k_meta(km)
+        s_v, z_v = olayout.unpack_v_meta(vm)
+    ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))
+    ring_v = pl("v_ring", np.float16, (b, hkv, rs, d))
+    slots = (np.arange(n_q, n_q + r) % rs).astype(np.int64)
+    s_cap = olay.sink_tokens
+    if s_cap:
+        sk = pl("k_sink", np.float16, (b, hkv, s_cap, d))[:, :, :n_sink]
+        sv = pl("v_sink", np.float16, (b, hkv, s_cap, d))[:, :, :n_sink]
+    else:
+        sk = sv = np.zeros((b, hkv, 0, d), np.float16)
+    st = ocache.CacheState(olay, n, n_sink, n_q, r, sk.copy(), sv.copy(), codes_k, codes_v, s_k, z_k, s_v,
+                           z_v, ring_k[:, :, slots].copy(), ring_v[:, :, slots].copy(), slots)
+    return st
+
+
+def assert_states_equal(got: ocache.CacheState, exp: ocache.CacheState, heads=None) -> None:
+    """Bitwise equality of codes, scales, zero-points, residual and sinks."""
+    assert (got.n_sink, got.n_q, got.r) == (exp.n_sink, exp.n_q, exp.r)
+    sel = (slice(None), slice(None)) if heads is None else tuple(np.array(heads).T)
+
+    def eq(a, b, what):
+        if a is None and b is None:
+            return
+        a = np.asarray(a)[sel]
+        b = np.asarray(b)[sel]
+        if a.dtype.kind == "f":
+            a = a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+            b = b.view(np.uint32 if b.dtype == np.float32 else np.uint16)
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+    eq(got.codes_k, exp.codes_k, "K codes")
+    eq(got.codes_v, exp.codes_v, "V codes")
+    eq(got.s_k, exp.s_k, "K scale")
+    eq(got.z_k, exp.z_k, "K zero-point")
+    eq(got.s_v, exp.s_v, "V scale")
+    eq(got.z_v, exp.z_v, "V zero-point")
+    eq(got.res_k, exp.res_k, "K residual")
+    eq(got.res_v, exp.res_v, "V residual")
+    eq(got.sink_k, exp.sink_k, "K sinks")
+    eq(got.sink_v, exp.sink_v, "V sinks")
+
+
+def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_wave: int = 0) -> np.ndarray:
+    qd = to_dev(q)
+    out = torch.empty_like(qd)
+    ws = torch.empty(c.workspace_bytes(blocks_per_wave) // 4 + 4, dtype=torch.float32, device="cuda")
+    c.attention(qd, out, ws, blocks_per_wave)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def substate(st: ocache.CacheState, bi: int, gi: int) -> ocache.CacheState:
+    """The (sequence bi, KV head gi) slice of a cache state, as a 1 x 1 state."""
+    def cut(a):
+        return None if a is None else a[bi:bi + 1, gi:gi + 1]
+    lay = st.layout
+    sub = ocache.Layout(1, 1, lay.n_rep, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
+                        lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale)
+    return ocache.CacheState(sub, st.n, st.n_sink, st.n_q, st.r, cut(st.sink_k), cut(st.sink_v),
+                             cut(st.codes_k), cut(st.codes_v), cut(st.s_k), cut(st.z_k), cut(st.s_v),
+                             cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots)

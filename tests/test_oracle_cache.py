@@ -193,3 +193,15 @@ def test_step_bytes_of_the_workloads(name, fmt, total):
     # bits per value in the quantized region: codes + fp32 s/z
     bits = 8 * (sb["codes"] + sb["meta"]) / (2 * w.batch * w.num_kv_heads * sb["n_q"] * w.head_dim)
     assert bits == {"fp8": 8, "int8": 10, "int4": 6, "int2": 4}[fmt]
+
+
+def test_library_side_byte_count_agrees_with_oracle():
+    from quantized_kv_cache_quant_amd import accounting
+    for name in synth.WORKLOADS:
+        w = synth.WORKLOADS[name]
+        for fmt in ("int8", "int4", "int2", "fp8"):
+            for n in (1, 100, w.seq_len, w.seq_len + 37):
+                lay = cache.Layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
+                                   residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens)
+                assert accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
+                                                  w.sink_tokens, w.residual_tokens) == nbytes.step_bytes(lay, n)["total"]
