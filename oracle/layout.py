@@ -55,7 +55,7 @@ def unpack_bits(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
     per = 8 // bits
     shifts = (np.arange(per) * bits).astype(np.uint8)
     c = (packed[..., :, None] >> shifts) & ((1 << bits) - 1)
-    return c.reshape(packed.shape[:-1] + (-1,))[..., :n].astype(np.uint8)
+    return c.reshape(packed.shape[:-1] + (packed.shape[-1] * per,))[..., :n].astype(np.uint8)
 
 
 def _record_tokens(qd: int):

@@ -73,3 +73,12 @@ def test_meta_layouts():
     assert mv[1, 1, 0, 3, 7] == sv[1, 32 + 7, 3] and mv[0, 0, 1, 2, 31] == zv[0, 31, 2]
     s2, z2 = layout.unpack_v_meta(mv)
     assert np.array_equal(s2, sv) and np.array_equal(z2, zv)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int2", "fp8"])
+def test_empty_planes_unpack(fmt):
+    bits = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}[fmt]
+    k = layout.unpack_k_codes(np.zeros((2, 3, 0, 128 * bits // 8), np.uint8), fmt, 128)
+    assert k.shape == (2, 3, 0, 128)
+    v = layout.unpack_v_codes(np.zeros((2, 3, 0, 32 * 128 * bits // 8), np.uint8), fmt, 128)
+    assert v.shape == (2, 3, 0, 128)
