@@ -53,8 +53,9 @@
  *                         of T[0..3], byte 2 / 3 = the same channels of T[4..7]
  *            (the order in which the attention kernel's matrix-core operands
  *            are loaded).
- *   K meta   [B][Hkv][NB][2][D] fp32: s then z per channel (INT only)
- *   V meta   [B][Hkv][NB][2][D/32][32] fp32: s then z, [group][token] (INT)
+ *   K meta   [B][Hkv][NB][D][2] fp32: (s, z) of each channel (INT only)
+ *   V meta   [B][Hkv][NB][D/32][32][2] fp32: (s, z) of each channel group
+ *            and token (INT only)
  *   K ring, V ring  [B][Hkv][R+32][D] fp16
  *   K sink, V sink  [B][Hkv][S][D] fp16
  * Each plane starts on a 256-byte boundary.

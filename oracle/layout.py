@@ -23,8 +23,8 @@ Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
     INT2  word p (channels 16*(2p) + r = "A" and 16*(2p+1) + r = "B"):
           byte 0 = A's T[0..3], byte 1 = B's T[0..3], byte 2 = A's T[4..7],
           byte 3 = B's T[4..7], two bits per code, LSB first.
-* K meta    [B][Hkv][NB][2][D]        fp32: s[D] then z[D] of the block's group
-* V meta    [B][Hkv][NB][2][D/G_v][32] fp32: s then z, [channel group][token]
+* K meta    [B][Hkv][NB][D][2]        fp32: (s, z) of each channel of the block's group
+* V meta    [B][Hkv][NB][D/G_v][32][2] fp32: (s, z) of each channel group and token
 * K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
 """
 from __future__ import annotations
@@ -126,30 +126,31 @@ def unpack_v_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
 
 
 def pack_k_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """s, z [..., NB, D] -> [..., NB, 2, D] fp32."""
-    return np.stack([np.asarray(s, np.float32), np.asarray(z, np.float32)], axis=-2)
+    """s, z [..., NB, D] -> [..., NB, D, 2] fp32 (interleaved pairs)."""
+    return np.stack([np.asarray(s, np.float32), np.asarray(z, np.float32)], axis=-1)
 
 
 def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """s, z [..., NB*32, Gn] -> [..., NB, 2, Gn, 32] fp32."""
+    """s, z [..., NB*32, Gn] -> [..., NB, Gn, 32, 2] fp32 (interleaved pairs)."""
     s = np.asarray(s, np.float32)
     z = np.asarray(z, np.float32)
     n, gn = s.shape[-2:]
     nb = n // BLOCK
     sb = np.swapaxes(s.reshape(s.shape[:-2] + (nb, BLOCK, gn)), -1, -2)
     zb = np.swapaxes(z.reshape(z.shape[:-2] + (nb, BLOCK, gn)), -1, -2)
-    return np.stack([sb, zb], axis=-3)
+    return np.stack([sb, zb], axis=-1)
 
 
 def unpack_k_meta(m: np.ndarray):
+    """[..., NB, D, 2] -> s, z [..., NB, D]."""
     m = np.asarray(m, np.float32)
-    return m[..., 0, :].copy(), m[..., 1, :].copy()
+    return m[..., 0].copy(), m[..., 1].copy()
 
 
 def unpack_v_meta(m: np.ndarray):
-    """[..., NB, 2, Gn, 32] -> s, z [..., NB*32, Gn]."""
+    """[..., NB, Gn, 32, 2] -> s, z [..., NB*32, Gn]."""
     m = np.asarray(m, np.float32)
-    nb, _, gn, blk = m.shape[-4:]
-    s = np.swapaxes(m[..., 0, :, :], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
-    z = np.swapaxes(m[..., 1, :, :], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
+    nb, gn, blk, _ = m.shape[-4:]
+    s = np.swapaxes(m[..., 0], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
+    z = np.swapaxes(m[..., 1], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
     return s.copy(), z.copy()

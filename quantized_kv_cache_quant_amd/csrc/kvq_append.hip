@@ -120,9 +120,9 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       const float z = (-mn) / s;
       sk[c] = s;
       zk[c] = z;
-      float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);
-      km[c] = s;
-      km[kHeadDim + c] = z;
+      float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);   // [D][s, z]
+      km[2 * c] = s;
+      km[2 * c + 1] = z;
     } else {
       const int e = tid - kHeadDim;
       const int t = e >> 2, g = e & 3;
@@ -137,9 +137,9 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       const float z = (-mn) / s;
       sv[t][g] = s;
       zv[t][g] = z;
-      float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);
-      vm[g * kBlock + t] = s;
-      vm[kVGroups * kBlock + g * kBlock + t] = z;
+      float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);  // [group][token][s, z]
+      vm[2 * (g * kBlock + t)] = s;
+      vm[2 * (g * kBlock + t) + 1] = z;
     }
     __syncthreads();
   }

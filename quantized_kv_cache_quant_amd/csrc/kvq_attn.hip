@@ -13,9 +13,9 @@
 //    (sequence, KV head) with plain fp32 VALU code;
 //  * every other workgroup owns a range of 4 * blocks_per_wave quantized
 //    32-token blocks of one (sequence, KV head); each of its four wavefronts
-//    streams blocks_per_wave consecutive blocks and keeps an online softmax
-//    for all n_rep query heads of the KV head (GQA: every KV byte is read
-//    once per step);
+//    streams blocks_per_wave consecutive blocks, keeping the next kDepth
+//    blocks' loads in flight, and runs an online softmax for all n_rep query
+//    heads of the KV head (GQA: every KV byte is read once per step);
 //  * each workgroup writes one partial (max, sum, unnormalised output) per
 //    query head; reduce_kernel combines the partials in a fixed order.
 //
@@ -27,8 +27,11 @@
 // columns 0-7 carry the fp16 "hi" part of the fp32 operand and columns 8-15
 // its "lo" remainder (hi = f16(x), lo = f16(x - hi)), so the fp32 operand is
 // represented to ~22 bits and the two column halves are summed after the
-// product (DPP row_ror:8).  Codes enter as exact small integers in f16 (or
-// exact E4M3 values), so no dequantization error is added:
+// product (DPP row_ror:8).  Integer codes enter the matrix cores as exact
+// f16 subnormals (the code's bits placed in the low mantissa bits, value
+// code * 2^-24, times a power of two that depends on the code's position and
+// is divided out of the staged scale); E4M3 codes are converted exactly by
+// the hardware.  No dequantization error is added:
 //  * Key fold: q . k_hat = sum_c (q_c s_c) code_c - sum_c q_c s_c z_c, with
 //    q' = q * s per channel (recomputed per block: the Key scale varies per
 //    32-token group) and the zero-point sum as the accumulator's initial value;
@@ -46,6 +49,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kQScale = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kTwoM24 = 1.0f / 16777216.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -55,50 +61,68 @@ __device__ __forceinline__ float ror8(float x) {
                                                                0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
+// Sum / max over the four 16-lane rows of the wavefront (lanes l, l^16, l^32,
+// l^48).  v_permlane32_swap / v_permlane16_swap swap the upper half of their
+// first operand with the lower half of the second; with both operands holding
+// x the two results are {x[l], x[l^32]} (resp. {x[l], x[l^16]}).  The results
+// are copied to scalars before __builtin_bit_cast: applied directly to an
+// element of the returned vector, the cast reads element 0 for both.
+__device__ __forceinline__ float rows_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  x = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  u = __builtin_bit_cast(unsigned, x);
+  const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+__device__ __forceinline__ float rows_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  x = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  u = __builtin_bit_cast(unsigned, x);
+  const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
 
 __device__ __forceinline__ f16x2 u2h(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
-// (0x6400 | c) is the f16 value 1024 + c for c < 1024; subtracting 1024 is exact.
-__device__ __forceinline__ f16x2 magic_sub(uint32_t w) {
-  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  return u2h(w | 0x64006400u) - k1024;
+__device__ __forceinline__ f16x8 cat(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const f16x2 x = u2h(a), y = u2h(b), z = u2h(c), t = u2h(d);
+  return f16x8{x[0], x[1], y[0], y[1], z[0], z[1], t[0], t[1]};
 }
 
-__device__ __forceinline__ f16x8 cat(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// 8 nibbles -> slots (n0, n4, 16*n1, 16*n5, n2, n6, 16*n3, 16*n7)
+// 8 nibbles -> slots (n0, n4, 16*n1, 16*n5, n2, n6, 16*n3, 16*n7) x 2^-24
 __device__ __forceinline__ f16x8 cvt_int4(uint32_t w) {
   const uint32_t w8 = w >> 8;
-  return cat(magic_sub(w & 0x000F000Fu), magic_sub(w & 0x00F000F0u), magic_sub(w8 & 0x000F000Fu),
-             magic_sub(w8 & 0x00F000F0u));
+  return cat(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
 }
 
-// 8 bytes (two words) -> slots in byte order
+// 8 bytes (two words) -> slots in byte order, x 2^-24
 __device__ __forceinline__ f16x8 cvt_u8(uint32_t w0, uint32_t w1) {
-  const uint32_t lo = 0x04010400u, hi = 0x04030402u;   // [0x64, b1, 0x64, b0] / [.., b3, .., b2]
-  return cat(u2h(__builtin_amdgcn_perm(0x64646464u, w0, lo)) - f16x2{1024, 1024},
-             u2h(__builtin_amdgcn_perm(0x64646464u, w0, hi)) - f16x2{1024, 1024},
-             u2h(__builtin_amdgcn_perm(0x64646464u, w1, lo)) - f16x2{1024, 1024},
-             u2h(__builtin_amdgcn_perm(0x64646464u, w1, hi)) - f16x2{1024, 1024});
+  const uint32_t lo = 0x0C010C00u, hi = 0x0C030C02u;   // [0, b1, 0, b0] / [0, b3, 0, b2]
+  return cat(__builtin_amdgcn_perm(0u, w0, lo), __builtin_amdgcn_perm(0u, w0, hi),
+             __builtin_amdgcn_perm(0u, w1, lo), __builtin_amdgcn_perm(0u, w1, hi));
 }
 
 // 16 two-bit codes c0..c15: low half -> slots (c_k, c_{8+k}) * 4^k, high half
-// (codes shifted down a byte) -> (c_{4+k}, c_{12+k}) * 4^k, k = 0..3
+// (codes shifted down a byte) -> (c_{4+k}, c_{12+k}) * 4^k, k = 0..3, x 2^-24
 __device__ __forceinline__ f16x8 cvt_int2(uint32_t w, bool high) {
   const uint32_t x = high ? (w >> 8) : w;
-  return cat(magic_sub(x & 0x00030003u), magic_sub(x & 0x000C000Cu), magic_sub(x & 0x00300030u),
-             magic_sub(x & 0x00C000C0u));
+  return cat(x & 0x00030003u, x & 0x000C000Cu, x & 0x00300030u, x & 0x00C000C0u);
 }
 
 // 8 OCP E4M3 bytes -> exact f16 values in byte order (hardware conversion)
 __device__ __forceinline__ f16x8 cvt_fp8(uint32_t w0, uint32_t w1) {
-  return cat(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false),
-             __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true),
-             __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false),
-             __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 template <int FMT>
@@ -108,6 +132,11 @@ struct Traits {
   static constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   static constexpr int kKWords = 32 * kBits / 32;          // words per lane per 16-token tile
   static constexpr int kVWords = kRowBytes / 8;            // words per V record (= per lane)
+  // blocks kept in flight besides the one being processed (bytes in flight
+  // per wavefront: INT8 10 KiB, FP8 16 KiB, INT4 18 KiB, INT2 16 KiB; the
+  // counts keep every format at or under 256 VGPRs, two wavefronts per SIMD)
+  static constexpr int kDepth = kFp8 ? 2 : (kBits == 8 ? 1 : (kBits == 4 ? 3 : 4));
+  static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
 // Matrix-core operand number a (K: k-block kb of the lane's 32 channels;
@@ -141,7 +170,7 @@ template <int FMT>
 struct Raw {
   uint32_t k[2][Traits<FMT>::kKWords];   // two 16-token tiles
   uint32_t v[Traits<FMT>::kVWords];
-  float4 km, vm;                         // this lane's 16 bytes of each meta block
+  float4 km, vm;                         // this lane's 16 bytes of each metadata block
 };
 
 template <int FMT>
@@ -185,42 +214,49 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
 //   [256,384) V scale / divisor [g][t]   [384,512) V s*z [g][t]
 constexpr int kStage = 512;
 
+// Lane L holds the (s, z) pairs 2L and 2L+1 of each metadata block.
 template <int FMT>
 __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
-  // lane L < 32 holds s[4L..4L+3], lane L + 32 the matching z
-  const float kz0 = __shfl_down(r.km.x, 32, 64), kz1 = __shfl_down(r.km.y, 32, 64);
-  const float kz2 = __shfl_down(r.km.z, 32, 64), kz3 = __shfl_down(r.km.w, 32, 64);
-  const float vz0 = __shfl_down(r.vm.x, 32, 64), vz1 = __shfl_down(r.vm.y, 32, 64);
-  const float vz2 = __shfl_down(r.vm.z, 32, 64), vz3 = __shfl_down(r.vm.w, 32, 64);
-  if (lane < 32) {
-    const int c = 4 * lane;                      // K channel
-    float4 ks = {r.km.x / slot_div<FMT>(c), r.km.y / slot_div<FMT>(c + 1),
-                 r.km.z / slot_div<FMT>(c + 2), r.km.w / slot_div<FMT>(c + 3)};
-    float4 kz = {r.km.x * kz0, r.km.y * kz1, r.km.z * kz2, r.km.w * kz3};
-    *reinterpret_cast<float4*>(st + c) = ks;
-    *reinterpret_cast<float4*>(st + 128 + c) = kz;
-    const int t = c & 31;                        // V: group lane / 8, tokens t..t+3
-    float4 vs = {r.vm.x / slot_div<FMT>(t), r.vm.y / slot_div<FMT>(t + 1),
-                 r.vm.z / slot_div<FMT>(t + 2), r.vm.w / slot_div<FMT>(t + 3)};
-    float4 vz = {r.vm.x * vz0, r.vm.y * vz1, r.vm.z * vz2, r.vm.w * vz3};
-    *reinterpret_cast<float4*>(st + 256 + c) = vs;
-    *reinterpret_cast<float4*>(st + 384 + c) = vz;
-  }
+  const int c = 2 * lane;                 // K channel; V index g * 32 + t
+  const int t = c & 31;
+  const float2 ks = {r.km.x / slot_div<FMT>(c), r.km.z / slot_div<FMT>(c + 1)};
+  const float2 kz = {r.km.x * r.km.y, r.km.z * r.km.w};
+  const float2 vs = {r.vm.x / slot_div<FMT>(t), r.vm.z / slot_div<FMT>(t + 1)};
+  const float2 vz = {r.vm.x * r.vm.y, r.vm.z * r.vm.w};
+  *reinterpret_cast<float2*>(st + c) = ks;
+  *reinterpret_cast<float2*>(st + 128 + c) = kz;
+  *reinterpret_cast<float2*>(st + 256 + c) = vs;
+  *reinterpret_cast<float2*>(st + 384 + c) = vz;
 }
 
 struct WaveState {
   float m;          // running max (base-2 logits) of this lane's column
   float l;          // this lane's partial softmax denominator
   f32x4 o[8];       // PV accumulator: rows 16m + 4qd + i, column col
-  float zacc[4];    // Value zero-point sums per channel group
+  float z[2];       // Value zero-point sums of channel groups zg, zg + 1
 };
 
+struct LaneInfo {
+  int qd;           // quarter (16-lane row) of the wavefront
+  bool is_lo;       // column carries the lo remainder
+  uint32_t hmask;   // 0xFFFFFFFF in lo columns, 0 in hi columns
+  int zg;           // first Value channel group whose zero-point sum this lane keeps
+};
+
+// hi / lo split of x = a * b into this column's f16 part (hi in hi columns,
+// lo = f16(x - hi) in lo columns), for two values at once.
+__device__ __forceinline__ uint32_t split2(float a0, float b0, float a1, float b1, uint32_t hmask) {
+  const f16x2 h = {(_Float16)(a0 * b0), (_Float16)(a1 * b1)};
+  const f16x2 hm = u2h(__builtin_bit_cast(uint32_t, h) & hmask);
+  const f16x2 r = {(_Float16)__builtin_fmaf(a0, b0, -(float)hm[0]), (_Float16)__builtin_fmaf(a1, b1, -(float)hm[1])};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int FMT>
-__device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws,
-                                              const float* qf, const float* qfb, const f16x8* bk_static,
-                                              bool is_lo, int lane) {
+__device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const float* qf,
+                                              const f16x8* bk_static, const LaneInfo& li, int lane) {
   using T = Traits<FMT>;
-  const int qd = lane >> 4;
+  const int qd = li.qd;
 
   // ---- QK: Key codes (rows = tokens) x q' (columns)
   f32x4 acc[2];
@@ -228,41 +264,43 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
     acc[0] = f32x4{0, 0, 0, 0};
     acc[1] = acc[0];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bk_static[kb],
                                                            acc[tile], 0, 0, 0);
-    }
   } else {
     stage_meta<FMT>(r, st, lane);
-    float sk[32], szk[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 a = *reinterpret_cast<const float4*>(st + 32 * qd + 4 * i);
-      const float4 b = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 4 * i);
-      sk[4 * i] = a.x; sk[4 * i + 1] = a.y; sk[4 * i + 2] = a.z; sk[4 * i + 3] = a.w;
-      szk[4 * i] = b.x; szk[4 * i + 1] = b.y; szk[4 * i + 2] = b.z; szk[4 * i + 3] = b.w;
-    }
-    // zero-point term sum_c q_c s_c z_c of this lane's 32 channels, then the
-    // other three quarters
+    // zero-point term sum_c q_c s_c z_c over this lane's 32 channels, then
+    // over the four quarters
     float bias = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) bias = __builtin_fmaf(qf[c], szk[c], bias);
-    bias += xor_shfl(bias, 16);
-    bias += xor_shfl(bias, 32);
-    const float c0 = is_lo ? 0.f : -bias;
+    for (int i = 0; i < 8; ++i) {
+      const float4 z4 = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 4 * i);
+      bias = __builtin_fmaf(qf[4 * i], z4.x, bias);
+      bias = __builtin_fmaf(qf[4 * i + 1], z4.y, bias);
+      bias = __builtin_fmaf(qf[4 * i + 2], z4.z, bias);
+      bias = __builtin_fmaf(qf[4 * i + 3], z4.w, bias);
+    }
+    bias = rows_sum(bias);
+    const float c0 = li.is_lo ? 0.f : -bias * kTwoM24;
     acc[0] = f32x4{c0, c0, c0, c0};
     acc[1] = acc[0];
+    float sk[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 s4 = *reinterpret_cast<const float4*>(st + 32 * qd + 4 * i);
+      sk[4 * i] = s4.x; sk[4 * i + 1] = s4.y; sk[4 * i + 2] = s4.z; sk[4 * i + 3] = s4.w;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      f16x8 bq;
+      uint32_t bw[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = k_chan<FMT>(kb, j);
-        const _Float16 hi = (_Float16)(qfb[c] * sk[c]);          // 0 in hi columns
-        bq[j] = (_Float16)__builtin_fmaf(qf[c], sk[c], -(float)hi); // hi, or the lo remainder
+      for (int v = 0; v < 4; ++v) {
+        const int c0i = k_chan<FMT>(kb, 2 * v), c1i = k_chan<FMT>(kb, 2 * v + 1);
+        bw[v] = split2(qf[c0i], sk[c0i], qf[c1i], sk[c1i], li.hmask);
       }
+      const f16x8 bq = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bq, acc[tile], 0,
@@ -277,18 +315,17 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[tile][i] = acc[tile][i] + ror8(acc[tile][i]);
+      lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * T::kCodeScale;
       mx = fmaxf(mx, lg[tile][i]);
     }
-  mx = fmaxf(mx, xor_shfl(mx, 16));
-  mx = fmaxf(mx, xor_shfl(mx, 32));
+  mx = rows_max(mx);
   const float m_new = fmaxf(ws.m, mx);
   if (__any(m_new > ws.m)) {
     const float alpha = exp2f(ws.m - m_new);     // 0 on the first block (m = -inf)
 #pragma unroll
     for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) ws.zacc[g] *= alpha;
+    ws.z[0] *= alpha;
+    ws.z[1] *= alpha;
     ws.l *= alpha;
     ws.m = m_new;
   }
@@ -303,46 +340,38 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 
   // ---- PV: Value codes (rows = channels) x P' (columns)
   if constexpr (T::kFp8) {
-    f16x8 bp;
+    uint32_t bw[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        const float x = pr[tile][v];
-        const _Float16 hi = (_Float16)(is_lo ? x : 0.f);
-        bp[2 * v + tile] = (_Float16)(x - (float)hi);
-      }
-    }
+    for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], 1.0f, pr[1][v], 1.0f, li.hmask);
+    const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.v, m), bp, ws.o[m], 0, 0, 0);
   } else {
-    float pb[2][4];
+    // Value zero-point sums: this lane keeps groups zg and zg + 1
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[tile][i] = is_lo ? pr[tile][i] : 0.f;
+    for (int gg = 0; gg < 2; ++gg) {
+      const float* zs = st + 384 + 32 * (li.zg + gg);
+      const float4 z0 = *reinterpret_cast<const float4*>(zs + 4 * qd);
+      const float4 z1 = *reinterpret_cast<const float4*>(zs + 16 + 4 * qd);
+      float za = ws.z[gg];
+      za = __builtin_fmaf(pr[0][0], z0.x, za); za = __builtin_fmaf(pr[0][1], z0.y, za);
+      za = __builtin_fmaf(pr[0][2], z0.z, za); za = __builtin_fmaf(pr[0][3], z0.w, za);
+      za = __builtin_fmaf(pr[1][0], z1.x, za); za = __builtin_fmaf(pr[1][1], z1.y, za);
+      za = __builtin_fmaf(pr[1][2], z1.z, za); za = __builtin_fmaf(pr[1][3], z1.w, za);
+      ws.z[gg] = za;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // scales of tokens 4qd..4qd+3 (tile 0) and 16+4qd..16+4qd+3 (tile 1)
       const float4 s0 = *reinterpret_cast<const float4*>(st + 256 + 32 * g + 4 * qd);
       const float4 s1 = *reinterpret_cast<const float4*>(st + 256 + 32 * g + 16 + 4 * qd);
-      const float4 z0 = *reinterpret_cast<const float4*>(st + 384 + 32 * g + 4 * qd);
-      const float4 z1 = *reinterpret_cast<const float4*>(st + 384 + 32 * g + 16 + 4 * qd);
-      const float sv[2][4] = {{s0.x, s0.y, s0.z, s0.w}, {s1.x, s1.y, s1.z, s1.w}};
-      const float zv[2][4] = {{z0.x, z0.y, z0.z, z0.w}, {z1.x, z1.y, z1.z, z1.w}};
-      f16x8 bp;
-      float za = ws.zacc[g];
+      const float sv0[4] = {s0.x, s0.y, s0.z, s0.w};
+      const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
+      uint32_t bw[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-          const _Float16 hi = (_Float16)(pb[tile][v] * sv[tile][v]);
-          bp[2 * v + tile] = (_Float16)__builtin_fmaf(pr[tile][v], sv[tile][v], -(float)hi);
-          za = __builtin_fmaf(pr[tile][v], zv[tile][v], za);
-        }
-      }
-      ws.zacc[g] = za;
+      for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], sv0[v], pr[1][v], sv1[v], li.hmask);
+      const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const int m = 2 * g + mm;
@@ -354,8 +383,8 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 
 // ---------------------------------------------------------------- LDS map
 constexpr int kCombineFloats = kWavesPerSplit * 8 * 130;                 // m, l, o[128] per head
-constexpr int kBodyLdsFloats = kWavesPerSplit * 2 * kStage > kCombineFloats ? kWavesPerSplit * 2 * kStage
-                                                                            : kCombineFloats;
+constexpr int kBodyLdsFloats = kWavesPerSplit * kStage > kCombineFloats ? kWavesPerSplit * kStage
+                                                                        : kCombineFloats;
 constexpr int kSegChunk = 32;
 constexpr int kSegKStride = 130;                                         // halves per K row (bank spread)
 constexpr int kSegBytes = 8 * 128 * 4 + kSegChunk * kSegKStride * 2 + kSegChunk * 128 * 2 + 8 * kSegChunk * 4;
@@ -368,45 +397,44 @@ __device__ void body_split(const AttnParams& p, int b, int g, int split, char* l
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane & 15;
-  const int qd = lane >> 4;
   const int head = col & 7;
-  const bool is_lo = col >= 8;
   const bool valid_head = head < p.nrep;
+  LaneInfo li;
+  li.qd = lane >> 4;
+  li.is_lo = col >= 8;
+  li.hmask = li.is_lo ? 0xFFFFFFFFu : 0u;
+  li.zg = li.is_lo ? 2 : 0;
   const int64_t bh = (int64_t)b * p.hkv + g;
   float* ldsf = reinterpret_cast<float*>(lds);
-  float* stage = ldsf + wave * 2 * kStage;
+  float* stage = ldsf + wave * kStage;
 
   // query in base-2 logit units, this lane's head and 32 channels
-  const float qscale = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
-  float qf[32], qfb[32];
+  float qf[32];
   {
-    const uint16_t* qsrc = p.q + (((int64_t)b * p.hkv + g) * p.nrep + (valid_head ? head : 0)) * kHeadDim + 32 * qd;
+    const uint16_t* qsrc =
+        p.q + (((int64_t)b * p.hkv + g) * p.nrep + (valid_head ? head : 0)) * kHeadDim + 32 * li.qd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 w = reinterpret_cast<const uint4*>(qsrc)[i];
-      const uint32_t ws_[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = valid_head ? (float)u2h(ws_[j])[0] * qscale : 0.f;
-        const float c = valid_head ? (float)u2h(ws_[j])[1] * qscale : 0.f;
-        qf[8 * i + 2 * j] = a;
-        qf[8 * i + 2 * j + 1] = c;
+        qf[8 * i + 2 * j] = valid_head ? (float)u2h(wv[j])[0] * kQScale : 0.f;
+        qf[8 * i + 2 * j + 1] = valid_head ? (float)u2h(wv[j])[1] * kQScale : 0.f;
       }
     }
   }
   f16x8 bk_static[4];
   if constexpr (T::kFp8) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t bw[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = qf[k_chan<FMT>(kb, j)] * p.k_scale;
-        const _Float16 hi = (_Float16)(is_lo ? x : 0.f);
-        bk_static[kb][j] = (_Float16)(x - (float)hi);
-      }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) qfb[c] = is_lo ? qf[c] : 0.f;
+      for (int v = 0; v < 4; ++v)
+        bw[v] = split2(qf[k_chan<FMT>(kb, 2 * v)], p.k_scale, qf[k_chan<FMT>(kb, 2 * v + 1)], p.k_scale,
+                       li.hmask);
+      bk_static[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
+    }
   }
 
   WaveState ws;
@@ -414,47 +442,51 @@ __device__ void body_split(const AttnParams& p, int b, int g, int split, char* l
   ws.l = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) ws.o[m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg) ws.zacc[gg] = 0.f;
+  ws.z[0] = ws.z[1] = 0.f;
 
   const int64_t first = ((int64_t)split * kWavesPerSplit + wave) * p.blocks_per_wave;
   int64_t nb = (int64_t)p.nblk - first;
   if (nb > p.blocks_per_wave) nb = p.blocks_per_wave;
   if (nb > 0) {
-    Raw<FMT> ra, rb;
-    load_block<FMT>(ra, p, bh, first, lane);
-    for (int64_t i = 0; i < nb; i += 2) {
-      if (i + 1 < nb) load_block<FMT>(rb, p, bh, first + i + 1, lane);
-      process_block<FMT>(ra, stage, ws, qf, qfb, bk_static, is_lo, lane);
-      if (i + 1 >= nb) break;
-      if (i + 2 < nb) load_block<FMT>(ra, p, bh, first + i + 2, lane);
-      process_block<FMT>(rb, stage + kStage, ws, qf, qfb, bk_static, is_lo, lane);
+    // kDepth blocks in flight while one is processed; prefetches past the
+    // wavefront's last block re-read that block (always in bounds), so the
+    // loads need no branch and the waits stay static.
+    constexpr int D = T::kDepth + 1;
+    const int64_t last = first + nb - 1;
+    Raw<FMT> buf[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load_block<FMT>(buf[d], p, bh, first + d < last ? first + d : last, lane);
+    for (int64_t i = 0; i < nb; i += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int64_t nxt = first + i + d + D - 1;
+        load_block<FMT>(buf[(d + D - 1) % D], p, bh, nxt < last ? nxt : last, lane);
+        if (i + d < nb) process_block<FMT>(buf[d], stage, ws, qf, bk_static, li, lane);
+      }
     }
   }
 
   // ---- finish this wavefront: sum over quarters, hi + lo columns
-  float l = ws.l;
-  l += xor_shfl(l, 16);
-  l += xor_shfl(l, 32);
-  float z[4];
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg) {
-    z[gg] = ws.zacc[gg];
-    z[gg] += xor_shfl(z[gg], 16);
-    z[gg] += xor_shfl(z[gg], 32);
+  const float l = rows_sum(ws.l);
+  float zs[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!T::kFp8) {
+    const float z0 = rows_sum(ws.z[0]), z1 = rows_sum(ws.z[1]);
+    // hi columns hold groups 0, 1; their lo partners (lane + 8) groups 2, 3
+    zs[0] = z0; zs[1] = z1; zs[2] = ror8(z0); zs[3] = ror8(z1);
   }
-  const float vscale = T::kFp8 ? p.v_scale : 1.0f;
+  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
   __syncthreads();                                   // staging area is reused below
   float* cm = ldsf + wave * 8 * 130;                 // [head][m, l, o[128]]
+  const bool writer = !li.is_lo && valid_head;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float o = (ws.o[m][i] + ror8(ws.o[m][i]) - z[m >> 1]) * vscale;
-      if (!is_lo && valid_head) cm[head * 130 + 2 + 16 * m + 4 * qd + i] = o;
+      const float o = (ws.o[m][i] + ror8(ws.o[m][i])) * oscale - zs[m >> 1];
+      if (writer) cm[head * 130 + 2 + 16 * m + 4 * li.qd + i] = o;
     }
   }
-  if (!is_lo && valid_head && qd == 0) {
+  if (writer && li.qd == 0) {
     cm[head * 130] = ws.m;
     cm[head * 130 + 1] = l;
   }
@@ -497,12 +529,11 @@ __device__ void fp16_segment(const AttnParams& p, int b, int g, char* lds) {
   uint16_t* vc = kc + kSegChunk * kSegKStride;                                // [32][128]
   float* lgs = reinterpret_cast<float*>(vc + kSegChunk * 128);                // [8][32]
   const int64_t bh = (int64_t)b * p.hkv + g;
-  const float qscale = kLog2e * 0.08838834764831845f;
   if (hh < p.nrep) {
     const uint16_t* qsrc = p.q + (bh * p.nrep + hh) * kHeadDim + 4 * c4;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      qs[hh * 128 + 4 * c4 + j] = (float)__builtin_bit_cast(_Float16, qsrc[j]) * qscale;
+      qs[hh * 128 + 4 * c4 + j] = (float)__builtin_bit_cast(_Float16, qsrc[j]) * kQScale;
   }
   float m = neg_inf(), l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
   const int nt = p.n_sink + p.n_res;
@@ -588,22 +619,71 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   }
 }
 
+constexpr int kReduceThreads = 128;
+constexpr int kReduceLdsSplits = 4096;
+
 // out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s
-__global__ __launch_bounds__(128) void reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) {
+  __shared__ float wts[kReduceLdsSplits];
+  __shared__ float red[2][kReduceThreads / 64];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int lane = c & 63, wave = c >> 6;
   const int g = hq / p.nrep, hh = hq % p.nrep;
   const int64_t stride = (int64_t)p.nrep * kPartStride;
   const float* base = p.part + (((int64_t)b * p.hkv + g) * p.nsplit * p.nrep + hh) * kPartStride;
+  // the maximum over splits, one split per thread
   float M = neg_inf();
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, base[s * stride]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
+  for (int s = c; s < p.nsplit; s += kReduceThreads) M = fmaxf(M, base[s * stride]);
+  for (int off = 32; off; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / 64; ++w) M = fmaxf(M, red[0][w]);
+  // split weights 2^(m_s - M) and the denominator
+  float L = 0.f;
+  for (int s = c; s < p.nsplit; s += kReduceThreads) {
     const float ms = base[s * stride];
-    if (ms != neg_inf()) {
-      const float f = exp2f(ms - M);
-      L = __builtin_fmaf(f, base[s * stride + 1], L);
-      O = __builtin_fmaf(f, base[s * stride + 4 + c], O);
+    const float wgt = ms == neg_inf() ? 0.f : exp2f(ms - M);
+    if (s < kReduceLdsSplits) wts[s] = wgt;
+    L = __builtin_fmaf(wgt, base[s * stride + 1], L);
+  }
+  for (int off = 32; off; off >>= 1) L += __shfl_xor(L, off, 64);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kReduceThreads / 64; ++w) L += red[1][w];
+  // this thread's channel: independent loads, eight splits at a time
+  float O = 0.f;
+  const float* oc = base + 4 + c;
+  int s = 0;
+  for (; s + 8 <= p.nsplit; s += 8) {
+    float v[8], w8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = oc[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sj = s + j;
+      if (sj < kReduceLdsSplits) {
+        w8[j] = wts[sj];
+      } else {
+        const float ms = base[sj * stride];
+        w8[j] = ms == neg_inf() ? 0.f : exp2f(ms - M);
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) O = __builtin_fmaf(w8[j], v[j], O);
+  }
+  for (; s < p.nsplit; ++s) {
+    float wgt;
+    if (s < kReduceLdsSplits) {
+      wgt = wts[s];
+    } else {
+      const float ms = base[s * stride];
+      wgt = ms == neg_inf() ? 0.f : exp2f(ms - M);
+    }
+    O = __builtin_fmaf(wgt, oc[s * stride], O);
   }
   const _Float16 r = (_Float16)(O / L);
   p.out[((int64_t)b * p.hkv * p.nrep + hq) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
@@ -624,7 +704,7 @@ hipError_t launch_attention(int fmt, const AttnParams& p, int batch, hipStream_t
 }
 
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_kernel, dim3(p.hkv * p.nrep, batch), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(reduce_kernel, dim3(p.hkv * p.nrep, batch), dim3(kReduceThreads), 0, s, p);
   return hipGetLastError();
 }
 

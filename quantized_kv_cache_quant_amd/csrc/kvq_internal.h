@@ -26,8 +26,8 @@ struct FlushParams {
   const uint16_t* v_ring;
   uint8_t* k_codes;       // [B][Hkv][NB*32][D*b/8]
   uint8_t* v_codes;       // [B][Hkv][NB][32*D*b/8]
-  float* k_meta;          // [B][Hkv][NB][2][D]
-  float* v_meta;          // [B][Hkv][NB][2][D/32][32]
+  float* k_meta;          // [B][Hkv][NB][D][2]       (s, z) per channel
+  float* v_meta;          // [B][Hkv][NB][D/32][32][2] (s, z) per group and token
   int64_t n_old;          // tokens per sequence before this append
   int32_t T;              // tokens appended
   int32_t hkv;

@@ -74,8 +74,8 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
     codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
     s_k = z_k = s_v = z_v = None
     if olay.fmt != "fp8":
-        km = pl("k_meta", np.float32, (b, hkv, nb_cap, 2, d))[:, :, :nb]
-        vm = pl("v_meta", np.float32, (b, hkv, nb_cap, 2, 4, 32))[:, :, :nb]
+        km = pl("k_meta", np.float32, (b, hkv, nb_cap, d, 2))[:, :, :nb]
+        vm = pl("v_meta", np.float32, (b, hkv, nb_cap, 4, 32, 2))[:, :, :nb]
         s_k, z_k = olayout.unpack_k_meta(km)
         s_v, z_v = olayout.unpack_v_meta(vm)
     ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))

@@ -65,12 +65,18 @@ def test_meta_layouts():
     s = rng.standard_normal((2, 3, 128)).astype(np.float32)
     z = rng.standard_normal((2, 3, 128)).astype(np.float32)
     m = layout.pack_k_meta(s, z)
-    assert m.shape == (2, 3, 2, 128) and np.array_equal(m[:, :, 1], z)
+    assert m.shape == (2, 3, 128, 2) and np.array_equal(m[..., 1], z)
+    flat = m.reshape(2, 3, 256)                       # (s, z) pairs per channel
+    assert flat[1, 2, 2 * 77] == s[1, 2, 77] and flat[1, 2, 2 * 77 + 1] == z[1, 2, 77]
+    s2, z2 = layout.unpack_k_meta(m)
+    assert np.array_equal(s2, s) and np.array_equal(z2, z)
     sv = rng.standard_normal((2, 64, 4)).astype(np.float32)
     zv = rng.standard_normal((2, 64, 4)).astype(np.float32)
     mv = layout.pack_v_meta(sv, zv)
-    assert mv.shape == (2, 2, 2, 4, 32)
-    assert mv[1, 1, 0, 3, 7] == sv[1, 32 + 7, 3] and mv[0, 0, 1, 2, 31] == zv[0, 31, 2]
+    assert mv.shape == (2, 2, 4, 32, 2)
+    flat = mv.reshape(2, 2, 256)                      # block: [group][token][s, z]
+    assert flat[1, 1, 2 * (3 * 32 + 7)] == sv[1, 32 + 7, 3]
+    assert flat[0, 0, 2 * (2 * 32 + 31) + 1] == zv[0, 31, 2]
     s2, z2 = layout.unpack_v_meta(mv)
     assert np.array_equal(s2, sv) and np.array_equal(z2, zv)
 
