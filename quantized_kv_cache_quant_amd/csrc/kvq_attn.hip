@@ -8,16 +8,18 @@
 // s * E4M3 for FP8) or the fp16 sink / residual entries.  Dequantization is
 // fused into the two matrix products, so only packed bytes cross HBM.
 //
-// Work decomposition (grid = [1 + body splits, Hkv, B], 256 threads):
-//  * blockIdx.x == 0 handles the fp16 segment (sinks + residual ring) of one
-//    (sequence, KV head) with plain fp32 VALU code;
-//  * every other workgroup owns a range of 4 * blocks_per_wave quantized
-//    32-token blocks of one (sequence, KV head); each of its four wavefronts
-//    streams blocks_per_wave consecutive blocks, keeping the next kDepth
-//    blocks' loads in flight, and runs an online softmax for all n_rep query
-//    heads of the KV head (GQA: every KV byte is read once per step);
-//  * each workgroup writes one partial (max, sum, unnormalised output) per
-//    query head; reduce_kernel combines the partials in a fixed order.
+// Work decomposition (one wavefront per 64-thread workgroup):
+//  * fp16 wavefronts handle the fp16 segment (sinks + residual ring) of one
+//    (sequence, KV head), up to fp16_per_wave 32-token blocks each;
+//  * body wavefronts each stream an equal share of the flattened
+//    (head-major) list of quantized 32-token blocks of all heads, keeping
+//    the next kDepth blocks' loads in flight.  A share covers one or two
+//    heads; for every head it touches the wavefront runs an online softmax
+//    for all n_rep query heads of that KV head (GQA: every KV byte is read
+//    once per step) and writes one partial (max, sum, unnormalised output);
+//  * the grid is sized to about one resident round of wavefronts, so no
+//    wavefront waits for another to finish;
+//  * reduce_kernel combines each head's partials in a fixed order.
 //
 // Per 32-token block a wavefront runs both products on the matrix cores with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate):
@@ -173,16 +175,19 @@ struct Raw {
   float4 km, vm;                         // this lane's 16 bytes of each metadata block
 };
 
+// Loads one block.  bh and blk are wave-uniform, so the block base is a
+// scalar and the per-lane parts are 32-bit offsets.
 template <int FMT>
 __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int64_t bh, int64_t blk,
                                            int lane) {
   using T = Traits<FMT>;
-  const int64_t blkoff = (bh * p.nb_cap + blk) * (int64_t)(kBlock * T::kRowBytes);
-  const int qd = lane >> 4;
+  const int64_t id = bh * p.nb_cap + blk;
+  const uint8_t* kb = p.k_codes + id * (int64_t)(kBlock * T::kRowBytes);
+  const uint8_t* vb = p.v_codes + id * (int64_t)(kBlock * T::kRowBytes);
+  const uint32_t qd = (uint32_t)lane >> 4;
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
-    const uint8_t* src = p.k_codes + blkoff + (int64_t)(16 * tile + (lane & 15)) * T::kRowBytes +
-                         qd * (T::kKWords * 4);
+    const uint8_t* src = kb + ((16u * tile + ((uint32_t)lane & 15u)) * T::kRowBytes + qd * (T::kKWords * 4));
     if constexpr (T::kKWords == 8) {
       const uint4 a = reinterpret_cast<const uint4*>(src)[0];
       const uint4 b = reinterpret_cast<const uint4*>(src)[1];
@@ -196,18 +201,24 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
       r.k[tile][0] = a.x; r.k[tile][1] = a.y;
     }
   }
-  const uint4* vsrc = reinterpret_cast<const uint4*>(p.v_codes + blkoff + (int64_t)lane * (T::kVWords * 4));
+  const uint4* vsrc = reinterpret_cast<const uint4*>(vb + (uint32_t)lane * (T::kVWords * 4));
 #pragma unroll
   for (int i = 0; i < T::kVWords / 4; ++i) {
     const uint4 a = vsrc[i];
     r.v[4 * i] = a.x; r.v[4 * i + 1] = a.y; r.v[4 * i + 2] = a.z; r.v[4 * i + 3] = a.w;
   }
   if constexpr (!T::kFp8) {
-    const int64_t moff = (bh * p.nb_cap + blk) * 256 + lane * 4;
-    r.km = *reinterpret_cast<const float4*>(p.k_meta + moff);
-    r.vm = *reinterpret_cast<const float4*>(p.v_meta + moff);
+    r.km = reinterpret_cast<const float4*>(p.k_meta + id * 256)[lane];
+    r.vm = reinterpret_cast<const float4*>(p.v_meta + id * 256)[lane];
   }
 }
+
+// The running max may grow by up to 2^kSlack before the accumulators are
+// rescaled, so p = 2^(logit - m) <= 2^kSlack.  The P' operands p * s stay
+// finite in f16 as long as s <= 255; a block holding a larger Value scale is
+// processed with an exact running max instead (p <= 1, p * s <= s).
+constexpr float kSlack = 8.0f;
+constexpr float kLazyScaleMax = 255.0f;
 
 // LDS staging area of one wavefront for one block (floats):
 //   [0,128) K scale / slot divisor   [128,256) K s*z
@@ -219,9 +230,9 @@ template <int FMT>
 __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
   const int c = 2 * lane;                 // K channel; V index g * 32 + t
   const int t = c & 31;
-  const float2 ks = {r.km.x / slot_div<FMT>(c), r.km.z / slot_div<FMT>(c + 1)};
+  const float2 ks = {r.km.x * (1.0f / slot_div<FMT>(c)), r.km.z * (1.0f / slot_div<FMT>(c + 1))};
   const float2 kz = {r.km.x * r.km.y, r.km.z * r.km.w};
-  const float2 vs = {r.vm.x / slot_div<FMT>(t), r.vm.z / slot_div<FMT>(t + 1)};
+  const float2 vs = {r.vm.x * (1.0f / slot_div<FMT>(t)), r.vm.z * (1.0f / slot_div<FMT>(t + 1))};
   const float2 vz = {r.vm.x * r.vm.y, r.vm.z * r.vm.w};
   *reinterpret_cast<float2*>(st + c) = ks;
   *reinterpret_cast<float2*>(st + 128 + c) = kz;
@@ -237,24 +248,123 @@ struct WaveState {
 };
 
 struct LaneInfo {
-  int qd;           // quarter (16-lane row) of the wavefront
+  int lane, qd, head;
   bool is_lo;       // column carries the lo remainder
+  bool writer;      // hi column of a real query head: writes the results
   uint32_t hmask;   // 0xFFFFFFFF in lo columns, 0 in hi columns
   int zg;           // first Value channel group whose zero-point sum this lane keeps
 };
 
+__device__ __forceinline__ LaneInfo lane_info(int nrep) {
+  LaneInfo li;
+  li.lane = threadIdx.x & 63;
+  const int col = li.lane & 15;
+  li.qd = li.lane >> 4;
+  li.head = col & 7;
+  li.is_lo = col >= 8;
+  li.writer = !li.is_lo && li.head < nrep;
+  li.hmask = li.is_lo ? 0xFFFFFFFFu : 0u;
+  li.zg = li.is_lo ? 2 : 0;
+  return li;
+}
+
+__device__ __forceinline__ void reset(WaveState& ws) {
+  ws.m = neg_inf();
+  ws.l = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) ws.o[m] = f32x4{0, 0, 0, 0};
+  ws.z[0] = ws.z[1] = 0.f;
+}
+
 // hi / lo split of x = a * b into this column's f16 part (hi in hi columns,
 // lo = f16(x - hi) in lo columns), for two values at once.
 __device__ __forceinline__ uint32_t split2(float a0, float b0, float a1, float b1, uint32_t hmask) {
-  const f16x2 h = {(_Float16)(a0 * b0), (_Float16)(a1 * b1)};
+  const f16x2 h = {(_Float16)__builtin_fmaf(a0, b0, 0.0f), (_Float16)__builtin_fmaf(a1, b1, 0.0f)};
   const f16x2 hm = u2h(__builtin_bit_cast(uint32_t, h) & hmask);
   const f16x2 r = {(_Float16)__builtin_fmaf(a0, b0, -(float)hm[0]), (_Float16)__builtin_fmaf(a1, b1, -(float)hm[1])};
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// The same split with the hi part already zeroed in hi columns (ab = a or 0).
+__device__ __forceinline__ uint32_t split2z(float a0, float ab0, float b0, float a1, float ab1, float b1) {
+  const f16x2 h = {(_Float16)__builtin_fmaf(ab0, b0, 0.0f), (_Float16)__builtin_fmaf(ab1, b1, 0.0f)};
+  const f16x2 r = {(_Float16)__builtin_fmaf(a0, b0, -(float)h[0]), (_Float16)__builtin_fmaf(a1, b1, -(float)h[1])};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Query of head bh (this lane's column head, its quarter's 32 channels), in
+// base-2 logit units; zero in columns of heads past n_rep.
+__device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, float* qf) {
+  const bool valid = li.head < p.nrep;
+  const uint4* qsrc = reinterpret_cast<const uint4*>(p.q + (bh * p.nrep + (valid ? li.head : 0)) * kHeadDim +
+                                                     32 * li.qd);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = qsrc[i];
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x2 h = u2h(wv[j]);
+      qf[8 * i + 2 * j] = valid ? (float)h[0] * kQScale : 0.f;
+      qf[8 * i + 2 * j + 1] = valid ? (float)h[1] * kQScale : 0.f;
+    }
+  }
+}
+
+// Static q operands (hi / lo) for Keys without a per-block scale (FP8 with
+// its per-tensor scale, fp16 segment with scale 1).
+template <int FMT>
+__device__ __forceinline__ void static_q(const float* qf, float scale, const LaneInfo& li, f16x8* bk) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint32_t bw[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      bw[v] = split2(qf[k_chan<FMT>(kb, 2 * v)], scale, qf[k_chan<FMT>(kb, 2 * v + 1)], scale, li.hmask);
+    bk[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
+  }
+}
+
+// Online softmax over one block's 32 tokens (this lane: 8 of them, logits
+// lg[tile][i] for tokens 16*tile + 4qd + i); returns p = 2^(lg - m).
+__device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, float pr[2][4], float slack) {
+  float mx = neg_inf();
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[tile][i]);
+  mx = rows_max(mx);
+  if (__any(mx > ws.m + slack)) {                // always true on the first block (m = -inf)
+    const float m_new = fmaxf(ws.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(ws.m - m_new);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
+    ws.z[0] *= alpha;
+    ws.z[1] *= alpha;
+    ws.l *= alpha;
+    ws.m = m_new;
+  }
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[tile][i] = __builtin_amdgcn_exp2f(lg[tile][i] - ws.m);
+      ws.l += pr[tile][i];
+    }
+}
+
+// P operand without a per-token scale (FP8: the per-tensor scale is applied
+// at the end; fp16 segment: none).
+__device__ __forceinline__ f16x8 p_operand(const float pr[2][4], const LaneInfo& li) {
+  uint32_t bw[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], 1.0f, pr[1][v], 1.0f, li.hmask);
+  return cat(bw[0], bw[1], bw[2], bw[3]);
+}
+
 template <int FMT>
 __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const float* qf,
-                                              const f16x8* bk_static, const LaneInfo& li, int lane) {
+                                              const f16x8* bk_static, const LaneInfo& li) {
   using T = Traits<FMT>;
   const int qd = li.qd;
 
@@ -270,7 +380,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bk_static[kb],
                                                            acc[tile], 0, 0, 0);
   } else {
-    stage_meta<FMT>(r, st, lane);
+    stage_meta<FMT>(r, st, li.lane);
     // zero-point term sum_c q_c s_c z_c over this lane's 32 channels, then
     // over the four quarters
     float bias = 0.f;
@@ -308,42 +418,20 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
     }
   }
 
-  // ---- online softmax over the block's 32 tokens (this lane: 8 of them)
-  float lg[2][4];
-  float mx = neg_inf();
+  float lg[2][4], pr[2][4];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * T::kCodeScale;
-      mx = fmaxf(mx, lg[tile][i]);
-    }
-  mx = rows_max(mx);
-  const float m_new = fmaxf(ws.m, mx);
-  if (__any(m_new > ws.m)) {
-    const float alpha = exp2f(ws.m - m_new);     // 0 on the first block (m = -inf)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
-    ws.z[0] *= alpha;
-    ws.z[1] *= alpha;
-    ws.l *= alpha;
-    ws.m = m_new;
+    for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * T::kCodeScale;
+  float slack = kSlack;
+  if constexpr (!T::kFp8) {
+    if (__any(r.vm.x > kLazyScaleMax || r.vm.z > kLazyScaleMax)) slack = 0.f;
   }
-  float pr[2][4];
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[tile][i] = exp2f(lg[tile][i] - ws.m);
-      ws.l += pr[tile][i];
-    }
+  softmax_block(lg, ws, pr, slack);
 
   // ---- PV: Value codes (rows = channels) x P' (columns)
   if constexpr (T::kFp8) {
-    uint32_t bw[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], 1.0f, pr[1][v], 1.0f, li.hmask);
-    const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
+    const f16x8 bp = p_operand(pr, li);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.v, m), bp, ws.o[m], 0, 0, 0);
@@ -361,6 +449,11 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       za = __builtin_fmaf(pr[1][2], z1.z, za); za = __builtin_fmaf(pr[1][3], z1.w, za);
       ws.z[gg] = za;
     }
+    float pb[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[tile][i] = li.is_lo ? pr[tile][i] : 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // scales of tokens 4qd..4qd+3 (tile 0) and 16+4qd..16+4qd+3 (tile 1)
@@ -370,7 +463,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
       uint32_t bw[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], sv0[v], pr[1][v], sv1[v], li.hmask);
+      for (int v = 0; v < 4; ++v) bw[v] = split2z(pr[0][v], pb[0][v], sv0[v], pr[1][v], pb[1][v], sv1[v]);
       const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
@@ -381,272 +474,235 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   }
 }
 
-// ---------------------------------------------------------------- LDS map
-constexpr int kCombineFloats = kWavesPerSplit * 8 * 130;                 // m, l, o[128] per head
-constexpr int kBodyLdsFloats = kWavesPerSplit * kStage > kCombineFloats ? kWavesPerSplit * kStage
-                                                                        : kCombineFloats;
-constexpr int kSegChunk = 32;
-constexpr int kSegKStride = 130;                                         // halves per K row (bank spread)
-constexpr int kSegBytes = 8 * 128 * 4 + kSegChunk * kSegKStride * 2 + kSegChunk * 128 * 2 + 8 * kSegChunk * 4;
-constexpr int kLdsBytes = kBodyLdsFloats * 4 > kSegBytes ? kBodyLdsFloats * 4 : kSegBytes;
-
-template <int FMT>
-__device__ void body_split(const AttnParams& p, int b, int g, int split, char* lds) {
-  using T = Traits<FMT>;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15;
-  const int head = col & 7;
-  const bool valid_head = head < p.nrep;
-  LaneInfo li;
-  li.qd = lane >> 4;
-  li.is_lo = col >= 8;
-  li.hmask = li.is_lo ? 0xFFFFFFFFu : 0u;
-  li.zg = li.is_lo ? 2 : 0;
-  const int64_t bh = (int64_t)b * p.hkv + g;
-  float* ldsf = reinterpret_cast<float*>(lds);
-  float* stage = ldsf + wave * kStage;
-
-  // query in base-2 logit units, this lane's head and 32 channels
-  float qf[32];
-  {
-    const uint16_t* qsrc =
-        p.q + (((int64_t)b * p.hkv + g) * p.nrep + (valid_head ? head : 0)) * kHeadDim + 32 * li.qd;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 w = reinterpret_cast<const uint4*>(qsrc)[i];
-      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qf[8 * i + 2 * j] = valid_head ? (float)u2h(wv[j])[0] * kQScale : 0.f;
-        qf[8 * i + 2 * j + 1] = valid_head ? (float)u2h(wv[j])[1] * kQScale : 0.f;
-      }
-    }
-  }
-  f16x8 bk_static[4];
-  if constexpr (T::kFp8) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        bw[v] = split2(qf[k_chan<FMT>(kb, 2 * v)], p.k_scale, qf[k_chan<FMT>(kb, 2 * v + 1)], p.k_scale,
-                       li.hmask);
-      bk_static[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
-    }
-  }
-
-  WaveState ws;
-  ws.m = neg_inf();
-  ws.l = 0.f;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) ws.o[m] = f32x4{0, 0, 0, 0};
-  ws.z[0] = ws.z[1] = 0.f;
-
-  const int64_t first = ((int64_t)split * kWavesPerSplit + wave) * p.blocks_per_wave;
-  int64_t nb = (int64_t)p.nblk - first;
-  if (nb > p.blocks_per_wave) nb = p.blocks_per_wave;
-  if (nb > 0) {
-    // kDepth blocks in flight while one is processed; prefetches past the
-    // wavefront's last block re-read that block (always in bounds), so the
-    // loads need no branch and the waits stay static.
-    constexpr int D = T::kDepth + 1;
-    const int64_t last = first + nb - 1;
-    Raw<FMT> buf[D];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) load_block<FMT>(buf[d], p, bh, first + d < last ? first + d : last, lane);
-    for (int64_t i = 0; i < nb; i += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const int64_t nxt = first + i + d + D - 1;
-        load_block<FMT>(buf[(d + D - 1) % D], p, bh, nxt < last ? nxt : last, lane);
-        if (i + d < nb) process_block<FMT>(buf[d], stage, ws, qf, bk_static, li, lane);
-      }
-    }
-  }
-
-  // ---- finish this wavefront: sum over quarters, hi + lo columns
+// Sums over quarters and hi + lo columns, then writes one partial slot:
+// m, l, o[128] per query head (o unnormalised).
+__device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneInfo& li, float* slot, float oscale,
+                                               bool has_z) {
   const float l = rows_sum(ws.l);
   float zs[4] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (!T::kFp8) {
+  if (has_z) {
     const float z0 = rows_sum(ws.z[0]), z1 = rows_sum(ws.z[1]);
     // hi columns hold groups 0, 1; their lo partners (lane + 8) groups 2, 3
     zs[0] = z0; zs[1] = z1; zs[2] = ror8(z0); zs[3] = ror8(z1);
   }
-  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
-  __syncthreads();                                   // staging area is reused below
-  float* cm = ldsf + wave * 8 * 130;                 // [head][m, l, o[128]]
-  const bool writer = !li.is_lo && valid_head;
+  float* dst = slot + li.head * kPartStride;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float o = (ws.o[m][i] + ror8(ws.o[m][i])) * oscale - zs[m >> 1];
-      if (writer) cm[head * 130 + 2 + 16 * m + 4 * li.qd + i] = o;
-    }
+    float4 o;
+    o.x = (ws.o[m][0] + ror8(ws.o[m][0])) * oscale - zs[m >> 1];
+    o.y = (ws.o[m][1] + ror8(ws.o[m][1])) * oscale - zs[m >> 1];
+    o.z = (ws.o[m][2] + ror8(ws.o[m][2])) * oscale - zs[m >> 1];
+    o.w = (ws.o[m][3] + ror8(ws.o[m][3])) * oscale - zs[m >> 1];
+    if (li.writer) *reinterpret_cast<float4*>(dst + 4 + 16 * m + 4 * li.qd) = o;
   }
-  if (writer && li.qd == 0) {
-    cm[head * 130] = ws.m;
-    cm[head * 130 + 1] = l;
-  }
-  __syncthreads();
-
-  // ---- combine the four wavefronts and write this split's partials
-  for (int e = tid; e < p.nrep * kHeadDim; e += 256) {
-    const int h = e >> 7, c = e & 127;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < kWavesPerSplit; ++w) M = fmaxf(M, ldsf[w * 8 * 130 + h * 130]);
-    float L = 0.f, O = 0.f;
-    if (M != neg_inf()) {
-#pragma unroll
-      for (int w = 0; w < kWavesPerSplit; ++w) {
-        const float mw = ldsf[w * 8 * 130 + h * 130];
-        if (mw != neg_inf()) {
-          const float f = exp2f(mw - M);
-          L = __builtin_fmaf(f, ldsf[w * 8 * 130 + h * 130 + 1], L);
-          O = __builtin_fmaf(f, ldsf[w * 8 * 130 + h * 130 + 2 + c], O);
-        }
-      }
-    }
-    float* dst = p.part + ((bh * p.nsplit + split + 1) * p.nrep + h) * kPartStride;
-    dst[4 + c] = O;
-    if (c == 0) {
-      dst[0] = M;
-      dst[1] = L;
-    }
+  if (li.writer && li.qd == 0) {
+    dst[0] = ws.m;
+    dst[1] = l;
   }
 }
 
-// fp16 segment: sink tokens and the residual ring, plain fp32 arithmetic.
-__device__ void fp16_segment(const AttnParams& p, int b, int g, char* lds) {
-  const int tid = threadIdx.x;
-  const int hh = tid >> 5;            // query head of the group
-  const int c4 = tid & 31;            // channels 4*c4 .. 4*c4+3
-  float* qs = reinterpret_cast<float*>(lds);                                  // [8][128]
-  uint16_t* kc = reinterpret_cast<uint16_t*>(lds + 8 * 128 * 4);              // [32][130]
-  uint16_t* vc = kc + kSegChunk * kSegKStride;                                // [32][128]
-  float* lgs = reinterpret_cast<float*>(vc + kSegChunk * 128);                // [8][32]
-  const int64_t bh = (int64_t)b * p.hkv + g;
-  if (hh < p.nrep) {
-    const uint16_t* qsrc = p.q + (bh * p.nrep + hh) * kHeadDim + 4 * c4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qs[hh * 128 + 4 * c4 + j] = (float)__builtin_bit_cast(_Float16, qsrc[j]) * kQScale;
-  }
-  float m = neg_inf(), l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-  const int nt = p.n_sink + p.n_res;
-  for (int base = 0; base < nt; base += kSegChunk) {
-    __syncthreads();
-    for (int e = tid; e < kSegChunk * 16; e += 256) {
-      const int t = e >> 4, c8 = (e & 15) * 8;
-      const int k = base + t;
-      uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (k < nt) {
-        const uint16_t* kp;
-        const uint16_t* vp;
-        if (k < p.n_sink) {
-          const int64_t s_off = (bh * (int64_t)p.sink_cap + k) * kHeadDim + c8;
-          kp = p.k_sink + s_off;
-          vp = p.v_sink + s_off;
-        } else {
-          const int slot = (p.ring_first + (k - p.n_sink)) % p.ring_slots;
-          const int64_t r_off = (bh * p.ring_slots + slot) * kHeadDim + c8;
-          kp = p.k_ring + r_off;
-          vp = p.v_ring + r_off;
-        }
-        kk = *reinterpret_cast<const uint4*>(kp);
-        vv = *reinterpret_cast<const uint4*>(vp);
-      }
-      uint32_t* kd = reinterpret_cast<uint32_t*>(kc + t * kSegKStride + c8);
-      kd[0] = kk.x; kd[1] = kk.y; kd[2] = kk.z; kd[3] = kk.w;
-      *reinterpret_cast<uint4*>(vc + t * 128 + c8) = vv;
-    }
-    __syncthreads();
-    {
-      const int t = tid & 31;                 // token of the chunk
-      if (hh < p.nrep) {
-        float acc = 0.f;
-        if (base + t < nt) {
-          for (int c = 0; c < kHeadDim; ++c)
-            acc = __builtin_fmaf(qs[hh * 128 + c], (float)__builtin_bit_cast(_Float16, kc[t * kSegKStride + c]),
-                                 acc);
-        }
-        lgs[hh * kSegChunk + t] = (base + t < nt) ? acc : neg_inf();
-      }
-    }
-    __syncthreads();
-    if (hh < p.nrep) {
-      float cmax = neg_inf();
-      for (int t = 0; t < kSegChunk; ++t) cmax = fmaxf(cmax, lgs[hh * kSegChunk + t]);
-      const float m_new = fmaxf(m, cmax);
-      const float alpha = exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] *= alpha;
-      m = m_new;
-      for (int t = 0; t < kSegChunk; ++t) {
-        const float pt = exp2f(lgs[hh * kSegChunk + t] - m);
-        l += pt;
-        const uint2 vw = *reinterpret_cast<const uint2*>(vc + t * 128 + 4 * c4);
-        o[0] = __builtin_fmaf(pt, (float)u2h(vw.x)[0], o[0]);
-        o[1] = __builtin_fmaf(pt, (float)u2h(vw.x)[1], o[1]);
-        o[2] = __builtin_fmaf(pt, (float)u2h(vw.y)[0], o[2]);
-        o[3] = __builtin_fmaf(pt, (float)u2h(vw.y)[1], o[3]);
-      }
-    }
-  }
-  if (hh < p.nrep) {
-    float* dst = p.part + ((bh * p.nsplit + 0) * p.nrep + hh) * kPartStride;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[4 + 4 * c4 + j] = o[j];
-    if (c4 == 0) {
-      dst[0] = m;
-      dst[1] = l;
-    }
-  }
-}
-
+// A body wavefront: the flattened quantized blocks [w*L, (w+1)*L) of all
+// heads, kDepth blocks in flight while one is processed.  Prefetches past the
+// range re-read its last block (always in bounds), so the loads need no
+// branch and the waits stay static.
 template <int FMT>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+__device__ void body_wave(const AttnParams& p, int64_t w, float* stage) {
+  using T = Traits<FMT>;
+  constexpr int D = T::kDepth + 1;
+  const LaneInfo li = lane_info(p.nrep);
+  const int64_t nblk = p.nblk;
+  const int64_t total = (int64_t)p.bh_count * nblk;
+  const int64_t j0 = w * p.body_per_wave;
+  const int64_t cnt = (total - j0 < p.body_per_wave) ? total - j0 : p.body_per_wave;
+  float* part_body = p.part + ((int64_t)p.bh_count * p.fp16_waves_per_head + w) * (int64_t)p.nrep * kPartStride;
+  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
+
+  // processing and prefetch cursors (head, block), all wave-uniform
+  int64_t cur = j0 / nblk;
+  int64_t pbh = cur, pblk = j0 - cur * nblk;
+  int64_t fbh = pbh, fblk = pblk, lbh = pbh, lblk = pblk, issued = 0;
+  auto next_fetch = [&](int64_t& bh, int64_t& blk) {
+    if (issued < cnt) {
+      lbh = fbh; lblk = fblk; ++issued;
+      if (++fblk == nblk) { fblk = 0; ++fbh; }
+    }
+    bh = lbh; blk = lblk;
+  };
+
+  float qf[32];
+  f16x8 bk_static[4];
+  load_query(p, cur, li, qf);
+  if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
+  WaveState ws;
+  reset(ws);
+
+  Raw<FMT> buf[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    int64_t bh, blk;
+    next_fetch(bh, blk);
+    load_block<FMT>(buf[d], p, bh, blk, li.lane);
+  }
+  for (int64_t i = 0; i < cnt; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      {
+        int64_t bh, blk;
+        next_fetch(bh, blk);
+        load_block<FMT>(buf[(d + D - 1) % D], p, bh, blk, li.lane);
+      }
+      if (i + d < cnt) {
+        if (pbh != cur) {                      // the range crossed into the next head
+          finish_segment(ws, li, part_body + cur * p.nrep * kPartStride, oscale, !T::kFp8);
+          reset(ws);
+          cur = pbh;
+          load_query(p, cur, li, qf);
+          if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
+        }
+        process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
+        if (++pblk == nblk) { pblk = 0; ++pbh; }
+      }
+    }
+  }
+  finish_segment(ws, li, part_body + cur * p.nrep * kPartStride, oscale, !T::kFp8);
+}
+
+// fp16 segment: sink tokens then the residual ring, in blocks of 32 tokens.
+// Keys feed the matrix cores straight from their rows; Values are transposed
+// through LDS into the (channel, 8 tokens) operand order.
+constexpr int kSegVStride = 136;     // halves per staged Value row (16-byte aligned)
+
+__device__ __forceinline__ const uint16_t* seg_row(const AttnParams& p, const uint16_t* sink,
+                                                   const uint16_t* ring, int64_t bh, int k) {
+  if (k < p.n_sink) return sink + (bh * p.sink_cap + k) * kHeadDim;
+  const int slot = (p.ring_first + (k - p.n_sink)) % p.ring_slots;
+  return ring + (bh * p.ring_slots + slot) * kHeadDim;
+}
+
+__device__ void fp16_wave(const AttnParams& p, int64_t bh, int f, uint16_t* vt) {
+  const LaneInfo li = lane_info(p.nrep);
+  const int lane = li.lane;
+  const int nt = p.n_sink + p.n_res;
+  float qf[32];
+  f16x8 bk[4];
+  load_query(p, bh, li, qf);
+  static_q<KVQ_INT8>(qf, 1.0f, li, bk);                 // natural channel order, scale 1
+  WaveState ws;
+  reset(ws);
+  const int fb_end = (f + 1) * p.fp16_per_wave < p.fp16_blocks ? (f + 1) * p.fp16_per_wave : p.fp16_blocks;
+  for (int fb = f * p.fp16_per_wave; fb < fb_end; ++fb) {
+    // Key rows of this lane's two tokens (one per 16-token tile), its quarter's 32 channels
+    uint4 kr[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      int k = 32 * fb + 16 * tile + (lane & 15);
+      k = k < nt ? k : nt - 1;                         // masked below; any valid row keeps values finite
+      const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.k_sink, p.k_ring, bh, k) + 32 * li.qd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[tile][i] = src[i];
+    }
+    // Value row of token lane % 32, channel half lane / 32, into LDS
+    {
+      int k = 32 * fb + (lane & 31);
+      k = k < nt ? k : nt - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.v_sink, p.v_ring, bh, k) + 64 * (lane >> 5));
+      uint4* dst = reinterpret_cast<uint4*>(vt + (lane & 31) * kSegVStride + 64 * (lane >> 5));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = src[i];
+    }
+    f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const uint4 w = kr[tile][kb];
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(w.x, w.y, w.z, w.w), bk[kb], acc[tile], 0, 0, 0);
+      }
+    float lg[2][4], pr[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = 32 * fb + 16 * tile + 4 * li.qd + i;
+        const float x = acc[tile][i] + ror8(acc[tile][i]);
+        lg[tile][i] = k < nt ? x : neg_inf();
+      }
+    softmax_block(lg, ws, pr, kSlack);
+    const f16x8 bp = p_operand(pr, li);
+    __syncthreads();                                    // staged Value rows visible to every lane
+    const int r = lane & 15;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      // channel 16m + r of tokens T0, T4, T1, T5, T2, T6, T3, T7 (T = 4qd + 0..3, 16 + 4qd + 0..3)
+      f16x8 a;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        a[2 * v] = __builtin_bit_cast(_Float16, vt[(4 * li.qd + v) * kSegVStride + 16 * m + r]);
+        a[2 * v + 1] = __builtin_bit_cast(_Float16, vt[(16 + 4 * li.qd + v) * kSegVStride + 16 * m + r]);
+      }
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, ws.o[m], 0, 0, 0);
+    }
+    __syncthreads();                                    // before the next block overwrites the rows
+  }
+  float* slot = p.part + (bh * p.fp16_waves_per_head + f) * (int64_t)p.nrep * kPartStride;
+  finish_segment(ws, li, slot, 1.0f, false);
+}
+
+constexpr int kLdsBytes = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
+
+// One wavefront per workgroup: the fp16 wavefronts first (bh_count *
+// fp16_waves_per_head of them), then the body wavefronts.
+template <int FMT>
+__global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int g = blockIdx.y, b = blockIdx.z;
-  if (blockIdx.x == 0) {
-    fp16_segment(p, b, g, lds);
+  const int64_t wid = blockIdx.x;
+  const int64_t nf = (int64_t)p.bh_count * p.fp16_waves_per_head;
+  if (wid < nf) {
+    fp16_wave(p, wid / p.fp16_waves_per_head, (int)(wid % p.fp16_waves_per_head), reinterpret_cast<uint16_t*>(lds));
   } else {
-    body_split<FMT>(p, b, g, blockIdx.x - 1, lds);
+    body_wave<FMT>(p, wid - nf, reinterpret_cast<float*>(lds));
   }
 }
 
 constexpr int kReduceThreads = 128;
 constexpr int kReduceLdsSplits = 4096;
 
-// out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s
+// out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s,
+// over the head's fp16 slots and body slots.
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) {
   __shared__ float wts[kReduceLdsSplits];
   __shared__ float red[2][kReduceThreads / 64];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int lane = c & 63, wave = c >> 6;
   const int g = hq / p.nrep, hh = hq % p.nrep;
-  const int64_t stride = (int64_t)p.nrep * kPartStride;
-  const float* base = p.part + (((int64_t)b * p.hkv + g) * p.nsplit * p.nrep + hh) * kPartStride;
-  // the maximum over splits, one split per thread
+  const int64_t bh = (int64_t)b * p.hkv + g;
+  const int nf = p.fp16_waves_per_head;
+  int64_t wf = 0, nbody = 0;
+  if (p.nblk > 0) {
+    wf = bh * p.nblk / p.body_per_wave;
+    nbody = ((bh + 1) * p.nblk - 1) / p.body_per_wave - wf + 1;
+  }
+  const int ns = nf + (int)nbody;
+  const int64_t fslots = (int64_t)p.bh_count * nf;
+  auto slot_ptr = [&](int s) -> const float* {
+    const int64_t slot = s < nf ? bh * nf + s : fslots + wf + (s - nf) + bh;
+    return p.part + (slot * p.nrep + hh) * kPartStride;
+  };
   float M = neg_inf();
-  for (int s = c; s < p.nsplit; s += kReduceThreads) M = fmaxf(M, base[s * stride]);
+  for (int s = c; s < ns; s += kReduceThreads) M = fmaxf(M, slot_ptr(s)[0]);
   for (int off = 32; off; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   if (lane == 0) red[0][wave] = M;
   __syncthreads();
   M = red[0][0];
 #pragma unroll
   for (int w = 1; w < kReduceThreads / 64; ++w) M = fmaxf(M, red[0][w]);
-  // split weights 2^(m_s - M) and the denominator
   float L = 0.f;
-  for (int s = c; s < p.nsplit; s += kReduceThreads) {
-    const float ms = base[s * stride];
+  for (int s = c; s < ns; s += kReduceThreads) {
+    const float* ps = slot_ptr(s);
+    const float ms = ps[0];
     const float wgt = ms == neg_inf() ? 0.f : exp2f(ms - M);
     if (s < kReduceLdsSplits) wts[s] = wgt;
-    L = __builtin_fmaf(wgt, base[s * stride + 1], L);
+    L = __builtin_fmaf(wgt, ps[1], L);
   }
   for (int off = 32; off; off >>= 1) L += __shfl_xor(L, off, 64);
   if (lane == 0) red[1][wave] = L;
@@ -654,45 +710,29 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) 
   L = 0.f;
 #pragma unroll
   for (int w = 0; w < kReduceThreads / 64; ++w) L += red[1][w];
-  // this thread's channel: independent loads, eight splits at a time
+  auto weight = [&](int s) -> float {
+    if (s < kReduceLdsSplits) return wts[s];
+    const float ms = slot_ptr(s)[0];
+    return ms == neg_inf() ? 0.f : exp2f(ms - M);
+  };
   float O = 0.f;
-  const float* oc = base + 4 + c;
   int s = 0;
-  for (; s + 8 <= p.nsplit; s += 8) {
-    float v[8], w8[8];
+  for (; s + 8 <= ns; s += 8) {
+    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = oc[(s + j) * stride];
+    for (int j = 0; j < 8; ++j) v[j] = slot_ptr(s + j)[4 + c];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sj = s + j;
-      if (sj < kReduceLdsSplits) {
-        w8[j] = wts[sj];
-      } else {
-        const float ms = base[sj * stride];
-        w8[j] = ms == neg_inf() ? 0.f : exp2f(ms - M);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) O = __builtin_fmaf(w8[j], v[j], O);
+    for (int j = 0; j < 8; ++j) O = __builtin_fmaf(weight(s + j), v[j], O);
   }
-  for (; s < p.nsplit; ++s) {
-    float wgt;
-    if (s < kReduceLdsSplits) {
-      wgt = wts[s];
-    } else {
-      const float ms = base[s * stride];
-      wgt = ms == neg_inf() ? 0.f : exp2f(ms - M);
-    }
-    O = __builtin_fmaf(wgt, oc[s * stride], O);
-  }
+  for (; s < ns; ++s) O = __builtin_fmaf(weight(s), slot_ptr(s)[4 + c], O);
   const _Float16 r = (_Float16)(O / L);
   p.out[((int64_t)b * p.hkv * p.nrep + hq) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
 }
 
 }  // namespace
 
-hipError_t launch_attention(int fmt, const AttnParams& p, int batch, hipStream_t s) {
-  const dim3 grid(p.nsplit, p.hkv, batch), block(256);
+hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStream_t s) {
+  const dim3 grid((unsigned)waves), block(64);
   switch (fmt) {
     case KVQ_INT8: hipLaunchKernelGGL(attn_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(attn_kernel<KVQ_INT4>, grid, block, 0, s, p); break;

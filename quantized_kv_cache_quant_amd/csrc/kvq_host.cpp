@@ -54,19 +54,47 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
 }
 
-int32_t choose_blocks_per_wave(const kvq_cache& c, int64_t nblk) {
-  // Aim for about 2048 body workgroups (8 per CU on 256 CUs): enough to fill
-  // the chip several times over while keeping the split-K partials small.
-  const int64_t total = (int64_t)c.layout.batch * c.layout.num_kv_heads * nblk;
-  int64_t bpw = (total + (int64_t)kWavesPerSplit * 2048 - 1) / ((int64_t)kWavesPerSplit * 2048);
-  if (bpw < 1) bpw = 1;
-  if (bpw > 16) bpw = 16;
-  return (int32_t)bpw;
+// Wavefronts one resident round can hold: 2 per SIMD x 4 SIMDs per CU (the
+// attention kernel uses at most 256 VGPRs).
+int64_t resident_waves() {
+  static int64_t waves = 0;
+  if (waves == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    waves = 8LL * cus;
+  }
+  return waves;
 }
 
-int32_t body_splits(int64_t nblk, int32_t bpw) {
-  const int64_t per = (int64_t)bpw * kWavesPerSplit;
-  return (int32_t)((nblk + per - 1) / per);
+struct AttnPlan {
+  int64_t blocks_per_wave, body_waves, fp16_blocks, fp16_waves_per_head, slots;
+};
+
+// Split the work: fp16 wavefronts take up to kFp16BlocksPerWave blocks of a
+// head's fp16 segment; the body wavefronts share the quantized blocks
+// equally, one resident round of them unless blocks_per_wave is given.
+AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpw) {
+  AttnPlan a{};
+  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
+  a.fp16_blocks = (n_fp16_tokens + kBlock - 1) / kBlock;
+  a.fp16_waves_per_head = (a.fp16_blocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
+  const int64_t total = bh * nblk;
+  if (bpw > 0) {
+    a.blocks_per_wave = bpw;
+  } else {
+    int64_t target = resident_waves() - bh * a.fp16_waves_per_head;
+    if (target < 256) target = 256;
+    a.blocks_per_wave = total > 0 ? (total + target - 1) / target : 1;
+  }
+  a.body_waves = total > 0 ? (total + a.blocks_per_wave - 1) / a.blocks_per_wave : 0;
+  a.slots = bh * a.fp16_waves_per_head + (total > 0 ? a.body_waves + bh : 0);
+  return a;
+}
+
+uint64_t slot_bytes(const kvq_layout& L) {
+  return (uint64_t)(L.num_q_heads / L.num_kv_heads) * kPartStride * sizeof(float);
 }
 
 }  // namespace
@@ -234,13 +262,21 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
 
 int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpw, uint64_t* bytes) {
   if (!c || !bytes) return KVQ_ERR_NULL;
-  if (bpw < 0 || bpw > 16) return KVQ_ERR_LAYOUT;
+  if (bpw < 0 || bpw > kMaxBlocksPerWave) return KVQ_ERR_LAYOUT;
   const kvq_layout& L = c->layout;
-  // the library's own choice never uses fewer blocks per wave than 1
-  const int32_t b = bpw == 0 ? 1 : bpw;
-  const uint64_t nsplit = 1 + (uint64_t)body_splits(c->n_blocks_cap, b);
-  *bytes = (uint64_t)L.batch * L.num_kv_heads * nsplit * (L.num_q_heads / L.num_kv_heads) *
-           kPartStride * sizeof(float);
+  const uint64_t bh = (uint64_t)L.batch * L.num_kv_heads;
+  // worst case over every cache length: all NB blocks quantized, the largest
+  // fp16 segment (S sinks + R + 31 residual tokens), and for the library's
+  // own choice at most one resident round of body wavefronts
+  const uint64_t total = bh * (uint64_t)c->n_blocks_cap;
+  const uint64_t fblocks = ((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock;
+  const uint64_t fwaves = (fblocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
+  uint64_t body = bpw > 0 ? (total + bpw - 1) / bpw : total;
+  if (bpw == 0 && total > 0) {
+    uint64_t cap = 8ull * 1024 * 256;          // any device: at most 1024 CUs, 8 wavefronts per CU
+    if (body > cap) body = cap;
+  }
+  *bytes = (bh * fwaves + (total > 0 ? body + bh : 0)) * slot_bytes(L);
   return KVQ_OK;
 }
 
@@ -250,18 +286,26 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   const kvq_layout& L = c->layout;
   int32_t st = kvq_layout_validate(&L);
   if (st != KVQ_OK) return st;
-  if (bpw < 0 || bpw > 16) return KVQ_ERR_LAYOUT;
+  if (bpw < 0 || bpw > kMaxBlocksPerWave) return KVQ_ERR_LAYOUT;
   if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
   if (c->n_tokens == 0) return KVQ_ERR_EMPTY;
   const Window w = window(L, c->n_tokens);
   const int64_t nblk = w.n_q / kBlock;
-  const int32_t b = bpw == 0 ? choose_blocks_per_wave(*c, nblk) : bpw;
-  const int32_t nsplit = 1 + body_splits(nblk, b);
-  const uint64_t need = (uint64_t)L.batch * L.num_kv_heads * nsplit *
-                        (L.num_q_heads / L.num_kv_heads) * kPartStride * sizeof(float);
-  if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  // workspace is checked before anything touches the device
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
+  const int64_t fblocks = (w.n_sink + w.r + kBlock - 1) / kBlock;
+  const int64_t fwaves = (fblocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
+  if (bpw > 0) {
+    const int64_t total = bh * nblk;
+    const int64_t body = total > 0 ? (total + bpw - 1) / bpw : 0;
+    if ((uint64_t)(bh * fwaves + (total > 0 ? body + bh : 0)) * slot_bytes(L) > ws_bytes) return KVQ_ERR_WORKSPACE;
+  }
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
-  if (nsplit > 0x7fff) return KVQ_ERR_UNSUPPORTED;
+  const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpw);
+  if ((uint64_t)a.slots * slot_bytes(L) > ws_bytes) return KVQ_ERR_WORKSPACE;
+  const int64_t waves = bh * a.fp16_waves_per_head + a.body_waves;
+  if (waves > 0x7fffffffLL || a.fp16_waves_per_head > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
 
   char* base = static_cast<char*>(c->base);
   auto plane = [&](int i) { return base + c->plane_off[i]; };
@@ -285,18 +329,25 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.n_sink = (int32_t)w.n_sink;
   p.n_res = (int32_t)w.r;
   p.ring_first = (int32_t)(w.n_q % c->ring_slots);
-  p.blocks_per_wave = b;
-  p.nsplit = nsplit;
+  p.bh_count = (int32_t)bh;
+  p.body_per_wave = (int32_t)a.blocks_per_wave;
+  p.body_waves = (int32_t)a.body_waves;
+  p.fp16_blocks = (int32_t)a.fp16_blocks;
+  p.fp16_per_wave = kFp16BlocksPerWave;
+  p.fp16_waves_per_head = (int32_t)a.fp16_waves_per_head;
   p.k_scale = L.k_scale;
   p.v_scale = L.v_scale;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (launch_attention(L.format, p, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_attention(L.format, p, waves, s) != hipSuccess) return KVQ_ERR_HIP;
   ReduceParams rp{};
   rp.part = p.part;
   rp.out = static_cast<uint16_t*>(out);
   rp.hkv = p.hkv;
   rp.nrep = p.nrep;
-  rp.nsplit = nsplit;
+  rp.nblk = p.nblk;
+  rp.body_per_wave = p.body_per_wave;
+  rp.fp16_waves_per_head = p.fp16_waves_per_head;
+  rp.bh_count = p.bh_count;
   if (launch_reduce(rp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }

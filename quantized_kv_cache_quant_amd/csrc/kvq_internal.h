@@ -14,7 +14,8 @@ constexpr int kHeadDim = 128;     // the only head_dim of this version
 constexpr int kVGroup = 32;       // channels per Value group
 constexpr int kVGroups = kHeadDim / kVGroup;
 constexpr int kPartStride = 132;  // floats per partial: m, l, 2 pad, o[128]
-constexpr int kWavesPerSplit = 4;
+constexpr int kMaxBlocksPerWave = 1024;
+constexpr int kFp16BlocksPerWave = 8;
 
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
@@ -55,6 +56,12 @@ hipError_t launch_flush(int fmt, const FlushParams& p, int n_blocks, int batch, 
 hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 
 // ------------------------------------------------------------- attention
+// Partial results: kPartStride floats per query head, n_rep heads per slot.
+//   fp16 region  slot bh * fp16_waves_per_head + f   (f-th fp16 wavefront of head bh)
+//   body region  slot fp16_slots + w + bh            (body wavefront w's share of head bh)
+// A body wavefront w streams the flattened quantized blocks [w*L, (w+1)*L) of
+// all heads (head-major), so head bh is covered by the wavefronts
+// floor(bh*nblk/L) .. floor(((bh+1)*nblk - 1)/L) and w + bh never collides.
 struct AttnParams {
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -65,28 +72,32 @@ struct AttnParams {
   const uint16_t* k_sink;
   const uint16_t* v_sink;
   const uint16_t* q;      // fp16 [B][Hq][D]
-  float* part;            // [B][Hkv][nsplit][NR][kPartStride]
+  float* part;            // partial slots (see above)
   int32_t hkv;
   int32_t nrep;           // NR = Hq / Hkv (1, 2, 4 or 8)
   int32_t nb_cap;         // NB (block stride of the code / meta planes)
-  int32_t nblk;           // quantized blocks currently held (n_q / 32)
+  int32_t nblk;           // quantized blocks currently held per head (n_q / 32)
   int32_t ring_slots;
   int32_t sink_cap;       // S of the layout (row stride of the sink planes)
   int32_t n_sink;         // sink tokens held
   int32_t n_res;          // residual tokens held
   int32_t ring_first;     // ring slot of the oldest residual token (n_q mod RS)
-  int32_t blocks_per_wave;
-  int32_t nsplit;         // 1 (fp16 segment) + body splits
+  int32_t bh_count;       // B * Hkv
+  int32_t body_per_wave;  // L: quantized blocks per body wavefront
+  int32_t body_waves;     // ceil(bh_count * nblk / L)
+  int32_t fp16_blocks;    // ceil((n_sink + n_res) / 32) per head
+  int32_t fp16_per_wave;  // fp16 blocks per fp16 wavefront
+  int32_t fp16_waves_per_head;
   float k_scale, v_scale; // FP8
 };
 
 struct ReduceParams {
   const float* part;
   uint16_t* out;          // fp16 [B][Hq][D]
-  int32_t hkv, nrep, nsplit;
+  int32_t hkv, nrep, nblk, body_per_wave, fp16_waves_per_head, bh_count;
 };
 
-hipError_t launch_attention(int fmt, const AttnParams& p, int batch, hipStream_t s);
+hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s);
 
 }  // namespace kvq

@@ -145,20 +145,29 @@ def test_attention_errors():
     lay, h = _cache(max_tokens=2000)
     need = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 0, ctypes.byref(need)) == 0
-    nb = (2000 - 4 - 32) // 32
-    assert need.value == 2 * 2 * (1 + (nb + 3) // 4) * 4 * 132 * 4
-    assert L.kvq_workspace_bytes(ctypes.byref(h), 17, ctypes.byref(need)) == -2
+    # slots: one per fp16 wavefront of each head (ceil((S + R + 31) / 32) blocks, 8 per
+    # wavefront) plus, for the quantized blocks, one per body wavefront and one per head
+    bh, nb = 4, (2000 - 4 - 32) // 32
+    fwaves = -(-(-(-(4 + 32 + 31) // 32)) // 8)
+    assert need.value == (bh * fwaves + bh * nb + bh) * 4 * 132 * 4
+    assert L.kvq_workspace_bytes(ctypes.byref(h), 1025, ctypes.byref(need)) == -2
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == -8  # empty
     h.n_tokens = 1500
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 16, None) == -6
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), None, 1 << 30, None) == -6
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE + 2), P(FAKE), P(FAKE), 1 << 30, None) == -5
     assert L.kv_decode_attention(ctypes.byref(h), None, P(FAKE), P(FAKE), 1 << 30, None) == -1
-    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 17, None) == -2
-    # the library's default split never needs more than blocks_per_wave = 1
-    for n in (1, 37, 1500, 2000):
-        h.n_tokens = n
-        for bpw in range(1, 17):
-            w = ctypes.c_uint64()
-            assert L.kvq_workspace_bytes(ctypes.byref(h), bpw, ctypes.byref(w)) == 0
-            assert w.value <= need.value if bpw >= 1 else True
+    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 1025, None) == -2
+    # an explicit split needing more than the caller's workspace is refused before any
+    # launch (at full capacity the requirement equals kvq_workspace_bytes' bound)
+    h.n_tokens = 2000
+    w1 = ctypes.c_uint64()
+    assert L.kvq_workspace_bytes(ctypes.byref(h), 1, ctypes.byref(w1)) == 0
+    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), w1.value - 1, 1, None) == -6
+    # larger blocks per wavefront never need more workspace than smaller ones
+    prev = w1.value
+    for bpw in (2, 3, 7, 16, 1024):
+        w = ctypes.c_uint64()
+        assert L.kvq_workspace_bytes(ctypes.byref(h), bpw, ctypes.byref(w)) == 0
+        assert w.value <= prev
+        prev = w.value

@@ -174,3 +174,24 @@ def test_long_context_layer(fmt):
     """batch 1, 131072 tokens: the two layer formats of the mixed-precision stack."""
     require_gpu()
     _full_size("long_ctx", fmt)
+
+
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8"])
+def test_huge_value_ranges_stay_finite(fmt):
+    """Value scales far above 255 (|V| up to ~6e4): P' = p * s must not overflow f16.
+
+    Outputs are thousands in magnitude and come from cancelling sums of
+    terms near 1e4, so the check is relative to the output scale (the fp16
+    output rounding alone is 2^-11 of it)."""
+    require_gpu()
+    b, hkv, nrep, n = 1, 2, 4, 32 * 12 + 40
+    k, v = synth.kv_tokens(W["llama3_8b"], 21, 22, b, n, hkv, 128)
+    v = np.clip(v.astype(np.float32) * 20000.0, -65504, 65504).astype(np.float16)
+    kw = dict(batch=b, num_kv_heads=hkv, num_q_heads=hkv * nrep, max_tokens=n, fmt=fmt, residual_tokens=32)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [n])
+    q = synth.queries(W["llama3_8b"], b, hkv * nrep, 128)
+    out = attention_gpu(c, q).astype(np.float64)
+    ref = _oracle_out(c, kw, q)
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out - ref)) <= TOL * np.max(np.abs(ref))
