@@ -159,7 +159,10 @@ int32_t kv_quant_append(kvq_cache* cache, const void* K, const void* V, int32_t 
 
 /* Workspace bytes kv_decode_attention_split needs for any n_tokens up to
  * max_tokens with the given blocks_per_wave (0 = the library's choice, which
- * needs no more than blocks_per_wave = 1). */
+ * needs no more than blocks_per_wave = 1): one partial of (4 + 128) floats
+ * per query head for every fp16 wavefront, every body wavefront and every
+ * head.  A larger blocks_per_wave never needs more.  Errors: KVQ_ERR_NULL,
+ * KVQ_ERR_LAYOUT for blocks_per_wave outside [0, 1024]. */
 int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_wave, uint64_t* bytes);
 
 /* Fused-dequant decode attention ("KV Cache Quantization Analysis", sec. 4
@@ -176,10 +179,16 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_wave, uin
 int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream);
 
-/* kv_decode_attention with an explicit token range per split:
- * blocks_per_wave in [1, 16] blocks of 32 quantized tokens per wavefront
- * (four wavefronts per split).  Results agree with every other choice up to
- * fp32 rounding.  0 selects the library's choice. */
+/* kv_decode_attention with an explicit split of the quantized tokens:
+ * blocks_per_wave in [1, 1024] is the number of 32-token quantized blocks
+ * each wavefront streams (the flattened block list of all heads is cut into
+ * equal shares, so a share may cross from one head into the next); 0 selects
+ * the library's choice, about one resident round of wavefronts on the device.
+ * The fp16 segment (sinks + residual ring) is always split into two 32-token
+ * blocks per wavefront.  Results agree with every other choice up to fp32
+ * rounding, and each choice is deterministic.  Errors: KVQ_ERR_LAYOUT for a
+ * blocks_per_wave outside [0, 1024]; KVQ_ERR_WORKSPACE if ws_bytes is below
+ * what this n_tokens and split need (checked before any launch). */
 int32_t kv_decode_attention_split(const kvq_cache* cache, const void* q, void* out, void* ws,
                                   uint64_t ws_bytes, int32_t blocks_per_wave, void* stream);
 

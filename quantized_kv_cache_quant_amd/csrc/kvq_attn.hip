@@ -127,6 +127,21 @@ __device__ __forceinline__ f16x8 cvt_fp8(uint32_t w0, uint32_t w1) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Prefetch depths (blocks in flight besides the one being processed); build
+// knobs for tuning, the defaults keep every format at or under 256 VGPRs.
+#ifndef KVQ_DEPTH_INT8
+#define KVQ_DEPTH_INT8 1
+#endif
+#ifndef KVQ_DEPTH_FP8
+#define KVQ_DEPTH_FP8 2
+#endif
+#ifndef KVQ_DEPTH_INT4
+#define KVQ_DEPTH_INT4 3
+#endif
+#ifndef KVQ_DEPTH_INT2
+#define KVQ_DEPTH_INT2 4
+#endif
+
 template <int FMT>
 struct Traits {
   static constexpr bool kFp8 = FMT == KVQ_FP8_E4M3;
@@ -137,7 +152,7 @@ struct Traits {
   // blocks kept in flight besides the one being processed (bytes in flight
   // per wavefront: INT8 10 KiB, FP8 16 KiB, INT4 18 KiB, INT2 16 KiB; the
   // counts keep every format at or under 256 VGPRs, two wavefronts per SIMD)
-  static constexpr int kDepth = kFp8 ? 2 : (kBits == 8 ? 1 : (kBits == 4 ? 3 : 4));
+  static constexpr int kDepth = kFp8 ? KVQ_DEPTH_FP8 : (kBits == 8 ? KVQ_DEPTH_INT8 : (kBits == 4 ? KVQ_DEPTH_INT4 : KVQ_DEPTH_INT2));
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -665,15 +680,15 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
 }
 
 constexpr int kReduceThreads = 128;
-constexpr int kReduceLdsSplits = 4096;
+constexpr int kReduceRegSlots = 32;       // slots whose output this thread loads at once
 
 // out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s,
-// over the head's fp16 slots and body slots.
+// over the head's fp16 slots and body slots.  All loads of a pass of up to
+// kReduceRegSlots slots are issued together (one memory round trip).
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) {
-  __shared__ float wts[kReduceLdsSplits];
-  __shared__ float red[2][kReduceThreads / 64];
+  __shared__ float wts[kReduceRegSlots];
+  __shared__ float msh[kReduceRegSlots], lsh[kReduceRegSlots];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int lane = c & 63, wave = c >> 6;
   const int g = hq / p.nrep, hh = hq % p.nrep;
   const int64_t bh = (int64_t)b * p.hkv + g;
   const int nf = p.fp16_waves_per_head;
@@ -688,43 +703,36 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) 
     const int64_t slot = s < nf ? bh * nf + s : fslots + wf + (s - nf) + bh;
     return p.part + (slot * p.nrep + hh) * kPartStride;
   };
-  float M = neg_inf();
-  for (int s = c; s < ns; s += kReduceThreads) M = fmaxf(M, slot_ptr(s)[0]);
-  for (int off = 32; off; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  if (lane == 0) red[0][wave] = M;
-  __syncthreads();
-  M = red[0][0];
+  float M = neg_inf(), L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kReduceRegSlots) {
+    const int cnt = ns - s0 < kReduceRegSlots ? ns - s0 : kReduceRegSlots;
+    float v[kReduceRegSlots];
 #pragma unroll
-  for (int w = 1; w < kReduceThreads / 64; ++w) M = fmaxf(M, red[0][w]);
-  float L = 0.f;
-  for (int s = c; s < ns; s += kReduceThreads) {
-    const float* ps = slot_ptr(s);
-    const float ms = ps[0];
-    const float wgt = ms == neg_inf() ? 0.f : exp2f(ms - M);
-    if (s < kReduceLdsSplits) wts[s] = wgt;
-    L = __builtin_fmaf(wgt, ps[1], L);
+    for (int j = 0; j < kReduceRegSlots; ++j) v[j] = j < cnt ? slot_ptr(s0 + j)[4 + c] : 0.f;
+    if (c < cnt) {
+      msh[c] = slot_ptr(s0 + c)[0];
+      lsh[c] = slot_ptr(s0 + c)[1];
+    }
+    __syncthreads();
+    float Mn = M;
+    for (int j = 0; j < cnt; ++j) Mn = fmaxf(Mn, msh[j]);
+    if (Mn != neg_inf()) {                       // rescale what earlier passes summed
+      const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
+      L *= a;
+      O *= a;
+    }
+    M = Mn;
+    if (c < cnt) wts[c] = msh[c] == neg_inf() ? 0.f : exp2f(msh[c] - M);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kReduceRegSlots; ++j) {
+      if (j < cnt) {
+        L = __builtin_fmaf(wts[j], lsh[j], L);
+        O = __builtin_fmaf(wts[j], v[j], O);
+      }
+    }
+    __syncthreads();
   }
-  for (int off = 32; off; off >>= 1) L += __shfl_xor(L, off, 64);
-  if (lane == 0) red[1][wave] = L;
-  __syncthreads();
-  L = 0.f;
-#pragma unroll
-  for (int w = 0; w < kReduceThreads / 64; ++w) L += red[1][w];
-  auto weight = [&](int s) -> float {
-    if (s < kReduceLdsSplits) return wts[s];
-    const float ms = slot_ptr(s)[0];
-    return ms == neg_inf() ? 0.f : exp2f(ms - M);
-  };
-  float O = 0.f;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = slot_ptr(s + j)[4 + c];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) O = __builtin_fmaf(weight(s + j), v[j], O);
-  }
-  for (; s < ns; ++s) O = __builtin_fmaf(weight(s), slot_ptr(s)[4 + c], O);
   const _Float16 r = (_Float16)(O / L);
   p.out[((int64_t)b * p.hkv * p.nrep + hq) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
 }
@@ -741,6 +749,23 @@ hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStre
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+int attention_waves_per_cu(int fmt) {
+  static int cached[4] = {0, 0, 0, 0};
+  if (fmt < 0 || fmt > 3) return 0;
+  if (cached[fmt] == 0) {
+    int blocks = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (fmt) {
+      case KVQ_INT8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT8>, 64, 0); break;
+      case KVQ_INT4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT4>, 64, 0); break;
+      case KVQ_INT2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT2>, 64, 0); break;
+      default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_FP8_E4M3>, 64, 0); break;
+    }
+    cached[fmt] = (e == hipSuccess && blocks > 0) ? blocks : 8;
+  }
+  return cached[fmt];
 }
 
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s) {

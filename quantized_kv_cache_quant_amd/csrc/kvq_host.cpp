@@ -54,18 +54,17 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
 }
 
-// Wavefronts one resident round can hold: 2 per SIMD x 4 SIMDs per CU (the
-// attention kernel uses at most 256 VGPRs).
-int64_t resident_waves() {
-  static int64_t waves = 0;
-  if (waves == 0) {
-    int dev = 0, cus = 0;
+// Attention wavefronts one resident round can hold on the current device.
+int64_t resident_waves(int fmt) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    waves = 8LL * cus;
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
   }
-  return waves;
+  return (int64_t)cus * attention_waves_per_cu(fmt);
 }
 
 struct AttnPlan {
@@ -84,8 +83,9 @@ AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t 
   if (bpw > 0) {
     a.blocks_per_wave = bpw;
   } else {
-    int64_t target = resident_waves() - bh * a.fp16_waves_per_head;
-    if (target < 256) target = 256;
+    // the fp16 wavefronts come first in the grid and finish early; the body
+    // wavefronts fill one resident round
+    const int64_t target = resident_waves(L.format);
     a.blocks_per_wave = total > 0 ? (total + target - 1) / target : 1;
   }
   a.body_waves = total > 0 ? (total + a.blocks_per_wave - 1) / a.blocks_per_wave : 0;
@@ -273,7 +273,7 @@ int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpw, uint64_t* bytes) {
   const uint64_t fwaves = (fblocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
   uint64_t body = bpw > 0 ? (total + bpw - 1) / bpw : total;
   if (bpw == 0 && total > 0) {
-    uint64_t cap = 8ull * 1024 * 256;          // any device: at most 1024 CUs, 8 wavefronts per CU
+    uint64_t cap = 32ull * 1024;               // any device: at most 1024 CUs, 32 wavefronts per CU
     if (body > cap) body = cap;
   }
   *bytes = (bh * fwaves + (total > 0 ? body + bh : 0)) * slot_bytes(L);

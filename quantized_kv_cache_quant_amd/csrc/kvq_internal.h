@@ -15,7 +15,7 @@ constexpr int kVGroup = 32;       // channels per Value group
 constexpr int kVGroups = kHeadDim / kVGroup;
 constexpr int kPartStride = 132;  // floats per partial: m, l, 2 pad, o[128]
 constexpr int kMaxBlocksPerWave = 1024;
-constexpr int kFp16BlocksPerWave = 8;
+constexpr int kFp16BlocksPerWave = 2;
 
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
@@ -99,5 +99,7 @@ struct ReduceParams {
 
 hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s);
+// Attention workgroups (one wavefront each) a compute unit holds at once.
+int attention_waves_per_cu(int fmt);
 
 }  // namespace kvq

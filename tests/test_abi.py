@@ -145,10 +145,10 @@ def test_attention_errors():
     lay, h = _cache(max_tokens=2000)
     need = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 0, ctypes.byref(need)) == 0
-    # slots: one per fp16 wavefront of each head (ceil((S + R + 31) / 32) blocks, 8 per
+    # slots: one per fp16 wavefront of each head (ceil((S + R + 31) / 32) blocks, 2 per
     # wavefront) plus, for the quantized blocks, one per body wavefront and one per head
     bh, nb = 4, (2000 - 4 - 32) // 32
-    fwaves = -(-(-(-(4 + 32 + 31) // 32)) // 8)
+    fwaves = -(-(-(-(4 + 32 + 31) // 32)) // 2)
     assert need.value == (bh * fwaves + bh * nb + bh) * 4 * 132 * 4
     assert L.kvq_workspace_bytes(ctypes.byref(h), 1025, ctypes.byref(need)) == -2
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == -8  # empty
@@ -159,11 +159,14 @@ def test_attention_errors():
     assert L.kv_decode_attention(ctypes.byref(h), None, P(FAKE), P(FAKE), 1 << 30, None) == -1
     assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 1025, None) == -2
     # an explicit split needing more than the caller's workspace is refused before any
-    # launch (at full capacity the requirement equals kvq_workspace_bytes' bound)
+    # launch: at n = 2000 there are 61 blocks per head and 4 + 44 fp16 tokens (one fp16
+    # wavefront per head), so blocks_per_wave = 1 needs 4 + 4 * 61 + 4 slots
     h.n_tokens = 2000
+    exact = (4 + 4 * 61 + 4) * 4 * 132 * 4
+    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, None) == -6
     w1 = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 1, ctypes.byref(w1)) == 0
-    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), w1.value - 1, 1, None) == -6
+    assert w1.value >= exact
     # larger blocks per wavefront never need more workspace than smaller ones
     prev = w1.value
     for bpw in (2, 3, 7, 16, 1024):
