@@ -49,7 +49,7 @@ def parse():
                     choices=["llama3_8b", "llama3_8b_kivi2", "llama3_70b", "long_ctx"])
     ap.add_argument("--formats", default=None, help="comma list overriding the workload's formats")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
-    ap.add_argument("--blocks-per-wave", type=int, default=0)
+    ap.add_argument("--blocks-per-group", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -104,7 +104,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         steps_v.append(torch.from_numpy(vs).cuda())
     q = torch.from_numpy(synth.queries(w)).cuda()
     out = torch.empty_like(q)
-    ws = torch.empty(max(c.workspace_bytes(args.blocks_per_wave) for c in caches) // 4 + 4,
+    ws = torch.empty(max(c.workspace_bytes(args.blocks_per_group) for c in caches) // 4 + 4,
                      dtype=torch.float32, device="cuda")
 
     def step(j, ev=None):
@@ -112,7 +112,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
             c.append(steps_k[j], steps_v[j])
             if ev is not None:
                 ev[li][0].record()
-            c.attention(q, out, ws, args.blocks_per_wave)
+            c.attention(q, out, ws, args.blocks_per_group)
             if ev is not None:
                 ev[li][1].record()
 

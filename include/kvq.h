@@ -157,13 +157,14 @@ int32_t kvq_cache_window(const kvq_cache* cache, int64_t* n_sink, int64_t* n_q, 
  * n_tokens + T > max_tokens (nothing enqueued). */
 int32_t kv_quant_append(kvq_cache* cache, const void* K, const void* V, int32_t T, void* stream);
 
-/* Workspace bytes kv_decode_attention_split needs for any n_tokens up to
- * max_tokens with the given blocks_per_wave (0 = the library's choice, which
- * needs no more than blocks_per_wave = 1): one partial of (4 + 128) floats
- * per query head for every fp16 wavefront, every body wavefront and every
- * head.  A larger blocks_per_wave never needs more.  Errors: KVQ_ERR_NULL,
- * KVQ_ERR_LAYOUT for blocks_per_wave outside [0, 1024]. */
-int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_wave, uint64_t* bytes);
+/* Workspace bytes kv_decode_attention_split needs on the current device for
+ * any n_tokens up to max_tokens with the given blocks_per_group (0 = the
+ * library's choice): one partial of (4 + 128) floats per query head for every
+ * fp16 block of 32 tokens, and for every wavefront of every workgroup and
+ * every head its range touches.  A larger blocks_per_group never needs more.
+ * Errors: KVQ_ERR_NULL; KVQ_ERR_LAYOUT for blocks_per_group outside
+ * [0, 2^20]. */
+int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, uint64_t* bytes);
 
 /* Fused-dequant decode attention ("KV Cache Quantization Analysis", sec. 4
  * and sec. 5: dequantization fused into the attention matmuls; "W4A16 + KV
@@ -172,25 +173,32 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_wave, uin
  * For every sequence b and query head h:
  *   out[b][h] = sum_t softmax_t(q[b][h] . k_hat[b][g][t] / sqrt(D)) v_hat[b][g][t]
  * over all n_tokens cached tokens, g = h / (Hq/Hkv), with k_hat, v_hat the
- * dequantized (or fp16) cache entries.  Split-K: a first kernel writes one
- * partial (max, sum, unnormalised output) per token range into ws, a second
- * combines them.  ws: device scratch of >= kvq_workspace_bytes(cache, 0)
- * bytes, overwritten.  Errors: KVQ_ERR_EMPTY if n_tokens == 0. */
+ * dequantized (or fp16) cache entries.  Split-K: a first kernel writes
+ * partials (max, sum, unnormalised output) into ws, a second combines them.
+ * ws: device scratch of >= kvq_workspace_bytes(cache, 0) bytes, overwritten;
+ * calls that share a workspace must be ordered on one stream.  Blocks are
+ * handed to wavefronts as the memory system serves them, so repeated calls
+ * may differ in the last bits (see the deterministic mode below).
+ * Errors: KVQ_ERR_EMPTY if n_tokens == 0. */
 int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream);
 
-/* kv_decode_attention with an explicit split of the quantized tokens:
- * blocks_per_wave in [1, 1024] is the number of 32-token quantized blocks
- * each wavefront streams (the flattened block list of all heads is cut into
- * equal shares, so a share may cross from one head into the next); 0 selects
- * the library's choice, about one resident round of wavefronts on the device.
- * The fp16 segment (sinks + residual ring) is always split into two 32-token
- * blocks per wavefront.  Results agree with every other choice up to fp32
- * rounding, and each choice is deterministic.  Errors: KVQ_ERR_LAYOUT for a
- * blocks_per_wave outside [0, 1024]; KVQ_ERR_WORKSPACE if ws_bytes is below
- * what this n_tokens and split need (checked before any launch). */
+/* kv_decode_attention with an explicit split.  The quantized 32-token blocks
+ * of all heads, flattened head-major, are cut into ranges of blocks_per_group
+ * blocks (a range may cross from one head into the next), one per workgroup
+ * of 8 wavefronts; 0 selects the library's choice, one range per compute
+ * unit.  deterministic = 0: a workgroup's wavefronts take its blocks in the
+ * order they become free; deterministic = 1: wavefront w takes blocks w,
+ * w + 8, w + 16, ... of the range, and repeated calls give identical bits.
+ * The fp16 segment (sinks + residual ring) is handled in 32-token blocks.
+ * Results of every choice agree up to fp32 rounding.  Errors: KVQ_ERR_LAYOUT
+ * for blocks_per_group outside [0, 2^20] or deterministic not 0 or 1;
+ * KVQ_ERR_WORKSPACE if ws_bytes is below what this n_tokens and split need
+ * (checked before any launch); KVQ_ERR_UNSUPPORTED beyond 2^31 - 1
+ * quantized blocks. */
 int32_t kv_decode_attention_split(const kvq_cache* cache, const void* q, void* out, void* ws,
-                                  uint64_t ws_bytes, int32_t blocks_per_wave, void* stream);
+                                  uint64_t ws_bytes, int32_t blocks_per_group, int32_t deterministic,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

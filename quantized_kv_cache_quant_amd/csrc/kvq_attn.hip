@@ -8,17 +8,20 @@
 // s * E4M3 for FP8) or the fp16 sink / residual entries.  Dequantization is
 // fused into the two matrix products, so only packed bytes cross HBM.
 //
-// Work decomposition (one wavefront per 64-thread workgroup):
-//  * fp16 wavefronts handle the fp16 segment (sinks + residual ring) of one
-//    (sequence, KV head), up to fp16_per_wave 32-token blocks each;
-//  * body wavefronts each stream an equal share of the flattened
-//    (head-major) list of quantized 32-token blocks of all heads, keeping
-//    the next kDepth blocks' loads in flight.  A share covers one or two
-//    heads; for every head it touches the wavefront runs an online softmax
-//    for all n_rep query heads of that KV head (GQA: every KV byte is read
-//    once per step) and writes one partial (max, sum, unnormalised output);
-//  * the grid is sized to about one resident round of wavefronts, so no
-//    wavefront waits for another to finish;
+// Work decomposition (workgroups of eight wavefronts, one per compute unit
+// by default):
+//  * the quantized 32-token blocks of all heads, flattened head-major, are
+//    cut into equal ranges, one per workgroup.  The wavefronts of a
+//    workgroup take the blocks of its range from a shared counter in LDS,
+//    each keeping its next kDepth blocks' loads in flight, so wavefronts the
+//    memory system serves faster take more blocks and the workgroup's
+//    wavefronts finish together.  For every head it meets a wavefront runs
+//    an online softmax for all n_rep query heads of that KV head (GQA: every
+//    KV byte is read once per step) and writes one partial (max, sum,
+//    unnormalised output);
+//  * the fp16 segment (sinks + residual ring) of every head is cut into
+//    32-token blocks, spread one per wavefront over the grid and handled
+//    while the wavefront's first quantized blocks load;
 //  * reduce_kernel combines each head's partials in a fixed order.
 //
 // Per 32-token block a wavefront runs both products on the matrix cores with
@@ -307,16 +310,28 @@ __device__ __forceinline__ uint32_t split2z(float a0, float ab0, float b0, float
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Query of head bh (this lane's column head, its quarter's 32 channels), in
-// base-2 logit units; zero in columns of heads past n_rep.
-__device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, float* qf) {
-  const bool valid = li.head < p.nrep;
-  const uint4* qsrc = reinterpret_cast<const uint4*>(p.q + (bh * p.nrep + (valid ? li.head : 0)) * kHeadDim +
-                                                     32 * li.qd);
+// Query operand values of this lane's column head (its quarter's 32
+// channels) from a KV head's n_rep query rows ([n_rep][128] fp16), in
+// base-2 logit units; zero in columns of heads past n_rep.  The raw load and
+// the conversion are separate so the load can be issued early.
+struct QRaw {
+  uint4 w[4];
+};
+
+__device__ __forceinline__ QRaw load_query_raw(const uint16_t* rows, int nrep, const LaneInfo& li) {
+  const bool valid = li.head < nrep;
+  const uint4* qsrc = reinterpret_cast<const uint4*>(rows + (valid ? li.head : 0) * kHeadDim + 32 * li.qd);
+  QRaw r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.w[i] = qsrc[i];
+  return r;
+}
+
+__device__ __forceinline__ void query_operand(const QRaw& r, int nrep, const LaneInfo& li, float* qf) {
+  const bool valid = li.head < nrep;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 w = qsrc[i];
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t wv[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f16x2 h = u2h(wv[j]);
@@ -324,6 +339,11 @@ __device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, cons
       qf[8 * i + 2 * j + 1] = valid ? (float)h[1] * kQScale : 0.f;
     }
   }
+}
+
+// The same from the query rows of KV head bh in global memory.
+__device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, float* qf) {
+  query_operand(load_query_raw(p.q + bh * p.nrep * kHeadDim, p.nrep, li), p.nrep, li, qf);
 }
 
 // Static q operands (hi / lo) for Keys without a per-block scale (FP8 with
@@ -516,75 +536,16 @@ __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneIn
   }
 }
 
-// A body wavefront: the flattened quantized blocks [w*L, (w+1)*L) of all
-// heads, kDepth blocks in flight while one is processed.  Prefetches past the
-// range re-read its last block (always in bounds), so the loads need no
-// branch and the waits stay static.
-template <int FMT>
-__device__ void body_wave(const AttnParams& p, int64_t w, float* stage) {
-  using T = Traits<FMT>;
-  constexpr int D = T::kDepth + 1;
-  const LaneInfo li = lane_info(p.nrep);
-  const int64_t nblk = p.nblk;
-  const int64_t total = (int64_t)p.bh_count * nblk;
-  const int64_t j0 = w * p.body_per_wave;
-  const int64_t cnt = (total - j0 < p.body_per_wave) ? total - j0 : p.body_per_wave;
-  float* part_body = p.part + ((int64_t)p.bh_count * p.fp16_waves_per_head + w) * (int64_t)p.nrep * kPartStride;
-  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
+// Wavefront-local LDS hand-over: the LDS unit serves one wavefront's
+// instructions in order, so once this wavefront's writes have completed its
+// lanes read each other's data; the clobber keeps the compiler from moving
+// LDS accesses across the point.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-  // processing and prefetch cursors (head, block), all wave-uniform
-  int64_t cur = j0 / nblk;
-  int64_t pbh = cur, pblk = j0 - cur * nblk;
-  int64_t fbh = pbh, fblk = pblk, lbh = pbh, lblk = pblk, issued = 0;
-  auto next_fetch = [&](int64_t& bh, int64_t& blk) {
-    if (issued < cnt) {
-      lbh = fbh; lblk = fblk; ++issued;
-      if (++fblk == nblk) { fblk = 0; ++fbh; }
-    }
-    bh = lbh; blk = lblk;
-  };
-
-  float qf[32];
-  f16x8 bk_static[4];
-  load_query(p, cur, li, qf);
-  if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
-  WaveState ws;
-  reset(ws);
-
-  Raw<FMT> buf[D];
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d) {
-    int64_t bh, blk;
-    next_fetch(bh, blk);
-    load_block<FMT>(buf[d], p, bh, blk, li.lane);
-  }
-  for (int64_t i = 0; i < cnt; i += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      {
-        int64_t bh, blk;
-        next_fetch(bh, blk);
-        load_block<FMT>(buf[(d + D - 1) % D], p, bh, blk, li.lane);
-      }
-      if (i + d < cnt) {
-        if (pbh != cur) {                      // the range crossed into the next head
-          finish_segment(ws, li, part_body + cur * p.nrep * kPartStride, oscale, !T::kFp8);
-          reset(ws);
-          cur = pbh;
-          load_query(p, cur, li, qf);
-          if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
-        }
-        process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
-        if (++pblk == nblk) { pblk = 0; ++pbh; }
-      }
-    }
-  }
-  finish_segment(ws, li, part_body + cur * p.nrep * kPartStride, oscale, !T::kFp8);
-}
-
-// fp16 segment: sink tokens then the residual ring, in blocks of 32 tokens.
-// Keys feed the matrix cores straight from their rows; Values are transposed
-// through LDS into the (channel, 8 tokens) operand order.
+// One 32-token block fb of the fp16 segment (sink tokens, then the residual
+// ring) of head bh, into its own partial slot.  Keys feed the matrix cores
+// straight from their rows; Values are transposed through the wavefront's
+// LDS area into the (channel, 8 tokens) operand order.
 constexpr int kSegVStride = 136;     // halves per staged Value row (16-byte aligned)
 
 __device__ __forceinline__ const uint16_t* seg_row(const AttnParams& p, const uint16_t* sink,
@@ -594,7 +555,7 @@ __device__ __forceinline__ const uint16_t* seg_row(const AttnParams& p, const ui
   return ring + (bh * p.ring_slots + slot) * kHeadDim;
 }
 
-__device__ void fp16_wave(const AttnParams& p, int64_t bh, int f, uint16_t* vt) {
+__device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt, float* slot) {
   const LaneInfo li = lane_info(p.nrep);
   const int lane = li.lane;
   const int nt = p.n_sink + p.n_res;
@@ -604,103 +565,242 @@ __device__ void fp16_wave(const AttnParams& p, int64_t bh, int f, uint16_t* vt) 
   static_q<KVQ_INT8>(qf, 1.0f, li, bk);                 // natural channel order, scale 1
   WaveState ws;
   reset(ws);
-  const int fb_end = (f + 1) * p.fp16_per_wave < p.fp16_blocks ? (f + 1) * p.fp16_per_wave : p.fp16_blocks;
-  for (int fb = f * p.fp16_per_wave; fb < fb_end; ++fb) {
-    // Key rows of this lane's two tokens (one per 16-token tile), its quarter's 32 channels
-    uint4 kr[2][4];
+  // Key rows of this lane's two tokens (one per 16-token tile), its quarter's 32 channels
+  uint4 kr[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    int k = 32 * fb + 16 * tile + (lane & 15);
+    k = k < nt ? k : nt - 1;                           // masked below; any valid row keeps values finite
+    const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.k_sink, p.k_ring, bh, k) + 32 * li.qd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[tile][i] = src[i];
+  }
+  // Value row of token lane % 32, channel half lane / 32, into LDS
+  {
+    int k = 32 * fb + (lane & 31);
+    k = k < nt ? k : nt - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.v_sink, p.v_ring, bh, k) + 64 * (lane >> 5));
+    uint4* dst = reinterpret_cast<uint4*>(vt + (lane & 31) * kSegVStride + 64 * (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = src[i];
+  }
+  f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      int k = 32 * fb + 16 * tile + (lane & 15);
-      k = k < nt ? k : nt - 1;                         // masked below; any valid row keeps values finite
-      const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.k_sink, p.k_ring, bh, k) + 32 * li.qd);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[tile][i] = src[i];
+      const uint4 w = kr[tile][kb];
+      acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(w.x, w.y, w.z, w.w), bk[kb], acc[tile], 0, 0, 0);
     }
-    // Value row of token lane % 32, channel half lane / 32, into LDS
-    {
-      int k = 32 * fb + (lane & 31);
-      k = k < nt ? k : nt - 1;
-      const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.v_sink, p.v_ring, bh, k) + 64 * (lane >> 5));
-      uint4* dst = reinterpret_cast<uint4*>(vt + (lane & 31) * kSegVStride + 64 * (lane >> 5));
+  float lg[2][4], pr[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = src[i];
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 32 * fb + 16 * tile + 4 * li.qd + i;
+      const float x = acc[tile][i] + ror8(acc[tile][i]);
+      lg[tile][i] = k < nt ? x : neg_inf();
     }
-    f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  softmax_block(lg, ws, pr, kSlack);
+  const f16x8 bp = p_operand(pr, li);
+  wave_lds_sync();                                      // staged Value rows visible to every lane
+  const int r = lane & 15;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+  for (int m = 0; m < 8; ++m) {
+    // channel 16m + r of tokens T0, T4, T1, T5, T2, T6, T3, T7 (T = 4qd + 0..3, 16 + 4qd + 0..3)
+    f16x8 a;
 #pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        const uint4 w = kr[tile][kb];
-        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(w.x, w.y, w.z, w.w), bk[kb], acc[tile], 0, 0, 0);
-      }
-    float lg[2][4], pr[2][4];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = 32 * fb + 16 * tile + 4 * li.qd + i;
-        const float x = acc[tile][i] + ror8(acc[tile][i]);
-        lg[tile][i] = k < nt ? x : neg_inf();
-      }
-    softmax_block(lg, ws, pr, kSlack);
-    const f16x8 bp = p_operand(pr, li);
-    __syncthreads();                                    // staged Value rows visible to every lane
-    const int r = lane & 15;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      // channel 16m + r of tokens T0, T4, T1, T5, T2, T6, T3, T7 (T = 4qd + 0..3, 16 + 4qd + 0..3)
-      f16x8 a;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        a[2 * v] = __builtin_bit_cast(_Float16, vt[(4 * li.qd + v) * kSegVStride + 16 * m + r]);
-        a[2 * v + 1] = __builtin_bit_cast(_Float16, vt[(16 + 4 * li.qd + v) * kSegVStride + 16 * m + r]);
-      }
-      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, ws.o[m], 0, 0, 0);
+    for (int v = 0; v < 4; ++v) {
+      a[2 * v] = __builtin_bit_cast(_Float16, vt[(4 * li.qd + v) * kSegVStride + 16 * m + r]);
+      a[2 * v + 1] = __builtin_bit_cast(_Float16, vt[(16 + 4 * li.qd + v) * kSegVStride + 16 * m + r]);
     }
-    __syncthreads();                                    // before the next block overwrites the rows
+    ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp, ws.o[m], 0, 0, 0);
   }
-  float* slot = p.part + (bh * p.fp16_waves_per_head + f) * (int64_t)p.nrep * kPartStride;
+  wave_lds_sync();                                      // reads done before the area is reused
   finish_segment(ws, li, slot, 1.0f, false);
 }
 
-constexpr int kLdsBytes = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
+constexpr int kGroupThreads = 64 * kGroupWaves;
+// per-wavefront LDS area: the block staging of process_block, or the Value
+// rows of an fp16 block (never both at once)
+constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
 
-// One wavefront per workgroup: the fp16 wavefronts first (bh_count *
-// fp16_waves_per_head of them), then the body wavefronts.
+// One workgroup: range [jb, jb + len) of the flattened quantized blocks,
+// touching heads h0..h1.
+struct GroupRange {
+  int64_t jb;
+  int len, h0, h1;
+};
+
+__device__ __forceinline__ GroupRange group_range(const AttnParams& p, int g) {
+  GroupRange r;
+  const int64_t total = (int64_t)p.bh_count * p.nblk;
+  r.jb = (int64_t)g * p.group_blocks;
+  r.len = r.jb < total ? (int)(total - r.jb < p.group_blocks ? total - r.jb : p.group_blocks) : 0;
+  r.h0 = r.len ? (int)(r.jb / p.nblk) : 0;
+  r.h1 = r.len ? (int)((r.jb + r.len - 1) / p.nblk) : -1;
+  return r;
+}
+
+// The workgroup's wavefronts stream the blocks of its range: each keeps
+// kDepth blocks in flight beyond the one it processes and takes its next
+// block from a counter in LDS, so a wavefront that the memory system serves
+// faster processes more blocks and all finish together (in deterministic
+// mode wavefront w takes blocks w, w + 8, w + 16, ... instead).  Every
+// wavefront keeps one online softmax per head it meets and writes one partial
+// slot per head of the range.  Before its first block it handles its share of
+// the fp16 blocks (one partial slot each), while its first blocks load.
 template <int FMT>
-__global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int64_t wid = blockIdx.x;
-  const int64_t nf = (int64_t)p.bh_count * p.fp16_waves_per_head;
-  if (wid < nf) {
-    fp16_wave(p, wid / p.fp16_waves_per_head, (int)(wid % p.fp16_waves_per_head), reinterpret_cast<uint16_t*>(lds));
-  } else {
-    body_wave<FMT>(p, wid - nf, reinterpret_cast<float*>(lds));
+__device__ void group_main(const AttnParams& p, char* lds) {
+  using T = Traits<FMT>;
+  constexpr int D = T::kDepth + 1;
+  const int g = blockIdx.x;
+  const int v = threadIdx.x >> 6;
+  const LaneInfo li = lane_info(p.nrep);
+  const GroupRange gr = group_range(p, g);
+  const uint32_t nblk = (uint32_t)p.nblk;
+  float* stage = reinterpret_cast<float*>(lds + v * kWaveLds);
+  int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
+
+  // query rows of the range's first head, loaded before the blocks
+  const QRaw q0 = load_query_raw(p.q + (int64_t)gr.h0 * p.nrep * kHeadDim, p.nrep, li);
+
+  // block ring: D - 1 blocks prefetched ahead of the one being processed;
+  // rid = block index within the range (-1 past its end), rbh = its head.
+  // Loads past the end re-read the last block taken (in bounds, cached); a
+  // workgroup without a range reads the last block of all (its loads are
+  // never used, but keep the load count static).
+  const uint32_t jlast = (uint32_t)((int64_t)p.bh_count * p.nblk - 1);
+  const uint32_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;
+  Raw<FMT> buf[D];
+  int rid[D], rbh[D];
+  int last = 0, kst = 0;
+  auto fetch = [&](Raw<FMT>& r, int& id, int& bhout, bool fixed) {
+    int idx;
+    if (fixed || p.deterministic) {
+      idx = v + kGroupWaves * kst;
+      ++kst;
+    } else {
+      idx = 0;
+      if (li.lane == 0) idx = atomicAdd(ctr, 1);
+      idx = __builtin_amdgcn_readfirstlane(idx);
+    }
+    const bool ok = idx < gr.len;
+    if (ok) last = idx;
+    id = ok ? idx : -1;
+    uint32_t j = gr.len ? (uint32_t)(gr.jb + last) : jlast;
+    const uint32_t bh = j / nblk;
+    if (gr.len) {
+      // visit the blocks of each head's part of the range starting at a
+      // per-workgroup offset, so that the workgroups' streams sit at
+      // unrelated addresses rather than in step
+      const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
+      const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
+      j = ps + (j - ps + rot) % (pe - ps);
+    }
+    bhout = (int)bh;
+    load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
+  };
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], true);
+
+  if (threadIdx.x == 0) *ctr = kGroupWaves * (D - 1);   // the prefetched blocks were fixed
+  // the counter's LDS write done, then the workgroup barrier; the loads
+  // stay in flight (vmcnt 63, expcnt 7, lgkmcnt 0)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+
+  // fp16 blocks: wavefront v * groups + g takes every (8 * groups)-th one
+  const int64_t nf = (int64_t)p.bh_count * p.fp16_blocks;
+  for (int64_t f = (int64_t)v * p.groups + g; f < nf; f += (int64_t)kGroupWaves * p.groups)
+    fp16_block(p, f / p.fp16_blocks, (int)(f % p.fp16_blocks), reinterpret_cast<uint16_t*>(stage),
+               p.part + f * p.nrep * kPartStride);
+  if (!gr.len) return;
+
+  const int64_t slot0 = nf + (int64_t)kGroupWaves * g + v;
+  auto slot_ptr = [&](int h) { return p.part + (slot0 + (int64_t)kGroupWaves * h) * p.nrep * kPartStride; };
+  if (li.writer && li.qd == 0) {
+    for (int h = gr.h0; h <= gr.h1; ++h) {
+      float* dst = slot_ptr(h) + li.head * kPartStride;
+      dst[0] = neg_inf();
+      dst[1] = 0.f;
+    }
   }
+
+  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
+  float qf[32];
+  f16x8 bk_static[4];
+  query_operand(q0, p.nrep, li, qf);          // qf holds the query of head qhead
+  int qhead = gr.h0;
+  WaveState ws;
+  reset(ws);
+  int cur = -1;
+  for (;;) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], false);
+      if (rid[d] < 0) goto done;             // blocks are taken in order: none left
+      if (rbh[d] != cur) {
+        if (cur >= 0) {
+          finish_segment(ws, li, slot_ptr(cur), oscale, !T::kFp8);
+          reset(ws);
+        }
+        cur = rbh[d];
+        if (cur != qhead) {
+          load_query(p, cur, li, qf);
+          qhead = cur;
+        }
+        if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
+      }
+      process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
+    }
+  }
+done:
+  if (cur >= 0) finish_segment(ws, li, slot_ptr(cur), oscale, !T::kFp8);
+}
+
+constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16;
+
+// No quantized blocks yet: every wavefront only takes its fp16 blocks.
+__device__ void fp16_only(const AttnParams& p, char* lds) {
+  const int g = blockIdx.x;
+  const int v = threadIdx.x >> 6;
+  const int64_t nf = (int64_t)p.bh_count * p.fp16_blocks;
+  for (int64_t f = (int64_t)v * p.groups + g; f < nf; f += (int64_t)kGroupWaves * p.groups)
+    fp16_block(p, f / p.fp16_blocks, (int)(f % p.fp16_blocks), reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
+               p.part + f * p.nrep * kPartStride);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kGroupThreads) void attn_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  if (p.nblk == 0) fp16_only(p, lds);
+  else group_main<FMT>(p, lds);
 }
 
 constexpr int kReduceThreads = 128;
 constexpr int kReduceRegSlots = 32;       // slots whose output this thread loads at once
 
 // out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s,
-// over the head's fp16 slots and body slots.  All loads of a pass of up to
-// kReduceRegSlots slots are issued together (one memory round trip).
+// over the head's fp16 slots and body slots (empty slots weigh 0).  All loads
+// of a pass of up to kReduceRegSlots slots are issued together (one memory
+// round trip).
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) {
   __shared__ float wts[kReduceRegSlots];
   __shared__ float msh[kReduceRegSlots], lsh[kReduceRegSlots];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int g = hq / p.nrep, hh = hq % p.nrep;
   const int64_t bh = (int64_t)b * p.hkv + g;
-  const int nf = p.fp16_waves_per_head;
-  int64_t wf = 0, nbody = 0;
+  const int nf = p.fp16_blocks;
+  int64_t g_lo = 0, ng = 0;
   if (p.nblk > 0) {
-    wf = bh * p.nblk / p.body_per_wave;
-    nbody = ((bh + 1) * p.nblk - 1) / p.body_per_wave - wf + 1;
+    g_lo = bh * p.nblk / p.group_blocks;
+    ng = ((bh + 1) * p.nblk - 1) / p.group_blocks - g_lo + 1;
   }
-  const int ns = nf + (int)nbody;
+  const int ns = nf + kGroupWaves * (int)ng;
   const int64_t fslots = (int64_t)p.bh_count * nf;
   auto slot_ptr = [&](int s) -> const float* {
-    const int64_t slot = s < nf ? bh * nf + s : fslots + wf + (s - nf) + bh;
+    const int64_t slot = s < nf ? bh * nf + s : fslots + (int64_t)kGroupWaves * (g_lo + bh) + (s - nf);
     return p.part + (slot * p.nrep + hh) * kPartStride;
   };
   float M = neg_inf(), L = 0.f, O = 0.f;
@@ -726,7 +826,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kReduceRegSlots; ++j) {
-      if (j < cnt) {
+      if (j < cnt && wts[j] != 0.f) {           // an empty slot's output is not read
         L = __builtin_fmaf(wts[j], lsh[j], L);
         O = __builtin_fmaf(wts[j], v[j], O);
       }
@@ -739,8 +839,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) 
 
 }  // namespace
 
-hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStream_t s) {
-  const dim3 grid((unsigned)waves), block(64);
+hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.groups), block(kGroupThreads);
   switch (fmt) {
     case KVQ_INT8: hipLaunchKernelGGL(attn_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(attn_kernel<KVQ_INT4>, grid, block, 0, s, p); break;
@@ -749,23 +849,6 @@ hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStre
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-int attention_waves_per_cu(int fmt) {
-  static int cached[4] = {0, 0, 0, 0};
-  if (fmt < 0 || fmt > 3) return 0;
-  if (cached[fmt] == 0) {
-    int blocks = 0;
-    hipError_t e = hipErrorInvalidValue;
-    switch (fmt) {
-      case KVQ_INT8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT8>, 64, 0); break;
-      case KVQ_INT4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT4>, 64, 0); break;
-      case KVQ_INT2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_INT2>, 64, 0); break;
-      default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_kernel<KVQ_FP8_E4M3>, 64, 0); break;
-    }
-    cached[fmt] = (e == hipSuccess && blocks > 0) ? blocks : 8;
-  }
-  return cached[fmt];
 }
 
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s) {

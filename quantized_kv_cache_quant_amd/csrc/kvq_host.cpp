@@ -1,6 +1,7 @@
 // Host side of the C ABI in include/kvq.h: layout validation, byte sizing,
 // plane placement, token routing and launch configuration.  Nothing here
 // touches device memory; kernels are enqueued on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -54,8 +55,8 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
 }
 
-// Attention wavefronts one resident round can hold on the current device.
-int64_t resident_waves(int fmt) {
+// Compute units of the current device (256 when no device answers).
+int64_t device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -64,32 +65,28 @@ int64_t resident_waves(int fmt) {
       n = 256;
     cus = n;
   }
-  return (int64_t)cus * attention_waves_per_cu(fmt);
+  return cus;
 }
 
 struct AttnPlan {
-  int64_t blocks_per_wave, body_waves, fp16_blocks, fp16_waves_per_head, slots;
+  int64_t group_blocks, groups, fp16_blocks, slots;
 };
 
-// Split the work: fp16 wavefronts take up to kFp16BlocksPerWave blocks of a
-// head's fp16 segment; the body wavefronts share the quantized blocks
-// equally, one resident round of them unless blocks_per_wave is given.
-AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpw) {
+// Split the work: the quantized blocks of all heads into ranges of
+// group_blocks blocks, one per workgroup (by default one range per compute
+// unit); the fp16 segment of each head into 32-token blocks, at most one per
+// wavefront of the grid at a time.
+AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpg) {
   AttnPlan a{};
   const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
   a.fp16_blocks = (n_fp16_tokens + kBlock - 1) / kBlock;
-  a.fp16_waves_per_head = (a.fp16_blocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
+  const int64_t nf = bh * a.fp16_blocks;
   const int64_t total = bh * nblk;
-  if (bpw > 0) {
-    a.blocks_per_wave = bpw;
-  } else {
-    // the fp16 wavefronts come first in the grid and finish early; the body
-    // wavefronts fill one resident round
-    const int64_t target = resident_waves(L.format);
-    a.blocks_per_wave = total > 0 ? (total + target - 1) / target : 1;
-  }
-  a.body_waves = total > 0 ? (total + a.blocks_per_wave - 1) / a.blocks_per_wave : 0;
-  a.slots = bh * a.fp16_waves_per_head + (total > 0 ? a.body_waves + bh : 0);
+  if (bpg > 0) a.group_blocks = bpg;
+  else a.group_blocks = total > 0 ? (total + device_cus() - 1) / device_cus() : 1;
+  const int64_t body_groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : 0;
+  a.groups = std::max<int64_t>(std::max<int64_t>(body_groups, (nf + kGroupWaves - 1) / kGroupWaves), 1);
+  a.slots = nf + (total > 0 ? kGroupWaves * (a.groups + bh) : 0);
   return a;
 }
 
@@ -260,52 +257,41 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
   return KVQ_OK;
 }
 
-int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpw, uint64_t* bytes) {
+int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpg, uint64_t* bytes) {
   if (!c || !bytes) return KVQ_ERR_NULL;
-  if (bpw < 0 || bpw > kMaxBlocksPerWave) return KVQ_ERR_LAYOUT;
+  if (bpg < 0 || bpg > kMaxBlocksPerGroup) return KVQ_ERR_LAYOUT;
   const kvq_layout& L = c->layout;
   const uint64_t bh = (uint64_t)L.batch * L.num_kv_heads;
-  // worst case over every cache length: all NB blocks quantized, the largest
-  // fp16 segment (S sinks + R + 31 residual tokens), and for the library's
-  // own choice at most one resident round of body wavefronts
+  // worst case over every cache length: all NB blocks quantized and the
+  // largest fp16 segment (S sinks + R + 31 residual tokens); the library's
+  // own split uses at most one workgroup per compute unit for the body
   const uint64_t total = bh * (uint64_t)c->n_blocks_cap;
-  const uint64_t fblocks = ((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock;
-  const uint64_t fwaves = (fblocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
-  uint64_t body = bpw > 0 ? (total + bpw - 1) / bpw : total;
-  if (bpw == 0 && total > 0) {
-    uint64_t cap = 32ull * 1024;               // any device: at most 1024 CUs, 32 wavefronts per CU
-    if (body > cap) body = cap;
-  }
-  *bytes = (bh * fwaves + (total > 0 ? body + bh : 0)) * slot_bytes(L);
+  const uint64_t nf = bh * (((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock);
+  uint64_t groups = 0;
+  if (total > 0) groups = bpg > 0 ? (total + bpg - 1) / bpg : std::min<uint64_t>(total, (uint64_t)device_cus());
+  groups = std::max<uint64_t>(std::max<uint64_t>(groups, (nf + kGroupWaves - 1) / kGroupWaves), 1);
+  *bytes = (nf + (total > 0 ? kGroupWaves * (groups + bh) : 0)) * slot_bytes(L);
   return KVQ_OK;
 }
 
 int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, void* ws,
-                                  uint64_t ws_bytes, int32_t bpw, void* stream) {
+                                  uint64_t ws_bytes, int32_t bpg, int32_t deterministic, void* stream) {
   if (!c || !c->base || !q || !out) return KVQ_ERR_NULL;
   const kvq_layout& L = c->layout;
   int32_t st = kvq_layout_validate(&L);
   if (st != KVQ_OK) return st;
-  if (bpw < 0 || bpw > kMaxBlocksPerWave) return KVQ_ERR_LAYOUT;
+  if (bpg < 0 || bpg > kMaxBlocksPerGroup || (deterministic != 0 && deterministic != 1)) return KVQ_ERR_LAYOUT;
   if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
   if (c->n_tokens == 0) return KVQ_ERR_EMPTY;
   const Window w = window(L, c->n_tokens);
   const int64_t nblk = w.n_q / kBlock;
+  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
   // workspace is checked before anything touches the device
   if (!ws) return KVQ_ERR_WORKSPACE;
-  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
-  const int64_t fblocks = (w.n_sink + w.r + kBlock - 1) / kBlock;
-  const int64_t fwaves = (fblocks + kFp16BlocksPerWave - 1) / kFp16BlocksPerWave;
-  if (bpw > 0) {
-    const int64_t total = bh * nblk;
-    const int64_t body = total > 0 ? (total + bpw - 1) / bpw : 0;
-    if ((uint64_t)(bh * fwaves + (total > 0 ? body + bh : 0)) * slot_bytes(L) > ws_bytes) return KVQ_ERR_WORKSPACE;
-  }
-  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
-  const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpw);
+  const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpg);
   if ((uint64_t)a.slots * slot_bytes(L) > ws_bytes) return KVQ_ERR_WORKSPACE;
-  const int64_t waves = bh * a.fp16_waves_per_head + a.body_waves;
-  if (waves > 0x7fffffffLL || a.fp16_waves_per_head > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
 
   char* base = static_cast<char*>(c->base);
   auto plane = [&](int i) { return base + c->plane_off[i]; };
@@ -330,23 +316,22 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.n_res = (int32_t)w.r;
   p.ring_first = (int32_t)(w.n_q % c->ring_slots);
   p.bh_count = (int32_t)bh;
-  p.body_per_wave = (int32_t)a.blocks_per_wave;
-  p.body_waves = (int32_t)a.body_waves;
+  p.group_blocks = (int32_t)a.group_blocks;
+  p.groups = (int32_t)a.groups;
   p.fp16_blocks = (int32_t)a.fp16_blocks;
-  p.fp16_per_wave = kFp16BlocksPerWave;
-  p.fp16_waves_per_head = (int32_t)a.fp16_waves_per_head;
+  p.deterministic = deterministic;
   p.k_scale = L.k_scale;
   p.v_scale = L.v_scale;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (launch_attention(L.format, p, waves, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_attention(L.format, p, s) != hipSuccess) return KVQ_ERR_HIP;
   ReduceParams rp{};
   rp.part = p.part;
   rp.out = static_cast<uint16_t*>(out);
   rp.hkv = p.hkv;
   rp.nrep = p.nrep;
   rp.nblk = p.nblk;
-  rp.body_per_wave = p.body_per_wave;
-  rp.fp16_waves_per_head = p.fp16_waves_per_head;
+  rp.group_blocks = p.group_blocks;
+  rp.fp16_blocks = p.fp16_blocks;
   rp.bh_count = p.bh_count;
   if (launch_reduce(rp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
@@ -354,7 +339,7 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
 
 int32_t kv_decode_attention(const kvq_cache* c, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream) {
-  return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, stream);
+  return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, 0, stream);
 }
 
 }  // extern "C"

@@ -14,8 +14,8 @@ constexpr int kHeadDim = 128;     // the only head_dim of this version
 constexpr int kVGroup = 32;       // channels per Value group
 constexpr int kVGroups = kHeadDim / kVGroup;
 constexpr int kPartStride = 132;  // floats per partial: m, l, 2 pad, o[128]
-constexpr int kMaxBlocksPerWave = 1024;
-constexpr int kFp16BlocksPerWave = 2;
+constexpr int kGroupWaves = 8;           // wavefronts per attention workgroup
+constexpr int kMaxBlocksPerGroup = 1 << 20;
 
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
@@ -56,12 +56,20 @@ hipError_t launch_flush(int fmt, const FlushParams& p, int n_blocks, int batch, 
 hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 
 // ------------------------------------------------------------- attention
+// Work: the quantized blocks of all heads, flattened head-major (block j is
+// block j mod nblk of head j / nblk), are cut into ranges of group_blocks
+// blocks, one per workgroup of kGroupWaves wavefronts; the wavefronts of a
+// workgroup take blocks of its range in turn.  The fp16 segment of every head
+// (sinks, then residual ring) is cut into 32-token blocks handled one per
+// wavefront.
 // Partial results: kPartStride floats per query head, n_rep heads per slot.
-//   fp16 region  slot bh * fp16_waves_per_head + f   (f-th fp16 wavefront of head bh)
-//   body region  slot fp16_slots + w + bh            (body wavefront w's share of head bh)
-// A body wavefront w streams the flattened quantized blocks [w*L, (w+1)*L) of
-// all heads (head-major), so head bh is covered by the wavefronts
-// floor(bh*nblk/L) .. floor(((bh+1)*nblk - 1)/L) and w + bh never collides.
+//   fp16 region  slot bh * fp16_blocks + fb              (fp16 block fb of head bh)
+//   body region  slot F + kGroupWaves * (g + bh) + w     (wavefront w of workgroup g,
+//                F = bh_count * fp16_blocks               its blocks of head bh)
+// Workgroup g covers heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk), so
+// g + bh never collides between workgroups, and the body slots of one head
+// are contiguous.  A wavefront that gets no block of a head of its range
+// marks the slot empty (m = -inf, l = 0).
 struct AttnParams {
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -83,23 +91,20 @@ struct AttnParams {
   int32_t n_res;          // residual tokens held
   int32_t ring_first;     // ring slot of the oldest residual token (n_q mod RS)
   int32_t bh_count;       // B * Hkv
-  int32_t body_per_wave;  // L: quantized blocks per body wavefront
-  int32_t body_waves;     // ceil(bh_count * nblk / L)
+  int32_t group_blocks;   // R: quantized blocks per workgroup range
+  int32_t groups;         // workgroups in the grid
   int32_t fp16_blocks;    // ceil((n_sink + n_res) / 32) per head
-  int32_t fp16_per_wave;  // fp16 blocks per fp16 wavefront
-  int32_t fp16_waves_per_head;
+  int32_t deterministic;  // 1: wavefront w takes blocks w, w + 8, ... of its range
   float k_scale, v_scale; // FP8
 };
 
 struct ReduceParams {
   const float* part;
   uint16_t* out;          // fp16 [B][Hq][D]
-  int32_t hkv, nrep, nblk, body_per_wave, fp16_waves_per_head, bh_count;
+  int32_t hkv, nrep, nblk, group_blocks, fp16_blocks, bh_count;
 };
 
-hipError_t launch_attention(int fmt, const AttnParams& p, int64_t waves, hipStream_t s);
+hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s);
-// Attention workgroups (one wavefront each) a compute unit holds at once.
-int attention_waves_per_cu(int fmt);
 
 }  // namespace kvq

@@ -54,6 +54,11 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: run quantized_kv_cache_quant_amd.build first")
+        # torch ships its own HIP runtime; load it first so that the library
+        # binds to the runtime that owns torch's memory and streams (the
+        # other order leaves two runtimes in the process and torch's kernel
+        # launches fail with "invalid device function")
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32, U64, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_int64
         LP, CP = ctypes.POINTER(Layout), ctypes.POINTER(CacheStruct)
@@ -67,7 +72,7 @@ def lib() -> ctypes.CDLL:
             "kv_quant_append": (I32, [CP, P, P, I32, P]),
             "kvq_workspace_bytes": (I32, [CP, I32, ctypes.POINTER(U64)]),
             "kv_decode_attention": (I32, [CP, P, P, P, U64, P]),
-            "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, P]),
+            "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -143,20 +148,22 @@ class Cache:
         check(lib().kv_quant_append(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
                                     ctypes.c_void_p(v.data_ptr()), int(t), _stream(stream)), "kv_quant_append")
 
-    def workspace_bytes(self, blocks_per_wave: int = 0) -> int:
+    def workspace_bytes(self, blocks_per_group: int = 0) -> int:
         n = ctypes.c_uint64()
-        check(lib().kvq_workspace_bytes(ctypes.byref(self.handle), int(blocks_per_wave), ctypes.byref(n)),
+        check(lib().kvq_workspace_bytes(ctypes.byref(self.handle), int(blocks_per_group), ctypes.byref(n)),
               "kvq_workspace_bytes")
         return n.value
 
-    def attention(self, q, out, ws, blocks_per_wave: int = 0, stream=None) -> None:
+    def attention(self, q, out, ws, blocks_per_group: int = 0, deterministic: bool = False,
+                  stream=None) -> None:
         """q, out: contiguous fp16 device tensors [B][Hq][D]; ws: device scratch tensor."""
         _check_tensor(q, "q")
         _check_tensor(out, "out")
         check(lib().kv_decode_attention_split(ctypes.byref(self.handle), ctypes.c_void_p(q.data_ptr()),
                                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
-                                              ws.numel() * ws.element_size(), int(blocks_per_wave),
-                                              _stream(stream)), "kv_decode_attention")
+                                              ws.numel() * ws.element_size(), int(blocks_per_group),
+                                              int(bool(deterministic)), _stream(stream)),
+              "kv_decode_attention")
 
 
 def _check_tensor(t, name: str) -> None:

@@ -120,11 +120,12 @@ def assert_states_equal(got: ocache.CacheState, exp: ocache.CacheState, heads=No
     eq(got.sink_v, exp.sink_v, "V sinks")
 
 
-def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_wave: int = 0) -> np.ndarray:
+def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_group: int = 0,
+                  deterministic: bool = False) -> np.ndarray:
     qd = to_dev(q)
     out = torch.empty_like(qd)
-    ws = torch.empty(c.workspace_bytes(blocks_per_wave) // 4 + 4, dtype=torch.float32, device="cuda")
-    c.attention(qd, out, ws, blocks_per_wave)
+    ws = torch.empty(c.workspace_bytes(blocks_per_group) // 4 + 4, dtype=torch.float32, device="cuda")
+    c.attention(qd, out, ws, blocks_per_group, deterministic)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

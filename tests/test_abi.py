@@ -143,34 +143,41 @@ def test_attention_errors():
     L = kvq.lib()
     P = ctypes.c_void_p
     lay, h = _cache(max_tokens=2000)
+    slot = 4 * 132 * 4                       # n_rep partials of (m, l, 2 pad, o[128]) floats
     need = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 0, ctypes.byref(need)) == 0
-    # slots: one per fp16 wavefront of each head (ceil((S + R + 31) / 32) blocks, 2 per
-    # wavefront) plus, for the quantized blocks, one per body wavefront and one per head
+    # worst case: one slot per fp16 block (ceil((S + R + 31) / 32) per head) plus, for the
+    # quantized blocks, 8 per workgroup and 8 per head; without a device the library
+    # assumes 256 compute units, so its split uses min(256, 4 * 61) workgroups
     bh, nb = 4, (2000 - 4 - 32) // 32
-    fwaves = -(-(-(-(4 + 32 + 31) // 32)) // 2)
-    assert need.value == (bh * fwaves + bh * nb + bh) * 4 * 132 * 4
-    assert L.kvq_workspace_bytes(ctypes.byref(h), 1025, ctypes.byref(need)) == -2
+    nf = bh * (-(-(4 + 32 + 31) // 32))
+    assert need.value == (nf + 8 * (min(256, bh * nb) + bh)) * slot
+    big = (1 << 20) + 1
+    assert L.kvq_workspace_bytes(ctypes.byref(h), big, ctypes.byref(need)) == -2
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == -8  # empty
     h.n_tokens = 1500
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 16, None) == -6
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), None, 1 << 30, None) == -6
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE + 2), P(FAKE), P(FAKE), 1 << 30, None) == -5
     assert L.kv_decode_attention(ctypes.byref(h), None, P(FAKE), P(FAKE), 1 << 30, None) == -1
-    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 1025, None) == -2
+    split = L.kv_decode_attention_split
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, big, 0, None) == -2
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, -1, 0, None) == -2
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 0, 2, None) == -2
     # an explicit split needing more than the caller's workspace is refused before any
-    # launch: at n = 2000 there are 61 blocks per head and 4 + 44 fp16 tokens (one fp16
-    # wavefront per head), so blocks_per_wave = 1 needs 4 + 4 * 61 + 4 slots
+    # launch: at n = 2000 there are 61 blocks per head and 4 + 44 fp16 tokens (2 fp16
+    # blocks per head), so blocks_per_group = 1 needs 8 + 8 * (244 + 4) slots
     h.n_tokens = 2000
-    exact = (4 + 4 * 61 + 4) * 4 * 132 * 4
-    assert L.kv_decode_attention_split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, None) == -6
+    exact = (8 + 8 * (244 + 4)) * slot
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, 0, None) == -6
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, 1, None) == -6
     w1 = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 1, ctypes.byref(w1)) == 0
     assert w1.value >= exact
-    # larger blocks per wavefront never need more workspace than smaller ones
+    # larger ranges never need more workspace than smaller ones
     prev = w1.value
-    for bpw in (2, 3, 7, 16, 1024):
+    for bpg in (2, 3, 7, 16, 1024, 1 << 20):
         w = ctypes.c_uint64()
-        assert L.kvq_workspace_bytes(ctypes.byref(h), bpw, ctypes.byref(w)) == 0
+        assert L.kvq_workspace_bytes(ctypes.byref(h), bpg, ctypes.byref(w)) == 0
         assert w.value <= prev
         prev = w.value

@@ -103,19 +103,23 @@ def test_empty_cache_is_an_error():
 
 
 @pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8"])
-def test_split_count_invariance_and_determinism(fmt):
+def test_split_invariance_and_determinism(fmt):
     require_gpu()
     n = 32 * 70 + 40
     c, kw, q = _build(fmt, 2, 2, 4, n, 32, 0, seed=4)
-    outs = {bpw: attention_gpu(c, q, bpw).astype(np.float64) for bpw in (1, 2, 3, 5, 16, 0)}
     ref = _oracle_out(c, kw, q)
-    base = outs[0]
-    for bpw, o in outs.items():
-        assert np.max(np.abs(o - ref)) <= TOL, bpw
-        # split sizes change fp32 summation order only: at most one fp16 ulp apart
-        assert np.all(np.abs(o - base) <= np.maximum(np.abs(base), 1.0) * 2.0**-10), bpw
-    again = attention_gpu(c, q)
-    assert np.array_equal(again.astype(np.float64), base)      # bitwise repeatable
+    outs = {}
+    for bpg in (1, 2, 3, 5, 16, 64, 0):          # 1: one block per workgroup; 64: ranges across heads
+        for det in (True, False):
+            outs[bpg, det] = attention_gpu(c, q, bpg, det).astype(np.float64)
+    base = outs[0, True]
+    for key, o in outs.items():
+        assert np.max(np.abs(o - ref)) <= TOL, key
+        # the split changes the fp32 summation order only: at most one fp16 ulp apart
+        assert np.all(np.abs(o - base) <= np.maximum(np.abs(base), 1.0) * 2.0**-10), key
+    for bpg in (3, 0):
+        again = attention_gpu(c, q, bpg, True)
+        assert np.array_equal(again.astype(np.float64), outs[bpg, True]), bpg   # bitwise repeatable
 
 
 def test_closed_forms_on_gpu():
