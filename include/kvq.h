@@ -159,9 +159,9 @@ int32_t kv_quant_append(kvq_cache* cache, const void* K, const void* V, int32_t 
 
 /* Workspace bytes kv_decode_attention_split needs on the current device for
  * any n_tokens up to max_tokens with the given blocks_per_group (0 = the
- * library's choice): one partial of (4 + 128) floats per query head for every
- * fp16 block of 32 tokens, and for every wavefront of every workgroup and
- * every head its range touches.  A larger blocks_per_group never needs more.
+ * library's choice): partials of (4 + 128) floats per query head, one per
+ * fp16 block of 32 tokens and, for the quantized blocks, nine per (workgroup
+ * + head) index (eight wavefronts' and their merge).  A larger blocks_per_group never needs more.
  * Errors: KVQ_ERR_NULL; KVQ_ERR_LAYOUT for blocks_per_group outside
  * [0, 2^20]. */
 int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, uint64_t* bytes);
@@ -174,12 +174,13 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, ui
  *   out[b][h] = sum_t softmax_t(q[b][h] . k_hat[b][g][t] / sqrt(D)) v_hat[b][g][t]
  * over all n_tokens cached tokens, g = h / (Hq/Hkv), with k_hat, v_hat the
  * dequantized (or fp16) cache entries.  Split-K: a first kernel writes
- * partials (max, sum, unnormalised output) into ws, a second combines them.
- * ws: device scratch of >= kvq_workspace_bytes(cache, 0) bytes, overwritten;
- * calls that share a workspace must be ordered on one stream.  Blocks are
- * handed to wavefronts as the memory system serves them, so repeated calls
- * may differ in the last bits (see the deterministic mode below).
- * Errors: KVQ_ERR_EMPTY if n_tokens == 0. */
+ * partials (max, sum, unnormalised output) into ws, merged per workgroup; a
+ * second combines each head's partials into out.
+ * ws: device scratch of >= kvq_workspace_bytes(cache, 0) bytes, 16-B
+ * aligned, any contents, overwritten; calls that share a workspace must be
+ * ordered on one stream.  Blocks are handed to wavefronts as the memory
+ * system serves them, so repeated calls may differ in the last bits (see the
+ * deterministic mode below).  Errors: KVQ_ERR_EMPTY if n_tokens == 0. */
 int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream);
 

@@ -22,7 +22,9 @@
 //  * the fp16 segment (sinks + residual ring) of every head is cut into
 //    32-token blocks, spread one per wavefront over the grid and handled
 //    while the wavefront's first quantized blocks load;
-//  * reduce_kernel combines each head's partials in a fixed order.
+//  * at the end a workgroup merges its wavefronts' partials per head, and
+//    reduce_kernel combines each head's workgroup and fp16 partials in a
+//    fixed order.
 //
 // Per 32-token block a wavefront runs both products on the matrix cores with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate):
@@ -642,6 +644,16 @@ __device__ __forceinline__ GroupRange group_range(const AttnParams& p, int g) {
   return r;
 }
 
+// Workgroups whose range touches head h: g_lo .. g_lo + count - 1.
+__device__ __forceinline__ int64_t covering_lo(const AttnParams& p, int64_t h) {
+  return h * p.nblk / p.group_blocks;
+}
+__device__ __forceinline__ int64_t covering_count(const AttnParams& p, int64_t h) {
+  return ((h + 1) * p.nblk - 1) / p.group_blocks - covering_lo(p, h) + 1;
+}
+
+__device__ __forceinline__ int64_t slot_floats(const AttnParams& p) { return (int64_t)p.nrep * kPartStride; }
+
 // The workgroup's wavefronts stream the blocks of its range: each keeps
 // kDepth blocks in flight beyond the one it processes and takes its next
 // block from a counter in LDS, so a wavefront that the memory system serves
@@ -649,7 +661,8 @@ __device__ __forceinline__ GroupRange group_range(const AttnParams& p, int g) {
 // mode wavefront w takes blocks w, w + 8, w + 16, ... instead).  Every
 // wavefront keeps one online softmax per head it meets and writes one partial
 // slot per head of the range.  Before its first block it handles its share of
-// the fp16 blocks (one partial slot each), while its first blocks load.
+// the workgroup's fp16 blocks, while its first blocks load.  At the end the
+// workgroup merges its wavefronts' partials into one slot per head.
 template <int FMT>
 __device__ void group_main(const AttnParams& p, char* lds) {
   using T = Traits<FMT>;
@@ -658,6 +671,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   const int v = threadIdx.x >> 6;
   const LaneInfo li = lane_info(p.nrep);
   const GroupRange gr = group_range(p, g);
+  if (!gr.len) return;                        // (never: every workgroup has a range)
   const uint32_t nblk = (uint32_t)p.nblk;
   float* stage = reinterpret_cast<float*>(lds + v * kWaveLds);
   int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
@@ -667,10 +681,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
 
   // block ring: D - 1 blocks prefetched ahead of the one being processed;
   // rid = block index within the range (-1 past its end), rbh = its head.
-  // Loads past the end re-read the last block taken (in bounds, cached); a
-  // workgroup without a range reads the last block of all (its loads are
-  // never used, but keep the load count static).
-  const uint32_t jlast = (uint32_t)((int64_t)p.bh_count * p.nblk - 1);
+  // Loads past the end re-read the last block taken (in bounds, cached).
   const uint32_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;
   Raw<FMT> buf[D];
   int rid[D], rbh[D];
@@ -688,16 +699,14 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     const bool ok = idx < gr.len;
     if (ok) last = idx;
     id = ok ? idx : -1;
-    uint32_t j = gr.len ? (uint32_t)(gr.jb + last) : jlast;
+    uint32_t j = (uint32_t)(gr.jb + last);
     const uint32_t bh = j / nblk;
-    if (gr.len) {
-      // visit the blocks of each head's part of the range starting at a
-      // per-workgroup offset, so that the workgroups' streams sit at
-      // unrelated addresses rather than in step
-      const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
-      const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
-      j = ps + (j - ps + rot) % (pe - ps);
-    }
+    // visit the blocks of each head's part of the range starting at a
+    // per-workgroup offset, so that the workgroups' streams sit at
+    // unrelated addresses rather than in step
+    const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
+    const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
+    j = ps + (j - ps + rot) % (pe - ps);
     bhout = (int)bh;
     load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
   };
@@ -710,71 +719,109 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
 
-  // fp16 blocks: wavefront v * groups + g takes every (8 * groups)-th one
-  const int64_t nf = (int64_t)p.bh_count * p.fp16_blocks;
-  for (int64_t f = (int64_t)v * p.groups + g; f < nf; f += (int64_t)kGroupWaves * p.groups)
-    fp16_block(p, f / p.fp16_blocks, (int)(f % p.fp16_blocks), reinterpret_cast<uint16_t*>(stage),
-               p.part + f * p.nrep * kPartStride);
-  if (!gr.len) return;
+  // fp16 block fb of head h belongs to covering workgroup g_lo(h) + fb mod
+  // count(h); the workgroup's fp16 blocks go round robin to its wavefronts
+  {
+    int k = 0;
+    for (int h = gr.h0; h <= gr.h1; ++h) {
+      const int64_t glo = covering_lo(p, h), nc = covering_count(p, h);
+      for (int fb = 0; fb < p.fp16_blocks; ++fb) {
+        if (glo + fb % nc != g) continue;
+        if ((k & (kGroupWaves - 1)) == v)
+          fp16_block(p, h, fb, reinterpret_cast<uint16_t*>(stage),
+                     p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p));
+        ++k;
+      }
+    }
+  }
 
-  const int64_t slot0 = nf + (int64_t)kGroupWaves * g + v;
-  auto slot_ptr = [&](int h) { return p.part + (slot0 + (int64_t)kGroupWaves * h) * p.nrep * kPartStride; };
+  auto wave_slot = [&](int h, int w) { return p.part_wave + ((int64_t)kGroupWaves * (g + h) + w) * slot_floats(p); };
   if (li.writer && li.qd == 0) {
     for (int h = gr.h0; h <= gr.h1; ++h) {
-      float* dst = slot_ptr(h) + li.head * kPartStride;
+      float* dst = wave_slot(h, v) + li.head * kPartStride;
       dst[0] = neg_inf();
       dst[1] = 0.f;
     }
   }
 
-  const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
-  float qf[32];
-  f16x8 bk_static[4];
-  query_operand(q0, p.nrep, li, qf);          // qf holds the query of head qhead
-  int qhead = gr.h0;
-  WaveState ws;
-  reset(ws);
-  int cur = -1;
-  for (;;) {
+  {
+    const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
+    float qf[32];
+    f16x8 bk_static[4];
+    query_operand(q0, p.nrep, li, qf);        // qf holds the query of head qhead
+    int qhead = gr.h0;
+    WaveState ws;
+    reset(ws);
+    int cur = -1;
+    for (;;) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], false);
-      if (rid[d] < 0) goto done;             // blocks are taken in order: none left
-      if (rbh[d] != cur) {
-        if (cur >= 0) {
-          finish_segment(ws, li, slot_ptr(cur), oscale, !T::kFp8);
-          reset(ws);
+      for (int d = 0; d < D; ++d) {
+        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], false);
+        if (rid[d] < 0) goto done;           // blocks are taken in order: none left
+        if (rbh[d] != cur) {
+          if (cur >= 0) {
+            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+            reset(ws);
+          }
+          cur = rbh[d];
+          if (cur != qhead) {
+            load_query(p, cur, li, qf);
+            qhead = cur;
+          }
+          if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
         }
-        cur = rbh[d];
-        if (cur != qhead) {
-          load_query(p, cur, li, qf);
-          qhead = cur;
-        }
-        if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
+        process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
       }
-      process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
+    }
+  done:
+    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+  }
+  __syncthreads();                            // every wavefront's partials written
+
+  // merge the wavefronts' partials of each head into the workgroup's slot
+  for (int h = gr.h0; h <= gr.h1; ++h) {
+    for (int idx = threadIdx.x; idx < p.nrep * kHeadDim; idx += kGroupThreads) {
+      const int hh = idx / kHeadDim, c = idx % kHeadDim;
+      float M = neg_inf();
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) M = fmaxf(M, wave_slot(h, w)[hh * kPartStride]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) {
+        const float* sp = wave_slot(h, w) + hh * kPartStride;
+        const float m = sp[0];
+        if (m != neg_inf()) {
+          const float wt = exp2f(m - M);
+          L = __builtin_fmaf(wt, sp[1], L);
+          O = __builtin_fmaf(wt, sp[4 + c], O);
+        }
+      }
+      float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
+      if (c == 0) {
+        dst[0] = M;
+        dst[1] = L;
+      }
+      dst[4 + c] = O;
     }
   }
-done:
-  if (cur >= 0) finish_segment(ws, li, slot_ptr(cur), oscale, !T::kFp8);
+
 }
 
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16;
 
-// No quantized blocks yet: every wavefront only takes its fp16 blocks.
-__device__ void fp16_only(const AttnParams& p, char* lds) {
+// No quantized blocks yet: workgroup g takes the fp16 blocks of head g.
+__device__ void fp16_group(const AttnParams& p, char* lds) {
   const int g = blockIdx.x;
   const int v = threadIdx.x >> 6;
-  const int64_t nf = (int64_t)p.bh_count * p.fp16_blocks;
-  for (int64_t f = (int64_t)v * p.groups + g; f < nf; f += (int64_t)kGroupWaves * p.groups)
-    fp16_block(p, f / p.fp16_blocks, (int)(f % p.fp16_blocks), reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
-               p.part + f * p.nrep * kPartStride);
+  for (int fb = v; fb < p.fp16_blocks; fb += kGroupWaves)
+    fp16_block(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
+               p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kGroupThreads) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  if (p.nblk == 0) fp16_only(p, lds);
+  if (p.nblk == 0) fp16_group(p, lds);
   else group_main<FMT>(p, lds);
 }
 
@@ -782,26 +829,23 @@ constexpr int kReduceThreads = 128;
 constexpr int kReduceRegSlots = 32;       // slots whose output this thread loads at once
 
 // out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s,
-// over the head's fp16 slots and body slots (empty slots weigh 0).  All loads
-// of a pass of up to kReduceRegSlots slots are issued together (one memory
-// round trip).
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) {
+// over the head's workgroup slots and fp16 slots (empty slots weigh 0 and
+// their output is not read).  All loads of a pass of up to kReduceRegSlots
+// slots are issued together (one memory round trip).
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnParams p) {
   __shared__ float wts[kReduceRegSlots];
   __shared__ float msh[kReduceRegSlots], lsh[kReduceRegSlots];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int g = hq / p.nrep, hh = hq % p.nrep;
-  const int64_t bh = (int64_t)b * p.hkv + g;
+  const int hh = hq % p.nrep;
+  const int64_t h = (int64_t)b * p.hkv + hq / p.nrep;
   const int nf = p.fp16_blocks;
-  int64_t g_lo = 0, ng = 0;
-  if (p.nblk > 0) {
-    g_lo = bh * p.nblk / p.group_blocks;
-    ng = ((bh + 1) * p.nblk - 1) / p.group_blocks - g_lo + 1;
-  }
-  const int ns = nf + kGroupWaves * (int)ng;
-  const int64_t fslots = (int64_t)p.bh_count * nf;
+  const int64_t g_lo = p.nblk > 0 ? covering_lo(p, h) : 0;
+  const int ng = p.nblk > 0 ? (int)covering_count(p, h) : 0;
+  const int ns = ng + nf;
   auto slot_ptr = [&](int s) -> const float* {
-    const int64_t slot = s < nf ? bh * nf + s : fslots + (int64_t)kGroupWaves * (g_lo + bh) + (s - nf);
-    return p.part + (slot * p.nrep + hh) * kPartStride;
+    const float* base = s < ng ? p.part_group + (g_lo + s + h) * slot_floats(p)
+                               : p.part_fp16 + (h * nf + (s - ng)) * slot_floats(p);
+    return base + hh * kPartStride;
   };
   float M = neg_inf(), L = 0.f, O = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kReduceRegSlots) {
@@ -834,7 +878,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceParams p) 
     __syncthreads();
   }
   const _Float16 r = (_Float16)(O / L);
-  p.out[((int64_t)b * p.hkv * p.nrep + hq) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
+  p.out[(h * p.nrep + hh) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
 }
 
 }  // namespace
@@ -848,11 +892,8 @@ hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s) {
     case KVQ_FP8_E4M3: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E4M3>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_kernel, dim3(p.hkv * p.nrep, batch), dim3(kReduceThreads), 0, s, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(reduce_kernel, dim3(p.hkv * p.nrep, p.bh_count / p.hkv), dim3(kReduceThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -74,19 +74,19 @@ struct AttnPlan {
 
 // Split the work: the quantized blocks of all heads into ranges of
 // group_blocks blocks, one per workgroup (by default one range per compute
-// unit); the fp16 segment of each head into 32-token blocks, at most one per
-// wavefront of the grid at a time.
+// unit); the fp16 segment of each head into 32-token blocks handled by the
+// workgroups whose range touches the head (one workgroup per head when no
+// block is quantized yet).  Partial slots: one per fp16 block, plus, for the
+// quantized blocks, kGroupWaves + 1 per (workgroup, head) index g + bh.
 AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpg) {
   AttnPlan a{};
   const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
   a.fp16_blocks = (n_fp16_tokens + kBlock - 1) / kBlock;
-  const int64_t nf = bh * a.fp16_blocks;
   const int64_t total = bh * nblk;
   if (bpg > 0) a.group_blocks = bpg;
   else a.group_blocks = total > 0 ? (total + device_cus() - 1) / device_cus() : 1;
-  const int64_t body_groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : 0;
-  a.groups = std::max<int64_t>(std::max<int64_t>(body_groups, (nf + kGroupWaves - 1) / kGroupWaves), 1);
-  a.slots = nf + (total > 0 ? kGroupWaves * (a.groups + bh) : 0);
+  a.groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : bh;
+  a.slots = bh * a.fp16_blocks + (total > 0 ? (kGroupWaves + 1) * (a.groups + bh) : 0);
   return a;
 }
 
@@ -264,13 +264,12 @@ int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpg, uint64_t* bytes) {
   const uint64_t bh = (uint64_t)L.batch * L.num_kv_heads;
   // worst case over every cache length: all NB blocks quantized and the
   // largest fp16 segment (S sinks + R + 31 residual tokens); the library's
-  // own split uses at most one workgroup per compute unit for the body
+  // own split uses at most one workgroup per compute unit
   const uint64_t total = bh * (uint64_t)c->n_blocks_cap;
   const uint64_t nf = bh * (((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock);
   uint64_t groups = 0;
   if (total > 0) groups = bpg > 0 ? (total + bpg - 1) / bpg : std::min<uint64_t>(total, (uint64_t)device_cus());
-  groups = std::max<uint64_t>(std::max<uint64_t>(groups, (nf + kGroupWaves - 1) / kGroupWaves), 1);
-  *bytes = (nf + (total > 0 ? kGroupWaves * (groups + bh) : 0)) * slot_bytes(L);
+  *bytes = (nf + (total > 0 ? (kGroupWaves + 1) * (groups + bh) : 0)) * slot_bytes(L);
   return KVQ_OK;
 }
 
@@ -289,7 +288,8 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   // workspace is checked before anything touches the device
   if (!ws) return KVQ_ERR_WORKSPACE;
   const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpg);
-  if ((uint64_t)a.slots * slot_bytes(L) > ws_bytes) return KVQ_ERR_WORKSPACE;
+  const uint64_t sb = slot_bytes(L);
+  if ((uint64_t)a.slots * sb > ws_bytes) return KVQ_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
 
@@ -305,7 +305,10 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));
   p.v_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_SINK));
   p.q = static_cast<const uint16_t*>(q);
-  p.part = static_cast<float*>(ws);
+  p.out = static_cast<uint16_t*>(out);
+  p.part_fp16 = static_cast<float*>(ws);
+  p.part_wave = p.part_fp16 + bh * a.fp16_blocks * (sb / sizeof(float));
+  p.part_group = p.part_wave + (nblk > 0 ? kGroupWaves * (a.groups + bh) : 0) * (int64_t)(sb / sizeof(float));
   p.hkv = L.num_kv_heads;
   p.nrep = L.num_q_heads / L.num_kv_heads;
   p.nb_cap = c->n_blocks_cap;
@@ -324,16 +327,6 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.v_scale = L.v_scale;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_attention(L.format, p, s) != hipSuccess) return KVQ_ERR_HIP;
-  ReduceParams rp{};
-  rp.part = p.part;
-  rp.out = static_cast<uint16_t*>(out);
-  rp.hkv = p.hkv;
-  rp.nrep = p.nrep;
-  rp.nblk = p.nblk;
-  rp.group_blocks = p.group_blocks;
-  rp.fp16_blocks = p.fp16_blocks;
-  rp.bh_count = p.bh_count;
-  if (launch_reduce(rp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }
 

@@ -59,17 +59,17 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 // Work: the quantized blocks of all heads, flattened head-major (block j is
 // block j mod nblk of head j / nblk), are cut into ranges of group_blocks
 // blocks, one per workgroup of kGroupWaves wavefronts; the wavefronts of a
-// workgroup take blocks of its range in turn.  The fp16 segment of every head
-// (sinks, then residual ring) is cut into 32-token blocks handled one per
-// wavefront.
-// Partial results: kPartStride floats per query head, n_rep heads per slot.
-//   fp16 region  slot bh * fp16_blocks + fb              (fp16 block fb of head bh)
-//   body region  slot F + kGroupWaves * (g + bh) + w     (wavefront w of workgroup g,
-//                F = bh_count * fp16_blocks               its blocks of head bh)
-// Workgroup g covers heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk), so
-// g + bh never collides between workgroups, and the body slots of one head
-// are contiguous.  A wavefront that gets no block of a head of its range
-// marks the slot empty (m = -inf, l = 0).
+// workgroup take the blocks of its range in turn.  The fp16 segment of every
+// head (sinks, then residual ring) is cut into 32-token blocks, dealt round
+// robin to the workgroups whose range touches the head.
+// Partial results (kPartStride floats per query head, n_rep heads per slot):
+//   part_fp16   slot bh * fp16_blocks + fb       fp16 block fb of head bh
+//   part_wave   slot kGroupWaves * (g + bh) + w   wavefront w of workgroup g, head bh
+//   part_group  slot g + bh                      workgroup g, head bh (its wavefronts merged)
+// Workgroup g's range touches heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk),
+// so g + bh never collides between workgroups.  A second kernel combines each
+// head's workgroup and fp16 partials and writes the output rows.
+// With no quantized block (nblk == 0) workgroup g takes the fp16 blocks of head g.
 struct AttnParams {
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -80,7 +80,10 @@ struct AttnParams {
   const uint16_t* k_sink;
   const uint16_t* v_sink;
   const uint16_t* q;      // fp16 [B][Hq][D]
-  float* part;            // partial slots (see above)
+  uint16_t* out;          // fp16 [B][Hq][D]
+  float* part_fp16;
+  float* part_wave;
+  float* part_group;
   int32_t hkv;
   int32_t nrep;           // NR = Hq / Hkv (1, 2, 4 or 8)
   int32_t nb_cap;         // NB (block stride of the code / meta planes)
@@ -98,13 +101,6 @@ struct AttnParams {
   float k_scale, v_scale; // FP8
 };
 
-struct ReduceParams {
-  const float* part;
-  uint16_t* out;          // fp16 [B][Hq][D]
-  int32_t hkv, nrep, nblk, group_blocks, fp16_blocks, bh_count;
-};
-
 hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s);
-hipError_t launch_reduce(const ReduceParams& p, int batch, hipStream_t s);
 
 }  // namespace kvq

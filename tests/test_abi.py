@@ -147,11 +147,12 @@ def test_attention_errors():
     need = ctypes.c_uint64()
     assert L.kvq_workspace_bytes(ctypes.byref(h), 0, ctypes.byref(need)) == 0
     # worst case: one slot per fp16 block (ceil((S + R + 31) / 32) per head) plus, for the
-    # quantized blocks, 8 per workgroup and 8 per head; without a device the library
-    # assumes 256 compute units, so its split uses min(256, 4 * 61) workgroups
+    # quantized blocks, 8 wavefront slots and 1 workgroup slot per (workgroup + head)
+    # index; without a device the library assumes 256 compute units, so its split uses
+    # min(256, 4 * 61) workgroups
     bh, nb = 4, (2000 - 4 - 32) // 32
     nf = bh * (-(-(4 + 32 + 31) // 32))
-    assert need.value == (nf + 8 * (min(256, bh * nb) + bh)) * slot
+    assert need.value == (nf + 9 * (min(256, bh * nb) + bh)) * slot
     big = (1 << 20) + 1
     assert L.kvq_workspace_bytes(ctypes.byref(h), big, ctypes.byref(need)) == -2
     assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == -8  # empty
@@ -166,9 +167,9 @@ def test_attention_errors():
     assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 0, 2, None) == -2
     # an explicit split needing more than the caller's workspace is refused before any
     # launch: at n = 2000 there are 61 blocks per head and 4 + 44 fp16 tokens (2 fp16
-    # blocks per head), so blocks_per_group = 1 needs 8 + 8 * (244 + 4) slots
+    # blocks per head), so blocks_per_group = 1 needs 8 + 9 * (244 + 4) slots
     h.n_tokens = 2000
-    exact = (8 + 8 * (244 + 4)) * slot
+    exact = (8 + 9 * (244 + 4)) * slot
     assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, 0, None) == -6
     assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), exact - 1, 1, 1, None) == -6
     w1 = ctypes.c_uint64()

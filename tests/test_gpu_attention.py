@@ -7,6 +7,7 @@ the fp16 output rounding alone contributes up to 2^-11 |out|.
 """
 import numpy as np
 import pytest
+import torch
 
 from oracle import attention as oattn
 from oracle import cache as ocache
@@ -14,7 +15,7 @@ from oracle import quant
 from quantized_kv_cache_quant_amd import kvq, synth
 
 from kvq_testlib import (append_chunks, attention_gpu, make_cache, olayout_of, read_state,
-                         require_gpu, substate)
+                         require_gpu, substate, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +121,27 @@ def test_split_invariance_and_determinism(fmt):
     for bpg in (3, 0):
         again = attention_gpu(c, q, bpg, True)
         assert np.array_equal(again.astype(np.float64), outs[bpg, True]), bpg   # bitwise repeatable
+
+
+def test_workspace_reuse_any_contents():
+    """One workspace, filled with NaN to start with, serves repeated calls and caches of
+    other shapes; the deterministic mode repeats bit for bit."""
+    require_gpu()
+    ca, kwa, qa = _build("int8", 2, 4, 4, 32 * 80 + 7, 32, 0, seed=11)
+    cb, kwb, qb = _build("int4", 1, 2, 8, 32 * 300 + 50, 128, 4, seed=12)
+    wsb = max(ca.workspace_bytes(5), cb.workspace_bytes(0), ca.workspace_bytes(0))
+    ws = torch.full((wsb // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    outs = []
+    for c, q, bpg in ((ca, qa, 0), (cb, qb, 0), (ca, qa, 5), (ca, qa, 0), (cb, qb, 0)):
+        qd = to_dev(q)
+        out = torch.empty_like(qd)
+        c.attention(qd, out, ws, bpg, True)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().astype(np.float64))
+    assert np.array_equal(outs[0], outs[3]) and np.array_equal(outs[1], outs[4])
+    assert np.max(np.abs(outs[0] - _oracle_out(ca, kwa, qa))) <= TOL
+    assert np.max(np.abs(outs[1] - _oracle_out(cb, kwb, qb))) <= TOL
+    assert np.max(np.abs(outs[2] - outs[0])) <= TOL
 
 
 def test_closed_forms_on_gpu():
