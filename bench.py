@@ -2,21 +2,30 @@
 
 One step = for every layer of the model: append one new token's K / V to
 that layer's packed cache (quantize-on-append) and run fused-dequant decode
-attention for all query heads (split-K kernel + reduce).  Inputs are
-synthetic and already resident in HBM when the timed region starts.  Each
-layer owns its own cache buffer, so the timed loop streams every layer's
-packed cache from HBM (one layer's cache is larger than the 256 MB
-last-level cache, and the 32 layers together are ~10 GB).
+attention for all query heads (split-K attention kernel + reduce).  Inputs
+are synthetic and already resident in HBM when the timed region starts.
+Each layer owns its own cache buffer, so the timed loop streams every
+layer's packed cache from HBM (one layer's cache is larger than the 256 MB
+last-level cache, and the 32 layers together are ~8 GB).
 
 Default workload: the Llama-3-8B layer shape (32 query / 8 KV heads,
 head_dim 128) at batch 16 and 8192 cached tokens, 32 layers, with the cache
 quantized to INT8 (headline) and to FP8 E4M3.  The single JSON line on
 stdout carries the INT8 numbers as "value" and the FP8 numbers under "fp8".
 
-Reported: effective KV GB/s = algorithmic attention bytes of the timed steps
-/ their wall time (appends included), tokens/s = batch / step time, and a
-roofline entry for the decode-attention call measured with HIP events on
-the stream it runs on.
+Timed regions, both bracketed by HIP events on the stream the library
+launches on (torch's current stream):
+  * steps: `--steps` decode steps back to back -> value (effective KV GB/s =
+    algorithmic attention bytes / wall time, appends included), ms_per_step,
+    tokens/s;
+  * attention sweep: every layer's kv_decode_attention call, each bracketed
+    by its own event pair -> the roofline entry (algorithmic bytes per call /
+    mean call time).  The events sit outside the step loop because an event
+    record between launches adds a few microseconds of idle time per call.
+roofline.traffic comes from the FETCH_SIZE / WRITE_SIZE counter passes
+recorded in profiles/attn_counters.json, scaled by the plain-copy
+calibration stored there, and is null when the attention source has changed
+since those counters were taken.
 """
 from __future__ import annotations
 
@@ -107,36 +116,43 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     ws = torch.empty(max(c.workspace_bytes(args.blocks_per_group) for c in caches) // 4 + 4,
                      dtype=torch.float32, device="cuda")
 
-    def step(j, ev=None):
-        for li, c in enumerate(caches):
+    def step(j):
+        for c in caches:
             c.append(steps_k[j], steps_v[j])
-            if ev is not None:
-                ev[li][0].record()
             c.attention(q, out, ws, args.blocks_per_group)
-            if ev is not None:
-                ev[li][1].record()
 
     for j in range(args.warmup):
         step(j)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
-           for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for s in range(args.steps):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    attn_ms = [evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps) for li in range(layers)]
+
+    # attention sweep: each call between its own pair of events
+    rounds = max(2, args.steps // 8)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in caches]
+           for _ in range(rounds)]
+    for r in range(rounds):
+        for li, c in enumerate(caches):
+            evs[r][li][0].record()
+            c.attention(q, out, ws, args.blocks_per_group)
+            evs[r][li][1].record()
+    torch.cuda.synchronize()
+    attn_ms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
+    n_final = n0 + total_steps
+    sweep_bytes = sum(accounting.attention_bytes(b, hkv, hq, d, n_final, fmt, w.sink_tokens, w.residual_tokens)
+                      for fmt in fmt_list) / layers
     nbytes = 0
     for s in range(args.steps):
         n = n0 + args.warmup + s + 1
         for fmt in fmt_list:
             nbytes += accounting.attention_bytes(b, hkv, hq, d, n, fmt, w.sink_tokens, w.residual_tokens)
-    per_call_bytes = nbytes / (args.steps * layers)
     ms_step = total_ms / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
     res = {
@@ -146,17 +162,37 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         "effective_gbps": nbytes / (total_ms * 1e-3) / 1e9,
         "tokens_per_s": b / (ms_step * 1e-3),
         "attn_call_us": attn_avg_ms * 1e3,
-        "attn_gbps": per_call_bytes / (attn_avg_ms * 1e-3) / 1e9,
-        "append_us_per_layer": (ms_step - attn_avg_ms * layers) * 1e3 / layers,
-        "bytes_per_attn_call": per_call_bytes,
+        "attn_gbps": sweep_bytes / (attn_avg_ms * 1e-3) / 1e9,
+        "step_us_per_layer": ms_step * 1e3 / layers,
+        "bytes_per_attn_call": sweep_bytes,
+        "attn_calls_timed": len(attn_ms),
     }
     res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
     log(f"{'/'.join(res['formats'])}: {ms_step:.3f} ms/step, {res['tokens_per_s']:.0f} tok/s, "
-        f"effective {res['effective_gbps']:.0f} GB/s, attention call {res['attn_call_us']:.1f} us "
+        f"effective {res['effective_gbps']:.0f} GB/s; attention call {res['attn_call_us']:.1f} us "
         f"= {res['attn_gbps']:.0f} GB/s")
     del caches, steps_k, steps_v, ws
     torch.cuda.empty_cache()
     return res
+
+
+def counter_traffic(fmt):
+    """Per-call HBM bytes of the attention kernels from profiles/attn_counters.json, or None
+    when the file is absent, has no entry for fmt, or was taken on another attention source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_counters.json")
+    src = os.path.join(ROOT, "quantized_kv_cache_quant_amd", "csrc", "kvq_attn.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kvq_attn_hip_sha256") != digest or fmt not in rec.get("per_call", {}):
+        return None
+    c = rec["per_call"][fmt]
+    cal = rec["calibration"]
+    kib = 1024.0
+    return (c["fetch_kib"] * cal["fetch_factor"] + c["write_kib"] * cal["write_factor"]) * kib
 
 
 def cpu_baseline(w, fmt, seconds):
@@ -246,12 +282,14 @@ def main():
         "tokens_per_s": round(head["tokens_per_s"], 1),
         "pct_of_hbm_peak": round(head["pct_of_hbm_peak"], 2),
         "attn_call_us": round(head["attn_call_us"], 2),
-        "append_us_per_layer": round(head["append_us_per_layer"], 2),
+        "step_us_per_layer": round(head["step_us_per_layer"], 2),
         "copy_gbps_measured": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(head["attn_gbps"], 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(variants[0]),
                      "kernel": "attn_kernel + reduce_kernel (one kv_decode_attention call)",
-                     "bytes_per_launch": head["bytes_per_attn_call"]},
+                     "bytes_per_launch": head["bytes_per_attn_call"],
+                     "call_us": round(head["attn_call_us"], 2)},
     }
     for var in variants[1:]:
         r = results[var]
