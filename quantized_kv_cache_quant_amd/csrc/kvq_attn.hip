@@ -676,6 +676,11 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   float* stage = reinterpret_cast<float*>(lds + v * kWaveLds);
   int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
 
+  // the block counter starts at zero; the barrier comes before any load is
+  // issued, so no wavefront waits on another's loads
+  if (threadIdx.x == 0) *ctr = 0;
+  __syncthreads();
+
   // query rows of the range's first head, loaded before the blocks
   const QRaw q0 = load_query_raw(p.q + (int64_t)gr.h0 * p.nrep * kHeadDim, p.nrep, li);
 
@@ -686,9 +691,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   Raw<FMT> buf[D];
   int rid[D], rbh[D];
   int last = 0, kst = 0;
-  auto fetch = [&](Raw<FMT>& r, int& id, int& bhout, bool fixed) {
+  auto fetch = [&](Raw<FMT>& r, int& id, int& bhout) {
     int idx;
-    if (fixed || p.deterministic) {
+    if (p.deterministic) {
       idx = v + kGroupWaves * kst;
       ++kst;
     } else {
@@ -711,13 +716,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
   };
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], true);
-
-  if (threadIdx.x == 0) *ctr = kGroupWaves * (D - 1);   // the prefetched blocks were fixed
-  // the counter's LDS write done, then the workgroup barrier; the loads
-  // stay in flight (vmcnt 63, expcnt 7, lgkmcnt 0)
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
+  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d]);
 
   // fp16 block fb of head h belongs to covering workgroup g_lo(h) + fb mod
   // count(h); the workgroup's fp16 blocks go round robin to its wavefronts
@@ -756,7 +755,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], false);
+        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D]);
         if (rid[d] < 0) goto done;           // blocks are taken in order: none left
         if (rbh[d] != cur) {
           if (cur >= 0) {
@@ -778,33 +777,52 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   }
   __syncthreads();                            // every wavefront's partials written
 
-  // merge the wavefronts' partials of each head into the workgroup's slot
-  for (int h = gr.h0; h <= gr.h1; ++h) {
-    for (int idx = threadIdx.x; idx < p.nrep * kHeadDim; idx += kGroupThreads) {
-      const int hh = idx / kHeadDim, c = idx % kHeadDim;
-      float M = neg_inf();
+  // merge the wavefronts' partials of each head into the workgroup's slot:
+  // thread (c, hh0) takes channel c of query heads hh0 and hh0 + 4, all
+  // loads of a head issued before any is used
+  {
+    const int c = threadIdx.x % kHeadDim, hh0 = threadIdx.x / kHeadDim;
+    static_assert(kGroupThreads == 4 * kHeadDim, "merge: four query heads per pass");
+    for (int h = gr.h0; h <= gr.h1; ++h) {
+      float m[2][kGroupWaves], l[2][kGroupWaves], o[2][kGroupWaves];
 #pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) M = fmaxf(M, wave_slot(h, w)[hh * kPartStride]);
-      float L = 0.f, O = 0.f;
+      for (int k = 0; k < 2; ++k) {
+        const int hh = k ? hh0 + 4 : hh0;
+        if (hh < p.nrep) {
 #pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) {
-        const float* sp = wave_slot(h, w) + hh * kPartStride;
-        const float m = sp[0];
-        if (m != neg_inf()) {
-          const float wt = exp2f(m - M);
-          L = __builtin_fmaf(wt, sp[1], L);
-          O = __builtin_fmaf(wt, sp[4 + c], O);
+          for (int w = 0; w < kGroupWaves; ++w) {
+            const float* sp = wave_slot(h, w) + hh * kPartStride;
+            m[k][w] = sp[0];
+            l[k][w] = sp[1];
+            o[k][w] = sp[4 + c];
+          }
         }
       }
-      float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
-      if (c == 0) {
-        dst[0] = M;
-        dst[1] = L;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int hh = k ? hh0 + 4 : hh0;
+        if (hh >= p.nrep) continue;
+        float M = neg_inf();
+#pragma unroll
+        for (int w = 0; w < kGroupWaves; ++w) M = fmaxf(M, m[k][w]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGroupWaves; ++w) {
+          if (m[k][w] != neg_inf()) {
+            const float wt = exp2f(m[k][w] - M);
+            L = __builtin_fmaf(wt, l[k][w], L);
+            O = __builtin_fmaf(wt, o[k][w], O);
+          }
+        }
+        float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
+        if (c == 0) {
+          dst[0] = M;
+          dst[1] = L;
+        }
+        dst[4 + c] = O;
       }
-      dst[4 + c] = O;
     }
   }
-
 }
 
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16;
