@@ -179,6 +179,16 @@ __device__ constexpr int k_chan(int kb, int j) {
   else return 8 * kb + j;
 }
 
+// Within-quarter position ("slot") of channel w (0..31) in the Key operand
+// order: slot 8 kb + j carries channel k_chan(kb, j).
+template <int FMT>
+__device__ constexpr int k_slot(int w) {
+  for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 8; ++j)
+      if (k_chan<FMT>(kb, j) == w) return 8 * kb + j;
+  return 0;
+}
+
 // Power-of-two factor the conversion leaves on code i (channel for K, token
 // for V); it is divided out of the staged scale.
 template <int FMT>
@@ -245,17 +255,55 @@ constexpr float kLazyScaleMax = 255.0f;
 //   [256,384) V scale / divisor [g][t]   [384,512) V s*z [g][t]
 constexpr int kStage = 512;
 
-// Lane L holds the (s, z) pairs 2L and 2L+1 of each metadata block.
+// Slot (see k_slot) of within-quarter channel w, by formula.
+template <int FMT>
+__device__ __forceinline__ int k_slot_of(int w) {
+  if constexpr (FMT == KVQ_INT4) {
+    const int r = w & 7;
+    return (w & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
+  } else if constexpr (FMT == KVQ_INT2) {
+    const int rem = w & 15, rem2 = rem & 7;
+    return 8 * (2 * (w >> 4) + (rem2 >> 2)) + 2 * (rem2 & 3) + (rem >> 3);
+  } else {
+    return w;
+  }
+}
+
+template <int FMT>
+__device__ constexpr bool k_slot_formula_ok() {
+  for (int w = 0; w < 32; ++w) {
+    int r = w & 7, rem = w & 15, rem2 = rem & 7;
+    int f = FMT == KVQ_INT4 ? (w & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1)
+          : FMT == KVQ_INT2 ? 8 * (2 * (w >> 4) + (rem2 >> 2)) + 2 * (rem2 & 3) + (rem >> 3) : w;
+    if (f != k_slot<FMT>(w)) return false;
+  }
+  return true;
+}
+static_assert(k_slot_formula_ok<KVQ_INT8>() && k_slot_formula_ok<KVQ_INT4>() && k_slot_formula_ok<KVQ_INT2>(),
+              "Key slot formula");
+
+// Lane L holds the (s, z) pairs 2L and 2L+1 of each metadata block.  The
+// Key scale (with log2(e) / sqrt(D) and the slot divisor folded in) and
+// s * z (with log2(e) / sqrt(D)) go to LDS in Key slot order per quarter.
 template <int FMT>
 __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
   const int c = 2 * lane;                 // K channel; V index g * 32 + t
   const int t = c & 31;
-  const float2 ks = {r.km.x * (1.0f / slot_div<FMT>(c)), r.km.z * (1.0f / slot_div<FMT>(c + 1))};
-  const float2 kz = {r.km.x * r.km.y, r.km.z * r.km.w};
+  const float sq0 = r.km.x * kQScale, sq1 = r.km.z * kQScale;
+  const float ks0 = sq0 * (1.0f / slot_div<FMT>(c)), ks1 = sq1 * (1.0f / slot_div<FMT>(c + 1));
+  const float kz0 = sq0 * r.km.y, kz1 = sq1 * r.km.w;
+  const int q0 = (c & ~31) + k_slot_of<FMT>(c & 31), q1 = (c & ~31) + k_slot_of<FMT>((c + 1) & 31);
+  if constexpr (FMT == KVQ_INT8) {
+    *reinterpret_cast<float2*>(st + q0) = float2{ks0, ks1};
+    *reinterpret_cast<float2*>(st + 128 + q0) = float2{kz0, kz1};
+  } else {
+    st[q0] = ks0;
+    st[q1] = ks1;
+    st[128 + q0] = kz0;
+    st[128 + q1] = kz1;
+  }
   const float2 vs = {r.vm.x * (1.0f / slot_div<FMT>(t)), r.vm.z * (1.0f / slot_div<FMT>(t + 1))};
   const float2 vz = {r.vm.x * r.vm.y, r.vm.z * r.vm.w};
-  *reinterpret_cast<float2*>(st + c) = ks;
-  *reinterpret_cast<float2*>(st + 128 + c) = kz;
   *reinterpret_cast<float2*>(st + 256 + c) = vs;
   *reinterpret_cast<float2*>(st + 384 + c) = vz;
 }
@@ -296,28 +344,45 @@ __device__ __forceinline__ void reset(WaveState& ws) {
   ws.z[0] = ws.z[1] = 0.f;
 }
 
-// hi / lo split of x = a * b into this column's f16 part (hi in hi columns,
-// lo = f16(x - hi) in lo columns), for two values at once.
-__device__ __forceinline__ uint32_t split2(float a0, float b0, float a1, float b1, uint32_t hmask) {
-  const f16x2 h = {(_Float16)__builtin_fmaf(a0, b0, 0.0f), (_Float16)__builtin_fmaf(a1, b1, 0.0f)};
-  const f16x2 hm = u2h(__builtin_bit_cast(uint32_t, h) & hmask);
-  const f16x2 r = {(_Float16)__builtin_fmaf(a0, b0, -(float)hm[0]), (_Float16)__builtin_fmaf(a1, b1, -(float)hm[1])};
-  return __builtin_bit_cast(uint32_t, r);
+// hi / lo operand pairs.  A column's operand is hi = f16(x) in hi columns and
+// lo = f16(x - f16(x)) in lo columns; with xz = x in lo columns and 0 in hi
+// columns both are r = f16(x - f16(xz)).  v_fma_mix rounds the fp32 fma
+// a * b - c once to f16; its operands may be fp32 or a half of a packed f16
+// register (op_sel / op_sel_hi), so one instruction forms each half.
+
+// x = q * s for two channels: q from packed f16 (both halves of qh, and of
+// qz = qh in lo columns, 0 in hi columns), s0 / s1 fp32.
+__device__ __forceinline__ uint32_t split_q(uint32_t qz, uint32_t qh, float s0, float s1) {
+  uint32_t hz, r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(hz) : "v"(qz), "v"(s0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(hz) : "v"(qz), "v"(s1));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(qh), "v"(s0), "v"(hz));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
+  return r;
 }
 
-// The same split with the hi part already zeroed in hi columns (ab = a or 0).
-__device__ __forceinline__ uint32_t split2z(float a0, float ab0, float b0, float a1, float ab1, float b1) {
-  const f16x2 h = {(_Float16)__builtin_fmaf(ab0, b0, 0.0f), (_Float16)__builtin_fmaf(ab1, b1, 0.0f)};
-  const f16x2 r = {(_Float16)__builtin_fmaf(a0, b0, -(float)h[0]), (_Float16)__builtin_fmaf(a1, b1, -(float)h[1])};
-  return __builtin_bit_cast(uint32_t, r);
+// x = a * b for two values, all fp32; az = a in lo columns, 0 in hi columns.
+__device__ __forceinline__ uint32_t split_p(float a0, float az0, float b0, float a1, float az1, float b1) {
+  uint32_t hz, r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hz) : "v"(az0), "v"(b0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(hz) : "v"(az1), "v"(b1));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a0), "v"(b0), "v"(hz));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
+  return r;
 }
 
-// Query operand values of this lane's column head (its quarter's 32
-// channels) from a KV head's n_rep query rows ([n_rep][128] fp16), in
-// base-2 logit units; zero in columns of heads past n_rep.  The raw load and
-// the conversion are separate so the load can be issued early.
+// Query of this lane's column head (its quarter's 32 channels) from a KV
+// head's n_rep query rows ([n_rep][128] fp16): packed f16 pairs in Key
+// operand slot order (h[p] = slots 2p, 2p+1), and the same zeroed in hi
+// columns (z).  Both are zero in columns of heads past n_rep.  The scale
+// log2(e) / sqrt(D) is applied with the Key scales.  The raw load and the
+// conversion are separate so the load can be issued early.
 struct QRaw {
   uint4 w[4];
+};
+
+struct QOp {
+  uint32_t h[16], z[16];
 };
 
 __device__ __forceinline__ QRaw load_query_raw(const uint16_t* rows, int nrep, const LaneInfo& li) {
@@ -329,35 +394,36 @@ __device__ __forceinline__ QRaw load_query_raw(const uint16_t* rows, int nrep, c
   return r;
 }
 
-__device__ __forceinline__ void query_operand(const QRaw& r, int nrep, const LaneInfo& li, float* qf) {
-  const bool valid = li.head < nrep;
+template <int FMT>
+__device__ __forceinline__ void query_operand(const QRaw& r, int nrep, const LaneInfo& li, QOp& q) {
+  const uint32_t keep = li.head < nrep ? 0xFFFFFFFFu : 0u;
+  const uint32_t w[16] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w,
+                          r.w[2].x, r.w[2].y, r.w[2].z, r.w[2].w, r.w[3].x, r.w[3].y, r.w[3].z, r.w[3].w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t wv[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f16x2 h = u2h(wv[j]);
-      qf[8 * i + 2 * j] = valid ? (float)h[0] * kQScale : 0.f;
-      qf[8 * i + 2 * j + 1] = valid ? (float)h[1] * kQScale : 0.f;
-    }
+  for (int pr = 0; pr < 16; ++pr) {
+    const int c0 = k_chan<FMT>(pr >> 2, 2 * (pr & 3)), c1 = k_chan<FMT>(pr >> 2, 2 * (pr & 3) + 1);
+    const uint32_t lo = (w[c0 >> 1] >> (16 * (c0 & 1))) & 0xFFFFu;
+    const uint32_t hi = (w[c1 >> 1] >> (16 * (c1 & 1))) & 0xFFFFu;
+    q.h[pr] = (lo | (hi << 16)) & keep;
+    q.z[pr] = q.h[pr] & li.hmask;
   }
 }
 
 // The same from the query rows of KV head bh in global memory.
-__device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, float* qf) {
-  query_operand(load_query_raw(p.q + bh * p.nrep * kHeadDim, p.nrep, li), p.nrep, li, qf);
+template <int FMT>
+__device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, QOp& q) {
+  query_operand<FMT>(load_query_raw(p.q + bh * p.nrep * kHeadDim, p.nrep, li), p.nrep, li, q);
 }
 
 // Static q operands (hi / lo) for Keys without a per-block scale (FP8 with
-// its per-tensor scale, fp16 segment with scale 1).
-template <int FMT>
-__device__ __forceinline__ void static_q(const float* qf, float scale, const LaneInfo& li, f16x8* bk) {
+// its per-tensor scale, fp16 segment with scale 1); scale includes
+// log2(e) / sqrt(D).
+__device__ __forceinline__ void static_q(const QOp& q, float scale, f16x8* bk) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     uint32_t bw[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      bw[v] = split2(qf[k_chan<FMT>(kb, 2 * v)], scale, qf[k_chan<FMT>(kb, 2 * v + 1)], scale, li.hmask);
+    for (int v = 0; v < 4; ++v) bw[v] = split_q(q.z[4 * kb + v], q.h[4 * kb + v], scale, scale);
     bk[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
   }
 }
@@ -395,12 +461,13 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
 __device__ __forceinline__ f16x8 p_operand(const float pr[2][4], const LaneInfo& li) {
   uint32_t bw[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) bw[v] = split2(pr[0][v], 1.0f, pr[1][v], 1.0f, li.hmask);
+  for (int v = 0; v < 4; ++v)
+    bw[v] = split_p(pr[0][v], li.is_lo ? pr[0][v] : 0.f, 1.0f, pr[1][v], li.is_lo ? pr[1][v] : 0.f, 1.0f);
   return cat(bw[0], bw[1], bw[2], bw[3]);
 }
 
 template <int FMT>
-__device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const float* qf,
+__device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const QOp& q,
                                               const f16x8* bk_static, const LaneInfo& li) {
   using T = Traits<FMT>;
   const int qd = li.qd;
@@ -418,36 +485,30 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
                                                            acc[tile], 0, 0, 0);
   } else {
     stage_meta<FMT>(r, st, li.lane);
-    // zero-point term sum_c q_c s_c z_c over this lane's 32 channels, then
-    // over the four quarters
-    float bias = 0.f;
+    // zero-point term sum_c q_c s_c z_c over this lane's 32 channels (in
+    // slot order), then over the four quarters
+    float bias0 = 0.f, bias1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float4 z4 = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 4 * i);
-      bias = __builtin_fmaf(qf[4 * i], z4.x, bias);
-      bias = __builtin_fmaf(qf[4 * i + 1], z4.y, bias);
-      bias = __builtin_fmaf(qf[4 * i + 2], z4.z, bias);
-      bias = __builtin_fmaf(qf[4 * i + 3], z4.w, bias);
+      const f16x2 qa = u2h(q.h[2 * i]), qb = u2h(q.h[2 * i + 1]);
+      bias0 = __builtin_fmaf((float)qa[0], z4.x, bias0);
+      bias1 = __builtin_fmaf((float)qa[1], z4.y, bias1);
+      bias0 = __builtin_fmaf((float)qb[0], z4.z, bias0);
+      bias1 = __builtin_fmaf((float)qb[1], z4.w, bias1);
     }
-    bias = rows_sum(bias);
+    const float bias = rows_sum(bias0 + bias1);
     const float c0 = li.is_lo ? 0.f : -bias * kTwoM24;
     acc[0] = f32x4{c0, c0, c0, c0};
     acc[1] = acc[0];
-    float sk[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 s4 = *reinterpret_cast<const float4*>(st + 32 * qd + 4 * i);
-      sk[4 * i] = s4.x; sk[4 * i + 1] = s4.y; sk[4 * i + 2] = s4.z; sk[4 * i + 3] = s4.w;
-    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c0i = k_chan<FMT>(kb, 2 * v), c1i = k_chan<FMT>(kb, 2 * v + 1);
-        bw[v] = split2(qf[c0i], sk[c0i], qf[c1i], sk[c1i], li.hmask);
-      }
-      const f16x8 bq = cat(bw[0], bw[1], bw[2], bw[3]);
+      const float4 sa = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb);
+      const float4 sb = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb + 4);
+      const f16x8 bq = cat(split_q(q.z[4 * kb], q.h[4 * kb], sa.x, sa.y),
+                           split_q(q.z[4 * kb + 1], q.h[4 * kb + 1], sa.z, sa.w),
+                           split_q(q.z[4 * kb + 2], q.h[4 * kb + 2], sb.x, sb.y),
+                           split_q(q.z[4 * kb + 3], q.h[4 * kb + 3], sb.z, sb.w));
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bq, acc[tile], 0,
@@ -500,7 +561,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
       uint32_t bw[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) bw[v] = split2z(pr[0][v], pb[0][v], sv0[v], pr[1][v], pb[1][v], sv1[v]);
+      for (int v = 0; v < 4; ++v) bw[v] = split_p(pr[0][v], pb[0][v], sv0[v], pr[1][v], pb[1][v], sv1[v]);
       const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
@@ -561,10 +622,10 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
   const LaneInfo li = lane_info(p.nrep);
   const int lane = li.lane;
   const int nt = p.n_sink + p.n_res;
-  float qf[32];
+  QOp q;
   f16x8 bk[4];
-  load_query(p, bh, li, qf);
-  static_q<KVQ_INT8>(qf, 1.0f, li, bk);                 // natural channel order, scale 1
+  load_query<KVQ_INT8>(p, bh, li, q);                   // natural channel order, scale 1
+  static_q(q, kQScale, bk);
   WaveState ws;
   reset(ws);
   // Key rows of this lane's two tokens (one per 16-token tile), its quarter's 32 channels
@@ -668,7 +729,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   using T = Traits<FMT>;
   constexpr int D = T::kDepth + 1;
   const int g = blockIdx.x;
-  const int v = threadIdx.x >> 6;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront index, uniform
   const LaneInfo li = lane_info(p.nrep);
   const GroupRange gr = group_range(p, g);
   if (!gr.len) return;                        // (never: every workgroup has a range)
@@ -745,9 +806,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
 
   {
     const float oscale = T::kFp8 ? p.v_scale : T::kCodeScale;
-    float qf[32];
+    QOp qop;
     f16x8 bk_static[4];
-    query_operand(q0, p.nrep, li, qf);        // qf holds the query of head qhead
+    query_operand<FMT>(q0, p.nrep, li, qop);  // qop holds the query of head qhead
     int qhead = gr.h0;
     WaveState ws;
     reset(ws);
@@ -764,12 +825,12 @@ __device__ void group_main(const AttnParams& p, char* lds) {
           }
           cur = rbh[d];
           if (cur != qhead) {
-            load_query(p, cur, li, qf);
+            load_query<FMT>(p, cur, li, qop);
             qhead = cur;
           }
-          if constexpr (T::kFp8) static_q<FMT>(qf, p.k_scale, li, bk_static);
+          if constexpr (T::kFp8) static_q(qop, p.k_scale * kQScale, bk_static);
         }
-        process_block<FMT>(buf[d], stage, ws, qf, bk_static, li);
+        process_block<FMT>(buf[d], stage, ws, qop, bk_static, li);
       }
     }
   done:
@@ -830,7 +891,7 @@ constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16;
 // No quantized blocks yet: workgroup g takes the fp16 blocks of head g.
 __device__ void fp16_group(const AttnParams& p, char* lds) {
   const int g = blockIdx.x;
-  const int v = threadIdx.x >> 6;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront index, uniform
   for (int fb = v; fb < p.fp16_blocks; fb += kGroupWaves)
     fp16_block(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
                p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
