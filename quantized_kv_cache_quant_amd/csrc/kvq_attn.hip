@@ -839,30 +839,30 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   __syncthreads();                            // every wavefront's partials written
 
   // merge the wavefronts' partials of each head into the workgroup's slot:
-  // thread (c, hh0) takes channel c of query heads hh0 and hh0 + 4, all
-  // loads of a head issued before any is used
+  // thread t takes (query head, channel) items t, t + threads, ...; all
+  // loads of a head are issued before any is used
   {
-    const int c = threadIdx.x % kHeadDim, hh0 = threadIdx.x / kHeadDim;
-    static_assert(kGroupThreads == 4 * kHeadDim, "merge: four query heads per pass");
+    constexpr int kItems = 8 * kHeadDim / kGroupThreads;     // items per thread at n_rep 8
     for (int h = gr.h0; h <= gr.h1; ++h) {
-      float m[2][kGroupWaves], l[2][kGroupWaves], o[2][kGroupWaves];
+      float m[kItems][kGroupWaves], l[kItems][kGroupWaves], o[kItems][kGroupWaves];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int hh = k ? hh0 + 4 : hh0;
-        if (hh < p.nrep) {
+      for (int k = 0; k < kItems; ++k) {
+        const int idx = (int)threadIdx.x + k * kGroupThreads;
+        if (idx < p.nrep * kHeadDim) {
 #pragma unroll
           for (int w = 0; w < kGroupWaves; ++w) {
-            const float* sp = wave_slot(h, w) + hh * kPartStride;
+            const float* sp = wave_slot(h, w) + (idx / kHeadDim) * kPartStride;
             m[k][w] = sp[0];
             l[k][w] = sp[1];
-            o[k][w] = sp[4 + c];
+            o[k][w] = sp[4 + idx % kHeadDim];
           }
         }
       }
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int hh = k ? hh0 + 4 : hh0;
-        if (hh >= p.nrep) continue;
+      for (int k = 0; k < kItems; ++k) {
+        const int idx = (int)threadIdx.x + k * kGroupThreads;
+        if (idx >= p.nrep * kHeadDim) continue;
+        const int hh = idx / kHeadDim, c = idx % kHeadDim;
         float M = neg_inf();
 #pragma unroll
         for (int w = 0; w < kGroupWaves; ++w) M = fmaxf(M, m[k][w]);
@@ -898,7 +898,7 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kGroupThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   if (p.nblk == 0) fp16_group(p, lds);
   else group_main<FMT>(p, lds);

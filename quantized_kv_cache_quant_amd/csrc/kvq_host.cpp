@@ -83,8 +83,9 @@ AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t 
   const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
   a.fp16_blocks = (n_fp16_tokens + kBlock - 1) / kBlock;
   const int64_t total = bh * nblk;
+  const int64_t target = device_cus() * kGroupsPerCu;
   if (bpg > 0) a.group_blocks = bpg;
-  else a.group_blocks = total > 0 ? (total + device_cus() - 1) / device_cus() : 1;
+  else a.group_blocks = total > 0 ? (total + target - 1) / target : 1;
   a.groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : bh;
   a.slots = bh * a.fp16_blocks + (total > 0 ? (kGroupWaves + 1) * (a.groups + bh) : 0);
   return a;
@@ -268,7 +269,7 @@ int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpg, uint64_t* bytes) {
   const uint64_t total = bh * (uint64_t)c->n_blocks_cap;
   const uint64_t nf = bh * (((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock);
   uint64_t groups = 0;
-  if (total > 0) groups = bpg > 0 ? (total + bpg - 1) / bpg : std::min<uint64_t>(total, (uint64_t)device_cus());
+  if (total > 0) groups = bpg > 0 ? (total + bpg - 1) / bpg : std::min<uint64_t>(total, (uint64_t)(device_cus() * kGroupsPerCu));
   *bytes = (nf + (total > 0 ? (kGroupWaves + 1) * (groups + bh) : 0)) * slot_bytes(L);
   return KVQ_OK;
 }

@@ -14,7 +14,14 @@ constexpr int kHeadDim = 128;     // the only head_dim of this version
 constexpr int kVGroup = 32;       // channels per Value group
 constexpr int kVGroups = kHeadDim / kVGroup;
 constexpr int kPartStride = 132;  // floats per partial: m, l, 2 pad, o[128]
-constexpr int kGroupWaves = 8;           // wavefronts per attention workgroup
+#ifndef KVQ_GROUP_WAVES
+#define KVQ_GROUP_WAVES 8
+#endif
+#ifndef KVQ_GROUPS_PER_CU
+#define KVQ_GROUPS_PER_CU 1
+#endif
+constexpr int kGroupWaves = KVQ_GROUP_WAVES;        // wavefronts per attention workgroup (power of 2)
+constexpr int kGroupsPerCu = KVQ_GROUPS_PER_CU;     // workgroup ranges per compute unit (library split)
 constexpr int kMaxBlocksPerGroup = 1 << 20;
 
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
