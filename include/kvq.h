@@ -41,10 +41,16 @@
  *
  * Planes inside the caller's device buffer (offsets from kvq_cache_plane;
  * NB = max(0, max_tokens - S - R) / 32 blocks, D = head_dim, b = bits):
- *   K codes  [B][Hkv][NB*32][D*b/8] token-major; channel c at bit (c*b mod 8)
- *            of byte floor(c*b/8).  FP8: one E4M3 byte per channel.
+ *   K codes  [B][Hkv][NB][32*D*b/8].  The codes of one token are D*b/8
+ *            bytes, channel c at bit (c*b mod 8) of byte floor(c*b/8)
+ *            (FP8: one E4M3 byte per channel).  INT4, INT2: the 32 tokens'
+ *            rows one after another.  INT8, FP8: 16-byte units, unit
+ *            (2*tile + half)*64 + 16*qd + r = bytes 32*qd + 16*half .. +15
+ *            of token 16*tile + r.
  *   V codes  [B][Hkv][NB][32*D*b/8] per 32-token block: 64 records of
- *            D*b/16 bytes.  Record l = 16*qd + r holds channels 16*m + r
+ *            D*b/16 bytes, cut into 16-byte groups; group i of record l
+ *            starts at byte 16*(64*i + l) of the block.
+ *            Record l = 16*qd + r holds channels 16*m + r
  *            (m = 0 .. D/16-1) of the tokens T = (4qd .. 4qd+3,
  *            16+4qd .. 16+4qd+3):
  *              INT4       word m, nibble j = code(T[j], 16m + r)

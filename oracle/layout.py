@@ -11,10 +11,14 @@ independently so that tests can compare the library's planes byte for byte.
 
 Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
 
-* K codes   [B][Hkv][NB*32][D*b/8]  token-major; channel c of a token sits at
-  bit (c*b mod 8) of byte floor(c*b/8) (LSB first).  FP8: one byte per code.
+* K codes   [B][Hkv][NB][32*D*b/8]  the codes of one token are D*b/8 bytes,
+  channel c at bit (c*b mod 8) of byte floor(c*b/8) (LSB first; FP8: one
+  byte per code).  INT4 / INT2: the 32 tokens' byte rows one after another.
+  INT8 / FP8: 16-byte units; unit u = (2*tile + half)*(D/2) + 16*qd + r holds
+  bytes 32*qd + 16*half .. +15 of token 16*tile + r.
 * V codes   [B][Hkv][NB][32*D*b/8]  one block of 32 tokens is 64 "records"
-  of D*b/16 bytes.  Record l = 16*qd + r holds channels {16*m + r} for
+  of D*b/16 bytes, split into 16-byte groups; group i of record l is stored
+  at byte 16*(64*i + l).  Record l = 16*qd + r holds channels {16*m + r} for
   m = 0 .. D/16-1 and the eight tokens T = (4qd, 4qd+1, 4qd+2, 4qd+3,
   16+4qd, 16+4qd+1, 16+4qd+2, 16+4qd+3) of the block, laid out per format:
     INT4  word m: nibble j (bits 4j..4j+3) = code(T[j], 16m + r)
@@ -62,8 +66,8 @@ def _record_tokens(qd: int):
     return [4 * qd + j for j in range(4)] + [16 + 4 * qd + j for j in range(4)]
 
 
-def v_block_stream_order(fmt: str, d: int):
-    """(token, channel) of every code of a V block in packed-stream order."""
+def _v_record_order(fmt: str, d: int):
+    """(token, channel) of every code of a V block, record after record."""
     if d % 32:
         raise ValueError("head_dim must be a multiple of 32")
     tok, ch = [], []
@@ -89,40 +93,77 @@ def v_block_stream_order(fmt: str, d: int):
     return np.array(tok), np.array(ch)
 
 
+def _group_major(order: np.ndarray, bits: int) -> np.ndarray:
+    """Reorder a 64-record stream so 16-byte group i of record l comes at 64*i + l."""
+    per16 = 16 * 8 // bits                          # codes per 16 bytes
+    return order.reshape(64, -1, per16).transpose(1, 0, 2).reshape(-1)
+
+
+def v_block_stream_order(fmt: str, d: int):
+    """(token, channel) of every code of a V block in packed-stream order."""
+    tok, ch = _v_record_order(fmt, d)
+    bits = _bits(fmt)
+    return _group_major(tok, bits), _group_major(ch, bits)
+
+
+def k_block_stream_order(fmt: str, d: int):
+    """(token, channel) of every code of a K block in packed-stream order."""
+    bits = _bits(fmt)
+    if bits < 8:
+        return np.repeat(np.arange(BLOCK), d), np.tile(np.arange(d), BLOCK)
+    if d % 32:
+        raise ValueError("head_dim must be a multiple of 32")
+    tok, ch = [], []
+    for tile in range(BLOCK // 16):
+        for half in range(2):
+            for lane in range(d // 2):
+                qd, r = divmod(lane, 16)
+                for e in range(16):
+                    tok.append(16 * tile + r); ch.append(32 * qd + 16 * half + e)
+    return np.array(tok), np.array(ch)
+
+
 def _bits(fmt: str) -> int:
     return {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}[fmt]
 
 
-def pack_k_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
-    """[..., N, D] codes -> [..., N, D*b/8] bytes (token-major, LSB first)."""
-    return pack_bits(codes, _bits(fmt))
-
-
-def unpack_k_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
-    return unpack_bits(packed, _bits(fmt), d)
-
-
-def pack_v_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
-    """[..., NB*32, D] codes -> [..., NB, 32*D*b/8] swizzled block bytes."""
+def _pack_blocks(codes: np.ndarray, fmt: str, order) -> np.ndarray:
     codes = np.asarray(codes, np.uint8)
     n, d = codes.shape[-2:]
     assert n % BLOCK == 0
-    nb = n // BLOCK
-    blk = codes.reshape(codes.shape[:-2] + (nb, BLOCK, d))
-    tok, ch = v_block_stream_order(fmt, d)
-    stream = blk[..., tok, ch]                      # [..., NB, 32*D]
-    return pack_bits(stream, _bits(fmt))
+    blk = codes.reshape(codes.shape[:-2] + (n // BLOCK, BLOCK, d))
+    tok, ch = order(fmt, d)
+    return pack_bits(blk[..., tok, ch], _bits(fmt))
+
+
+def _unpack_blocks(packed: np.ndarray, fmt: str, d: int, order) -> np.ndarray:
+    packed = np.asarray(packed, np.uint8)
+    nb = packed.shape[-2]
+    stream = unpack_bits(packed, _bits(fmt), BLOCK * d)
+    tok, ch = order(fmt, d)
+    out = np.zeros(packed.shape[:-1] + (BLOCK, d), np.uint8)
+    out[..., tok, ch] = stream
+    return out.reshape(packed.shape[:-2] + (nb * BLOCK, d))
+
+
+def pack_k_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """[..., NB*32, D] codes -> [..., NB, 32*D*b/8] K block bytes."""
+    return _pack_blocks(codes, fmt, k_block_stream_order)
+
+
+def unpack_k_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
+    """Inverse of :func:`pack_k_codes`: [..., NB, bytes] -> [..., NB*32, D]."""
+    return _unpack_blocks(packed, fmt, d, k_block_stream_order)
+
+
+def pack_v_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """[..., NB*32, D] codes -> [..., NB, 32*D*b/8] swizzled V block bytes."""
+    return _pack_blocks(codes, fmt, v_block_stream_order)
 
 
 def unpack_v_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
     """Inverse of :func:`pack_v_codes`: [..., NB, bytes] -> [..., NB*32, D]."""
-    packed = np.asarray(packed, np.uint8)
-    nb = packed.shape[-2]
-    stream = unpack_bits(packed, _bits(fmt), BLOCK * d)
-    tok, ch = v_block_stream_order(fmt, d)
-    out = np.zeros(packed.shape[:-1] + (BLOCK, d), np.uint8)
-    out[..., tok, ch] = stream
-    return out.reshape(packed.shape[:-2] + (nb * BLOCK, d))
+    return _unpack_blocks(packed, fmt, d, v_block_stream_order)
 
 
 def pack_k_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:

@@ -144,13 +144,24 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
     __syncthreads();
   }
 
-  // 3) K codes: token-major rows, channel c at bit (c * bits) (LSB first)
+  // 3) K codes, channel c at bit (c * bits) of its token's codes (LSB first).
+  //    INT4 / INT2: token-major rows.  8-bit codes: 16-byte units ordered
+  //    (tile, half, lane); unit (tile, half, 16 qd + r) holds channels
+  //    32 qd + 16 half .. + 15 of token 16 tile + r.
   {
     constexpr int kWordsPerRow = kRowBytes / 4;
     uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
     for (int w = tid; w < kBlock * kWordsPerRow; w += 256) {
-      const int t = w / kWordsPerRow;
-      const int wi = w % kWordsPerRow;
+      int t, wi;
+      if constexpr (kBits == 8) {
+        const int u = w >> 2;                       // 16-byte unit
+        const int lane = u & 63, half = (u >> 6) & 1, tile = u >> 7;
+        t = 16 * tile + (lane & 15);
+        wi = 8 * (lane >> 4) + 4 * half + (w & 3);
+      } else {
+        t = w / kWordsPerRow;
+        wi = w % kWordsPerRow;
+      }
       uint32_t word = 0;
       if constexpr (kFp8) {
         const int c = wi * 4;
@@ -168,13 +179,14 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
     }
   }
 
-  // 4) V codes: 64 records per block in the attention kernel's operand order
+  // 4) V codes: 64 records per block in the attention kernel's operand
+  //    order, stored as 16-byte groups: group i of record l at 16 (64 i + l)
   {
     constexpr int kRecWords = kHeadDim * kBits / 16 / 4;   // words per record
     uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
     for (int w = tid; w < 64 * kRecWords; w += 256) {
-      const int lane = w / kRecWords;
-      const int wi = w % kRecWords;
+      const int lane = (w >> 2) & 63;
+      const int wi = 4 * (w >> 8) + (w & 3);
       const int qd = lane >> 4, r = lane & 15;
       uint32_t word = 0;
       if constexpr (kBits == 4) {                 // word m: nibble j = T[j], channel 16m + r

@@ -205,8 +205,19 @@ struct Raw {
   float4 km, vm;                         // this lane's 16 bytes of each metadata block
 };
 
+// Code lines are read once per call: nontemporal loads keep them from
+// displacing the metadata, query and partials in the caches.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return uint4{t.x, t.y, t.z, t.w};
+}
+
 // Loads one block.  bh and blk are wave-uniform, so the block base is a
 // scalar and the per-lane parts are 32-bit offsets.
+// Every code load of a wavefront reads whole 128-byte lines: 8-bit K is
+// stored as 16-byte units (tile, half, lane) and V records are split into
+// 16-byte groups stored group-major, so lane l of a load reads unit l.
 template <int FMT>
 __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int64_t bh, int64_t blk,
                                            int lane) {
@@ -214,27 +225,30 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
   const int64_t id = bh * p.nb_cap + blk;
   const uint8_t* kb = p.k_codes + id * (int64_t)(kBlock * T::kRowBytes);
   const uint8_t* vb = p.v_codes + id * (int64_t)(kBlock * T::kRowBytes);
+  const uint4* k16 = reinterpret_cast<const uint4*>(kb);
   const uint32_t qd = (uint32_t)lane >> 4;
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
-    const uint8_t* src = kb + ((16u * tile + ((uint32_t)lane & 15u)) * T::kRowBytes + qd * (T::kKWords * 4));
     if constexpr (T::kKWords == 8) {
-      const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-      const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+      const uint4 a = load_stream(k16 + (2 * tile) * 64 + lane);
+      const uint4 b = load_stream(k16 + (2 * tile + 1) * 64 + lane);
       r.k[tile][0] = a.x; r.k[tile][1] = a.y; r.k[tile][2] = a.z; r.k[tile][3] = a.w;
       r.k[tile][4] = b.x; r.k[tile][5] = b.y; r.k[tile][6] = b.z; r.k[tile][7] = b.w;
-    } else if constexpr (T::kKWords == 4) {
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      r.k[tile][0] = a.x; r.k[tile][1] = a.y; r.k[tile][2] = a.z; r.k[tile][3] = a.w;
     } else {
-      const uint2 a = *reinterpret_cast<const uint2*>(src);
-      r.k[tile][0] = a.x; r.k[tile][1] = a.y;
+      const uint8_t* src = kb + ((16u * tile + ((uint32_t)lane & 15u)) * T::kRowBytes + qd * (T::kKWords * 4));
+      if constexpr (T::kKWords == 4) {
+        const uint4 a = load_stream(reinterpret_cast<const uint4*>(src));
+        r.k[tile][0] = a.x; r.k[tile][1] = a.y; r.k[tile][2] = a.z; r.k[tile][3] = a.w;
+      } else {
+        const uint2 a = *reinterpret_cast<const uint2*>(src);
+        r.k[tile][0] = a.x; r.k[tile][1] = a.y;
+      }
     }
   }
-  const uint4* vsrc = reinterpret_cast<const uint4*>(vb + (uint32_t)lane * (T::kVWords * 4));
+  const uint4* v16 = reinterpret_cast<const uint4*>(vb);
 #pragma unroll
   for (int i = 0; i < T::kVWords / 4; ++i) {
-    const uint4 a = vsrc[i];
+    const uint4 a = load_stream(v16 + i * 64 + lane);
     r.v[4 * i] = a.x; r.v[4 * i + 1] = a.y; r.v[4 * i + 2] = a.z; r.v[4 * i + 3] = a.w;
   }
   if constexpr (!T::kFp8) {

@@ -32,7 +32,7 @@ struct FlushParams {
   const uint16_t* v_in;
   const uint16_t* k_ring; // fp16 [B][Hkv][RS][D]
   const uint16_t* v_ring;
-  uint8_t* k_codes;       // [B][Hkv][NB*32][D*b/8]
+  uint8_t* k_codes;       // [B][Hkv][NB][32*D*b/8]
   uint8_t* v_codes;       // [B][Hkv][NB][32*D*b/8]
   float* k_meta;          // [B][Hkv][NB][D][2]       (s, z) per channel
   float* v_meta;          // [B][Hkv][NB][D/32][32][2] (s, z) per group and token

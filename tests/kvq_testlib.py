@@ -70,7 +70,7 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
 
     kc = pl("k_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
     vc = pl("v_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
-    codes_k = olayout.unpack_k_codes(kc.reshape(b, hkv, nb * 32, row), olay.fmt, d)
+    codes_k = olayout.unpack_k_codes(kc, olay.fmt, d)
     codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
     s_k = z_k = s_v = z_v = None
     if olay.fmt != "fp8":

@@ -23,40 +23,53 @@ def test_v_block_layout_rules(fmt, bits):
         codes = rng.integers(0, 256, size=(2, 32, d), dtype=np.uint8)
     packed = layout.pack_v_codes(codes.reshape(64, d), fmt)          # [2 blocks][bytes]
     assert packed.shape == (2, 32 * d * bits // 8)
-    rec = d * bits // 16
     sigma = [0, 4, 1, 5, 2, 6, 3, 7]
     for blk in range(2):
         for lane in range(64):
             qd, r = divmod(lane, 16)
-            base = lane * rec
+
+            def at(x):                            # byte x of record `lane`
+                i, e = divmod(x, 16)
+                return int(packed[blk, 16 * (64 * i + lane) + e])
             for m in range(d // 16):
                 ch = 16 * m + r
                 for j in range(8):
                     t = _tok(qd, j)
                     c = codes[blk, t, ch]
                     if fmt == "int4":
-                        word = int.from_bytes(packed[blk, base + 4 * m: base + 4 * m + 4].tobytes(), "little")
+                        word = sum(at(4 * m + i) << (8 * i) for i in range(4))
                         assert (word >> (4 * j)) & 0xF == c
                     elif bits == 8:
                         k = sigma.index(j)
-                        assert packed[blk, base + 8 * m + k] == c
+                        assert at(8 * m + k) == c
                     else:
                         p, tile_b = divmod(m, 2)
                         byte = (2 if j >= 4 else 0) + tile_b
                         jj = j % 4
-                        assert (packed[blk, base + 4 * p + byte] >> (2 * jj)) & 3 == c
+                        assert (at(4 * p + byte) >> (2 * jj)) & 3 == c
     assert np.array_equal(layout.unpack_v_codes(packed, fmt, d), codes.reshape(64, d))
 
 
-@pytest.mark.parametrize("bits,fmt", [(2, "int2"), (4, "int4"), (8, "int8")])
-def test_k_codes_are_lsb_first_token_major(bits, fmt):
+@pytest.mark.parametrize("bits,fmt", [(2, "int2"), (4, "int4"), (8, "int8"), (8, "fp8")])
+def test_k_block_layout_rules(bits, fmt):
     rng = np.random.default_rng(3)
-    codes = rng.integers(0, 1 << bits, size=(3, 5, 128), dtype=np.uint8)
+    codes = rng.integers(0, 1 << bits, size=(3, 64, 128), dtype=np.uint8)
     packed = layout.pack_k_codes(codes, fmt)
-    assert packed.shape == (3, 5, 128 * bits // 8)
-    for c in range(128):
-        byte, bit = divmod(c * bits, 8)
-        assert np.array_equal((packed[..., byte] >> bit) & ((1 << bits) - 1), codes[..., c])
+    assert packed.shape == (3, 2, 32 * 128 * bits // 8)
+    row = 128 * bits // 8
+    for blk in range(2):
+        for t in range(32):
+            for c in range(128):
+                if bits == 8:                      # unit (tile, half, 16 qd + r), byte e
+                    tile, r = divmod(t, 16)
+                    qd, rest = divmod(c, 32)
+                    half, e = divmod(rest, 16)
+                    off = ((2 * tile + half) * 64 + 16 * qd + r) * 16 + e
+                    got = packed[:, blk, off]
+                else:                              # token rows, LSB first
+                    byte, bit = divmod(c * bits, 8)
+                    got = (packed[:, blk, t * row + byte] >> bit) & ((1 << bits) - 1)
+                assert np.array_equal(got, codes[:, 32 * blk + t, c])
     assert np.array_equal(layout.unpack_k_codes(packed, fmt, 128), codes)
 
 
@@ -84,7 +97,7 @@ def test_meta_layouts():
 @pytest.mark.parametrize("fmt", ["int8", "int4", "int2", "fp8"])
 def test_empty_planes_unpack(fmt):
     bits = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}[fmt]
-    k = layout.unpack_k_codes(np.zeros((2, 3, 0, 128 * bits // 8), np.uint8), fmt, 128)
+    k = layout.unpack_k_codes(np.zeros((2, 3, 0, 32 * 128 * bits // 8), np.uint8), fmt, 128)
     assert k.shape == (2, 3, 0, 128)
     v = layout.unpack_v_codes(np.zeros((2, 3, 0, 32 * 128 * bits // 8), np.uint8), fmt, 128)
     assert v.shape == (2, 3, 0, 128)
