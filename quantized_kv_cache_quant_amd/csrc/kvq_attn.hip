@@ -208,9 +208,14 @@ struct Raw {
 // Code lines are read once per call: nontemporal loads keep them from
 // displacing the metadata, query and partials in the caches.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <bool kStream>
 __device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-  return uint4{t.x, t.y, t.z, t.w};
+  if constexpr (kStream) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+    return uint4{t.x, t.y, t.z, t.w};
+  } else {
+    return *ptr;
+  }
 }
 
 // Loads one block.  bh and blk are wave-uniform, so the block base is a
@@ -218,7 +223,7 @@ __device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
 // Every code load of a wavefront reads whole 128-byte lines: 8-bit K is
 // stored as 16-byte units (tile, half, lane) and V records are split into
 // 16-byte groups stored group-major, so lane l of a load reads unit l.
-template <int FMT>
+template <int FMT, bool kStream = true>
 __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int64_t bh, int64_t blk,
                                            int lane) {
   using T = Traits<FMT>;
@@ -230,14 +235,14 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
     if constexpr (T::kKWords == 8) {
-      const uint4 a = load_stream(k16 + (2 * tile) * 64 + lane);
-      const uint4 b = load_stream(k16 + (2 * tile + 1) * 64 + lane);
+      const uint4 a = load_stream<kStream>(k16 + (2 * tile) * 64 + lane);
+      const uint4 b = load_stream<kStream>(k16 + (2 * tile + 1) * 64 + lane);
       r.k[tile][0] = a.x; r.k[tile][1] = a.y; r.k[tile][2] = a.z; r.k[tile][3] = a.w;
       r.k[tile][4] = b.x; r.k[tile][5] = b.y; r.k[tile][6] = b.z; r.k[tile][7] = b.w;
     } else {
       const uint8_t* src = kb + ((16u * tile + ((uint32_t)lane & 15u)) * T::kRowBytes + qd * (T::kKWords * 4));
       if constexpr (T::kKWords == 4) {
-        const uint4 a = load_stream(reinterpret_cast<const uint4*>(src));
+        const uint4 a = load_stream<kStream>(reinterpret_cast<const uint4*>(src));
         r.k[tile][0] = a.x; r.k[tile][1] = a.y; r.k[tile][2] = a.z; r.k[tile][3] = a.w;
       } else {
         const uint2 a = *reinterpret_cast<const uint2*>(src);
@@ -248,7 +253,7 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
   const uint4* v16 = reinterpret_cast<const uint4*>(vb);
 #pragma unroll
   for (int i = 0; i < T::kVWords / 4; ++i) {
-    const uint4 a = load_stream(v16 + i * 64 + lane);
+    const uint4 a = load_stream<kStream>(v16 + i * 64 + lane);
     r.v[4 * i] = a.x; r.v[4 * i + 1] = a.y; r.v[4 * i + 2] = a.z; r.v[4 * i + 3] = a.w;
   }
   if constexpr (!T::kFp8) {
@@ -761,11 +766,12 @@ __device__ void group_main(const AttnParams& p, char* lds) {
 
   // block ring: D - 1 blocks prefetched ahead of the one being processed;
   // rid = block index within the range (-1 past its end), rbh = its head.
-  // Loads past the end re-read the last block taken (in bounds, cached).
+  // Loads past the end read block 0 of head 0 with ordinary loads: every
+  // wavefront's surplus loads hit the same lines, which stay in the cache.
   const uint32_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;
   Raw<FMT> buf[D];
   int rid[D], rbh[D];
-  int last = 0, kst = 0;
+  int kst = 0;
   auto fetch = [&](Raw<FMT>& r, int& id, int& bhout) {
     int idx;
     if (p.deterministic) {
@@ -776,19 +782,23 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       if (li.lane == 0) idx = atomicAdd(ctr, 1);
       idx = __builtin_amdgcn_readfirstlane(idx);
     }
-    const bool ok = idx < gr.len;
-    if (ok) last = idx;
-    id = ok ? idx : -1;
-    uint32_t j = (uint32_t)(gr.jb + last);
-    const uint32_t bh = j / nblk;
-    // visit the blocks of each head's part of the range starting at a
-    // per-workgroup offset, so that the workgroups' streams sit at
-    // unrelated addresses rather than in step
-    const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
-    const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
-    j = ps + (j - ps + rot) % (pe - ps);
-    bhout = (int)bh;
-    load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
+    if (idx < gr.len) {
+      id = idx;
+      uint32_t j = (uint32_t)(gr.jb + idx);
+      const uint32_t bh = j / nblk;
+      // visit the blocks of each head's part of the range starting at a
+      // per-workgroup offset, so that the workgroups' streams sit at
+      // unrelated addresses rather than in step
+      const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
+      const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
+      j = ps + (j - ps + rot) % (pe - ps);
+      bhout = (int)bh;
+      load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
+    } else {
+      id = -1;
+      bhout = 0;
+      load_block<FMT, false>(r, p, 0, 0, li.lane);
+    }
   };
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d]);
