@@ -41,8 +41,9 @@ import numpy as np
 
 from . import quant
 
-FORMATS = ("int8", "int4", "int2", "fp8")
-BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}
+FORMATS = ("int8", "int4", "int2", "fp8", "fp8_e5m2")
+FP8_FORMATS = ("fp8", "fp8_e5m2")
+BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8, "fp8_e5m2": 8}
 
 
 @dataclass
@@ -60,6 +61,7 @@ class Layout:
     sink_tokens: int = 0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    meta_fp16: bool = False       # INT only: fp16 (s, m) pairs instead of fp32 (s, z)
 
     @property
     def bits(self) -> int:
@@ -94,9 +96,9 @@ class CacheState:
     sink_v: np.ndarray
     codes_k: np.ndarray           # [B][Hkv][n_q][D] uint8 (int codes or E4M3 bytes)
     codes_v: np.ndarray
-    s_k: np.ndarray | None        # [B][Hkv][n_q/G_k][D] fp32 (INT only)
-    z_k: np.ndarray | None
-    s_v: np.ndarray | None        # [B][Hkv][n_q][D/G_v] fp32 (INT only)
+    s_k: np.ndarray | None        # [B][Hkv][n_q/G_k][D] fp32 (INT only; fp16 with meta_fp16)
+    z_k: np.ndarray | None        # zero-point z (fp32), or the fp16 offset m with meta_fp16
+    s_v: np.ndarray | None        # [B][Hkv][n_q][D/G_v], as s_k / z_k
     z_v: np.ndarray | None
     res_k: np.ndarray             # [B][Hkv][r][D] fp16, body order
     res_v: np.ndarray
@@ -121,15 +123,15 @@ def build_cache(k: np.ndarray, v: np.ndarray, lay: Layout) -> CacheState:
     body_k = kt[:, :, n_sink:n_sink + n_q]       # body tokens u < n_q (sinks come first)
     body_v = vt[:, :, n_sink:n_sink + n_q]
     s_k = z_k = s_v = z_v = None
-    if lay.fmt == "fp8":
-        codes_k = quant.fp8_encode(body_k, lay.k_scale)
-        codes_v = quant.fp8_encode(body_v, lay.v_scale)
+    if lay.fmt in FP8_FORMATS:
+        codes_k = quant.fp8_encode(body_k, lay.k_scale, lay.fmt)
+        codes_v = quant.fp8_encode(body_v, lay.v_scale, lay.fmt)
     else:
         bits = lay.bits
         kg = body_k.reshape(b, hkv, n_q // g, g, d)
-        ck, s_k, z_k = quant.quantize_k_group(kg, bits)
+        ck, s_k, z_k = quant.quantize_k_group(kg, bits, lay.meta_fp16)
         codes_k = ck.reshape(b, hkv, n_q, d)
-        codes_v, s_v, z_v = quant.quantize_v_tokens(body_v, bits, lay.v_group_channels)
+        codes_v, s_v, z_v = quant.quantize_v_tokens(body_v, bits, lay.v_group_channels, lay.meta_fp16)
     res_k = kt[:, :, s0 + n_q:]
     res_v = vt[:, :, s0 + n_q:]
     assert res_k.shape[2] == r
@@ -141,9 +143,9 @@ def build_cache(k: np.ndarray, v: np.ndarray, lay: Layout) -> CacheState:
 def dequantize(st: CacheState):
     """(K_hat, V_hat) in fp64, [B][Hkv][n][D], in absolute token order."""
     lay = st.layout
-    if lay.fmt == "fp8":
-        kq = quant.fp8_decode(st.codes_k, lay.k_scale)
-        vq = quant.fp8_decode(st.codes_v, lay.v_scale)
+    if lay.fmt in FP8_FORMATS:
+        kq = quant.fp8_decode(st.codes_k, lay.k_scale, lay.fmt)
+        vq = quant.fp8_decode(st.codes_v, lay.v_scale, lay.fmt)
     else:
         b, hkv, n_q, d = st.codes_k.shape
         g = lay.k_group_tokens

@@ -29,6 +29,7 @@ Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
           byte 3 = B's T[4..7], two bits per code, LSB first.
 * K meta    [B][Hkv][NB][D][2]        fp32: (s, z) of each channel of the block's group
 * V meta    [B][Hkv][NB][D/G_v][32][2] fp32: (s, z) of each channel group and token
+  (fp16 metadata: the same shapes holding fp16 (s, m) pairs, m the offset)
 * K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
 """
 from __future__ import annotations
@@ -79,7 +80,7 @@ def _v_record_order(fmt: str, d: int):
             for m in range(d // 16):
                 for j in range(8):
                     tok.append(t[j]); ch.append(16 * m + r)
-        elif fmt in ("int8", "fp8"):
+        elif fmt in ("int8", "fp8", "fp8_e5m2"):
             for m in range(d // 16):
                 for k in range(8):
                     tok.append(t[sigma[k]]); ch.append(16 * m + r)
@@ -124,7 +125,7 @@ def k_block_stream_order(fmt: str, d: int):
 
 
 def _bits(fmt: str) -> int:
-    return {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}[fmt]
+    return {"int8": 8, "int4": 4, "int2": 2, "fp8": 8, "fp8_e5m2": 8}[fmt]
 
 
 def _pack_blocks(codes: np.ndarray, fmt: str, order) -> np.ndarray:
@@ -166,15 +167,22 @@ def unpack_v_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
     return _unpack_blocks(packed, fmt, d, v_block_stream_order)
 
 
+def _meta_dtype(s):
+    """fp16 metadata stays fp16 (the fp16 (s, m) variant); anything else is fp32."""
+    return np.float16 if np.asarray(s).dtype == np.float16 else np.float32
+
+
 def pack_k_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """s, z [..., NB, D] -> [..., NB, D, 2] fp32 (interleaved pairs)."""
-    return np.stack([np.asarray(s, np.float32), np.asarray(z, np.float32)], axis=-1)
+    """s, z [..., NB, D] -> [..., NB, D, 2] (interleaved pairs, fp32 or fp16)."""
+    dt = _meta_dtype(s)
+    return np.stack([np.asarray(s, dt), np.asarray(z, dt)], axis=-1)
 
 
 def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """s, z [..., NB*32, Gn] -> [..., NB, Gn, 32, 2] fp32 (interleaved pairs)."""
-    s = np.asarray(s, np.float32)
-    z = np.asarray(z, np.float32)
+    """s, z [..., NB*32, Gn] -> [..., NB, Gn, 32, 2] (interleaved pairs, fp32 or fp16)."""
+    dt = _meta_dtype(s)
+    s = np.asarray(s, dt)
+    z = np.asarray(z, dt)
     n, gn = s.shape[-2:]
     nb = n // BLOCK
     sb = np.swapaxes(s.reshape(s.shape[:-2] + (nb, BLOCK, gn)), -1, -2)
@@ -184,13 +192,13 @@ def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
 
 def unpack_k_meta(m: np.ndarray):
     """[..., NB, D, 2] -> s, z [..., NB, D]."""
-    m = np.asarray(m, np.float32)
+    m = np.asarray(m, _meta_dtype(m))
     return m[..., 0].copy(), m[..., 1].copy()
 
 
 def unpack_v_meta(m: np.ndarray):
     """[..., NB, Gn, 32, 2] -> s, z [..., NB*32, Gn]."""
-    m = np.asarray(m, np.float32)
+    m = np.asarray(m, _meta_dtype(m))
     nb, gn, blk, _ = m.shape[-4:]
     s = np.swapaxes(m[..., 0], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
     z = np.swapaxes(m[..., 1], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))

@@ -13,14 +13,16 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   sizes 34 KiB for 8-bit q8_0 / EXL3, 32 KiB for fp8_e4m3 and 18 KiB for 4-bit
   q4_0 / EXL3, i.e. 8.5 : 8 : 4.5 bits per value).
 * :func:`step_bytes` is the algorithmic HBM traffic of one decode step of one
-  layer in this library's layout: packed codes + fp32 scale/zero planes +
+  layer in this library's layout: packed codes + scale/zero planes (fp32, or
+  fp16 with the fp16-metadata variant) +
   fp16 residual window + fp16 sinks + the fp16 query + the fp16 output.
 """
 from __future__ import annotations
 
 from .cache import Layout, window_split
 
-BYTES_PER_ELEM = {"fp16": 2.0, "bf16": 2.0, "fp8": 1.0, "int8": 1.0, "int4": 0.5, "int2": 0.25}
+BYTES_PER_ELEM = {"fp16": 2.0, "bf16": 2.0, "fp8": 1.0, "fp8_e5m2": 1.0, "int8": 1.0, "int4": 0.5,
+                  "int2": 0.25}
 
 
 def kv_bytes(layers: int, kv_heads: int, head_dim: int, seq_len: int, batch: int,
@@ -43,11 +45,12 @@ def step_bytes(lay: Layout, n: int) -> dict:
     b, hkv, hq, d = lay.batch, lay.num_kv_heads, lay.num_q_heads, lay.head_dim
     n_sink, n_q, r = window_split(n, lay.sink_tokens, lay.residual_tokens, lay.k_group_tokens)
     codes = 2 * b * hkv * n_q * d * lay.bits // 8
-    if lay.fmt == "fp8":
+    if lay.fmt in ("fp8", "fp8_e5m2"):
         meta = 0
     else:
-        meta_k = b * hkv * (n_q // lay.k_group_tokens) * d * 2 * 4
-        meta_v = b * hkv * n_q * (d // lay.v_group_channels) * 2 * 4
+        eb = 2 if lay.meta_fp16 else 4                 # bytes per scale / zero-point
+        meta_k = b * hkv * (n_q // lay.k_group_tokens) * d * 2 * eb
+        meta_v = b * hkv * n_q * (d // lay.v_group_channels) * 2 * eb
         meta = meta_k + meta_v
     fp16 = 2 * b * hkv * (r + n_sink) * d * 2
     qo = 2 * b * hq * d * 2

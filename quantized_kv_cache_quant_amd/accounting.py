@@ -1,7 +1,8 @@
 """Algorithmic HBM bytes of one decode-attention call (for throughput reporting).
 
 Counts what the method must move per layer and step, in this library's
-layout: packed codes, fp32 scale / zero-point planes (INT formats), the fp16
+layout: packed codes, scale / zero-point planes (INT formats: fp32 pairs, or
+fp16 pairs with the fp16-metadata variant), the fp16
 residual window and sinks, the fp16 query and the fp16 output.  Split-K
 partials are implementation overhead and are not counted.  The KV_bytes
 formula of "KV Cache Quantization Analysis" (memory-size sense box) is the
@@ -9,7 +10,7 @@ codes-only part of this count.
 """
 from __future__ import annotations
 
-BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}
+BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8, "fp8_e5m2": 8}
 BLOCK = 32
 
 
@@ -22,11 +23,13 @@ def routed(n: int, sink: int, residual: int):
 
 
 def attention_bytes(batch: int, kv_heads: int, q_heads: int, head_dim: int, n: int, fmt: str,
-                    sink: int = 0, residual: int = 128, v_group: int = 32) -> int:
+                    sink: int = 0, residual: int = 128, v_group: int = 32, meta_fp16: bool = False) -> int:
     ns, nq, r = routed(n, sink, residual)
     bh = batch * kv_heads
     codes = 2 * bh * nq * head_dim * BITS[fmt] // 8
-    meta = 0 if fmt == "fp8" else bh * (nq // BLOCK) * head_dim * 8 + bh * nq * (head_dim // v_group) * 8
+    pair = 4 if meta_fp16 else 8                  # bytes of one (scale, zero-point) pair
+    meta = 0 if fmt.startswith("fp8") else (bh * (nq // BLOCK) * head_dim * pair
+                                            + bh * nq * (head_dim // v_group) * pair)
     fp16 = 2 * bh * (ns + r) * head_dim * 2
     qo = 2 * batch * q_heads * head_dim * 2
     return codes + meta + fp16 + qo

@@ -195,13 +195,29 @@ def test_step_bytes_of_the_workloads(name, fmt, total):
     assert bits == {"fp8": 8, "int8": 10, "int4": 6, "int2": 4}[fmt]
 
 
+@pytest.mark.parametrize("fmt,bits", [("int8", 9), ("int4", 5), ("int2", 3), ("fp8_e5m2", 8)])
+def test_fp16_metadata_and_e5m2_bits_per_value(fmt, bits):
+    # one fp16 scale and one fp16 offset per 32 values add 1 bit per value;
+    # the 27B study's block formats (one 16-bit scale per 32 values) add 0.5
+    w = synth.WORKLOADS["llama3_8b"]
+    lay = cache.Layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.seq_len, fmt,
+                       residual_tokens=w.residual_tokens, meta_fp16=fmt != "fp8_e5m2")
+    sb = nbytes.step_bytes(lay, w.seq_len)
+    got = 8 * (sb["codes"] + sb["meta"]) / (2 * w.batch * w.num_kv_heads * sb["n_q"] * w.head_dim)
+    assert got == bits
+    assert nbytes.block_bits_per_value(8, 32, 16) + 0.5 == 9
+
+
 def test_library_side_byte_count_agrees_with_oracle():
     from quantized_kv_cache_quant_amd import accounting
     for name in synth.WORKLOADS:
         w = synth.WORKLOADS[name]
-        for fmt in ("int8", "int4", "int2", "fp8"):
+        for fmt, m16 in (("int8", 0), ("int4", 0), ("int2", 0), ("fp8", 0), ("fp8_e5m2", 0), ("int4", 1),
+                         ("int2", 1)):
             for n in (1, 100, w.seq_len, w.seq_len + 37):
                 lay = cache.Layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
-                                   residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens)
+                                   residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens,
+                                   meta_fp16=bool(m16))
                 assert accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
-                                                  w.sink_tokens, w.residual_tokens) == nbytes.step_bytes(lay, n)["total"]
+                                                  w.sink_tokens, w.residual_tokens,
+                                                  meta_fp16=bool(m16)) == nbytes.step_bytes(lay, n)["total"]

@@ -14,7 +14,7 @@ def _tok(qd, j):
     return 4 * qd + j if j < 4 else 16 + 4 * qd + (j - 4)
 
 
-@pytest.mark.parametrize("fmt,bits", [("int4", 4), ("int8", 8), ("fp8", 8), ("int2", 2)])
+@pytest.mark.parametrize("fmt,bits", [("int4", 4), ("int8", 8), ("fp8", 8), ("fp8_e5m2", 8), ("int2", 2)])
 def test_v_block_layout_rules(fmt, bits):
     rng = np.random.default_rng(bits)
     d = 128
@@ -92,6 +92,15 @@ def test_meta_layouts():
     assert flat[0, 0, 2 * (2 * 32 + 31) + 1] == zv[0, 31, 2]
     s2, z2 = layout.unpack_v_meta(mv)
     assert np.array_equal(s2, sv) and np.array_equal(z2, zv)
+    # fp16 (s, m) metadata keeps its type: 4-byte pairs in the same order
+    s16, m16 = s.astype(np.float16), z.astype(np.float16)
+    m = layout.pack_k_meta(s16, m16)
+    assert m.dtype == np.float16 and m.shape == (2, 3, 128, 2)
+    assert m.reshape(2, 3, 256)[1, 2, 2 * 77 + 1] == m16[1, 2, 77]
+    s2, z2 = layout.unpack_k_meta(m)
+    assert s2.dtype == np.float16 and np.array_equal(s2, s16) and np.array_equal(z2, m16)
+    mv = layout.pack_v_meta(sv.astype(np.float16), zv.astype(np.float16))
+    assert mv.dtype == np.float16 and mv.reshape(2, 2, 256)[1, 1, 2 * (3 * 32 + 7)] == np.float16(sv[1, 32 + 7, 3])
 
 
 @pytest.mark.parametrize("fmt", ["int8", "int4", "int2", "fp8"])
