@@ -36,8 +36,16 @@
  *    q = clamp(rint(x / s + z), 0, 2^b - 1), s = (max - min) / (2^b - 1)
  *    (s = 1 for a constant group), z = -min / s, each a single fp32 IEEE
  *    operation (same page, sec. 2, affine quantization);
- *  - FP8: OCP E4M3 (max 448) of clamp(x / s, -448, 448) with one fp32 scale
- *    for K and one for V per layer (same page, sec. 4, FP8 / INT8).
+ *  - FP8: OCP E4M3 (max 448) of clamp(x / s, -448, 448), or OCP E5M2 (max
+ *    57344) of clamp(x / s, -57344, 57344), rounded to nearest even, with
+ *    one fp32 scale for K and one for V per layer (same page, sec. 4, FP8 /
+ *    INT8, which names both formats);
+ *  - fp16 metadata (meta_fp16 = 1, INT formats): one fp16 scale and one fp16
+ *    offset per group, 16 bits each as in the block formats of the 27B KL
+ *    study's KV-cache size table.  s = (max - min) / (2^b - 1) in fp32,
+ *    rounded up to the next fp16 (1 for a constant group); the offset is
+ *    m = min (exact in fp16); q = clamp(rint((x - m) / s), 0, 2^b - 1) in
+ *    fp32 steps; x_hat = s * q + m (the same affine map, with s * z = -m).
  *
  * Planes inside the caller's device buffer (offsets from kvq_cache_plane;
  * NB = max(0, max_tokens - S - R) / 32 blocks, D = head_dim, b = bits):
@@ -62,9 +70,13 @@
  *   K meta   [B][Hkv][NB][D][2] fp32: (s, z) of each channel (INT only)
  *   V meta   [B][Hkv][NB][D/32][32][2] fp32: (s, z) of each channel group
  *            and token (INT only)
+ *            With meta_fp16 both meta planes have the same shapes and hold
+ *            fp16 (s, m) pairs (half the bytes).
  *   K ring, V ring  [B][Hkv][R+32][D] fp16
  *   K sink, V sink  [B][Hkv][S][D] fp16
  * Each plane starts on a 256-byte boundary.
+ *
+ * FP8 E5M2 codes use the INT8 / FP8 byte layouts above.
  *
  * Limits of this version (KVQ_ERR_UNSUPPORTED otherwise): head_dim == 128,
  * k_group_tokens == 32, v_group_channels == 32, num_q_heads / num_kv_heads
@@ -92,7 +104,7 @@ typedef enum {
   KVQ_ERR_EMPTY = -8         /* attention over an empty cache */
 } kvq_status;
 
-typedef enum { KVQ_INT8 = 0, KVQ_INT4 = 1, KVQ_INT2 = 2, KVQ_FP8_E4M3 = 3 } kvq_format;
+typedef enum { KVQ_INT8 = 0, KVQ_INT4 = 1, KVQ_INT2 = 2, KVQ_FP8_E4M3 = 3, KVQ_FP8_E5M2 = 4 } kvq_format;
 
 /* One layer's cache geometry.  Per-layer formats (e.g. INT8 on the first and
  * last layers, INT4 in between) use one layout and one cache per layer. */
@@ -109,6 +121,7 @@ typedef struct {
   int32_t sink_tokens;       /* S >= 0: first tokens always kept in fp16 */
   float k_scale;             /* FP8 only: Key scale, finite and > 0 */
   float v_scale;             /* FP8 only: Value scale, finite and > 0 */
+  int32_t meta_fp16;         /* INT only: 0 = fp32 (s, z) pairs, 1 = fp16 (s, m) pairs; 0 for FP8 */
 } kvq_layout;
 
 enum {

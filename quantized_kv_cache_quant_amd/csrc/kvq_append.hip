@@ -5,7 +5,9 @@
 // the cache.  Sec. 3 / sec. 4 (KIVI): Keys per channel, Values per token,
 // the most recent tokens kept in full precision.  Sec. 2: affine
 // quantization q = round(x / s + z), x_hat = s * (q - z).  Sec. 4 (FP8 /
-// INT8): OCP E4M3 with an fp32 scale.
+// INT8): OCP E4M3 or E5M2 with an fp32 scale.  With fp16 metadata a group
+// stores an fp16 scale (rounded up) and its minimum m as an fp16 offset:
+// q = round((x - m) / s), x_hat = s * q + m.
 //
 // Two kernels, enqueued in this order on one stream:
 //  flush_kernel  one workgroup per (32-token block leaving the residual
@@ -32,22 +34,43 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <int BITS>
+// Integer code of x in a group with scale s and zero-point z (fp32 pairs:
+// rint(x / s + z)) or, with fp16 metadata (OFFSET), offset z = m:
+// rint((x - m) / s).  One fp32 operation per step, clamped to the code range.
+template <int BITS, bool OFFSET>
 __device__ __forceinline__ uint32_t encode_int(float x, float s, float z) {
   constexpr float kQmax = (float)((1 << BITS) - 1);
-  float v = x / s;
-  v = v + z;
+  float v;
+  if constexpr (OFFSET) {
+    v = x - z;
+    v = v / s;
+  } else {
+    v = x / s;
+    v = v + z;
+  }
   v = __builtin_rintf(v);
   v = fminf(fmaxf(v, 0.0f), kQmax);
   return (uint32_t)v;
 }
 
-// Two fp32 values -> two OCP E4M3 bytes (low 16 bits of the result), after
-// the explicit clamp to +-448; the hardware conversion rounds to nearest even.
+// Smallest fp16 >= x, for finite 0 <= x <= 65504 (bit pattern; -0 gives -0).
+__device__ __forceinline__ uint32_t f16_round_up(float x) {
+  const _Float16 h = (_Float16)x;                  // round to nearest even
+  uint32_t b = __builtin_bit_cast(uint16_t, h);
+  if ((float)h < x) b += 1;                        // the next fp16 up (x > 0)
+  return b;
+}
+
+// Two fp32 values -> two OCP FP8 bytes (low 16 bits of the result) after the
+// explicit clamp to the format's largest finite value; the hardware
+// conversion rounds to nearest even.  E4M3: +-448; E5M2: +-57344.
+template <bool E5M2>
 __device__ __forceinline__ uint32_t encode_fp8_pair(float a, float b, float s) {
-  float va = fminf(fmaxf(a / s, -448.0f), 448.0f);
-  float vb = fminf(fmaxf(b / s, -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
+  constexpr float kMax = E5M2 ? 57344.0f : 448.0f;
+  float va = fminf(fmaxf(a / s, -kMax), kMax);
+  float vb = fminf(fmaxf(b / s, -kMax), kMax);
+  if constexpr (E5M2) return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(va, vb, 0, false) & 0xFFFFu;
+  else return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
 }
 
 // Token index (0..31 inside a block) of slot j (0..7) of V record quarter qd.
@@ -55,10 +78,13 @@ __device__ __forceinline__ int record_token(int qd, int j) {
   return (j < 4) ? (4 * qd + j) : (16 + 4 * qd + (j - 4));
 }
 
-template <int FMT>
+template <int VAR>
 __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
-  constexpr bool kFp8 = FMT == KVQ_FP8_E4M3;
-  constexpr int kBits = FMT == KVQ_INT4 ? 4 : (FMT == KVQ_INT2 ? 2 : 8);
+  constexpr int kKind = kind_of(VAR);
+  constexpr bool kFp8 = fp8_of(VAR);
+  constexpr bool kE5M2 = kKind == KVQ_FP8_E5M2;
+  constexpr bool kM16 = meta16_of(VAR);
+  constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   constexpr float kQmax = (float)((1 << kBits) - 1);
 
@@ -115,14 +141,23 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         mx = fmaxf(mx, ks[t][c]);
       }
       mn = mn + 0.0f;                                 // a zero minimum is +0
-      float s = (mx - mn) / kQmax;
-      if (s == 0.0f) s = 1.0f;
-      const float z = (-mn) / s;
-      sk[c] = s;
-      zk[c] = z;
-      float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);   // [D][s, z]
-      km[2 * c] = s;
-      km[2 * c + 1] = z;
+      if constexpr (kM16) {                           // fp16 (s rounded up, m = min)
+        uint32_t sb = f16_round_up((mx - mn) / kQmax);
+        if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;        // constant group (range +-0): s = 1
+        const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
+        sk[c] = half_bits_to_float(sb);
+        zk[c] = mn;
+        reinterpret_cast<uint32_t*>(p.k_meta)[(bh * p.nb_cap + blk) * kHeadDim + c] = sb | (mb << 16);
+      } else {
+        float s = (mx - mn) / kQmax;
+        if (s == 0.0f) s = 1.0f;
+        const float z = (-mn) / s;
+        sk[c] = s;
+        zk[c] = z;
+        float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);   // [D][s, z]
+        km[2 * c] = s;
+        km[2 * c + 1] = z;
+      }
     } else {
       const int e = tid - kHeadDim;
       const int t = e >> 2, g = e & 3;
@@ -132,14 +167,24 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         mx = fmaxf(mx, vs[t][kVGroup * g + c]);
       }
       mn = mn + 0.0f;
-      float s = (mx - mn) / kQmax;
-      if (s == 0.0f) s = 1.0f;
-      const float z = (-mn) / s;
-      sv[t][g] = s;
-      zv[t][g] = z;
-      float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);  // [group][token][s, z]
-      vm[2 * (g * kBlock + t)] = s;
-      vm[2 * (g * kBlock + t) + 1] = z;
+      if constexpr (kM16) {
+        uint32_t sb = f16_round_up((mx - mn) / kQmax);
+        if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;
+        const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);
+        sv[t][g] = half_bits_to_float(sb);
+        zv[t][g] = mn;
+        reinterpret_cast<uint32_t*>(p.v_meta)[(bh * p.nb_cap + blk) * (kVGroups * kBlock) + g * kBlock + t] =
+            sb | (mb << 16);
+      } else {
+        float s = (mx - mn) / kQmax;
+        if (s == 0.0f) s = 1.0f;
+        const float z = (-mn) / s;
+        sv[t][g] = s;
+        zv[t][g] = z;
+        float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);  // [group][token][s, z]
+        vm[2 * (g * kBlock + t)] = s;
+        vm[2 * (g * kBlock + t) + 1] = z;
+      }
     }
     __syncthreads();
   }
@@ -165,14 +210,14 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       uint32_t word = 0;
       if constexpr (kFp8) {
         const int c = wi * 4;
-        word = encode_fp8_pair(ks[t][c], ks[t][c + 1], p.k_scale) |
-               (encode_fp8_pair(ks[t][c + 2], ks[t][c + 3], p.k_scale) << 16);
+        word = encode_fp8_pair<kE5M2>(ks[t][c], ks[t][c + 1], p.k_scale) |
+               (encode_fp8_pair<kE5M2>(ks[t][c + 2], ks[t][c + 3], p.k_scale) << 16);
       } else {
         constexpr int kPer = 32 / kBits;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int c = wi * kPer + j;
-          word |= encode_int<kBits>(ks[t][c], sk[c], zk[c]) << (j * kBits);
+          word |= encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c]) << (j * kBits);
         }
       }
       dst[w] = word;
@@ -195,7 +240,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = record_token(qd, j);
-          word |= encode_int<4>(vs[t][ch], sv[t][g], zv[t][g]) << (4 * j);
+          word |= encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g]) << (4 * j);
         }
       } else if constexpr (kBits == 8) {          // bytes 8m..8m+7 = T0 T4 T1 T5 T2 T6 T3 T7
         const int ch = 16 * (wi >> 1) + r;
@@ -208,12 +253,12 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
           const float x1 = vs[record_token(qd, sel(base + 1))][ch];
           const float x2 = vs[record_token(qd, sel(base + 2))][ch];
           const float x3 = vs[record_token(qd, sel(base + 3))][ch];
-          word = encode_fp8_pair(x0, x1, p.v_scale) | (encode_fp8_pair(x2, x3, p.v_scale) << 16);
+          word = encode_fp8_pair<kE5M2>(x0, x1, p.v_scale) | (encode_fp8_pair<kE5M2>(x2, x3, p.v_scale) << 16);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int t = record_token(qd, sel(base + k));
-            word |= encode_int<8>(vs[t][ch], sv[t][g], zv[t][g]) << (8 * k);
+            word |= encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g]) << (8 * k);
           }
         }
       } else {                                    // INT2 word p: A = 32p + r, B = 32p + 16 + r
@@ -222,10 +267,10 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t0 = record_token(qd, j), t1 = record_token(qd, 4 + j);
-          word |= encode_int<2>(vs[t0][cha], sv[t0][ga], zv[t0][ga]) << (2 * j);
-          word |= encode_int<2>(vs[t0][chb], sv[t0][gb], zv[t0][gb]) << (8 + 2 * j);
-          word |= encode_int<2>(vs[t1][cha], sv[t1][ga], zv[t1][ga]) << (16 + 2 * j);
-          word |= encode_int<2>(vs[t1][chb], sv[t1][gb], zv[t1][gb]) << (24 + 2 * j);
+          word |= encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga]) << (2 * j);
+          word |= encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb]) << (8 + 2 * j);
+          word |= encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga]) << (16 + 2 * j);
+          word |= encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb]) << (24 + 2 * j);
         }
       }
       dst[w] = word;
@@ -262,13 +307,17 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
 
 }  // namespace
 
-hipError_t launch_flush(int fmt, const FlushParams& p, int n_blocks, int batch, hipStream_t s) {
+hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s) {
   const dim3 grid(n_blocks, p.hkv, batch), block(256);
-  switch (fmt) {
+  switch (variant) {
     case KVQ_INT8: hipLaunchKernelGGL(flush_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(flush_kernel<KVQ_INT4>, grid, block, 0, s, p); break;
     case KVQ_INT2: hipLaunchKernelGGL(flush_kernel<KVQ_INT2>, grid, block, 0, s, p); break;
     case KVQ_FP8_E4M3: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E4M3>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E5M2: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E5M2>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kMeta16>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

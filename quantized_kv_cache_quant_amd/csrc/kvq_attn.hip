@@ -123,6 +123,14 @@ __device__ __forceinline__ f16x8 cvt_int2(uint32_t w, bool high) {
   return cat(x & 0x00030003u, x & 0x000C000Cu, x & 0x00300030u, x & 0x00C000C0u);
 }
 
+// 8 OCP E5M2 bytes -> exact f16 values in byte order: an E5M2 code is the
+// upper byte of the f16 with the same value
+__device__ __forceinline__ f16x8 cvt_e5m2(uint32_t w0, uint32_t w1) {
+  const uint32_t lo = 0x010C000Cu, hi = 0x030C020Cu;   // [b1, 0, b0, 0] / [b3, 0, b2, 0]
+  return cat(__builtin_amdgcn_perm(0u, w0, lo), __builtin_amdgcn_perm(0u, w0, hi),
+             __builtin_amdgcn_perm(0u, w1, lo), __builtin_amdgcn_perm(0u, w1, hi));
+}
+
 // 8 OCP E4M3 bytes -> exact f16 values in byte order (hardware conversion)
 __device__ __forceinline__ f16x8 cvt_fp8(uint32_t w0, uint32_t w1) {
   const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
@@ -147,10 +155,13 @@ __device__ __forceinline__ f16x8 cvt_fp8(uint32_t w0, uint32_t w1) {
 #define KVQ_DEPTH_INT2 4
 #endif
 
+// FMT is a kernel variant: the kvq_format, plus kMeta16 for fp16 metadata.
 template <int FMT>
 struct Traits {
-  static constexpr bool kFp8 = FMT == KVQ_FP8_E4M3;
-  static constexpr int kBits = FMT == KVQ_INT4 ? 4 : (FMT == KVQ_INT2 ? 2 : 8);
+  static constexpr int kKind = kind_of(FMT);
+  static constexpr bool kMeta16 = meta16_of(FMT);
+  static constexpr bool kFp8 = fp8_of(FMT);
+  static constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   static constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   static constexpr int kKWords = 32 * kBits / 32;          // words per lane per 16-token tile
   static constexpr int kVWords = kRowBytes / 8;            // words per V record (= per lane)
@@ -165,17 +176,18 @@ struct Traits {
 // V: 16-channel tile m) from the lane's packed words.
 template <int FMT>
 __device__ __forceinline__ f16x8 operand(const uint32_t* w, int a) {
-  if constexpr (FMT == KVQ_INT4) return cvt_int4(w[a]);
-  else if constexpr (FMT == KVQ_INT2) return cvt_int2(w[a >> 1], (a & 1) != 0);
-  else if constexpr (FMT == KVQ_FP8_E4M3) return cvt_fp8(w[2 * a], w[2 * a + 1]);
+  if constexpr (kind_of(FMT) == KVQ_INT4) return cvt_int4(w[a]);
+  else if constexpr (kind_of(FMT) == KVQ_INT2) return cvt_int2(w[a >> 1], (a & 1) != 0);
+  else if constexpr (kind_of(FMT) == KVQ_FP8_E4M3) return cvt_fp8(w[2 * a], w[2 * a + 1]);
+  else if constexpr (kind_of(FMT) == KVQ_FP8_E5M2) return cvt_e5m2(w[2 * a], w[2 * a + 1]);
   else return cvt_u8(w[2 * a], w[2 * a + 1]);
 }
 
 // Channel (0..31 within the lane's quarter) carried by k-slot j of k-block kb.
 template <int FMT>
 __device__ constexpr int k_chan(int kb, int j) {
-  if constexpr (FMT == KVQ_INT4) return 8 * kb + (j >> 1) + 4 * (j & 1);
-  else if constexpr (FMT == KVQ_INT2) return 16 * (kb >> 1) + 4 * (kb & 1) + (j >> 1) + 8 * (j & 1);
+  if constexpr (kind_of(FMT) == KVQ_INT4) return 8 * kb + (j >> 1) + 4 * (j & 1);
+  else if constexpr (kind_of(FMT) == KVQ_INT2) return 16 * (kb >> 1) + 4 * (kb & 1) + (j >> 1) + 8 * (j & 1);
   else return 8 * kb + j;
 }
 
@@ -193,8 +205,8 @@ __device__ constexpr int k_slot(int w) {
 // for V); it is divided out of the staged scale.
 template <int FMT>
 __device__ constexpr float slot_div(int i) {
-  if constexpr (FMT == KVQ_INT4) return (i & 1) ? 16.0f : 1.0f;
-  else if constexpr (FMT == KVQ_INT2) return (float)(1 << (2 * (i & 3)));
+  if constexpr (kind_of(FMT) == KVQ_INT4) return (i & 1) ? 16.0f : 1.0f;
+  else if constexpr (kind_of(FMT) == KVQ_INT2) return (float)(1 << (2 * (i & 3)));
   else return 1.0f;
 }
 
@@ -202,7 +214,8 @@ template <int FMT>
 struct Raw {
   uint32_t k[2][Traits<FMT>::kKWords];   // two 16-token tiles
   uint32_t v[Traits<FMT>::kVWords];
-  float4 km, vm;                         // this lane's 16 bytes of each metadata block
+  float4 km, vm;                         // this lane's part of each metadata block: 16 bytes
+                                         // of fp32 pairs, or 8 bytes of fp16 pairs in .x / .y
 };
 
 // Code lines are read once per call: nontemporal loads keep them from
@@ -256,7 +269,12 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
     const uint4 a = load_stream<kStream>(v16 + i * 64 + lane);
     r.v[4 * i] = a.x; r.v[4 * i + 1] = a.y; r.v[4 * i + 2] = a.z; r.v[4 * i + 3] = a.w;
   }
-  if constexpr (!T::kFp8) {
+  if constexpr (T::kMeta16) {
+    const uint2 a = reinterpret_cast<const uint2*>(p.k_meta + id * 128)[lane];
+    const uint2 b = reinterpret_cast<const uint2*>(p.v_meta + id * 128)[lane];
+    r.km = float4{__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y), 0.f, 0.f};
+    r.vm = float4{__builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y), 0.f, 0.f};
+  } else if constexpr (!T::kFp8) {
     r.km = reinterpret_cast<const float4*>(p.k_meta + id * 256)[lane];
     r.vm = reinterpret_cast<const float4*>(p.v_meta + id * 256)[lane];
   }
@@ -277,10 +295,10 @@ constexpr int kStage = 512;
 // Slot (see k_slot) of within-quarter channel w, by formula.
 template <int FMT>
 __device__ __forceinline__ int k_slot_of(int w) {
-  if constexpr (FMT == KVQ_INT4) {
+  if constexpr (kind_of(FMT) == KVQ_INT4) {
     const int r = w & 7;
     return (w & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
-  } else if constexpr (FMT == KVQ_INT2) {
+  } else if constexpr (kind_of(FMT) == KVQ_INT2) {
     const int rem = w & 15, rem2 = rem & 7;
     return 8 * (2 * (w >> 4) + (rem2 >> 2)) + 2 * (rem2 & 3) + (rem >> 3);
   } else {
@@ -292,8 +310,8 @@ template <int FMT>
 __device__ constexpr bool k_slot_formula_ok() {
   for (int w = 0; w < 32; ++w) {
     int r = w & 7, rem = w & 15, rem2 = rem & 7;
-    int f = FMT == KVQ_INT4 ? (w & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1)
-          : FMT == KVQ_INT2 ? 8 * (2 * (w >> 4) + (rem2 >> 2)) + 2 * (rem2 & 3) + (rem >> 3) : w;
+    int f = kind_of(FMT) == KVQ_INT4 ? (w & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1)
+          : kind_of(FMT) == KVQ_INT2 ? 8 * (2 * (w >> 4) + (rem2 >> 2)) + 2 * (rem2 & 3) + (rem >> 3) : w;
     if (f != k_slot<FMT>(w)) return false;
   }
   return true;
@@ -301,18 +319,48 @@ __device__ constexpr bool k_slot_formula_ok() {
 static_assert(k_slot_formula_ok<KVQ_INT8>() && k_slot_formula_ok<KVQ_INT4>() && k_slot_formula_ok<KVQ_INT2>(),
               "Key slot formula");
 
-// Lane L holds the (s, z) pairs 2L and 2L+1 of each metadata block.  The
-// Key scale (with log2(e) / sqrt(D) and the slot divisor folded in) and
-// s * z (with log2(e) / sqrt(D)) go to LDS in Key slot order per quarter.
+// Scales of the lane's two metadata pairs (V: its two token / group
+// entries): fp32 (s, z) pairs or fp16 (s, m) pairs.
+template <int FMT>
+__device__ __forceinline__ float2 pair_scales(const float4& m) {
+  if constexpr (Traits<FMT>::kMeta16) {
+    const f16x2 a = u2h(__builtin_bit_cast(uint32_t, m.x)), b = u2h(__builtin_bit_cast(uint32_t, m.y));
+    return float2{(float)a[0], (float)b[0]};
+  } else {
+    return float2{m.x, m.z};
+  }
+}
+
+// Lane L holds the metadata pairs 2L and 2L+1 of each block.  The Key scale
+// (with log2(e) / sqrt(D) and the slot divisor folded in) and s * z (with
+// log2(e) / sqrt(D)) go to LDS in Key slot order per quarter.  fp16 pairs
+// hold (s, m) with x_hat = s * q + m, so their s * z is -m.
 template <int FMT>
 __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
   const int c = 2 * lane;                 // K channel; V index g * 32 + t
   const int t = c & 31;
-  const float sq0 = r.km.x * kQScale, sq1 = r.km.z * kQScale;
+  float sq0, sq1, kz0, kz1;
+  float2 vs, vz;
+  if constexpr (Traits<FMT>::kMeta16) {
+    const f16x2 ka = u2h(__builtin_bit_cast(uint32_t, r.km.x)), kb = u2h(__builtin_bit_cast(uint32_t, r.km.y));
+    const f16x2 va = u2h(__builtin_bit_cast(uint32_t, r.vm.x)), vb = u2h(__builtin_bit_cast(uint32_t, r.vm.y));
+    sq0 = (float)ka[0] * kQScale;
+    sq1 = (float)kb[0] * kQScale;
+    kz0 = -(float)ka[1] * kQScale;
+    kz1 = -(float)kb[1] * kQScale;
+    vs = float2{(float)va[0] * (1.0f / slot_div<FMT>(t)), (float)vb[0] * (1.0f / slot_div<FMT>(t + 1))};
+    vz = float2{-(float)va[1], -(float)vb[1]};
+  } else {
+    sq0 = r.km.x * kQScale;
+    sq1 = r.km.z * kQScale;
+    kz0 = sq0 * r.km.y;
+    kz1 = sq1 * r.km.w;
+    vs = float2{r.vm.x * (1.0f / slot_div<FMT>(t)), r.vm.z * (1.0f / slot_div<FMT>(t + 1))};
+    vz = float2{r.vm.x * r.vm.y, r.vm.z * r.vm.w};
+  }
   const float ks0 = sq0 * (1.0f / slot_div<FMT>(c)), ks1 = sq1 * (1.0f / slot_div<FMT>(c + 1));
-  const float kz0 = sq0 * r.km.y, kz1 = sq1 * r.km.w;
   const int q0 = (c & ~31) + k_slot_of<FMT>(c & 31), q1 = (c & ~31) + k_slot_of<FMT>((c + 1) & 31);
-  if constexpr (FMT == KVQ_INT8) {
+  if constexpr (kind_of(FMT) == KVQ_INT8) {
     *reinterpret_cast<float2*>(st + q0) = float2{ks0, ks1};
     *reinterpret_cast<float2*>(st + 128 + q0) = float2{kz0, kz1};
   } else {
@@ -321,8 +369,6 @@ __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lan
     st[128 + q0] = kz0;
     st[128 + q1] = kz1;
   }
-  const float2 vs = {r.vm.x * (1.0f / slot_div<FMT>(t)), r.vm.z * (1.0f / slot_div<FMT>(t + 1))};
-  const float2 vz = {r.vm.x * r.vm.y, r.vm.z * r.vm.w};
   *reinterpret_cast<float2*>(st + 256 + c) = vs;
   *reinterpret_cast<float2*>(st + 384 + c) = vz;
 }
@@ -542,7 +588,8 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
     for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * T::kCodeScale;
   float slack = kSlack;
   if constexpr (!T::kFp8) {
-    if (__any(r.vm.x > kLazyScaleMax || r.vm.z > kLazyScaleMax)) slack = 0.f;
+    const float2 sv = pair_scales<FMT>(r.vm);
+    if (__any(sv.x > kLazyScaleMax || sv.y > kLazyScaleMax)) slack = 0.f;
   }
   softmax_block(lg, ws, pr, slack);
 
@@ -986,13 +1033,17 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s) {
+hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.groups), block(kGroupThreads);
-  switch (fmt) {
+  switch (variant) {
     case KVQ_INT8: hipLaunchKernelGGL(attn_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(attn_kernel<KVQ_INT4>, grid, block, 0, s, p); break;
     case KVQ_INT2: hipLaunchKernelGGL(attn_kernel<KVQ_INT2>, grid, block, 0, s, p); break;
     case KVQ_FP8_E4M3: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E4M3>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E5M2: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E5M2>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kMeta16>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

@@ -44,11 +44,12 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   const uint64_t nb = (uint64_t)nb_cap(L);
   const uint64_t bits = (uint64_t)format_bits(L.format);
   const uint64_t d = (uint64_t)L.head_dim;
-  const bool fp8 = L.format == KVQ_FP8_E4M3;
+  const bool fp8 = fp8_of(L.format);
+  const uint64_t eb = L.meta_fp16 ? 2 : 4;           // bytes per scale / zero-point
   sz[KVQ_PLANE_K_CODES] = bh * nb * kBlock * d * bits / 8;
   sz[KVQ_PLANE_V_CODES] = sz[KVQ_PLANE_K_CODES];
-  sz[KVQ_PLANE_K_META] = fp8 ? 0 : bh * nb * 2 * d * sizeof(float);
-  sz[KVQ_PLANE_V_META] = fp8 ? 0 : bh * nb * 2 * (d / L.v_group_channels) * kBlock * sizeof(float);
+  sz[KVQ_PLANE_K_META] = fp8 ? 0 : bh * nb * 2 * d * eb;
+  sz[KVQ_PLANE_V_META] = fp8 ? 0 : bh * nb * 2 * (d / L.v_group_channels) * kBlock * eb;
   sz[KVQ_PLANE_K_RING] = bh * (uint64_t)(L.residual_tokens + kBlock) * d * 2;
   sz[KVQ_PLANE_V_RING] = sz[KVQ_PLANE_K_RING];
   sz[KVQ_PLANE_K_SINK] = bh * (uint64_t)L.sink_tokens * d * 2;
@@ -122,10 +123,11 @@ int32_t kvq_layout_validate(const kvq_layout* L) {
     return KVQ_ERR_LAYOUT;
   if (L->num_q_heads % L->num_kv_heads) return KVQ_ERR_LAYOUT;
   if (L->head_dim % L->v_group_channels) return KVQ_ERR_LAYOUT;
-  if (L->format < KVQ_INT8 || L->format > KVQ_FP8_E4M3) return KVQ_ERR_LAYOUT;
-  if (L->format == KVQ_FP8_E4M3) {
+  if (L->format < KVQ_INT8 || L->format > KVQ_FP8_E5M2) return KVQ_ERR_LAYOUT;
+  if (L->meta_fp16 != 0 && L->meta_fp16 != 1) return KVQ_ERR_LAYOUT;
+  if (fp8_of(L->format)) {
     if (!std::isfinite(L->k_scale) || !std::isfinite(L->v_scale) || !(L->k_scale > 0.f) ||
-        !(L->v_scale > 0.f))
+        !(L->v_scale > 0.f) || L->meta_fp16)
       return KVQ_ERR_LAYOUT;
   }
   if (L->sink_tokens > L->max_tokens) return KVQ_ERR_LAYOUT;
@@ -237,7 +239,7 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
     p.k_scale = L.k_scale;
     p.v_scale = L.v_scale;
     if (n_flush > 0x7fffffff) return KVQ_ERR_UNSUPPORTED;
-    if (launch_flush(L.format, p, (int)n_flush, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+    if (launch_flush(variant_of(L), p, (int)n_flush, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   }
   // 2) copy new sink tokens and new residual tokens to their fp16 planes
   CopyParams cp{};
@@ -327,7 +329,7 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.k_scale = L.k_scale;
   p.v_scale = L.v_scale;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (launch_attention(L.format, p, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }
 

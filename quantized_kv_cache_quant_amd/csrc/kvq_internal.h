@@ -24,6 +24,15 @@ constexpr int kGroupWaves = KVQ_GROUP_WAVES;        // wavefronts per attention 
 constexpr int kGroupsPerCu = KVQ_GROUPS_PER_CU;     // workgroup ranges per compute unit (library split)
 constexpr int kMaxBlocksPerGroup = 1 << 20;
 
+// Kernel variant: the kvq_format, plus kMeta16 when an INT format stores
+// fp16 (scale, offset) pairs.
+constexpr int kMeta16 = 8;
+__host__ __device__ constexpr int kind_of(int variant) { return variant & 7; }
+__host__ __device__ constexpr bool meta16_of(int variant) { return (variant & kMeta16) != 0; }
+__host__ __device__ constexpr bool fp8_of(int variant) {
+  return kind_of(variant) == KVQ_FP8_E4M3 || kind_of(variant) == KVQ_FP8_E5M2;
+}
+inline int variant_of(const kvq_layout& L) { return L.format | (L.meta_fp16 ? kMeta16 : 0); }
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
 // ---------------------------------------------------------------- append
@@ -34,7 +43,7 @@ struct FlushParams {
   const uint16_t* v_ring;
   uint8_t* k_codes;       // [B][Hkv][NB][32*D*b/8]
   uint8_t* v_codes;       // [B][Hkv][NB][32*D*b/8]
-  float* k_meta;          // [B][Hkv][NB][D][2]       (s, z) per channel
+  float* k_meta;          // [B][Hkv][NB][D][2]       (s, z) per channel (fp16 (s, m) pairs: meta16)
   float* v_meta;          // [B][Hkv][NB][D/32][32][2] (s, z) per group and token
   int64_t n_old;          // tokens per sequence before this append
   int32_t T;              // tokens appended
@@ -59,7 +68,7 @@ struct CopyParams {
   int32_t T, hkv, sink, ring_slots;
 };
 
-hipError_t launch_flush(int fmt, const FlushParams& p, int n_blocks, int batch, hipStream_t s);
+hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s);
 hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 
 // ------------------------------------------------------------- attention
@@ -108,6 +117,6 @@ struct AttnParams {
   float k_scale, v_scale; // FP8
 };
 
-hipError_t launch_attention(int fmt, const AttnParams& p, hipStream_t s);
+hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s);
 
 }  // namespace kvq

@@ -16,7 +16,7 @@ KVQ_OK = 0
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_LAYOUT", -3: "KVQ_ERR_UNSUPPORTED",
           -4: "KVQ_ERR_CAPACITY", -5: "KVQ_ERR_ALIGN", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP",
           -8: "KVQ_ERR_EMPTY"}
-FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3}
+FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3, "fp8_e5m2": 4}
 PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink")
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
@@ -35,7 +35,7 @@ class Layout(ctypes.Structure):
                 ("max_tokens", ctypes.c_int32), ("format", ctypes.c_int32),
                 ("k_group_tokens", ctypes.c_int32), ("v_group_channels", ctypes.c_int32),
                 ("residual_tokens", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("meta_fp16", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -88,9 +88,10 @@ def check(status: int, where: str) -> None:
 
 
 def make_layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, fmt, *, k_group_tokens=32,
-                v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0) -> Layout:
+                v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0,
+                meta_fp16=False) -> Layout:
     return Layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, FORMATS[fmt], k_group_tokens,
-                  v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale))
+                  v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale), int(meta_fp16))
 
 
 def cache_bytes(layout: Layout) -> int:

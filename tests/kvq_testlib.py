@@ -14,7 +14,13 @@ from oracle import cache as ocache
 from oracle import layout as olayout
 from quantized_kv_cache_quant_amd import kvq
 
-BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8}
+BITS = {"int8": 8, "int4": 4, "int2": 2, "fp8": 8, "fp8_e5m2": 8}
+FP8 = ("fp8", "fp8_e5m2")
+
+
+def split_fmt(name: str):
+    """Test format names: a kvq format, with suffix "_m16" for fp16 metadata."""
+    return (name[:-4], True) if name.endswith("_m16") else (name, False)
 
 
 def require_gpu():
@@ -26,7 +32,8 @@ def olayout_of(lay_kw: dict) -> ocache.Layout:
     k = dict(lay_kw)
     return ocache.Layout(k["batch"], k["num_kv_heads"], k["num_q_heads"], 128, k["max_tokens"], k["fmt"],
                          residual_tokens=k.get("residual_tokens", 128), sink_tokens=k.get("sink_tokens", 0),
-                         k_scale=k.get("k_scale", 1.0), v_scale=k.get("v_scale", 1.0))
+                         k_scale=k.get("k_scale", 1.0), v_scale=k.get("v_scale", 1.0),
+                         meta_fp16=bool(k.get("meta_fp16", False)))
 
 
 def make_cache(lay_kw: dict) -> kvq.Cache:
@@ -73,9 +80,10 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
     codes_k = olayout.unpack_k_codes(kc, olay.fmt, d)
     codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
     s_k = z_k = s_v = z_v = None
-    if olay.fmt != "fp8":
-        km = pl("k_meta", np.float32, (b, hkv, nb_cap, d, 2))[:, :, :nb]
-        vm = pl("v_meta", np.float32, (b, hkv, nb_cap, 4, 32, 2))[:, :, :nb]
+    if olay.fmt not in FP8:
+        mt = np.float16 if olay.meta_fp16 else np.float32
+        km = pl("k_meta", mt, (b, hkv, nb_cap, d, 2))[:, :, :nb]
+        vm = pl("v_meta", mt, (b, hkv, nb_cap, 4, 32, 2))[:, :, :nb]
         s_k, z_k = olayout.unpack_k_meta(km)
         s_v, z_v = olayout.unpack_v_meta(vm)
     ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))
@@ -136,7 +144,8 @@ def substate(st: ocache.CacheState, bi: int, gi: int) -> ocache.CacheState:
         return None if a is None else a[bi:bi + 1, gi:gi + 1]
     lay = st.layout
     sub = ocache.Layout(1, 1, lay.n_rep, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
-                        lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale)
+                        lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale,
+                        lay.meta_fp16)
     return ocache.CacheState(sub, st.n, st.n_sink, st.n_q, st.r, cut(st.sink_k), cut(st.sink_v),
                              cut(st.codes_k), cut(st.codes_v), cut(st.s_k), cut(st.z_k), cut(st.s_v),
                              cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots)

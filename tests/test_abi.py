@@ -63,26 +63,39 @@ def _lay(**kw):
     ({"fmt": "fp8", "k_scale": 0.0}, -2),
     ({"fmt": "fp8", "v_scale": float("inf")}, -2),
     ({"fmt": "fp8", "v_scale": float("nan")}, -2),
+    ({"fmt": "fp8_e5m2", "k_scale": 0.5, "v_scale": 2.0}, 0),
+    ({"fmt": "fp8_e5m2", "k_scale": -1.0}, -2),
+    ({"meta_fp16": 1}, 0),
+    ({"fmt": "int2", "meta_fp16": 1}, 0),
+    ({"meta_fp16": 2}, -2),
+    ({"fmt": "fp8", "meta_fp16": 1}, -2),                 # fp16 metadata is for INT formats
+    ({"fmt": "fp8_e5m2", "meta_fp16": 1}, -2),
 ])
 def test_layout_validation(kw, status):
     lay = _lay(**kw)
     assert kvq.lib().kvq_layout_validate(ctypes.byref(lay)) == status
+    bad = _lay()
+    bad.format = 5
+    assert kvq.lib().kvq_layout_validate(ctypes.byref(bad)) == -2
     assert kvq.lib().kvq_layout_validate(None) == -1
 
 
-@pytest.mark.parametrize("fmt,bits", [("int8", 8), ("int4", 4), ("int2", 2), ("fp8", 8)])
+@pytest.mark.parametrize("fmt,bits,m16", [("int8", 8, 0), ("int4", 4, 0), ("int2", 2, 0), ("fp8", 8, 0),
+                                          ("fp8_e5m2", 8, 0), ("int4", 4, 1), ("int2", 2, 1)])
 @pytest.mark.parametrize("s,r,maxt", [(0, 128, 8192 + 256), (4, 128, 8192), (0, 0, 33), (3, 40, 50)])
-def test_cache_bytes_and_planes(fmt, bits, s, r, maxt):
+def test_cache_bytes_and_planes(fmt, bits, m16, s, r, maxt):
     b, hkv, d = 3, 2, 128
     lay = _lay(batch=b, num_kv_heads=hkv, num_q_heads=hkv * 4, fmt=fmt, residual_tokens=r,
-               sink_tokens=s, max_tokens=maxt, k_scale=1.0, v_scale=1.0)
+               sink_tokens=s, max_tokens=maxt, k_scale=1.0, v_scale=1.0, meta_fp16=m16)
     total = kvq.cache_bytes(lay)
     nb = max(0, maxt - s - r) // 32
+    fp8 = fmt.startswith("fp8")
+    eb = 2 if m16 else 4
     expect = {
         "k_codes": b * hkv * nb * 32 * d * bits // 8,
         "v_codes": b * hkv * nb * 32 * d * bits // 8,
-        "k_meta": 0 if fmt == "fp8" else b * hkv * nb * 2 * d * 4,
-        "v_meta": 0 if fmt == "fp8" else b * hkv * nb * 2 * 4 * 32 * 4,
+        "k_meta": 0 if fp8 else b * hkv * nb * 2 * d * eb,
+        "v_meta": 0 if fp8 else b * hkv * nb * 2 * 4 * 32 * eb,
         "k_ring": b * hkv * (r + 32) * d * 2,
         "v_ring": b * hkv * (r + 32) * d * 2,
         "k_sink": b * hkv * s * d * 2,

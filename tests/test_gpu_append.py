@@ -7,8 +7,8 @@ from oracle import cache as ocache
 from oracle import quant
 from quantized_kv_cache_quant_amd import kvq, synth
 
-from kvq_testlib import (append_chunks, assert_states_equal, make_cache, olayout_of, read_state,
-                         require_gpu, substate, to_dev)
+from kvq_testlib import (FP8, append_chunks, assert_states_equal, make_cache, olayout_of, read_state,
+                         require_gpu, split_fmt, substate, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,15 +19,21 @@ def _inputs(b, n, hkv, seed, w="llama3_8b"):
     return synth.kv_tokens(W[w], seed, seed + 1, b, n, hkv, 128)
 
 
-def _lay_kw(fmt, b, hkv, nrep, maxt, r, s, k=None, v=None):
+def _lay_kw(name, b, hkv, nrep, maxt, r, s, k=None, v=None):
+    fmt, m16 = split_fmt(name)
     kw = dict(batch=b, num_kv_heads=hkv, num_q_heads=hkv * nrep, max_tokens=maxt, fmt=fmt,
               residual_tokens=r, sink_tokens=s)
-    if fmt == "fp8":
-        kw.update(k_scale=float(quant.fp8_scale(k)), v_scale=float(quant.fp8_scale(v)))
+    if m16:
+        kw.update(meta_fp16=True)
+    if fmt in FP8:
+        kw.update(k_scale=float(quant.fp8_scale(k, fmt)), v_scale=float(quant.fp8_scale(v, fmt)))
     return kw
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8"])
+ALL = ["int4", "int8", "int2", "fp8", "fp8_e5m2", "int4_m16", "int8_m16", "int2_m16"]
+
+
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("s,r", [(0, 32), (4, 32), (0, 0), (3, 45)])
 def test_prefill_bit_exact(fmt, s, r):
     require_gpu()
@@ -40,7 +46,7 @@ def test_prefill_bit_exact(fmt, s, r):
     assert_states_equal(read_state(c, olay), ocache.build_cache(k, v, olay))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8"])
+@pytest.mark.parametrize("fmt", ALL)
 def test_chunking_invariance(fmt):
     require_gpu()
     b, hkv, r, s = 2, 2, 32, 4
@@ -70,15 +76,17 @@ def test_chunking_invariance(fmt):
             assert_states_equal(read_state(c3, olay), ocache.build_cache(k[:, :t + 1], v[:, :t + 1], olay))
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.0078125, 0.013671875, 3.7, 146.28571])
-def test_fp8_encoder_every_fp16_value(scale):
+@pytest.mark.parametrize("fmt,scale", [("fp8", 1.0), ("fp8", 0.0078125), ("fp8", 0.013671875), ("fp8", 3.7),
+                                       ("fp8", 146.28571), ("fp8_e5m2", 1.0), ("fp8_e5m2", 2.0**-20),
+                                       ("fp8_e5m2", 1.1428571), ("fp8_e5m2", 0.013671875)])
+def test_fp8_encoder_every_fp16_value(fmt, scale):
     require_gpu()
     x = np.arange(65536, dtype=np.uint16).view(np.float16)
     x = x[np.isfinite(x)]
     x = np.concatenate([x, np.zeros(128 * 512 - len(x), np.float16)])   # 512 tokens of 128
     k = x.reshape(1, 512, 1, 128)
     v = np.ascontiguousarray(k[:, ::-1])
-    kw = dict(batch=1, num_kv_heads=1, num_q_heads=1, max_tokens=512, fmt="fp8", residual_tokens=0,
+    kw = dict(batch=1, num_kv_heads=1, num_q_heads=1, max_tokens=512, fmt=fmt, residual_tokens=0,
               sink_tokens=0, k_scale=scale, v_scale=scale)
     c = make_cache(kw)
     append_chunks(c, k, v, [512])
@@ -86,7 +94,7 @@ def test_fp8_encoder_every_fp16_value(scale):
     assert_states_equal(read_state(c, olay), ocache.build_cache(k, v, olay))
 
 
-@pytest.mark.parametrize("fmt", ["int8", "int4", "int2"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int2", "int8_m16", "int4_m16", "int2_m16"])
 def test_special_groups(fmt):
     """Constant groups (s = 1), signed zeros, fp16 extremes, exact ties."""
     require_gpu()
@@ -103,6 +111,8 @@ def test_special_groups(fmt):
     v[:, 40, 0, :] = np.float16(6.1e-5)
     grid = (np.arange(32) - 7) * 2.0**-6                   # on-grid values with ties
     k[:, 64:96, 1, 9] = grid.astype(np.float16)
+    k[:, 32:64, 0, 11] = (np.float16(1500.0) + np.arange(32) % 9 * 0.125).astype(np.float16)  # narrow, far from 0
+    v[:, 41, 1, 64:96] = np.float16(-20000.0) + np.arange(32).astype(np.float16) * np.float16(16)
     kw = _lay_kw(fmt, b, hkv, 1, n, 0, 0)
     c = make_cache(kw)
     append_chunks(c, k, v, [n])
@@ -125,17 +135,16 @@ def test_capacity_error_is_all_or_nothing():
 
 
 @pytest.mark.parametrize("name,fmt", [("llama3_8b", "int8"), ("llama3_8b", "fp8"),
-                                      ("llama3_8b_kivi2", "int2"), ("llama3_70b", "int4")])
+                                      ("llama3_8b_kivi2", "int2"), ("llama3_70b", "int4"),
+                                      ("llama3_8b", "fp8_e5m2"), ("llama3_70b", "int4_m16")])
 def test_full_size_prefill_and_decode_appends(name, fmt):
     """Full batch-16, 8192-token prefill, then 40 single-token appends (a flush boundary)."""
     require_gpu()
     w = W[name]
     k, v = synth.prefill(w)
     steps = [synth.append_step(w, j) for j in range(40)]
-    kw = dict(batch=w.batch, num_kv_heads=w.num_kv_heads, num_q_heads=w.num_q_heads,
-              max_tokens=w.seq_len + 64, fmt=fmt, residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens)
-    if fmt == "fp8":
-        kw.update(k_scale=float(quant.fp8_scale(k)), v_scale=float(quant.fp8_scale(v)))
+    kw = _lay_kw(fmt, w.batch, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.seq_len + 64,
+                 w.residual_tokens, w.sink_tokens, k, v)
     c = make_cache(kw)
     append_chunks(c, k, v, [w.seq_len])
     for ks, vs in steps:

@@ -14,8 +14,8 @@ from oracle import cache as ocache
 from oracle import quant
 from quantized_kv_cache_quant_amd import kvq, synth
 
-from kvq_testlib import (append_chunks, attention_gpu, make_cache, olayout_of, read_state,
-                         require_gpu, substate, to_dev)
+from kvq_testlib import (FP8, append_chunks, attention_gpu, make_cache, olayout_of, read_state,
+                         require_gpu, split_fmt, substate, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,14 +29,22 @@ def _oracle_out(c, kw, q):
     return oattn.attention(q, kh, vh)
 
 
+def _kw(name, b, hkv, nrep, maxt, r, s, k, v):
+    fmt, m16 = split_fmt(name)
+    kw = dict(batch=b, num_kv_heads=hkv, num_q_heads=hkv * nrep, max_tokens=maxt, fmt=fmt,
+              residual_tokens=r, sink_tokens=s)
+    if m16:
+        kw.update(meta_fp16=True)
+    if fmt in FP8:
+        kw.update(k_scale=float(quant.fp8_scale(k, fmt)), v_scale=float(quant.fp8_scale(v, fmt)))
+    return kw
+
+
 def _build(fmt, b, hkv, nrep, n, r, s, seed=1, w="llama3_8b", chunks=None):
     k, v = synth.kv_tokens(W[w], seed, seed + 1, b, n, hkv, 128)
     if s:                                                      # attention sinks with large logits
         k[:, :s] = (k[:, :s].astype(np.float32) * 10).astype(np.float16)
-    kw = dict(batch=b, num_kv_heads=hkv, num_q_heads=hkv * nrep, max_tokens=n + 64, fmt=fmt,
-              residual_tokens=r, sink_tokens=s)
-    if fmt == "fp8":
-        kw.update(k_scale=float(quant.fp8_scale(k)), v_scale=float(quant.fp8_scale(v)))
+    kw = _kw(fmt, b, hkv, nrep, n + 64, r, s, k, v)
     c = make_cache(kw)
     append_chunks(c, k, v, chunks or [n])
     q = synth.queries(W[w], b, hkv * nrep, 128, seed_offset=seed)
@@ -60,7 +68,7 @@ def test_tiny_workload():
     assert np.max(np.abs(out.astype(np.float64) - ref)) <= TOL
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8"])
+@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8", "fp8_e5m2", "int4_m16", "int8_m16", "int2_m16"])
 @pytest.mark.parametrize("nrep", [1, 2, 4, 8])
 def test_formats_and_gqa(fmt, nrep):
     require_gpu()
@@ -72,7 +80,7 @@ def test_formats_and_gqa(fmt, nrep):
     assert np.max(np.abs(out.astype(np.float64) - ref)) <= TOL
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8"])
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp8_e5m2", "int2_m16"])
 @pytest.mark.parametrize("s,r", [(4, 32), (4, 0), (0, 0), (3, 200)])
 def test_sinks_and_windows(fmt, s, r):
     require_gpu()
@@ -103,7 +111,7 @@ def test_empty_cache_is_an_error():
     assert e.value.status == -8
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8"])
+@pytest.mark.parametrize("fmt", ["int4", "int8", "int2", "fp8", "fp8_e5m2", "int4_m16"])
 def test_split_invariance_and_determinism(fmt):
     require_gpu()
     n = 32 * 70 + 40
@@ -165,10 +173,8 @@ def test_closed_forms_on_gpu():
 def _full_size(name, fmt, layers_formats=None, steps=0):
     w = W[name]
     k, v = synth.prefill(w)
-    kw = dict(batch=w.batch, num_kv_heads=w.num_kv_heads, num_q_heads=w.num_q_heads,
-              max_tokens=w.seq_len + 64, fmt=fmt, residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens)
-    if fmt == "fp8":
-        kw.update(k_scale=float(quant.fp8_scale(k)), v_scale=float(quant.fp8_scale(v)))
+    kw = _kw(fmt, w.batch, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.seq_len + 64,
+             w.residual_tokens, w.sink_tokens, k, v)
     c = make_cache(kw)
     append_chunks(c, k, v, [w.seq_len])
     for j in range(steps):
@@ -189,7 +195,9 @@ def _full_size(name, fmt, layers_formats=None, steps=0):
 
 
 @pytest.mark.parametrize("name,fmt,steps", [("llama3_8b", "fp8", 0), ("llama3_8b", "int8", 0),
-                                            ("llama3_8b_kivi2", "int2", 64), ("llama3_70b", "int4", 0)])
+                                            ("llama3_8b_kivi2", "int2", 64), ("llama3_70b", "int4", 0),
+                                            ("llama3_8b", "fp8_e5m2", 0), ("llama3_70b", "int4_m16", 0),
+                                            ("llama3_8b_kivi2", "int2_m16", 0)])
 def test_full_size_workloads(name, fmt, steps):
     require_gpu()
     _full_size(name, fmt, steps=steps)
