@@ -12,6 +12,9 @@ Default workload: the Llama-3-8B layer shape (32 query / 8 KV heads,
 head_dim 128) at batch 16 and 8192 cached tokens, 32 layers, with the cache
 quantized to INT8 (headline) and to FP8 E4M3.  The single JSON line on
 stdout carries the INT8 numbers as "value" and the FP8 numbers under "fp8".
+Under "variants" it adds attention-only sweeps of the same shape for the
+other cache variants (FP8 E5M2; INT8 / INT4 / INT2 with fp16 scale and
+offset metadata), eight layer caches each.
 
 Timed regions, both bracketed by HIP events on the stream the library
 launches on (torch's current stream):
@@ -60,6 +63,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--blocks-per-group", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the attention sweep of the other variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
 
@@ -82,6 +86,75 @@ def copy_bandwidth(torch) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+FP8_MAX = {"fp8": 448.0, "fp8_e5m2": 57344.0}
+VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16")
+
+
+def split_spec(spec: str):
+    """Format spec -> (kvq format, fp16 metadata): a suffix "_m16" selects fp16 (s, m) pairs."""
+    return (spec[:-4], True) if spec.endswith("_m16") else (spec, False)
+
+
+def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v):
+    fmt, m16 = split_spec(spec)
+    # FP8 calibration: amax / (largest finite value) of the prefill, per tensor (a caller input)
+    top = FP8_MAX.get(fmt, 448.0)
+    lay = kvq.make_layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_tokens, fmt,
+                          residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens,
+                          k_scale=np.float32(amax_k / top), v_scale=np.float32(amax_v / top), meta_fp16=m16)
+    return kvq.Cache.create(lay)
+
+
+def call_bytes(accounting, w, spec, n):
+    fmt, m16 = split_spec(spec)
+    return accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
+                                      w.sink_tokens, w.residual_tokens, meta_fp16=m16)
+
+
+def variant_sweep(torch, kvq, synth, accounting, w, specs, args, layers=8, rounds=8):
+    """Attention-only timing of each variant: `layers` caches, each call between its own events."""
+    log(f"variant sweep: generating synthetic prefill for {', '.join(specs)}")
+    kp, vp = synth.prefill(w)
+    kd = torch.from_numpy(kp).cuda()
+    vd = torch.from_numpy(vp).cuda()
+    del kp, vp
+    amax_k, amax_v = float(kd.abs().max().float().item()), float(vd.abs().max().float().item())
+    q = torch.from_numpy(synth.queries(w)).cuda()
+    out = torch.empty_like(q)
+    res = {}
+    for spec in specs:
+        caches = []
+        for _ in range(layers):
+            c = make_cache(kvq, w, spec, w.seq_len, amax_k, amax_v)
+            c.append(kd, vd)
+            caches.append(c)
+        ws = torch.empty(caches[0].workspace_bytes(args.blocks_per_group) // 4 + 4, dtype=torch.float32,
+                         device="cuda")
+        for c in caches:
+            c.attention(q, out, ws, args.blocks_per_group)
+        torch.cuda.synchronize()
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in caches]
+               for _ in range(rounds)]
+        for r in range(rounds):
+            for li, c in enumerate(caches):
+                evs[r][li][0].record()
+                c.attention(q, out, ws, args.blocks_per_group)
+                evs[r][li][1].record()
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([e0.elapsed_time(e1) for row in evs for (e0, e1) in row]))
+        nb = call_bytes(accounting, w, spec, w.seq_len)
+        res[spec] = {"attn_call_us": round(us, 2), "bytes_per_attn_call": nb,
+                     "attn_gbps": round(nb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "layers": layers, "attn_calls_timed": layers * rounds}
+        log(f"variant {spec}: attention call {us:.1f} us = {res[spec]['attn_gbps']:.0f} GB/s")
+        del caches, ws
+        torch.cuda.empty_cache()
+    del kd, vd
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     """Time the decode step with the given per-layer formats; returns a result dict."""
     layers = len(fmt_list)
@@ -93,14 +166,10 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     kd = torch.from_numpy(kp).cuda()
     vd = torch.from_numpy(vp).cuda()
     del kp, vp
-    # FP8 calibration: amax / 448 of the prefill, per tensor (a caller input)
-    k_scale = float(kd.abs().max().float().item()) / 448.0
-    v_scale = float(vd.abs().max().float().item()) / 448.0
+    amax_k, amax_v = float(kd.abs().max().float().item()), float(vd.abs().max().float().item())
     caches = []
     for li, fmt in enumerate(fmt_list):
-        lay = kvq.make_layout(b, hkv, hq, d, max_tokens, fmt, residual_tokens=w.residual_tokens,
-                              sink_tokens=w.sink_tokens, k_scale=np.float32(k_scale), v_scale=np.float32(v_scale))
-        c = kvq.Cache.create(lay)
+        c = make_cache(kvq, w, fmt, max_tokens, amax_k, amax_v)
         c.append(kd, vd)
         caches.append(c)
     torch.cuda.synchronize()
@@ -146,13 +215,12 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     torch.cuda.synchronize()
     attn_ms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
     n_final = n0 + total_steps
-    sweep_bytes = sum(accounting.attention_bytes(b, hkv, hq, d, n_final, fmt, w.sink_tokens, w.residual_tokens)
-                      for fmt in fmt_list) / layers
+    sweep_bytes = sum(call_bytes(accounting, w, fmt, n_final) for fmt in fmt_list) / layers
     nbytes = 0
     for s in range(args.steps):
         n = n0 + args.warmup + s + 1
         for fmt in fmt_list:
-            nbytes += accounting.attention_bytes(b, hkv, hq, d, n, fmt, w.sink_tokens, w.residual_tokens)
+            nbytes += call_bytes(accounting, w, fmt, n)
     ms_step = total_ms / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
     res = {
@@ -259,6 +327,9 @@ def main():
         else:
             fl = [var] * nl
         results[var] = run_format(torch, kvq, synth, accounting, w, fl, args)
+    vres = None
+    if not args.no_variants and args.workload == "llama3_8b" and not args.formats:
+        vres = variant_sweep(torch, kvq, synth, accounting, w, VARIANTS, args)
     copy_gbps = copy_bandwidth(torch)
     log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
     head = results[variants[0]]
@@ -294,6 +365,8 @@ def main():
     for var in variants[1:]:
         r = results[var]
         line[var] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+    if vres:
+        line["variants"] = vres
     if not args.no_cpu_baseline:
         fmt0 = variants[0] if variants[0] != "mixed" else "int4"
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
