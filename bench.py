@@ -14,7 +14,8 @@ quantized to INT8 (headline) and to FP8 E4M3.  The single JSON line on
 stdout carries the INT8 numbers as "value" and the FP8 numbers under "fp8".
 Under "variants" it adds attention-only sweeps of the same shape for the
 other cache variants (FP8 E5M2; INT8 / INT4 / INT2 with fp16 scale and
-offset metadata), eight layer caches each.
+offset metadata; INT8 in a paged pool of 32-token pages in shuffled
+order), eight layer caches each.
 
 Timed regions, both bracketed by HIP events on the stream the library
 launches on (torch's current stream):
@@ -87,26 +88,37 @@ def copy_bandwidth(torch) -> float:
 
 
 FP8_MAX = {"fp8": 448.0, "fp8_e5m2": 57344.0}
-VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16")
+VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16", "int8_paged")
 
 
 def split_spec(spec: str):
-    """Format spec -> (kvq format, fp16 metadata): a suffix "_m16" selects fp16 (s, m) pairs."""
-    return (spec[:-4], True) if spec.endswith("_m16") else (spec, False)
+    """Format spec -> (kvq format, fp16 metadata, paged): suffix "_m16" selects fp16 (s, m)
+    pairs, "_paged" a pool of 32-token pages."""
+    paged = spec.endswith("_paged")
+    spec = spec[:-6] if paged else spec
+    m16 = spec.endswith("_m16")
+    return (spec[:-4] if m16 else spec), m16, paged
 
 
-def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v):
-    fmt, m16 = split_spec(spec)
+def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v, seed=0):
+    import torch
+    fmt, m16, paged = split_spec(spec)
     # FP8 calibration: amax / (largest finite value) of the prefill, per tensor (a caller input)
     top = FP8_MAX.get(fmt, 448.0)
+    pps = max(1, (max_tokens - w.sink_tokens - w.residual_tokens) // 32)   # one block per page
     lay = kvq.make_layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_tokens, fmt,
                           residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens,
-                          k_scale=np.float32(amax_k / top), v_scale=np.float32(amax_v / top), meta_fp16=m16)
-    return kvq.Cache.create(lay)
+                          k_scale=np.float32(amax_k / top), v_scale=np.float32(amax_v / top), meta_fp16=m16,
+                          page_blocks=1 if paged else 0, num_pages=w.batch * pps if paged else 0)
+    c = kvq.Cache.create(lay)
+    if paged:                                    # every sequence's pages scattered over the pool
+        perm = np.random.default_rng(seed).permutation(w.batch * pps).astype(np.int32)
+        c.set_block_table(torch.from_numpy(perm.reshape(w.batch, pps)).cuda())
+    return c
 
 
 def call_bytes(accounting, w, spec, n):
-    fmt, m16 = split_spec(spec)
+    fmt, m16, _ = split_spec(spec)
     return accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
                                       w.sink_tokens, w.residual_tokens, meta_fp16=m16)
 
@@ -124,8 +136,8 @@ def variant_sweep(torch, kvq, synth, accounting, w, specs, args, layers=8, round
     res = {}
     for spec in specs:
         caches = []
-        for _ in range(layers):
-            c = make_cache(kvq, w, spec, w.seq_len, amax_k, amax_v)
+        for li in range(layers):
+            c = make_cache(kvq, w, spec, w.seq_len, amax_k, amax_v, seed=li)
             c.append(kd, vd)
             caches.append(c)
         ws = torch.empty(caches[0].workspace_bytes(args.blocks_per_group) // 4 + 4, dtype=torch.float32,

@@ -78,6 +78,27 @@
  *
  * FP8 E5M2 codes use the INT8 / FP8 byte layouts above.
  *
+ * Paged cache (page_blocks = P >= 1): the four quantized planes (K / V
+ * codes, K / V meta) are pools of num_pages pages instead of [B][Hkv][NB]
+ * arrays.  A page holds P consecutive 32-token blocks of one sequence for
+ * all Hkv heads: block-sized records ordered [page][Hkv][P], each record in
+ * the block layout above.  Logical block j (0 .. NB-1) of sequence b, head
+ * h, is record (page * Hkv + h) * P + j % P with page = table[b * stride +
+ * j / P] ("KV Cache Quantization Analysis", sec. 5: paged blocks are
+ * orthogonal to quantization, and low-bit blocks hold more tokens per page;
+ * "Quantization and the KV cache: two ways to run a model lighter", section
+ * on how the KV-cache side works: the cache is split into small blocks, a
+ * table per request lists its blocks, and requests with the same prompt may
+ * share blocks).  The table
+ * is an int32 device array set by kvq_cache_set_block_table, owned and
+ * filled by the caller before the calls that touch those blocks.  Pages of
+ * different sequences may be shared only where their quantized blocks are
+ * identical (the same tokens).  A page id outside [0, num_pages) is a
+ * caller error: the kernels never touch memory outside the pool for it (the
+ * block is not written, and attention reads page 0 in its place, so that
+ * sequence's output is undefined).  The fp16 ring and sink planes stay per
+ * sequence.
+ *
  * Limits of this version (KVQ_ERR_UNSUPPORTED otherwise): head_dim == 128,
  * k_group_tokens == 32, v_group_channels == 32, num_q_heads / num_kv_heads
  * in {1, 2, 4, 8}.
@@ -122,6 +143,8 @@ typedef struct {
   float k_scale;             /* FP8 only: Key scale, finite and > 0 */
   float v_scale;             /* FP8 only: Value scale, finite and > 0 */
   int32_t meta_fp16;         /* INT only: 0 = fp32 (s, z) pairs, 1 = fp16 (s, m) pairs; 0 for FP8 */
+  int32_t page_blocks;       /* 0: contiguous planes; P >= 1: paged, P 32-token blocks per page */
+  int32_t num_pages;         /* paged only: pages in the pool (>= 1) */
 } kvq_layout;
 
 enum {
@@ -143,6 +166,8 @@ typedef struct {
   int32_t ring_slots;                  /* R + 32 */
   uint64_t plane_off[KVQ_NUM_PLANES];  /* byte offsets from base */
   uint64_t plane_bytes[KVQ_NUM_PLANES];
+  const int32_t* block_table;          /* paged only: device int32 [B][table_stride] */
+  int32_t table_stride;                /* pages per sequence row of block_table */
 } kvq_cache;
 
 /* Static string naming a status code. */
@@ -165,6 +190,16 @@ int32_t kvq_cache_plane(const kvq_cache* cache, int32_t plane, uint64_t* offset,
 
 /* Current routing: sinks held, quantized body tokens, fp16 residual tokens. */
 int32_t kvq_cache_window(const kvq_cache* cache, int64_t* n_sink, int64_t* n_q, int64_t* n_residual);
+
+/* Paged layouts: bind the block table, an int32 device array [B][stride]
+ * (4-B aligned) whose row b lists the physical pages of sequence b's
+ * logical pages 0 .. ceil(NB / P) - 1 (stride >= that count).  The library
+ * keeps the pointer and reads the table on the device at every append and
+ * attention call; the caller may change its contents between calls.  NULL
+ * unbinds it.  Errors: KVQ_ERR_LAYOUT for a contiguous layout or a stride
+ * below ceil(NB / P), KVQ_ERR_ALIGN.  kv_quant_append and the attention
+ * calls return KVQ_ERR_NULL on a paged cache without a table. */
+int32_t kvq_cache_set_block_table(kvq_cache* cache, const void* table, int32_t stride);
 
 /* Quantize-on-append ("KV Cache Quantization Analysis", sec. 5: quantize
  * the new K, V right after they are computed, then store).

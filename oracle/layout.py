@@ -31,6 +31,14 @@ Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
 * V meta    [B][Hkv][NB][D/G_v][32][2] fp32: (s, z) of each channel group and token
   (fp16 metadata: the same shapes holding fp16 (s, m) pairs, m the offset)
 * K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
+
+Paged caches keep the four quantized planes as a pool of pages, each page
+P consecutive 32-token blocks of one sequence for all KV heads: records
+ordered [page][Hkv][P].  Logical block j of (sequence b, head h) is record
+(table[b][j // P] * Hkv + h) * P + j % P ("Quantization and the KV cache:
+two ways to run a model lighter", KV-cache side: small blocks and a table
+per request; "KV Cache Quantization Analysis", sec. 5: paging is orthogonal
+to quantization).
 """
 from __future__ import annotations
 
@@ -203,3 +211,20 @@ def unpack_v_meta(m: np.ndarray):
     s = np.swapaxes(m[..., 0], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
     z = np.swapaxes(m[..., 1], -1, -2).reshape(m.shape[:-4] + (nb * blk, gn))
     return s.copy(), z.copy()
+
+
+def paged_record(table: np.ndarray, b: int, h: int, blk: int, hkv: int, page_blocks: int) -> int:
+    """Pool record holding logical block ``blk`` of (sequence b, head h)."""
+    page = int(table[b, blk // page_blocks])
+    return (page * hkv + h) * page_blocks + blk % page_blocks
+
+
+def gather_paged(pool: np.ndarray, table: np.ndarray, hkv: int, page_blocks: int, nb: int) -> np.ndarray:
+    """Pool records [n_records, ...] -> logical blocks [B, Hkv, nb, ...] through the table."""
+    pool = np.asarray(pool)
+    table = np.asarray(table, np.int64)
+    b = table.shape[0]
+    blk = np.arange(nb)
+    page = table[:, blk // page_blocks]                           # [B, nb]
+    rec = (page[:, None, :] * hkv + np.arange(hkv)[None, :, None]) * page_blocks + (blk % page_blocks)[None, None]
+    return pool[rec.reshape(-1)].reshape((b, hkv, nb) + pool.shape[1:])

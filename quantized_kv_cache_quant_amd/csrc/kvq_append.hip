@@ -98,6 +98,10 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * p.hkv + h;
+  // record of this block in the code / meta planes (paged: through the block
+  // table); a page id outside the pool leaves the block unwritten
+  const int64_t rec = block_record(p.table, p.table_stride, p.page_blocks, p.num_pages, p.hkv, p.nb_cap, b, h, blk);
+  if (rec < 0) return;                                // uniform over the workgroup, before any barrier
 
   // 1) gather the block's 32 tokens (16-byte chunks, 16 per token row)
   for (int e = tid; e < kBlock * 16; e += 256) {
@@ -147,14 +151,14 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
         sk[c] = half_bits_to_float(sb);
         zk[c] = mn;
-        reinterpret_cast<uint32_t*>(p.k_meta)[(bh * p.nb_cap + blk) * kHeadDim + c] = sb | (mb << 16);
+        reinterpret_cast<uint32_t*>(p.k_meta)[rec * kHeadDim + c] = sb | (mb << 16);
       } else {
         float s = (mx - mn) / kQmax;
         if (s == 0.0f) s = 1.0f;
         const float z = (-mn) / s;
         sk[c] = s;
         zk[c] = z;
-        float* km = p.k_meta + (bh * p.nb_cap + blk) * (2 * kHeadDim);   // [D][s, z]
+        float* km = p.k_meta + rec * (2 * kHeadDim);   // [D][s, z]
         km[2 * c] = s;
         km[2 * c + 1] = z;
       }
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);
         sv[t][g] = half_bits_to_float(sb);
         zv[t][g] = mn;
-        reinterpret_cast<uint32_t*>(p.v_meta)[(bh * p.nb_cap + blk) * (kVGroups * kBlock) + g * kBlock + t] =
+        reinterpret_cast<uint32_t*>(p.v_meta)[rec * (kVGroups * kBlock) + g * kBlock + t] =
             sb | (mb << 16);
       } else {
         float s = (mx - mn) / kQmax;
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const float z = (-mn) / s;
         sv[t][g] = s;
         zv[t][g] = z;
-        float* vm = p.v_meta + (bh * p.nb_cap + blk) * (2 * kVGroups * kBlock);  // [group][token][s, z]
+        float* vm = p.v_meta + rec * (2 * kVGroups * kBlock);  // [group][token][s, z]
         vm[2 * (g * kBlock + t)] = s;
         vm[2 * (g * kBlock + t) + 1] = z;
       }
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   //    32 qd + 16 half .. + 15 of token 16 tile + r.
   {
     constexpr int kWordsPerRow = kRowBytes / 4;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + rec * kBlock * kRowBytes);
     for (int w = tid; w < kBlock * kWordsPerRow; w += 256) {
       int t, wi;
       if constexpr (kBits == 8) {
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   //    order, stored as 16-byte groups: group i of record l at 16 (64 i + l)
   {
     constexpr int kRecWords = kHeadDim * kBits / 16 / 4;   // words per record
-    uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + (bh * p.nb_cap + blk) * kBlock * kRowBytes);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + rec * kBlock * kRowBytes);
     for (int w = tid; w < 64 * kRecWords; w += 256) {
       const int lane = (w >> 2) & 63;
       const int wi = 4 * (w >> 8) + (w & 3);

@@ -231,16 +231,16 @@ __device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
   }
 }
 
-// Loads one block.  bh and blk are wave-uniform, so the block base is a
-// scalar and the per-lane parts are 32-bit offsets.
+// Loads one block, record rec of the code and meta planes.  rec is
+// wave-uniform, so the block base is a scalar and the per-lane parts are
+// 32-bit offsets.
 // Every code load of a wavefront reads whole 128-byte lines: 8-bit K is
 // stored as 16-byte units (tile, half, lane) and V records are split into
 // 16-byte groups stored group-major, so lane l of a load reads unit l.
 template <int FMT, bool kStream = true>
-__device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int64_t bh, int64_t blk,
-                                           int lane) {
+__device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int64_t rec, int lane) {
   using T = Traits<FMT>;
-  const int64_t id = bh * p.nb_cap + blk;
+  const int64_t id = rec;
   const uint8_t* kb = p.k_codes + id * (int64_t)(kBlock * T::kRowBytes);
   const uint8_t* vb = p.v_codes + id * (int64_t)(kBlock * T::kRowBytes);
   const uint4* k16 = reinterpret_cast<const uint4*>(kb);
@@ -802,9 +802,21 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   const uint32_t nblk = (uint32_t)p.nblk;
   float* stage = reinterpret_cast<float*>(lds + v * kWaveLds);
   int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
+  int* recs = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + 16);
 
-  // the block counter starts at zero; the barrier comes before any load is
-  // issued, so no wavefront waits on another's loads
+  // paged caches: the record ids of the range's blocks, read from the block
+  // table once (a page id outside the pool reads record 0 instead)
+  if (p.table) {
+    for (int i = threadIdx.x; i < gr.len; i += kGroupThreads) {
+      const int64_t j = gr.jb + i;
+      const int64_t bhj = j / nblk;
+      const int64_t r = block_record(p.table, p.table_stride, p.page_blocks, p.num_pages, p.hkv, p.nb_cap,
+                                     bhj / p.hkv, bhj % p.hkv, j - bhj * nblk);
+      recs[i] = r < 0 ? 0 : (int)r;
+    }
+  }
+  // the block counter starts at zero; the barrier comes before any block
+  // load is issued, so no wavefront waits on another's loads
   if (threadIdx.x == 0) *ctr = 0;
   __syncthreads();
 
@@ -840,11 +852,13 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
       j = ps + (j - ps + rot) % (pe - ps);
       bhout = (int)bh;
-      load_block<FMT>(r, p, bh, j - bh * nblk, li.lane);
+      const int64_t rec = p.table ? (int64_t)__builtin_amdgcn_readfirstlane(recs[j - (uint32_t)gr.jb])
+                                  : (int64_t)bh * p.nb_cap + (j - bh * nblk);
+      load_block<FMT>(r, p, rec, li.lane);
     } else {
       id = -1;
       bhout = 0;
-      load_block<FMT, false>(r, p, 0, 0, li.lane);
+      load_block<FMT, false>(r, p, 0, li.lane);
     }
   };
 #pragma unroll
@@ -957,7 +971,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   }
 }
 
-constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16;
+constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
 
 // No quantized blocks yet: workgroup g takes the fp16 blocks of head g.
 __device__ void fp16_group(const AttnParams& p, char* lds) {

@@ -41,15 +41,17 @@ int32_t nb_cap(const kvq_layout& L) {
 // Plane sizes in bytes for a validated layout.
 void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   const uint64_t bh = (uint64_t)L.batch * L.num_kv_heads;
-  const uint64_t nb = (uint64_t)nb_cap(L);
+  // block records of the quantized planes: [B][Hkv][NB], or the page pool
+  const uint64_t recs = L.page_blocks > 0 ? (uint64_t)L.num_pages * L.num_kv_heads * L.page_blocks
+                                          : bh * (uint64_t)nb_cap(L);
   const uint64_t bits = (uint64_t)format_bits(L.format);
   const uint64_t d = (uint64_t)L.head_dim;
   const bool fp8 = fp8_of(L.format);
   const uint64_t eb = L.meta_fp16 ? 2 : 4;           // bytes per scale / zero-point
-  sz[KVQ_PLANE_K_CODES] = bh * nb * kBlock * d * bits / 8;
+  sz[KVQ_PLANE_K_CODES] = recs * kBlock * d * bits / 8;
   sz[KVQ_PLANE_V_CODES] = sz[KVQ_PLANE_K_CODES];
-  sz[KVQ_PLANE_K_META] = fp8 ? 0 : bh * nb * 2 * d * eb;
-  sz[KVQ_PLANE_V_META] = fp8 ? 0 : bh * nb * 2 * (d / L.v_group_channels) * kBlock * eb;
+  sz[KVQ_PLANE_K_META] = fp8 ? 0 : recs * 2 * d * eb;
+  sz[KVQ_PLANE_V_META] = fp8 ? 0 : recs * 2 * (d / L.v_group_channels) * kBlock * eb;
   sz[KVQ_PLANE_K_RING] = bh * (uint64_t)(L.residual_tokens + kBlock) * d * 2;
   sz[KVQ_PLANE_V_RING] = sz[KVQ_PLANE_K_RING];
   sz[KVQ_PLANE_K_SINK] = bh * (uint64_t)L.sink_tokens * d * 2;
@@ -79,6 +81,8 @@ struct AttnPlan {
 // workgroups whose range touches the head (one workgroup per head when no
 // block is quantized yet).  Partial slots: one per fp16 block, plus, for the
 // quantized blocks, kGroupWaves + 1 per (workgroup, head) index g + bh.
+// Paged caches stage a range's record ids in LDS, so their ranges hold at
+// most kMaxPagedRange blocks.
 AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpg) {
   AttnPlan a{};
   const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
@@ -87,6 +91,7 @@ AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t 
   const int64_t target = device_cus() * kGroupsPerCu;
   if (bpg > 0) a.group_blocks = bpg;
   else a.group_blocks = total > 0 ? (total + target - 1) / target : 1;
+  if (L.page_blocks > 0 && a.group_blocks > kMaxPagedRange) a.group_blocks = kMaxPagedRange;
   a.groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : bh;
   a.slots = bh * a.fp16_blocks + (total > 0 ? (kGroupWaves + 1) * (a.groups + bh) : 0);
   return a;
@@ -131,6 +136,10 @@ int32_t kvq_layout_validate(const kvq_layout* L) {
       return KVQ_ERR_LAYOUT;
   }
   if (L->sink_tokens > L->max_tokens) return KVQ_ERR_LAYOUT;
+  if (L->page_blocks < 0 || (L->page_blocks > 0 && L->num_pages < 1)) return KVQ_ERR_LAYOUT;
+  // block records are 32-bit in the attention kernel
+  if (L->page_blocks > 0 && (int64_t)L->num_pages * L->num_kv_heads * L->page_blocks > 0x7fffffffLL)
+    return KVQ_ERR_UNSUPPORTED;
   if (L->head_dim != kHeadDim || L->k_group_tokens != kBlock || L->v_group_channels != kVGroup)
     return KVQ_ERR_UNSUPPORTED;
   const int nrep = L->num_q_heads / L->num_kv_heads;
@@ -196,11 +205,29 @@ int32_t kvq_cache_window(const kvq_cache* c, int64_t* n_sink, int64_t* n_q, int6
   return KVQ_OK;
 }
 
+int32_t kvq_cache_set_block_table(kvq_cache* c, const void* table, int32_t stride) {
+  if (!c) return KVQ_ERR_NULL;
+  const kvq_layout& L = c->layout;
+  if (L.page_blocks <= 0) return KVQ_ERR_LAYOUT;
+  if (!table) {
+    c->block_table = nullptr;
+    c->table_stride = 0;
+    return KVQ_OK;
+  }
+  const int64_t pages = ((int64_t)c->n_blocks_cap + L.page_blocks - 1) / L.page_blocks;
+  if (stride < pages || stride < 1) return KVQ_ERR_LAYOUT;
+  if (!aligned(table, 4)) return KVQ_ERR_ALIGN;
+  c->block_table = static_cast<const int32_t*>(table);
+  c->table_stride = stride;
+  return KVQ_OK;
+}
+
 int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, void* stream) {
   if (!c || !c->base) return KVQ_ERR_NULL;
   const kvq_layout& L = c->layout;
   int32_t st = kvq_layout_validate(&L);
   if (st != KVQ_OK) return st;
+  if (L.page_blocks > 0 && !c->block_table) return KVQ_ERR_NULL;
   if (T < 0) return KVQ_ERR_LAYOUT;
   if (T == 0) return KVQ_OK;
   if (!K || !V) return KVQ_ERR_NULL;
@@ -238,6 +265,10 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
     p.n_body_old = n_old - w0.n_sink;
     p.k_scale = L.k_scale;
     p.v_scale = L.v_scale;
+    p.table = c->block_table;
+    p.table_stride = c->table_stride;
+    p.page_blocks = L.page_blocks;
+    p.num_pages = L.num_pages;
     if (n_flush > 0x7fffffff) return KVQ_ERR_UNSUPPORTED;
     if (launch_flush(variant_of(L), p, (int)n_flush, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   }
@@ -272,6 +303,8 @@ int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpg, uint64_t* bytes) {
   const uint64_t nf = bh * (((uint64_t)L.sink_tokens + L.residual_tokens + kBlock - 1 + kBlock - 1) / kBlock);
   uint64_t groups = 0;
   if (total > 0) groups = bpg > 0 ? (total + bpg - 1) / bpg : std::min<uint64_t>(total, (uint64_t)(device_cus() * kGroupsPerCu));
+  if (total > 0 && L.page_blocks > 0)        // paged ranges hold at most kMaxPagedRange blocks
+    groups = std::max<uint64_t>(groups, (total + kMaxPagedRange - 1) / kMaxPagedRange);
   *bytes = (nf + (total > 0 ? (kGroupWaves + 1) * (groups + bh) : 0)) * slot_bytes(L);
   return KVQ_OK;
 }
@@ -283,6 +316,8 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   int32_t st = kvq_layout_validate(&L);
   if (st != KVQ_OK) return st;
   if (bpg < 0 || bpg > kMaxBlocksPerGroup || (deterministic != 0 && deterministic != 1)) return KVQ_ERR_LAYOUT;
+  if (L.page_blocks > 0 && bpg > kMaxPagedRange) return KVQ_ERR_LAYOUT;
+  if (L.page_blocks > 0 && !c->block_table) return KVQ_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
   if (c->n_tokens == 0) return KVQ_ERR_EMPTY;
   const Window w = window(L, c->n_tokens);
@@ -328,6 +363,10 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.deterministic = deterministic;
   p.k_scale = L.k_scale;
   p.v_scale = L.v_scale;
+  p.table = c->block_table;
+  p.table_stride = c->table_stride;
+  p.page_blocks = L.page_blocks;
+  p.num_pages = L.num_pages;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;

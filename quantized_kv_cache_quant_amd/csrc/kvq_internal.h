@@ -23,6 +23,7 @@ constexpr int kPartStride = 132;  // floats per partial: m, l, 2 pad, o[128]
 constexpr int kGroupWaves = KVQ_GROUP_WAVES;        // wavefronts per attention workgroup (power of 2)
 constexpr int kGroupsPerCu = KVQ_GROUPS_PER_CU;     // workgroup ranges per compute unit (library split)
 constexpr int kMaxBlocksPerGroup = 1 << 20;
+constexpr int kMaxPagedRange = 4096;     // paged caches: blocks per workgroup range (ids staged in LDS)
 
 // Kernel variant: the kvq_format, plus kMeta16 when an INT format stores
 // fp16 (scale, offset) pairs.
@@ -54,7 +55,24 @@ struct FlushParams {
   int32_t first_block;    // n_q_old / 32
   int64_t n_body_old;     // max(0, n_old - S)
   float k_scale, v_scale; // FP8
+  const int32_t* table;   // paged: block table [B][table_stride], else null
+  int32_t table_stride;
+  int32_t page_blocks;    // P
+  int32_t num_pages;
 };
+
+// Record index of logical block blk of (sequence b, head h) in the code and
+// meta planes: contiguous (b * Hkv + h) * NB + blk, or paged
+// (page * Hkv + h) * P + blk % P with page = table[b][blk / P]; -1 when the
+// page id lies outside the pool.
+__host__ __device__ inline int64_t block_record(const int32_t* table, int32_t stride, int32_t page_blocks,
+                                                int32_t num_pages, int32_t hkv, int32_t nb_cap, int64_t b,
+                                                int64_t h, int64_t blk) {
+  if (!table) return (b * hkv + h) * nb_cap + blk;
+  const int32_t page = table[b * stride + blk / page_blocks];
+  if (page < 0 || page >= num_pages) return -1;
+  return ((int64_t)page * hkv + h) * page_blocks + blk % page_blocks;
+}
 
 struct CopyParams {
   const uint16_t* k_in;
@@ -115,6 +133,10 @@ struct AttnParams {
   int32_t fp16_blocks;    // ceil((n_sink + n_res) / 32) per head
   int32_t deterministic;  // 1: wavefront w takes blocks w, w + 8, ... of its range
   float k_scale, v_scale; // FP8
+  const int32_t* table;   // paged: block table [B][table_stride] (record ids via block_record)
+  int32_t table_stride;
+  int32_t page_blocks;
+  int32_t num_pages;
 };
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s);

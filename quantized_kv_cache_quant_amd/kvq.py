@@ -20,7 +20,7 @@ FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3, "fp8_e5m2": 4}
 PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink")
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
-           "kv_decode_attention", "kv_decode_attention_split")
+           "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table")
 
 
 class KvqError(RuntimeError):
@@ -35,14 +35,16 @@ class Layout(ctypes.Structure):
                 ("max_tokens", ctypes.c_int32), ("format", ctypes.c_int32),
                 ("k_group_tokens", ctypes.c_int32), ("v_group_channels", ctypes.c_int32),
                 ("residual_tokens", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("meta_fp16", ctypes.c_int32)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("meta_fp16", ctypes.c_int32),
+                ("page_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
     _fields_ = [("layout", Layout), ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
                 ("n_tokens", ctypes.c_int64), ("n_blocks_cap", ctypes.c_int32),
                 ("ring_slots", ctypes.c_int32), ("plane_off", ctypes.c_uint64 * len(PLANES)),
-                ("plane_bytes", ctypes.c_uint64 * len(PLANES))]
+                ("plane_bytes", ctypes.c_uint64 * len(PLANES)), ("block_table", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "kvq_workspace_bytes": (I32, [CP, I32, ctypes.POINTER(U64)]),
             "kv_decode_attention": (I32, [CP, P, P, P, U64, P]),
             "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, I32, P]),
+            "kvq_cache_set_block_table": (I32, [CP, P, I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -89,9 +92,10 @@ def check(status: int, where: str) -> None:
 
 def make_layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, fmt, *, k_group_tokens=32,
                 v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0,
-                meta_fp16=False) -> Layout:
+                meta_fp16=False, page_blocks=0, num_pages=0) -> Layout:
     return Layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, FORMATS[fmt], k_group_tokens,
-                  v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale), int(meta_fp16))
+                  v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale), int(meta_fp16),
+                  int(page_blocks), int(num_pages))
 
 
 def cache_bytes(layout: Layout) -> int:
@@ -112,6 +116,7 @@ class Cache:
     layout: Layout
     buf: "object"          # torch.uint8 device tensor (keeps the memory alive)
     handle: CacheStruct
+    table: "object" = None  # paged caches: the bound int32 block table (kept alive here)
 
     @classmethod
     def create(cls, layout: Layout, device="cuda") -> "Cache":
@@ -140,6 +145,19 @@ class Cache:
         check(lib().kvq_cache_plane(ctypes.byref(self.handle), PLANES.index(name), ctypes.byref(off),
                                     ctypes.byref(nb)), "kvq_cache_plane")
         return self.buf[off.value:off.value + nb.value]
+
+    def set_block_table(self, table) -> None:
+        """Paged caches: bind an int32 device tensor [B][stride] of page ids (None unbinds)."""
+        import torch
+        if table is None:
+            check(lib().kvq_cache_set_block_table(ctypes.byref(self.handle), None, 0), "kvq_cache_set_block_table")
+            self.table = None
+            return
+        if not table.is_cuda or table.dtype != torch.int32 or table.dim() != 2 or not table.is_contiguous():
+            raise ValueError("block table must be a contiguous int32 device tensor [B][stride]")
+        check(lib().kvq_cache_set_block_table(ctypes.byref(self.handle), ctypes.c_void_p(table.data_ptr()),
+                                              int(table.shape[1])), "kvq_cache_set_block_table")
+        self.table = table
 
     def append(self, k, v, stream=None) -> None:
         """k, v: contiguous fp16 device tensors [B][T][Hkv][D]."""

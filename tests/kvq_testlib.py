@@ -75,15 +75,25 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
     def pl(name, dtype, shape):
         return plane_np(c, name).view(dtype).reshape(shape)
 
-    kc = pl("k_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
-    vc = pl("v_codes", np.uint8, (b, hkv, nb_cap, 32 * row))[:, :, :nb]
+    pb = c.handle.layout.page_blocks
+    if pb > 0:                                   # paged: gather the logical blocks through the table
+        recs = c.handle.layout.num_pages * hkv * pb
+        table = c.table.cpu().numpy()
+
+        def blocks(name, dtype, shape):
+            return olayout.gather_paged(pl(name, dtype, (recs,) + shape), table, hkv, pb, nb)
+    else:
+        def blocks(name, dtype, shape):
+            return pl(name, dtype, (b, hkv, nb_cap) + shape)[:, :, :nb]
+    kc = blocks("k_codes", np.uint8, (32 * row,))
+    vc = blocks("v_codes", np.uint8, (32 * row,))
     codes_k = olayout.unpack_k_codes(kc, olay.fmt, d)
     codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
     s_k = z_k = s_v = z_v = None
     if olay.fmt not in FP8:
         mt = np.float16 if olay.meta_fp16 else np.float32
-        km = pl("k_meta", mt, (b, hkv, nb_cap, d, 2))[:, :, :nb]
-        vm = pl("v_meta", mt, (b, hkv, nb_cap, 4, 32, 2))[:, :, :nb]
+        km = blocks("k_meta", mt, (d, 2))
+        vm = blocks("v_meta", mt, (4, 32, 2))
         s_k, z_k = olayout.unpack_k_meta(km)
         s_v, z_v = olayout.unpack_v_meta(vm)
     ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))

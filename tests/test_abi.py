@@ -195,3 +195,54 @@ def test_attention_errors():
         assert L.kvq_workspace_bytes(ctypes.byref(h), bpg, ctypes.byref(w)) == 0
         assert w.value <= prev
         prev = w.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"page_blocks": 1, "num_pages": 10}, 0),
+    ({"page_blocks": 4, "num_pages": 1}, 0),
+    ({"page_blocks": -1}, -2),
+    ({"page_blocks": 2, "num_pages": 0}, -2),
+    ({"page_blocks": 1 << 20, "num_pages": 1 << 20}, -3),      # records beyond 32 bits
+])
+def test_paged_layout_validation(kw, status):
+    lay = _lay(**kw)
+    assert kvq.lib().kvq_layout_validate(ctypes.byref(lay)) == status
+
+
+@pytest.mark.parametrize("fmt,bits,pb,pages", [("int8", 8, 1, 37), ("int4", 4, 3, 5), ("fp8", 8, 2, 9),
+                                               ("int2", 2, 1, 1)])
+def test_paged_planes_and_table_binding(fmt, bits, pb, pages):
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    b, hkv, d = 3, 2, 128
+    lay = _lay(batch=b, num_kv_heads=hkv, num_q_heads=hkv * 2, fmt=fmt, max_tokens=1000,
+               residual_tokens=32, sink_tokens=4, page_blocks=pb, num_pages=pages)
+    total = kvq.cache_bytes(lay)
+    h = kvq.CacheStruct()
+    assert L.kvq_cache_init(ctypes.byref(h), ctypes.byref(lay), P(FAKE), total) == 0
+    recs = pages * hkv * pb
+    fp8 = fmt.startswith("fp8")
+    expect = {"k_codes": recs * 32 * d * bits // 8, "v_codes": recs * 32 * d * bits // 8,
+              "k_meta": 0 if fp8 else recs * 2 * d * 4, "v_meta": 0 if fp8 else recs * 2 * 4 * 32 * 4,
+              "k_ring": b * hkv * 64 * d * 2, "v_ring": b * hkv * 64 * d * 2,
+              "k_sink": b * hkv * 4 * d * 2, "v_sink": b * hkv * 4 * d * 2}
+    for i, name in enumerate(kvq.PLANES):
+        assert h.plane_bytes[i] == expect[name], name
+    assert h.block_table is None and h.n_blocks_cap == (1000 - 36) // 32
+    need = -(-h.n_blocks_cap // pb)                       # table entries per sequence
+    # calls on a paged cache need a bound table
+    assert L.kv_quant_append(ctypes.byref(h), P(FAKE), P(FAKE), 4, None) == -1
+    h.n_tokens = 500
+    assert L.kv_decode_attention(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, None) == -1
+    assert L.kvq_cache_set_block_table(ctypes.byref(h), P(FAKE), need - 1) == -2
+    assert L.kvq_cache_set_block_table(ctypes.byref(h), P(FAKE + 2), need) == -5
+    assert L.kvq_cache_set_block_table(ctypes.byref(h), P(FAKE), need) == 0
+    assert h.block_table == FAKE and h.table_stride == need
+    # ranges of a paged cache hold at most 4096 blocks
+    split = L.kv_decode_attention_split
+    assert split(ctypes.byref(h), P(FAKE), P(FAKE), P(FAKE), 1 << 30, 4097, 0, None) == -2
+    assert L.kvq_cache_set_block_table(ctypes.byref(h), None, 0) == 0 and h.block_table is None
+    # a contiguous cache has no table
+    lay2, h2 = _cache()
+    assert L.kvq_cache_set_block_table(ctypes.byref(h2), P(FAKE), 100) == -2
+    assert L.kvq_cache_set_block_table(None, P(FAKE), 100) == -1

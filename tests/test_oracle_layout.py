@@ -110,3 +110,27 @@ def test_empty_planes_unpack(fmt):
     assert k.shape == (2, 3, 0, 128)
     v = layout.unpack_v_codes(np.zeros((2, 3, 0, 32 * 128 * bits // 8), np.uint8), fmt, 128)
     assert v.shape == (2, 3, 0, 128)
+
+
+@pytest.mark.parametrize("page_blocks", [1, 3])
+def test_paged_gather_follows_the_record_rule(page_blocks):
+    rng = np.random.default_rng(page_blocks)
+    b, hkv, nb = 3, 2, 7
+    pages_per_seq = -(-nb // page_blocks)
+    num_pages = b * pages_per_seq + 4
+    table = rng.permutation(num_pages)[:b * pages_per_seq].reshape(b, pages_per_seq)
+    pool = rng.integers(0, 256, size=(num_pages * hkv * page_blocks, 5), dtype=np.uint8)
+    got = layout.gather_paged(pool, table, hkv, page_blocks, nb)
+    assert got.shape == (b, hkv, nb, 5)
+    for bi in range(b):
+        for h in range(hkv):
+            for j in range(nb):
+                # page = table[b][j // P]; records ordered [page][Hkv][P]
+                page = table[bi, j // page_blocks]
+                rec = page * hkv * page_blocks + h * page_blocks + j % page_blocks
+                assert layout.paged_record(table, bi, h, j, hkv, page_blocks) == rec
+                assert np.array_equal(got[bi, h, j], pool[rec])
+    # distinct pages give distinct records: the logical blocks are a permutation of pool rows
+    recs = {layout.paged_record(table, bi, h, j, hkv, page_blocks)
+            for bi in range(b) for h in range(hkv) for j in range(nb)}
+    assert len(recs) == b * hkv * nb
