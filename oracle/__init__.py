@@ -26,6 +26,7 @@ quant      integer affine group quantization (fp32-exact) and OCP FP8 E4M3.
 cache      token routing: sinks, quantized body, fp16 residual window.
 layout     the library's documented byte layout, restated for comparison.
 attention  fp64 GQA decode attention over the dequantized cache.
+rope       rotary position embedding of pre-RoPE Keys (fp64).
 nbytes     the KV_bytes formula and per-step algorithmic byte counts.
 
 Parity status: every function is pinned by a ``-m "not gpu"`` test in

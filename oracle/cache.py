@@ -62,6 +62,7 @@ class Layout:
     k_scale: float = 1.0
     v_scale: float = 1.0
     meta_fp16: bool = False       # INT only: fp16 (s, m) pairs instead of fp32 (s, z)
+    rope_theta: float = 0.0       # > 0: Keys stored before RoPE, rotated with this base in attention
 
     @property
     def bits(self) -> int:
@@ -141,7 +142,11 @@ def build_cache(k: np.ndarray, v: np.ndarray, lay: Layout) -> CacheState:
 
 
 def dequantize(st: CacheState):
-    """(K_hat, V_hat) in fp64, [B][Hkv][n][D], in absolute token order."""
+    """(K_hat, V_hat) in fp64, [B][Hkv][n][D], in absolute token order.
+
+    For a pre-RoPE cache (rope_theta > 0) K_hat is the dequantized Key before
+    the rotation; :func:`attention_keys` applies it.
+    """
     lay = st.layout
     if lay.fmt in FP8_FORMATS:
         kq = quant.fp8_decode(st.codes_k, lay.k_scale, lay.fmt)
@@ -155,3 +160,13 @@ def dequantize(st: CacheState):
     kh = np.concatenate([st.sink_k.astype(np.float64), kq, st.res_k.astype(np.float64)], axis=2)
     vh = np.concatenate([st.sink_v.astype(np.float64), vq, st.res_v.astype(np.float64)], axis=2)
     return kh, vh
+
+
+def attention_keys(st: CacheState, k_hat: np.ndarray) -> np.ndarray:
+    """The Keys attention uses: K_hat itself, or for a pre-RoPE cache K_hat
+    rotated at each token's position t = 0 .. n-1 ("KV Cache Quantization
+    Analysis", sec. 4, KVQuant: quantize before RoPE, rotate after)."""
+    if not st.layout.rope_theta:
+        return k_hat
+    from .rope import apply_rope
+    return apply_rope(k_hat, np.arange(k_hat.shape[-2]), st.layout.rope_theta)

@@ -32,6 +32,10 @@ Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
   (fp16 metadata: the same shapes holding fp16 (s, m) pairs, m the offset)
 * K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
 
+Caches that store the Keys before RoPE keep each K row (codes and the K
+meta plane alike) in RoPE pair order: stored position 2i holds channel i and
+2i + 1 holds channel i + D/2, so each rotated pair sits side by side.
+
 Paged caches keep the four quantized planes as a pool of pages, each page
 P consecutive 32-token blocks of one sequence for all KV heads: records
 ordered [page][Hkv][P].  Logical block j of (sequence b, head h) is record
@@ -43,6 +47,8 @@ to quantization).
 from __future__ import annotations
 
 import numpy as np
+
+from .rope import stored_channel
 
 BLOCK = 32
 
@@ -155,14 +161,29 @@ def _unpack_blocks(packed: np.ndarray, fmt: str, d: int, order) -> np.ndarray:
     return out.reshape(packed.shape[:-2] + (nb * BLOCK, d))
 
 
-def pack_k_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+def _to_stored(x: np.ndarray, rope: bool) -> np.ndarray:
+    """Channel axis (last) in stored order: RoPE pair order for pre-RoPE caches."""
+    x = np.asarray(x)
+    return x[..., stored_channel(np.arange(x.shape[-1]), x.shape[-1])] if rope else x
+
+
+def _from_stored(x: np.ndarray, rope: bool) -> np.ndarray:
+    x = np.asarray(x)
+    if not rope:
+        return x
+    out = np.empty_like(x)
+    out[..., stored_channel(np.arange(x.shape[-1]), x.shape[-1])] = x
+    return out
+
+
+def pack_k_codes(codes: np.ndarray, fmt: str, rope: bool = False) -> np.ndarray:
     """[..., NB*32, D] codes -> [..., NB, 32*D*b/8] K block bytes."""
-    return _pack_blocks(codes, fmt, k_block_stream_order)
+    return _pack_blocks(_to_stored(codes, rope), fmt, k_block_stream_order)
 
 
-def unpack_k_codes(packed: np.ndarray, fmt: str, d: int) -> np.ndarray:
+def unpack_k_codes(packed: np.ndarray, fmt: str, d: int, rope: bool = False) -> np.ndarray:
     """Inverse of :func:`pack_k_codes`: [..., NB, bytes] -> [..., NB*32, D]."""
-    return _unpack_blocks(packed, fmt, d, k_block_stream_order)
+    return _from_stored(_unpack_blocks(packed, fmt, d, k_block_stream_order), rope)
 
 
 def pack_v_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
@@ -180,10 +201,10 @@ def _meta_dtype(s):
     return np.float16 if np.asarray(s).dtype == np.float16 else np.float32
 
 
-def pack_k_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """s, z [..., NB, D] -> [..., NB, D, 2] (interleaved pairs, fp32 or fp16)."""
+def pack_k_meta(s: np.ndarray, z: np.ndarray, rope: bool = False) -> np.ndarray:
+    """s, z [..., NB, D] -> [..., NB, D, 2] (interleaved pairs, fp32 or fp16; stored order)."""
     dt = _meta_dtype(s)
-    return np.stack([np.asarray(s, dt), np.asarray(z, dt)], axis=-1)
+    return np.stack([_to_stored(np.asarray(s, dt), rope), _to_stored(np.asarray(z, dt), rope)], axis=-1)
 
 
 def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
@@ -198,10 +219,10 @@ def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
     return np.stack([sb, zb], axis=-1)
 
 
-def unpack_k_meta(m: np.ndarray):
-    """[..., NB, D, 2] -> s, z [..., NB, D]."""
+def unpack_k_meta(m: np.ndarray, rope: bool = False):
+    """[..., NB, D, 2] -> s, z [..., NB, D] (channel order)."""
     m = np.asarray(m, _meta_dtype(m))
-    return m[..., 0].copy(), m[..., 1].copy()
+    return _from_stored(m[..., 0], rope).copy(), _from_stored(m[..., 1], rope).copy()
 
 
 def unpack_v_meta(m: np.ndarray):
