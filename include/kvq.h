@@ -78,6 +78,17 @@
  *
  * FP8 E5M2 codes use the INT8 / FP8 byte layouts above.
  *
+ * Pre-RoPE Keys (rope_theta > 0; "KV Cache Quantization Analysis", sec. 3
+ * RoPE problem and sec. 4 KVQuant: quantize Keys per channel before the
+ * rotary encoding, rotate after dequantization).  kv_quant_append then takes
+ * Keys *before* RoPE, and attention rotates every cached Key (sinks,
+ * quantized body, residual) at its position t (0-based index in the
+ * sequence) with the rotate-half pairs (i, i + D/2): angle t * theta_i,
+ * theta_i = rope_theta^(-2i/D).  The query passed to attention is already
+ * rotated at its own position.  Each K row of the code and meta planes is
+ * stored in pair order: stored position 2i holds channel i, 2i + 1 holds
+ * channel i + D/2 (the byte layout above applies to stored positions).
+ *
  * Paged cache (page_blocks = P >= 1): the four quantized planes (K / V
  * codes, K / V meta) are pools of num_pages pages instead of [B][Hkv][NB]
  * arrays.  A page holds P consecutive 32-token blocks of one sequence for
@@ -145,6 +156,7 @@ typedef struct {
   int32_t meta_fp16;         /* INT only: 0 = fp32 (s, z) pairs, 1 = fp16 (s, m) pairs; 0 for FP8 */
   int32_t page_blocks;       /* 0: contiguous planes; P >= 1: paged, P 32-token blocks per page */
   int32_t num_pages;         /* paged only: pages in the pool (>= 1) */
+  float rope_theta;          /* 0: Keys stored as given; > 0 (finite): pre-RoPE Keys, RoPE base */
 } kvq_layout;
 
 enum {

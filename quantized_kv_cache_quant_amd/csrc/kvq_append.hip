@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   constexpr bool kFp8 = fp8_of(VAR);
   constexpr bool kE5M2 = kKind == KVQ_FP8_E5M2;
   constexpr bool kM16 = meta16_of(VAR);
+  constexpr bool kRopeK = rope_of(VAR);     // K rows in RoPE pair order
   constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   constexpr float kQmax = (float)((1 << kBits) - 1);
@@ -151,16 +152,18 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
         sk[c] = half_bits_to_float(sb);
         zk[c] = mn;
-        reinterpret_cast<uint32_t*>(p.k_meta)[rec * kHeadDim + c] = sb | (mb << 16);
+        const int sp = kRopeK ? rope_stored_pos(c) : c;   // stored position of channel c
+        reinterpret_cast<uint32_t*>(p.k_meta)[rec * kHeadDim + sp] = sb | (mb << 16);
       } else {
         float s = (mx - mn) / kQmax;
         if (s == 0.0f) s = 1.0f;
         const float z = (-mn) / s;
         sk[c] = s;
         zk[c] = z;
-        float* km = p.k_meta + rec * (2 * kHeadDim);   // [D][s, z]
-        km[2 * c] = s;
-        km[2 * c + 1] = z;
+        float* km = p.k_meta + rec * (2 * kHeadDim);   // [stored position][s, z]
+        const int sp = kRopeK ? rope_stored_pos(c) : c;
+        km[2 * sp] = s;
+        km[2 * sp + 1] = z;
       }
     } else {
       const int e = tid - kHeadDim;
@@ -193,7 +196,9 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
     __syncthreads();
   }
 
-  // 3) K codes, channel c at bit (c * bits) of its token's codes (LSB first).
+  // 3) K codes, stored position p at bit (p * bits) of its token's codes (LSB
+  //    first); position p holds channel p, or in RoPE pair order channel
+  //    (p >> 1) + 64 (p & 1).
   //    INT4 / INT2: token-major rows.  8-bit codes: 16-byte units ordered
   //    (tile, half, lane); unit (tile, half, 16 qd + r) holds channels
   //    32 qd + 16 half .. + 15 of token 16 tile + r.
@@ -212,15 +217,17 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         wi = w % kWordsPerRow;
       }
       uint32_t word = 0;
+      // channel held by stored position sp of the row
+      auto chan = [](int sp) { return kRopeK ? rope_channel(sp) : sp; };
       if constexpr (kFp8) {
         const int c = wi * 4;
-        word = encode_fp8_pair<kE5M2>(ks[t][c], ks[t][c + 1], p.k_scale) |
-               (encode_fp8_pair<kE5M2>(ks[t][c + 2], ks[t][c + 3], p.k_scale) << 16);
+        word = encode_fp8_pair<kE5M2>(ks[t][chan(c)], ks[t][chan(c + 1)], p.k_scale) |
+               (encode_fp8_pair<kE5M2>(ks[t][chan(c + 2)], ks[t][chan(c + 3)], p.k_scale) << 16);
       } else {
         constexpr int kPer = 32 / kBits;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-          const int c = wi * kPer + j;
+          const int c = chan(wi * kPer + j);
           word |= encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c]) << (j * kBits);
         }
       }
@@ -322,6 +329,17 @@ hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int bat
     case KVQ_INT8 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kMeta16>, grid, block, 0, s, p); break;
     case KVQ_INT4 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kMeta16>, grid, block, 0, s, p); break;
     case KVQ_INT2 | kMeta16: hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E4M3 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E4M3 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E5M2 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E5M2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16 | kRope:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kMeta16 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16 | kRope:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kMeta16 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16 | kRope:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kMeta16 | kRope>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -160,6 +160,7 @@ template <int FMT>
 struct Traits {
   static constexpr int kKind = kind_of(FMT);
   static constexpr bool kMeta16 = meta16_of(FMT);
+  static constexpr bool kRope = rope_of(FMT);     // Keys stored before RoPE, in pair order
   static constexpr bool kFp8 = fp8_of(FMT);
   static constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   static constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
@@ -168,7 +169,9 @@ struct Traits {
   // blocks kept in flight besides the one being processed (bytes in flight
   // per wavefront: INT8 10 KiB, FP8 16 KiB, INT4 18 KiB, INT2 16 KiB; the
   // counts keep every format at or under 256 VGPRs, two wavefronts per SIMD)
-  static constexpr int kDepth = kFp8 ? KVQ_DEPTH_FP8 : (kBits == 8 ? KVQ_DEPTH_INT8 : (kBits == 4 ? KVQ_DEPTH_INT4 : KVQ_DEPTH_INT2));
+  static constexpr int kDepthBase = kFp8 ? KVQ_DEPTH_FP8 : (kBits == 8 ? KVQ_DEPTH_INT8 : (kBits == 4 ? KVQ_DEPTH_INT4 : KVQ_DEPTH_INT2));
+  // the rotation's temporaries leave room for at most two blocks in flight
+  static constexpr int kDepth = (kRope && kDepthBase > 2) ? 2 : kDepthBase;
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -335,26 +338,31 @@ __device__ __forceinline__ float2 pair_scales(const float4& m) {
 // (with log2(e) / sqrt(D) and the slot divisor folded in) and s * z (with
 // log2(e) / sqrt(D)) go to LDS in Key slot order per quarter.  fp16 pairs
 // hold (s, m) with x_hat = s * q + m, so their s * z is -m.
+// Pre-RoPE Keys are dequantized before the rotation instead: their staged
+// Key values are s * 2^24 / slot divisor and the offset -s * z (= m for
+// fp16 pairs), so that k_hat = operand value * [0] + [128].
 template <int FMT>
 __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
-  const int c = 2 * lane;                 // K channel; V index g * 32 + t
+  const int c = 2 * lane;                 // K stored position; V index g * 32 + t
   const int t = c & 31;
+  constexpr bool kRopeK = Traits<FMT>::kRope;
+  constexpr float kKs = kRopeK ? kTwo24 : kQScale;     // factor on the staged Key scale
   float sq0, sq1, kz0, kz1;
   float2 vs, vz;
   if constexpr (Traits<FMT>::kMeta16) {
     const f16x2 ka = u2h(__builtin_bit_cast(uint32_t, r.km.x)), kb = u2h(__builtin_bit_cast(uint32_t, r.km.y));
     const f16x2 va = u2h(__builtin_bit_cast(uint32_t, r.vm.x)), vb = u2h(__builtin_bit_cast(uint32_t, r.vm.y));
-    sq0 = (float)ka[0] * kQScale;
-    sq1 = (float)kb[0] * kQScale;
-    kz0 = -(float)ka[1] * kQScale;
-    kz1 = -(float)kb[1] * kQScale;
+    sq0 = (float)ka[0] * kKs;
+    sq1 = (float)kb[0] * kKs;
+    kz0 = kRopeK ? (float)ka[1] : -(float)ka[1] * kQScale;
+    kz1 = kRopeK ? (float)kb[1] : -(float)kb[1] * kQScale;
     vs = float2{(float)va[0] * (1.0f / slot_div<FMT>(t)), (float)vb[0] * (1.0f / slot_div<FMT>(t + 1))};
     vz = float2{-(float)va[1], -(float)vb[1]};
   } else {
-    sq0 = r.km.x * kQScale;
-    sq1 = r.km.z * kQScale;
-    kz0 = sq0 * r.km.y;
-    kz1 = sq1 * r.km.w;
+    sq0 = r.km.x * kKs;
+    sq1 = r.km.z * kKs;
+    kz0 = kRopeK ? -(r.km.x * r.km.y) : sq0 * r.km.y;
+    kz1 = kRopeK ? -(r.km.z * r.km.w) : sq1 * r.km.w;
     vs = float2{r.vm.x * (1.0f / slot_div<FMT>(t)), r.vm.z * (1.0f / slot_div<FMT>(t + 1))};
     vz = float2{r.vm.x * r.vm.y, r.vm.z * r.vm.w};
   }
@@ -414,27 +422,78 @@ __device__ __forceinline__ void reset(WaveState& ws) {
 // columns both are r = f16(x - f16(xz)).  v_fma_mix rounds the fp32 fma
 // a * b - c once to f16; its operands may be fp32 or a half of a packed f16
 // register (op_sel / op_sel_hi), so one instruction forms each half.
+//
+// The four words of one operand feed a matrix-core instruction, and the
+// compiler does not count inline assembly as a vector write when it spaces a
+// vector write from a matrix-core read of the same register (two wait
+// states).  So the four splits of an operand are chained (each one's first
+// instruction takes the previous result as an unused input, so they issue in
+// order) and the last one ends with s_nop 1: every word is then at least two
+// wait states old when the operand is read.
 
 // x = q * s for two channels: q from packed f16 (both halves of qh, and of
-// qz = qh in lo columns, 0 in hi columns), s0 / s1 fp32.
-__device__ __forceinline__ uint32_t split_q(uint32_t qz, uint32_t qh, float s0, float s1) {
+// qz = qh in lo columns, 0 in hi columns), s0 / s1 fp32.  dep: the previous
+// split of the operand (ordering only).
+template <bool LAST>
+__device__ __forceinline__ uint32_t split_q(uint32_t qz, uint32_t qh, float s0, float s1, uint32_t dep) {
   uint32_t hz, r;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(hz) : "v"(qz), "v"(s0));
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(hz) : "v"(qz), "v"(s0), "v"(dep));
   asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(hz) : "v"(qz), "v"(s1));
   asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(qh), "v"(s0), "v"(hz));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
+  if constexpr (LAST)
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\ts_nop 1" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
+  else
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
   return r;
 }
 
 // x = a * b for two values, all fp32; az = a in lo columns, 0 in hi columns.
-__device__ __forceinline__ uint32_t split_p(float a0, float az0, float b0, float a1, float az1, float b1) {
+template <bool LAST>
+__device__ __forceinline__ uint32_t split_p(float a0, float az0, float b0, float a1, float az1, float b1, uint32_t dep) {
   uint32_t hz, r;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hz) : "v"(az0), "v"(b0));
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hz) : "v"(az0), "v"(b0), "v"(dep));
   asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(hz) : "v"(az1), "v"(b1));
   asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a0), "v"(b0), "v"(hz));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
+  if constexpr (LAST)
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\ts_nop 1" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
+  else
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
   return r;
 }
+
+// hi / lo pair of a fully fp32 operand (both parts in every lane):
+// hi = f16(x), lo = f16(x - hi) (x - hi is exact in fp32), for two values;
+// returns {hi, lo} words.  Written as ordinary code, not inline assembly:
+// these registers go straight into a matrix-core instruction, and the
+// compiler only keeps the required distance between a vector write and a
+// matrix-core read of the same registers for instructions it can see.
+__device__ __forceinline__ uint2 split_a(float x0, float x1) {
+  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  return uint2{__builtin_bit_cast(uint32_t, f16x2{h0, h1}), __builtin_bit_cast(uint32_t, f16x2{l0, l1})};
+}
+
+// ---- rotary position embedding of pre-RoPE Keys (rotate-half pairs
+// (i, i + 64), angle t * theta_i, theta_i = base^(-i/64)).
+// theta_i in fp64.
+__device__ __forceinline__ double rope_freq(float base, int i) {
+  return exp2(-(double)i * (1.0 / 64.0) * log2((double)base));
+}
+
+// (cos, sin) of pos * freq: the angle is formed and reduced modulo 2 pi in
+// fp64, so large positions keep full accuracy, then evaluated in fp32.
+__device__ __forceinline__ float2 rope_cs(double pos, double freq) {
+  constexpr double kTwoPi = 6.283185307179586;
+  double a = pos * freq;
+  a = a - kTwoPi * floor(a * (1.0 / kTwoPi));
+  float sn, cs;
+  sincosf((float)a, &sn, &cs);
+  return float2{cs, sn};
+}
+
+// In-block offsets (cos, sin)(k * theta_i), k < 32, i < 64, shared by the
+// workgroup in LDS: entry 64 k + i.
+constexpr int kRopeTableBytes = 32 * 64 * 8;
 
 // Query of this lane's column head (its quarter's 32 channels) from a KV
 // head's n_rep query rows ([n_rep][128] fp16): packed f16 pairs in Key
@@ -450,12 +509,23 @@ struct QOp {
   uint32_t h[16], z[16];
 };
 
+// The lane's 32 query channels: its quarter 32qd .. 32qd + 31, or for
+// pre-RoPE Keys (PAIRS) the channels 16qd .. 16qd + 15 and 64 + 16qd ..
+// 64 + 16qd + 15 (stored positions 32qd .. 32qd + 31 in pair order).
+template <bool PAIRS = false>
 __device__ __forceinline__ QRaw load_query_raw(const uint16_t* rows, int nrep, const LaneInfo& li) {
   const bool valid = li.head < nrep;
-  const uint4* qsrc = reinterpret_cast<const uint4*>(rows + (valid ? li.head : 0) * kHeadDim + 32 * li.qd);
+  const uint16_t* row = rows + (valid ? li.head : 0) * kHeadDim;
   QRaw r;
+  if constexpr (PAIRS) {
+    const uint4* a = reinterpret_cast<const uint4*>(row + 16 * li.qd);
+    const uint4* b = reinterpret_cast<const uint4*>(row + kHeadDim / 2 + 16 * li.qd);
+    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = b[0]; r.w[3] = b[1];
+  } else {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(row + 32 * li.qd);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.w[i] = qsrc[i];
+    for (int i = 0; i < 4; ++i) r.w[i] = qsrc[i];
+  }
   return r;
 }
 
@@ -464,9 +534,12 @@ __device__ __forceinline__ void query_operand(const QRaw& r, int nrep, const Lan
   const uint32_t keep = li.head < nrep ? 0xFFFFFFFFu : 0u;
   const uint32_t w[16] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w,
                           r.w[2].x, r.w[2].y, r.w[2].z, r.w[2].w, r.w[3].x, r.w[3].y, r.w[3].z, r.w[3].w};
+  // element of the loaded 32 holding stored position c: pair order keeps
+  // channel i (position 2i) in the first 16 elements and i + 64 in the last
+  auto elem = [](int c) { return Traits<FMT>::kRope ? ((c & 1) ? 16 + (c >> 1) : (c >> 1)) : c; };
 #pragma unroll
   for (int pr = 0; pr < 16; ++pr) {
-    const int c0 = k_chan<FMT>(pr >> 2, 2 * (pr & 3)), c1 = k_chan<FMT>(pr >> 2, 2 * (pr & 3) + 1);
+    const int c0 = elem(k_chan<FMT>(pr >> 2, 2 * (pr & 3))), c1 = elem(k_chan<FMT>(pr >> 2, 2 * (pr & 3) + 1));
     const uint32_t lo = (w[c0 >> 1] >> (16 * (c0 & 1))) & 0xFFFFu;
     const uint32_t hi = (w[c1 >> 1] >> (16 * (c1 & 1))) & 0xFFFFu;
     q.h[pr] = (lo | (hi << 16)) & keep;
@@ -477,7 +550,7 @@ __device__ __forceinline__ void query_operand(const QRaw& r, int nrep, const Lan
 // The same from the query rows of KV head bh in global memory.
 template <int FMT>
 __device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, const LaneInfo& li, QOp& q) {
-  query_operand<FMT>(load_query_raw(p.q + bh * p.nrep * kHeadDim, p.nrep, li), p.nrep, li, q);
+  query_operand<FMT>(load_query_raw<Traits<FMT>::kRope>(p.q + bh * p.nrep * kHeadDim, p.nrep, li), p.nrep, li, q);
 }
 
 // Static q operands (hi / lo) for Keys without a per-block scale (FP8 with
@@ -487,8 +560,10 @@ __device__ __forceinline__ void static_q(const QOp& q, float scale, f16x8* bk) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     uint32_t bw[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) bw[v] = split_q(q.z[4 * kb + v], q.h[4 * kb + v], scale, scale);
+    bw[0] = split_q<false>(q.z[4 * kb], q.h[4 * kb], scale, scale, 0u);
+    bw[1] = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], scale, scale, bw[0]);
+    bw[2] = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], scale, scale, bw[1]);
+    bw[3] = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], scale, scale, bw[2]);
     bk[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
   }
 }
@@ -524,22 +599,100 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
 // P operand without a per-token scale (FP8: the per-tensor scale is applied
 // at the end; fp16 segment: none).
 __device__ __forceinline__ f16x8 p_operand(const float pr[2][4], const LaneInfo& li) {
-  uint32_t bw[4];
+  float z[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    bw[v] = split_p(pr[0][v], li.is_lo ? pr[0][v] : 0.f, 1.0f, pr[1][v], li.is_lo ? pr[1][v] : 0.f, 1.0f);
-  return cat(bw[0], bw[1], bw[2], bw[3]);
+  for (int v = 0; v < 4; ++v) {
+    z[0][v] = li.is_lo ? pr[0][v] : 0.f;
+    z[1][v] = li.is_lo ? pr[1][v] : 0.f;
+  }
+  const uint32_t b0 = split_p<false>(pr[0][0], z[0][0], 1.0f, pr[1][0], z[1][0], 1.0f, 0u);
+  const uint32_t b1 = split_p<false>(pr[0][1], z[0][1], 1.0f, pr[1][1], z[1][1], 1.0f, b0);
+  const uint32_t b2 = split_p<false>(pr[0][2], z[0][2], 1.0f, pr[1][2], z[1][2], 1.0f, b1);
+  const uint32_t b3 = split_p<true>(pr[0][3], z[0][3], 1.0f, pr[1][3], z[1][3], 1.0f, b2);
+  return cat(b0, b1, b2, b3);
 }
 
+// Pre-RoPE Keys: this lane's RoPE frequency (theta_lane, for the block base
+// angles) and the workgroup's in-block offset table.
+struct RopeCtx {
+  double freq;
+  const float2* table;
+};
+
+// Key slot holding the other member of slot j's RoPE pair (stored positions
+// 2i, 2i + 1), and whether slot j holds the first member.
+template <int FMT>
+__device__ constexpr int pair_slot(int j) {
+  return (kind_of(FMT) == KVQ_INT4 || kind_of(FMT) == KVQ_INT2) ? (j ^ 2) : (j ^ 1);
+}
+template <int FMT>
+__device__ constexpr bool pair_first(int j) {
+  return (kind_of(FMT) == KVQ_INT4 || kind_of(FMT) == KVQ_INT2) ? ((j & 2) == 0) : ((j & 1) == 0);
+}
+
+// t0: position of the block's first token (pre-RoPE Keys only).
 template <int FMT>
 __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const QOp& q,
-                                              const f16x8* bk_static, const LaneInfo& li) {
+                                              const f16x8* bk_static, const LaneInfo& li, const RopeCtx& rc,
+                                              double t0) {
   using T = Traits<FMT>;
   const int qd = li.qd;
 
   // ---- QK: Key codes (rows = tokens) x q' (columns)
   f32x4 acc[2];
-  if constexpr (T::kFp8) {
+  if constexpr (T::kRope) {
+    // Keys are dequantized, rotated at their positions t0 + token and split
+    // into hi / lo f16 operands; the query operand is static (q, hi / lo
+    // columns).  Rotation angle of (token k, frequency i) = base_i * offset_ki
+    // as complex numbers: base = (t0 theta_i), staged by lane i; offset from
+    // the workgroup table.
+    if constexpr (!T::kFp8) stage_meta<FMT>(r, st, li.lane);
+    *reinterpret_cast<float2*>(st + kStage + 2 * li.lane) = rope_cs(t0, rc.freq);
+    acc[0] = f32x4{0, 0, 0, 0};
+    acc[1] = acc[0];
+    const int tok = li.lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float sc[8], of[8];
+      if constexpr (!T::kFp8) {
+        const float4 sa = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb);
+        const float4 sb = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb + 4);
+        const float4 oa = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 8 * kb);
+        const float4 ob = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 8 * kb + 4);
+        sc[0] = sa.x; sc[1] = sa.y; sc[2] = sa.z; sc[3] = sa.w; sc[4] = sb.x; sc[5] = sb.y; sc[6] = sb.z; sc[7] = sb.w;
+        of[0] = oa.x; of[1] = oa.y; of[2] = oa.z; of[3] = oa.w; of[4] = ob.x; of[5] = ob.y; of[6] = ob.z; of[7] = ob.w;
+      }
+      float2 base[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (pair_first<FMT>(j))
+          base[j] = *reinterpret_cast<const float2*>(st + kStage + 2 * (16 * qd + (k_chan<FMT>(kb, j) >> 1)));
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const f16x8 a = operand<FMT>(r.k[tile], kb);
+        float x[8], y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = T::kFp8 ? (float)a[j] : __builtin_fmaf((float)a[j], sc[j], of[j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (!pair_first<FMT>(j)) continue;
+          const int js = pair_slot<FMT>(j);
+          const float2 o = rc.table[64 * (16 * tile + tok) + 16 * qd + (k_chan<FMT>(kb, j) >> 1)];
+          const float c = base[j].x * o.x - base[j].y * o.y;
+          const float sn = base[j].y * o.x + base[j].x * o.y;
+          y[j] = x[j] * c - x[js] * sn;
+          y[js] = x[js] * c + x[j] * sn;
+        }
+        const uint2 h0 = split_a(y[0], y[1]), h1 = split_a(y[2], y[3]), h2 = split_a(y[4], y[5]),
+                    h3 = split_a(y[6], y[7]);
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(h0.x, h1.x, h2.x, h3.x), bk_static[kb], acc[tile], 0, 0, 0);
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(h0.y, h1.y, h2.y, h3.y), bk_static[kb], acc[tile], 0, 0, 0);
+      }
+      // keep one k-block's temporaries live at a time (the unrolled loop
+      // otherwise runs out of registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (T::kFp8) {
     acc[0] = f32x4{0, 0, 0, 0};
     acc[1] = acc[0];
 #pragma unroll
@@ -570,10 +723,11 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
     for (int kb = 0; kb < 4; ++kb) {
       const float4 sa = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb);
       const float4 sb = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb + 4);
-      const f16x8 bq = cat(split_q(q.z[4 * kb], q.h[4 * kb], sa.x, sa.y),
-                           split_q(q.z[4 * kb + 1], q.h[4 * kb + 1], sa.z, sa.w),
-                           split_q(q.z[4 * kb + 2], q.h[4 * kb + 2], sb.x, sb.y),
-                           split_q(q.z[4 * kb + 3], q.h[4 * kb + 3], sb.z, sb.w));
+      const uint32_t b0 = split_q<false>(q.z[4 * kb], q.h[4 * kb], sa.x, sa.y, 0u);
+      const uint32_t b1 = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], sa.z, sa.w, b0);
+      const uint32_t b2 = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], sb.x, sb.y, b1);
+      const uint32_t b3 = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], sb.z, sb.w, b2);
+      const f16x8 bq = cat(b0, b1, b2, b3);
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bq, acc[tile], 0,
@@ -585,7 +739,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * T::kCodeScale;
+    for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * (T::kRope ? 1.0f : T::kCodeScale);
   float slack = kSlack;
   if constexpr (!T::kFp8) {
     const float2 sv = pair_scales<FMT>(r.vm);
@@ -626,8 +780,10 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       const float sv0[4] = {s0.x, s0.y, s0.z, s0.w};
       const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
       uint32_t bw[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) bw[v] = split_p(pr[0][v], pb[0][v], sv0[v], pr[1][v], pb[1][v], sv1[v]);
+      bw[0] = split_p<false>(pr[0][0], pb[0][0], sv0[0], pr[1][0], pb[1][0], sv1[0], 0u);
+      bw[1] = split_p<false>(pr[0][1], pb[0][1], sv0[1], pr[1][1], pb[1][1], sv1[1], bw[0]);
+      bw[2] = split_p<false>(pr[0][2], pb[0][2], sv0[2], pr[1][2], pb[1][2], sv1[2], bw[1]);
+      bw[3] = split_p<true>(pr[0][3], pb[0][3], sv0[3], pr[1][3], pb[1][3], sv1[3], bw[2]);
       const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
@@ -684,25 +840,40 @@ __device__ __forceinline__ const uint16_t* seg_row(const AttnParams& p, const ui
   return ring + (bh * p.ring_slots + slot) * kHeadDim;
 }
 
+// ROPE: the segment holds pre-RoPE Keys; each is rotated at its position
+// (sinks: their index; residual token u of the body: S + u) with angles
+// evaluated directly (fp64 reduction), the lane's channels taken in pair
+// order like the quantized blocks.
+template <bool ROPE>
 __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt, float* slot) {
   const LaneInfo li = lane_info(p.nrep);
   const int lane = li.lane;
   const int nt = p.n_sink + p.n_res;
   QOp q;
   f16x8 bk[4];
-  load_query<KVQ_INT8>(p, bh, li, q);                   // natural channel order, scale 1
+  load_query<ROPE ? (KVQ_INT8 | kRope) : KVQ_INT8>(p, bh, li, q);   // scale 1
   static_q(q, kQScale, bk);
   WaveState ws;
   reset(ws);
-  // Key rows of this lane's two tokens (one per 16-token tile), its quarter's 32 channels
+  // Key rows of this lane's two tokens (one per 16-token tile): its quarter's
+  // 32 channels, or in pair order channels 16qd .. +15 and 64 + 16qd .. +15
   uint4 kr[2][4];
+  int kpos[2];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
     int k = 32 * fb + 16 * tile + (lane & 15);
     k = k < nt ? k : nt - 1;                           // masked below; any valid row keeps values finite
-    const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.k_sink, p.k_ring, bh, k) + 32 * li.qd);
+    kpos[tile] = k < p.n_sink ? k : p.sink_cap + kBlock * p.nblk + (k - p.n_sink);
+    const uint16_t* row = seg_row(p, p.k_sink, p.k_ring, bh, k);
+    if constexpr (ROPE) {
+      const uint4* a = reinterpret_cast<const uint4*>(row + 16 * li.qd);
+      const uint4* b = reinterpret_cast<const uint4*>(row + kHeadDim / 2 + 16 * li.qd);
+      kr[tile][0] = a[0]; kr[tile][1] = a[1]; kr[tile][2] = b[0]; kr[tile][3] = b[1];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(row + 32 * li.qd);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kr[tile][i] = src[i];
+      for (int i = 0; i < 4; ++i) kr[tile][i] = src[i];
+    }
   }
   // Value row of token lane % 32, channel half lane / 32, into LDS
   {
@@ -715,12 +886,40 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
   }
   f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb) {
+    if constexpr (ROPE) {
+      // slot j of k-block kb holds stored position 8kb + j: channel pair
+      // m = 4kb + j / 2, member j % 2
+      double fr[4];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const uint4 w = kr[tile][kb];
-      acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(w.x, w.y, w.z, w.w), bk[kb], acc[tile], 0, 0, 0);
+      for (int mm = 0; mm < 4; ++mm) fr[mm] = rope_freq(p.rope_theta, 16 * li.qd + 4 * kb + mm);
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        float y[8];
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const int m = 4 * kb + mm;
+          const uint4 wa = kr[tile][m >> 3], wb = kr[tile][2 + (m >> 3)];
+          const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, ub[4] = {wb.x, wb.y, wb.z, wb.w};
+          const float x0 = (float)u2h(ua[(m & 7) >> 1])[m & 1];
+          const float x1 = (float)u2h(ub[(m & 7) >> 1])[m & 1];
+          const float2 cs = rope_cs((double)kpos[tile], fr[mm]);
+          y[2 * mm] = x0 * cs.x - x1 * cs.y;
+          y[2 * mm + 1] = x1 * cs.x + x0 * cs.y;
+        }
+        const uint2 h0 = split_a(y[0], y[1]), h1 = split_a(y[2], y[3]), h2 = split_a(y[4], y[5]),
+                    h3 = split_a(y[6], y[7]);
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(h0.x, h1.x, h2.x, h3.x), bk[kb], acc[tile], 0, 0, 0);
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(h0.y, h1.y, h2.y, h3.y), bk[kb], acc[tile], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const uint4 w = kr[tile][kb];
+        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(w.x, w.y, w.z, w.w), bk[kb], acc[tile], 0, 0, 0);
+      }
     }
+  }
   float lg[2][4], pr[2][4];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
@@ -753,6 +952,10 @@ constexpr int kGroupThreads = 64 * kGroupWaves;
 // per-wavefront LDS area: the block staging of process_block, or the Value
 // rows of an fp16 block (never both at once)
 constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
+// workgroup LDS: the wavefronts' areas, the block counter, the record ids of
+// a paged range (then, for pre-RoPE Keys, the in-block offset table)
+constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
+static_assert(kWaveLds >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
 // touching heads h0..h1.
@@ -815,13 +1018,21 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       recs[i] = r < 0 ? 0 : (int)r;
     }
   }
+  // pre-RoPE Keys: the in-block offsets (cos, sin)(k theta_i), k < 32, i < 64
+  float2* rtab = reinterpret_cast<float2*>(lds + kLdsBytes);
+  if constexpr (T::kRope) {
+    for (int e = threadIdx.x; e < 32 * 64; e += kGroupThreads)
+      rtab[e] = rope_cs((double)(e >> 6), rope_freq(p.rope_theta, e & 63));
+  }
+  RopeCtx rc{};
+  if constexpr (T::kRope) rc = RopeCtx{rope_freq(p.rope_theta, li.lane), rtab};
   // the block counter starts at zero; the barrier comes before any block
   // load is issued, so no wavefront waits on another's loads
   if (threadIdx.x == 0) *ctr = 0;
   __syncthreads();
 
   // query rows of the range's first head, loaded before the blocks
-  const QRaw q0 = load_query_raw(p.q + (int64_t)gr.h0 * p.nrep * kHeadDim, p.nrep, li);
+  const QRaw q0 = load_query_raw<T::kRope>(p.q + (int64_t)gr.h0 * p.nrep * kHeadDim, p.nrep, li);
 
   // block ring: D - 1 blocks prefetched ahead of the one being processed;
   // rid = block index within the range (-1 past its end), rbh = its head.
@@ -829,9 +1040,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   // wavefront's surplus loads hit the same lines, which stay in the cache.
   const uint32_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;
   Raw<FMT> buf[D];
-  int rid[D], rbh[D];
+  int rid[D], rbh[D], rblk[D];
   int kst = 0;
-  auto fetch = [&](Raw<FMT>& r, int& id, int& bhout) {
+  auto fetch = [&](Raw<FMT>& r, int& id, int& bhout, int& blkout) {
     int idx;
     if (p.deterministic) {
       idx = v + kGroupWaves * kst;
@@ -852,17 +1063,19 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
       j = ps + (j - ps + rot) % (pe - ps);
       bhout = (int)bh;
+      blkout = (int)(j - bh * nblk);
       const int64_t rec = p.table ? (int64_t)__builtin_amdgcn_readfirstlane(recs[j - (uint32_t)gr.jb])
                                   : (int64_t)bh * p.nb_cap + (j - bh * nblk);
       load_block<FMT>(r, p, rec, li.lane);
     } else {
       id = -1;
       bhout = 0;
+      blkout = 0;
       load_block<FMT, false>(r, p, 0, li.lane);
     }
   };
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d]);
+  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], rblk[d]);
 
   // fp16 block fb of head h belongs to covering workgroup g_lo(h) + fb mod
   // count(h); the workgroup's fp16 blocks go round robin to its wavefronts
@@ -873,7 +1086,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       for (int fb = 0; fb < p.fp16_blocks; ++fb) {
         if (glo + fb % nc != g) continue;
         if ((k & (kGroupWaves - 1)) == v)
-          fp16_block(p, h, fb, reinterpret_cast<uint16_t*>(stage),
+          fp16_block<T::kRope>(p, h, fb, reinterpret_cast<uint16_t*>(stage),
                      p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p));
         ++k;
       }
@@ -901,7 +1114,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D]);
+        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], rblk[(d + D - 1) % D]);
         if (rid[d] < 0) goto done;           // blocks are taken in order: none left
         if (rbh[d] != cur) {
           if (cur >= 0) {
@@ -913,9 +1126,10 @@ __device__ void group_main(const AttnParams& p, char* lds) {
             load_query<FMT>(p, cur, li, qop);
             qhead = cur;
           }
-          if constexpr (T::kFp8) static_q(qop, p.k_scale * kQScale, bk_static);
+          if constexpr (T::kFp8 || T::kRope) static_q(qop, T::kFp8 ? p.k_scale * kQScale : kQScale, bk_static);
         }
-        process_block<FMT>(buf[d], stage, ws, qop, bk_static, li);
+        process_block<FMT>(buf[d], stage, ws, qop, bk_static, li, rc,
+                           (double)p.sink_cap + (double)kBlock * rblk[d]);
       }
     }
   done:
@@ -971,21 +1185,21 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   }
 }
 
-constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
 
 // No quantized blocks yet: workgroup g takes the fp16 blocks of head g.
+template <bool ROPE>
 __device__ void fp16_group(const AttnParams& p, char* lds) {
   const int g = blockIdx.x;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront index, uniform
   for (int fb = v; fb < p.fp16_blocks; fb += kGroupWaves)
-    fp16_block(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
+    fp16_block<ROPE>(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
                p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  if (p.nblk == 0) fp16_group(p, lds);
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
+  if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
   else group_main<FMT>(p, lds);
 }
 
@@ -1058,6 +1272,17 @@ hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
     case KVQ_INT8 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kMeta16>, grid, block, 0, s, p); break;
     case KVQ_INT4 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kMeta16>, grid, block, 0, s, p); break;
     case KVQ_INT2 | kMeta16: hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kMeta16>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E4M3 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E4M3 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_FP8_E5M2 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E5M2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16 | kRope:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kMeta16 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16 | kRope:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kMeta16 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16 | kRope:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kMeta16 | kRope>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

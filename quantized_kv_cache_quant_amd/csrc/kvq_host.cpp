@@ -137,6 +137,7 @@ int32_t kvq_layout_validate(const kvq_layout* L) {
   }
   if (L->sink_tokens > L->max_tokens) return KVQ_ERR_LAYOUT;
   if (L->page_blocks < 0 || (L->page_blocks > 0 && L->num_pages < 1)) return KVQ_ERR_LAYOUT;
+  if (!std::isfinite(L->rope_theta) || L->rope_theta < 0.f) return KVQ_ERR_LAYOUT;
   // block records are 32-bit in the attention kernel
   if (L->page_blocks > 0 && (int64_t)L->num_pages * L->num_kv_heads * L->page_blocks > 0x7fffffffLL)
     return KVQ_ERR_UNSUPPORTED;
@@ -367,6 +368,7 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.table_stride = c->table_stride;
   p.page_blocks = L.page_blocks;
   p.num_pages = L.num_pages;
+  p.rope_theta = L.rope_theta;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;

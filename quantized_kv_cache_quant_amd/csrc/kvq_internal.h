@@ -26,14 +26,23 @@ constexpr int kMaxBlocksPerGroup = 1 << 20;
 constexpr int kMaxPagedRange = 4096;     // paged caches: blocks per workgroup range (ids staged in LDS)
 
 // Kernel variant: the kvq_format, plus kMeta16 when an INT format stores
-// fp16 (scale, offset) pairs.
+// fp16 (scale, offset) pairs and kRope when the Keys are stored before RoPE.
 constexpr int kMeta16 = 8;
+constexpr int kRope = 16;
 __host__ __device__ constexpr int kind_of(int variant) { return variant & 7; }
 __host__ __device__ constexpr bool meta16_of(int variant) { return (variant & kMeta16) != 0; }
+__host__ __device__ constexpr bool rope_of(int variant) { return (variant & kRope) != 0; }
 __host__ __device__ constexpr bool fp8_of(int variant) {
   return kind_of(variant) == KVQ_FP8_E4M3 || kind_of(variant) == KVQ_FP8_E5M2;
 }
-inline int variant_of(const kvq_layout& L) { return L.format | (L.meta_fp16 ? kMeta16 : 0); }
+inline int variant_of(const kvq_layout& L) {
+  return L.format | (L.meta_fp16 ? kMeta16 : 0) | (L.rope_theta > 0.f ? kRope : 0);
+}
+
+// Stored position of channel c in a pre-RoPE Key row (pairs side by side)
+// and the channel at stored position p.
+__host__ __device__ constexpr int rope_stored_pos(int c) { return 2 * (c % (kHeadDim / 2)) + c / (kHeadDim / 2); }
+__host__ __device__ constexpr int rope_channel(int p) { return (p >> 1) + (kHeadDim / 2) * (p & 1); }
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
 // ---------------------------------------------------------------- append
@@ -133,6 +142,7 @@ struct AttnParams {
   int32_t fp16_blocks;    // ceil((n_sink + n_res) / 32) per head
   int32_t deterministic;  // 1: wavefront w takes blocks w, w + 8, ... of its range
   float k_scale, v_scale; // FP8
+  float rope_theta;       // pre-RoPE Keys: the RoPE base
   const int32_t* table;   // paged: block table [B][table_stride] (record ids via block_record)
   int32_t table_stride;
   int32_t page_blocks;

@@ -36,7 +36,7 @@ class Layout(ctypes.Structure):
                 ("k_group_tokens", ctypes.c_int32), ("v_group_channels", ctypes.c_int32),
                 ("residual_tokens", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("meta_fp16", ctypes.c_int32),
-                ("page_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+                ("page_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -92,10 +92,10 @@ def check(status: int, where: str) -> None:
 
 def make_layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, fmt, *, k_group_tokens=32,
                 v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0,
-                meta_fp16=False, page_blocks=0, num_pages=0) -> Layout:
+                meta_fp16=False, page_blocks=0, num_pages=0, rope_theta=0.0) -> Layout:
     return Layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, FORMATS[fmt], k_group_tokens,
                   v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale), int(meta_fp16),
-                  int(page_blocks), int(num_pages))
+                  int(page_blocks), int(num_pages), float(rope_theta))
 
 
 def cache_bytes(layout: Layout) -> int:

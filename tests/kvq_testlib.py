@@ -33,7 +33,7 @@ def olayout_of(lay_kw: dict) -> ocache.Layout:
     return ocache.Layout(k["batch"], k["num_kv_heads"], k["num_q_heads"], 128, k["max_tokens"], k["fmt"],
                          residual_tokens=k.get("residual_tokens", 128), sink_tokens=k.get("sink_tokens", 0),
                          k_scale=k.get("k_scale", 1.0), v_scale=k.get("v_scale", 1.0),
-                         meta_fp16=bool(k.get("meta_fp16", False)))
+                         meta_fp16=bool(k.get("meta_fp16", False)), rope_theta=float(k.get("rope_theta", 0.0)))
 
 
 def make_cache(lay_kw: dict) -> kvq.Cache:
@@ -87,14 +87,15 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
             return pl(name, dtype, (b, hkv, nb_cap) + shape)[:, :, :nb]
     kc = blocks("k_codes", np.uint8, (32 * row,))
     vc = blocks("v_codes", np.uint8, (32 * row,))
-    codes_k = olayout.unpack_k_codes(kc, olay.fmt, d)
+    rope = olay.rope_theta > 0
+    codes_k = olayout.unpack_k_codes(kc, olay.fmt, d, rope=rope)
     codes_v = olayout.unpack_v_codes(vc, olay.fmt, d)
     s_k = z_k = s_v = z_v = None
     if olay.fmt not in FP8:
         mt = np.float16 if olay.meta_fp16 else np.float32
         km = blocks("k_meta", mt, (d, 2))
         vm = blocks("v_meta", mt, (4, 32, 2))
-        s_k, z_k = olayout.unpack_k_meta(km)
+        s_k, z_k = olayout.unpack_k_meta(km, rope=rope)
         s_v, z_v = olayout.unpack_v_meta(vm)
     ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))
     ring_v = pl("v_ring", np.float16, (b, hkv, rs, d))
@@ -155,7 +156,7 @@ def substate(st: ocache.CacheState, bi: int, gi: int) -> ocache.CacheState:
     lay = st.layout
     sub = ocache.Layout(1, 1, lay.n_rep, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
                         lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale,
-                        lay.meta_fp16)
+                        lay.meta_fp16, lay.rope_theta)
     return ocache.CacheState(sub, st.n, st.n_sink, st.n_q, st.r, cut(st.sink_k), cut(st.sink_v),
                              cut(st.codes_k), cut(st.codes_v), cut(st.s_k), cut(st.z_k), cut(st.s_v),
                              cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots)

@@ -70,6 +70,11 @@ def _lay(**kw):
     ({"meta_fp16": 2}, -2),
     ({"fmt": "fp8", "meta_fp16": 1}, -2),                 # fp16 metadata is for INT formats
     ({"fmt": "fp8_e5m2", "meta_fp16": 1}, -2),
+    ({"rope_theta": 500000.0}, 0),
+    ({"fmt": "fp8", "rope_theta": 10000.0}, 0),
+    ({"rope_theta": -1.0}, -2),
+    ({"rope_theta": float("nan")}, -2),
+    ({"rope_theta": float("inf")}, -2),
 ])
 def test_layout_validation(kw, status):
     lay = _lay(**kw)
