@@ -63,6 +63,7 @@ class Layout:
     v_scale: float = 1.0
     meta_fp16: bool = False       # INT only: fp16 (s, m) pairs instead of fp32 (s, z)
     rope_theta: float = 0.0       # > 0: Keys stored before RoPE, rotated with this base in attention
+    outliers: bool = False        # INT only: one exact fp16 outlier per quantization group
 
     @property
     def bits(self) -> int:
@@ -104,6 +105,12 @@ class CacheState:
     res_k: np.ndarray             # [B][Hkv][r][D] fp16, body order
     res_v: np.ndarray
     res_slots: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    # outliers: K [B][Hkv][n_q/G_k][D] token index in the block and fp16 value;
+    # V [B][Hkv][n_q][D/G_v] channel index in the group and fp16 value
+    ko_idx: np.ndarray | None = None
+    ko_val: np.ndarray | None = None
+    vo_idx: np.ndarray | None = None
+    vo_val: np.ndarray | None = None
 
 
 def build_cache(k: np.ndarray, v: np.ndarray, lay: Layout) -> CacheState:
@@ -130,15 +137,23 @@ def build_cache(k: np.ndarray, v: np.ndarray, lay: Layout) -> CacheState:
     else:
         bits = lay.bits
         kg = body_k.reshape(b, hkv, n_q // g, g, d)
-        ck, s_k, z_k = quant.quantize_k_group(kg, bits, lay.meta_fp16)
+        if lay.outliers:
+            ck, s_k, z_k, ko_i, ko_v = quant.quantize_k_group(kg, bits, lay.meta_fp16, outliers=True)
+            codes_v, s_v, z_v, vo_i, vo_v = quant.quantize_v_tokens(body_v, bits, lay.v_group_channels,
+                                                                    lay.meta_fp16, outliers=True)
+        else:
+            ck, s_k, z_k = quant.quantize_k_group(kg, bits, lay.meta_fp16)
+            codes_v, s_v, z_v = quant.quantize_v_tokens(body_v, bits, lay.v_group_channels, lay.meta_fp16)
         codes_k = ck.reshape(b, hkv, n_q, d)
-        codes_v, s_v, z_v = quant.quantize_v_tokens(body_v, bits, lay.v_group_channels, lay.meta_fp16)
     res_k = kt[:, :, s0 + n_q:]
     res_v = vt[:, :, s0 + n_q:]
     assert res_k.shape[2] == r
     slots = (np.arange(n_q, n_q + r) % lay.ring_slots).astype(np.int64)
-    return CacheState(lay, n, n_sink, n_q, r, kt[:, :, :n_sink].copy(), vt[:, :, :n_sink].copy(),
-                      codes_k, codes_v, s_k, z_k, s_v, z_v, res_k.copy(), res_v.copy(), slots)
+    st = CacheState(lay, n, n_sink, n_q, r, kt[:, :, :n_sink].copy(), vt[:, :, :n_sink].copy(),
+                    codes_k, codes_v, s_k, z_k, s_v, z_v, res_k.copy(), res_v.copy(), slots)
+    if lay.fmt not in FP8_FORMATS and lay.outliers:
+        st.ko_idx, st.ko_val, st.vo_idx, st.vo_val = ko_i, ko_v, vo_i, vo_v
+    return st
 
 
 def dequantize(st: CacheState):
@@ -155,8 +170,8 @@ def dequantize(st: CacheState):
         b, hkv, n_q, d = st.codes_k.shape
         g = lay.k_group_tokens
         kq = quant.dequantize_k_group(st.codes_k.reshape(b, hkv, n_q // g, g, d),
-                                      st.s_k, st.z_k).reshape(b, hkv, n_q, d)
-        vq = quant.dequantize_v_tokens(st.codes_v, st.s_v, st.z_v)
+                                      st.s_k, st.z_k, st.ko_idx, st.ko_val).reshape(b, hkv, n_q, d)
+        vq = quant.dequantize_v_tokens(st.codes_v, st.s_v, st.z_v, st.vo_idx, st.vo_val)
     kh = np.concatenate([st.sink_k.astype(np.float64), kq, st.res_k.astype(np.float64)], axis=2)
     vh = np.concatenate([st.sink_v.astype(np.float64), vq, st.res_v.astype(np.float64)], axis=2)
     return kh, vh

@@ -32,6 +32,12 @@ Planes (per layer; NB = quantized blocks of 32 tokens, b = bits per code):
   (fp16 metadata: the same shapes holding fp16 (s, m) pairs, m the offset)
 * K / V ring   [B][Hkv][R+32][D] fp16;  K / V sinks  [B][Hkv][S][D] fp16.
 
+Caches with dense-and-sparse outliers add two planes of 32-bit entries, the
+index in the group in the low 16 bits and the fp16 value in the high 16:
+K outliers [NB][D] (token index of each channel's outlier in the block) and
+V outliers [NB][D/G_v][32] (channel index in the group, per group and token,
+the V meta order).
+
 Caches that store the Keys before RoPE keep each K row (codes and the K
 meta plane alike) in RoPE pair order: stored position 2i holds channel i and
 2i + 1 holds channel i + D/2, so each rotated pair sits side by side.
@@ -249,3 +255,30 @@ def gather_paged(pool: np.ndarray, table: np.ndarray, hkv: int, page_blocks: int
     page = table[:, blk // page_blocks]                           # [B, nb]
     rec = (page[:, None, :] * hkv + np.arange(hkv)[None, :, None]) * page_blocks + (blk % page_blocks)[None, None]
     return pool[rec.reshape(-1)].reshape((b, hkv, nb) + pool.shape[1:])
+
+
+def pack_outliers(idx: np.ndarray, val: np.ndarray) -> np.ndarray:
+    """Outlier entries: index | fp16 bits << 16, as uint32."""
+    bits = np.asarray(val, np.float16).view(np.uint16).astype(np.uint32)
+    return (np.asarray(idx).astype(np.uint32) | (bits << 16)).astype(np.uint32)
+
+
+def unpack_outliers(e: np.ndarray):
+    """Inverse of :func:`pack_outliers`: (index int64, value fp16)."""
+    e = np.asarray(e, np.uint32)
+    return (e & 0xFFFF).astype(np.int64), (e >> 16).astype(np.uint16).view(np.float16)
+
+
+def pack_v_outliers(idx: np.ndarray, val: np.ndarray) -> np.ndarray:
+    """[..., NB*32, Gn] -> [..., NB, Gn, 32] entries (group-major like the V meta)."""
+    e = pack_outliers(idx, val)
+    n, gn = e.shape[-2:]
+    return np.swapaxes(e.reshape(e.shape[:-2] + (n // BLOCK, BLOCK, gn)), -1, -2)
+
+
+def unpack_v_outliers(e: np.ndarray):
+    """[..., NB, Gn, 32] -> index, value [..., NB*32, Gn]."""
+    e = np.asarray(e, np.uint32)
+    nb, gn, blk = e.shape[-3:]
+    t = np.swapaxes(e, -1, -2).reshape(e.shape[:-3] + (nb * blk, gn))
+    return unpack_outliers(t)

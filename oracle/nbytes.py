@@ -51,6 +51,9 @@ def step_bytes(lay: Layout, n: int) -> dict:
         eb = 2 if lay.meta_fp16 else 4                 # bytes per scale / zero-point
         meta_k = b * hkv * (n_q // lay.k_group_tokens) * d * 2 * eb
         meta_v = b * hkv * n_q * (d // lay.v_group_channels) * 2 * eb
+        if lay.outliers:                               # one 4-byte entry per group
+            meta_k += b * hkv * (n_q // lay.k_group_tokens) * d * 4
+            meta_v += b * hkv * n_q * (d // lay.v_group_channels) * 4
         meta = meta_k + meta_v
     fp16 = 2 * b * hkv * (r + n_sink) * d * 2
     qo = 2 * b * hq * d * 2

@@ -65,6 +65,22 @@ scale and per offset.  Readings (listed in the design doc):
 * q = clamp(rint((x - m) / s), 0, 2^b - 1), each step one fp32 operation
   (subtraction, true division, rint) on the stored fp16 s and m;
 * x_hat = s * q + m, in fp64 from the stored fp16 values.
+
+Dense-and-sparse outliers (INT formats)
+---------------------------------------
+"KV Cache Quantization Analysis", sec. 2 (outliers: a few large values widen
+the grid and cost every other value resolution) and sec. 4 (KVQuant, its
+fourth component: per-vector dense-and-sparse quantization keeps outliers
+apart from the quantized values).  The pages give no outlier count or
+selection rule.  Readings (listed in the design doc):
+
+* one outlier per quantization group (the vector: a Key channel's 32 tokens
+  of a block, a Value token's 32-channel group), about 3 % of the values;
+* the outlier is the value of largest magnitude, the lowest index on ties;
+* it is stored exactly (fp16) with its index; the group's scale and
+  zero-point (or fp16 scale and offset) come from the other 31 values with
+  the formulas above; its own code is 0;
+* x_hat is the stored outlier at its index and the affine decode elsewhere.
 """
 from __future__ import annotations
 
@@ -169,7 +185,31 @@ def int_decode_offset(q: np.ndarray, s: np.ndarray, m: np.ndarray) -> np.ndarray
     return np.asarray(s, np.float64) * np.asarray(q, np.float64) + np.asarray(m, np.float64)
 
 
-def quantize_k_group(kg: np.ndarray, bits: int, meta16: bool = False):
+def outlier_index(x: np.ndarray, axis: int) -> np.ndarray:
+    """Index along ``axis`` of each group's value of largest magnitude (lowest index on ties)."""
+    a = np.abs(np.moveaxis(np.asarray(x, F32), axis, -1))
+    n = a.shape[-1]
+    # sort key: larger magnitude first, then smaller index
+    order = np.lexsort((np.broadcast_to(np.arange(n), a.shape), -a), axis=-1)
+    return order[..., 0]
+
+
+def _dense_params(x: np.ndarray, bits: int, axis: int, meta16: bool):
+    """Group parameters over all values except each group's outlier."""
+    xm = np.moveaxis(np.asarray(x, F32), axis, -1)
+    idx = outlier_index(xm, -1)
+    keep = np.ones(xm.shape, bool)
+    np.put_along_axis(keep, idx[..., None], False, axis=-1)
+    # the excluded value is replaced by a value already in the group (its
+    # neighbour), which leaves min and max of the others unchanged
+    nb = np.take_along_axis(xm, np.where(idx == 0, 1, 0)[..., None], axis=-1)
+    xd = np.where(keep, xm, nb)
+    params = int_group_params_f16(xd, bits, -1) if meta16 else int_group_params(xd, bits, -1)
+    val = np.take_along_axis(xm, idx[..., None], axis=-1)[..., 0].astype(np.float16)
+    return params, idx, val
+
+
+def quantize_k_group(kg: np.ndarray, bits: int, meta16: bool = False, outliers: bool = False):
     """Key group of shape [..., G_k tokens, D]: per-channel (s, z) over tokens.
 
     "KV Cache Quantization Analysis", sec. 3: a few fixed Key channels hold
@@ -178,6 +218,12 @@ def quantize_k_group(kg: np.ndarray, bits: int, meta16: bool = False):
     ``meta16``: fp16 scale s and fp16 offset m in place of z).
     """
     x = np.asarray(kg, np.float16).astype(F32)
+    if outliers:
+        (s, z), idx, val = _dense_params(x, bits, -2, meta16)
+        enc = int_encode_offset if meta16 else int_encode
+        q = enc(x, s[..., None, :], z[..., None, :], bits)
+        np.put_along_axis(q, idx[..., None, :], 0, axis=-2)
+        return q, s, z, idx, val
     if meta16:
         s, m = int_group_params_f16(x, bits, axis=-2)
         return int_encode_offset(x, s[..., None, :], m[..., None, :], bits), s, m
@@ -186,7 +232,7 @@ def quantize_k_group(kg: np.ndarray, bits: int, meta16: bool = False):
     return q, s, z
 
 
-def quantize_v_tokens(v: np.ndarray, bits: int, g_v: int, meta16: bool = False):
+def quantize_v_tokens(v: np.ndarray, bits: int, g_v: int, meta16: bool = False, outliers: bool = False):
     """Values of shape [..., T, D]: per-token (s, z) over groups of g_v channels.
 
     "KV Cache Quantization Analysis", sec. 3: the attention output mixes
@@ -199,6 +245,12 @@ def quantize_v_tokens(v: np.ndarray, bits: int, g_v: int, meta16: bool = False):
     if d % g_v:
         raise ValueError("head_dim must be a multiple of the V channel group")
     xg = x.reshape(x.shape[:-1] + (d // g_v, g_v))
+    if outliers:
+        (s, z), idx, val = _dense_params(xg, bits, -1, meta16)
+        enc = int_encode_offset if meta16 else int_encode
+        q = enc(xg, s[..., None], z[..., None], bits)
+        np.put_along_axis(q, idx[..., None], 0, axis=-1)
+        return q.reshape(x.shape), s, z, idx, val
     if meta16:
         s, m = int_group_params_f16(xg, bits, axis=-1)
         return int_encode_offset(xg, s[..., None], m[..., None], bits).reshape(x.shape), s, m
@@ -214,17 +266,23 @@ def _decode(q, s, z):
     return int_decode(q, s, z)
 
 
-def dequantize_k_group(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """Inverse of :func:`quantize_k_group` in fp64."""
-    return _decode(q, s[..., None, :], z[..., None, :])
+def dequantize_k_group(q: np.ndarray, s: np.ndarray, z: np.ndarray, idx=None, val=None) -> np.ndarray:
+    """Inverse of :func:`quantize_k_group` in fp64 (outliers, if given, restored exactly)."""
+    x = _decode(q, s[..., None, :], z[..., None, :])
+    if idx is not None:
+        np.put_along_axis(x, np.asarray(idx)[..., None, :], np.asarray(val, np.float64)[..., None, :], axis=-2)
+    return x
 
 
-def dequantize_v_tokens(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """Inverse of :func:`quantize_v_tokens` in fp64."""
+def dequantize_v_tokens(q: np.ndarray, s: np.ndarray, z: np.ndarray, idx=None, val=None) -> np.ndarray:
+    """Inverse of :func:`quantize_v_tokens` in fp64 (outliers, if given, restored exactly)."""
     d = q.shape[-1]
     g = s.shape[-1]
     qg = q.reshape(q.shape[:-1] + (g, d // g))
-    return _decode(qg, s[..., None], z[..., None]).reshape(q.shape)
+    x = _decode(qg, s[..., None], z[..., None])
+    if idx is not None:
+        np.put_along_axis(x, np.asarray(idx)[..., None], np.asarray(val, np.float64)[..., None], axis=-1)
+    return x.reshape(q.shape)
 
 
 # --------------------------------------------------------------------------

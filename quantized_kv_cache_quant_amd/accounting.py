@@ -23,11 +23,12 @@ def routed(n: int, sink: int, residual: int):
 
 
 def attention_bytes(batch: int, kv_heads: int, q_heads: int, head_dim: int, n: int, fmt: str,
-                    sink: int = 0, residual: int = 128, v_group: int = 32, meta_fp16: bool = False) -> int:
+                    sink: int = 0, residual: int = 128, v_group: int = 32, meta_fp16: bool = False,
+                    outliers: bool = False) -> int:
     ns, nq, r = routed(n, sink, residual)
     bh = batch * kv_heads
     codes = 2 * bh * nq * head_dim * BITS[fmt] // 8
-    pair = 4 if meta_fp16 else 8                  # bytes of one (scale, zero-point) pair
+    pair = (4 if meta_fp16 else 8) + (4 if outliers else 0)   # bytes per group: (s, z) pair + outlier entry
     meta = 0 if fmt.startswith("fp8") else (bh * (nq // BLOCK) * head_dim * pair
                                             + bh * nq * (head_dim // v_group) * pair)
     fp16 = 2 * bh * (ns + r) * head_dim * 2
