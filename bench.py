@@ -16,7 +16,8 @@ Under "variants" it adds attention-only sweeps of the same shape for the
 other cache variants (FP8 E5M2; INT8 / INT4 / INT2 with fp16 scale and
 offset metadata; INT8 in a paged pool of 32-token pages in shuffled
 order; INT8 and INT4 with Keys stored before RoPE, rotated in attention
-with base 500000), eight layer caches each.
+with base 500000; INT4 and INT2 with one exact fp16 outlier per group),
+eight layer caches each.
 
 Timed regions, both bracketed by HIP events on the stream the library
 launches on (torch's current stream):
@@ -89,24 +90,28 @@ def copy_bandwidth(torch) -> float:
 
 
 FP8_MAX = {"fp8": 448.0, "fp8_e5m2": 57344.0}
-VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16", "int8_paged", "int8_rope", "int4_rope")
+VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16", "int8_paged", "int8_rope", "int4_rope", "int4_out",
+            "int2_out")
 ROPE_THETA = 500000.0
 
 
 def split_spec(spec: str):
-    """Format spec -> (kvq format, fp16 metadata, paged, pre-RoPE Keys): suffix "_m16" selects
-    fp16 (s, m) pairs, "_paged" a pool of 32-token pages, "_rope" Keys stored before RoPE."""
+    """Format spec -> (kvq format, fp16 metadata, paged, pre-RoPE Keys, outliers): suffix "_m16"
+    selects fp16 (s, m) pairs, "_paged" a pool of 32-token pages, "_rope" Keys stored before RoPE,
+    "_out" one exact outlier per group."""
+    out = spec.endswith("_out")
+    spec = spec[:-4] if out else spec
     rope = spec.endswith("_rope")
     spec = spec[:-5] if rope else spec
     paged = spec.endswith("_paged")
     spec = spec[:-6] if paged else spec
     m16 = spec.endswith("_m16")
-    return (spec[:-4] if m16 else spec), m16, paged, rope
+    return (spec[:-4] if m16 else spec), m16, paged, rope, out
 
 
 def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v, seed=0):
     import torch
-    fmt, m16, paged, rope = split_spec(spec)
+    fmt, m16, paged, rope, out = split_spec(spec)
     # FP8 calibration: amax / (largest finite value) of the prefill, per tensor (a caller input)
     top = FP8_MAX.get(fmt, 448.0)
     pps = max(1, (max_tokens - w.sink_tokens - w.residual_tokens) // 32)   # one block per page
@@ -114,7 +119,7 @@ def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v, seed=0):
                           residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens,
                           k_scale=np.float32(amax_k / top), v_scale=np.float32(amax_v / top), meta_fp16=m16,
                           page_blocks=1 if paged else 0, num_pages=w.batch * pps if paged else 0,
-                          rope_theta=ROPE_THETA if rope else 0.0)
+                          rope_theta=ROPE_THETA if rope else 0.0, outliers=out)
     c = kvq.Cache.create(lay)
     if paged:                                    # every sequence's pages scattered over the pool
         perm = np.random.default_rng(seed).permutation(w.batch * pps).astype(np.int32)
@@ -123,9 +128,9 @@ def make_cache(kvq, w, spec, max_tokens, amax_k, amax_v, seed=0):
 
 
 def call_bytes(accounting, w, spec, n):
-    fmt, m16, _, _ = split_spec(spec)
+    fmt, m16, _, _, out = split_spec(spec)
     return accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
-                                      w.sink_tokens, w.residual_tokens, meta_fp16=m16)
+                                      w.sink_tokens, w.residual_tokens, meta_fp16=m16, outliers=out)
 
 
 def variant_sweep(torch, kvq, synth, accounting, w, specs, args, layers=8, rounds=8):

@@ -78,6 +78,20 @@
  *
  * FP8 E5M2 codes use the INT8 / FP8 byte layouts above.
  *
+ * Dense-and-sparse outliers (outliers = 1, INT formats; "KV Cache
+ * Quantization Analysis", sec. 2 outliers and sec. 4 KVQuant per-vector
+ * dense-and-sparse): in every quantization group (a Key channel's 32 tokens
+ * of a block, a Value token's 32-channel group) the value of largest
+ * magnitude (lowest index on ties) is kept exactly as fp16 with its index,
+ * the group's scale and zero-point (or offset) come from the other 31
+ * values, and the outlier's own code is 0.  Entries are 32-bit: index in the
+ * group in the low 16 bits, fp16 value in the high 16 bits.
+ *   K out    [B][Hkv][NB][D] entries (token index in the block per channel;
+ *            stored-position order like K meta)
+ *   V out    [B][Hkv][NB][D/32][32] entries (channel index in the group per
+ *            group and token, the V meta order)
+ * Not combined with pre-RoPE Keys (KVQ_ERR_UNSUPPORTED).
+ *
  * Pre-RoPE Keys (rope_theta > 0; "KV Cache Quantization Analysis", sec. 3
  * RoPE problem and sec. 4 KVQuant: quantize Keys per channel before the
  * rotary encoding, rotate after dequantization).  kv_quant_append then takes
@@ -157,11 +171,13 @@ typedef struct {
   int32_t page_blocks;       /* 0: contiguous planes; P >= 1: paged, P 32-token blocks per page */
   int32_t num_pages;         /* paged only: pages in the pool (>= 1) */
   float rope_theta;          /* 0: Keys stored as given; > 0 (finite): pre-RoPE Keys, RoPE base */
+  int32_t outliers;          /* INT only: 1 = one exact fp16 outlier per quantization group */
 } kvq_layout;
 
 enum {
   KVQ_PLANE_K_CODES = 0, KVQ_PLANE_V_CODES, KVQ_PLANE_K_META, KVQ_PLANE_V_META,
   KVQ_PLANE_K_RING, KVQ_PLANE_V_RING, KVQ_PLANE_K_SINK, KVQ_PLANE_V_SINK,
+  KVQ_PLANE_K_OUT, KVQ_PLANE_V_OUT,
   KVQ_NUM_PLANES
 };
 

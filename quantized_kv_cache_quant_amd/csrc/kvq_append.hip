@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   constexpr bool kE5M2 = kKind == KVQ_FP8_E5M2;
   constexpr bool kM16 = meta16_of(VAR);
   constexpr bool kRopeK = rope_of(VAR);     // K rows in RoPE pair order
+  constexpr bool kOut = outliers_of(VAR);   // one exact outlier per group
   constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   constexpr float kQmax = (float)((1 << kBits) - 1);
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   __shared__ float vs[kBlock][kHeadDim + 1];
   __shared__ float sk[kHeadDim], zk[kHeadDim];
   __shared__ float sv[kBlock][kVGroups], zv[kBlock][kVGroups];
+  __shared__ int ko[kHeadDim];               // outliers: token of each channel's outlier
+  __shared__ int vo[kBlock][kVGroups];       // outliers: channel (in group) of each token's outlier
 
   const int tid = threadIdx.x;
   const int64_t blk = (int64_t)p.first_block + blockIdx.x;
@@ -140,10 +143,32 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   if constexpr (!kFp8) {
     if (tid < kHeadDim) {
       const int c = tid;
-      float mn = ks[0][c], mx = ks[0][c];
-      for (int t = 1; t < kBlock; ++t) {
-        mn = fminf(mn, ks[t][c]);
-        mx = fmaxf(mx, ks[t][c]);
+      float mn, mx;
+      if constexpr (kOut) {
+        // the outlier: largest magnitude, lowest token index on ties; the
+        // range comes from the other 31 values
+        int oi = 0;
+        float oa = fabsf(ks[0][c]);
+        for (int t = 1; t < kBlock; ++t)
+          if (fabsf(ks[t][c]) > oa) { oa = fabsf(ks[t][c]); oi = t; }
+        const int first = oi == 0 ? 1 : 0;
+        mn = ks[first][c];
+        mx = mn;
+        for (int t = 0; t < kBlock; ++t) {
+          if (t == oi) continue;
+          mn = fminf(mn, ks[t][c]);
+          mx = fmaxf(mx, ks[t][c]);
+        }
+        ko[c] = oi;
+        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)ks[oi][c]);   // exact: an fp16 input
+        p.k_out[rec * kHeadDim + (kRopeK ? rope_stored_pos(c) : c)] = (uint32_t)oi | (xb << 16);
+      } else {
+        mn = ks[0][c];
+        mx = ks[0][c];
+        for (int t = 1; t < kBlock; ++t) {
+          mn = fminf(mn, ks[t][c]);
+          mx = fmaxf(mx, ks[t][c]);
+        }
       }
       mn = mn + 0.0f;                                 // a zero minimum is +0
       if constexpr (kM16) {                           // fp16 (s rounded up, m = min)
@@ -168,10 +193,30 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
     } else {
       const int e = tid - kHeadDim;
       const int t = e >> 2, g = e & 3;
-      float mn = vs[t][kVGroup * g], mx = mn;
-      for (int c = 1; c < kVGroup; ++c) {
-        mn = fminf(mn, vs[t][kVGroup * g + c]);
-        mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+      float mn, mx;
+      if constexpr (kOut) {
+        int oi = 0;
+        float oa = fabsf(vs[t][kVGroup * g]);
+        for (int c = 1; c < kVGroup; ++c)
+          if (fabsf(vs[t][kVGroup * g + c]) > oa) { oa = fabsf(vs[t][kVGroup * g + c]); oi = c; }
+        const int first = oi == 0 ? 1 : 0;
+        mn = vs[t][kVGroup * g + first];
+        mx = mn;
+        for (int c = 0; c < kVGroup; ++c) {
+          if (c == oi) continue;
+          mn = fminf(mn, vs[t][kVGroup * g + c]);
+          mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+        }
+        vo[t][g] = oi;
+        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)vs[t][kVGroup * g + oi]);
+        p.v_out[rec * (kVGroups * kBlock) + g * kBlock + t] = (uint32_t)oi | (xb << 16);
+      } else {
+        mn = vs[t][kVGroup * g];
+        mx = mn;
+        for (int c = 1; c < kVGroup; ++c) {
+          mn = fminf(mn, vs[t][kVGroup * g + c]);
+          mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+        }
       }
       mn = mn + 0.0f;
       if constexpr (kM16) {
@@ -228,7 +273,9 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int c = chan(wi * kPer + j);
-          word |= encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c]) << (j * kBits);
+          uint32_t code = encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c]);
+          if constexpr (kOut) code = ko[c] == t ? 0u : code;            // the outlier's code is 0
+          word |= code << (j * kBits);
         }
       }
       dst[w] = word;
@@ -245,13 +292,17 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       const int wi = 4 * (w >> 8) + (w & 3);
       const int qd = lane >> 4, r = lane & 15;
       uint32_t word = 0;
+      // code of (token t, channel ch) in group g; an outlier's code is 0
+      auto oz = [&](uint32_t code, int t, int ch, int g) {
+        return (kOut && vo[t][g] == (ch & (kVGroup - 1))) ? 0u : code;
+      };
       if constexpr (kBits == 4) {                 // word m: nibble j = T[j], channel 16m + r
         const int ch = 16 * wi + r;
         const int g = ch / kVGroup;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = record_token(qd, j);
-          word |= encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g]) << (4 * j);
+          word |= oz(encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g]), t, ch, g) << (4 * j);
         }
       } else if constexpr (kBits == 8) {          // bytes 8m..8m+7 = T0 T4 T1 T5 T2 T6 T3 T7
         const int ch = 16 * (wi >> 1) + r;
@@ -269,7 +320,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int t = record_token(qd, sel(base + k));
-            word |= encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g]) << (8 * k);
+            word |= oz(encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g]), t, ch, g) << (8 * k);
           }
         }
       } else {                                    // INT2 word p: A = 32p + r, B = 32p + 16 + r
@@ -278,10 +329,10 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t0 = record_token(qd, j), t1 = record_token(qd, 4 + j);
-          word |= encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga]) << (2 * j);
-          word |= encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb]) << (8 + 2 * j);
-          word |= encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga]) << (16 + 2 * j);
-          word |= encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb]) << (24 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga]), t0, cha, ga) << (2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb]), t0, chb, gb) << (8 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga]), t1, cha, ga) << (16 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb]), t1, chb, gb) << (24 + 2 * j);
         }
       }
       dst[w] = word;
@@ -334,6 +385,15 @@ hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int bat
     case KVQ_INT2 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kRope>, grid, block, 0, s, p); break;
     case KVQ_FP8_E4M3 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E4M3 | kRope>, grid, block, 0, s, p); break;
     case KVQ_FP8_E5M2 | kRope: hipLaunchKernelGGL(flush_kernel<KVQ_FP8_E5M2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kOutliers: hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kOutliers: hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kOutliers: hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT4 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(flush_kernel<KVQ_INT2 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
     case KVQ_INT8 | kMeta16 | kRope:
       hipLaunchKernelGGL(flush_kernel<KVQ_INT8 | kMeta16 | kRope>, grid, block, 0, s, p); break;
     case KVQ_INT4 | kMeta16 | kRope:

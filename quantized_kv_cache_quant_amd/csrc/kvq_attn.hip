@@ -161,6 +161,7 @@ struct Traits {
   static constexpr int kKind = kind_of(FMT);
   static constexpr bool kMeta16 = meta16_of(FMT);
   static constexpr bool kRope = rope_of(FMT);     // Keys stored before RoPE, in pair order
+  static constexpr bool kOut = outliers_of(FMT);  // one exact outlier per quantization group
   static constexpr bool kFp8 = fp8_of(FMT);
   static constexpr int kBits = kKind == KVQ_INT4 ? 4 : (kKind == KVQ_INT2 ? 2 : 8);
   static constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
@@ -171,7 +172,7 @@ struct Traits {
   // counts keep every format at or under 256 VGPRs, two wavefronts per SIMD)
   static constexpr int kDepthBase = kFp8 ? KVQ_DEPTH_FP8 : (kBits == 8 ? KVQ_DEPTH_INT8 : (kBits == 4 ? KVQ_DEPTH_INT4 : KVQ_DEPTH_INT2));
   // the rotation's temporaries leave room for at most two blocks in flight
-  static constexpr int kDepth = (kRope && kDepthBase > 2) ? 2 : kDepthBase;
+  static constexpr int kDepth = ((kRope || kOut) && kDepthBase > 2) ? 2 : kDepthBase;
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -219,6 +220,7 @@ struct Raw {
   uint32_t v[Traits<FMT>::kVWords];
   float4 km, vm;                         // this lane's part of each metadata block: 16 bytes
                                          // of fp32 pairs, or 8 bytes of fp16 pairs in .x / .y
+  uint2 ko, vo;                          // outliers: this lane's two K and two V entries
 };
 
 // Code lines are read once per call: nontemporal loads keep them from
@@ -280,6 +282,10 @@ __device__ __forceinline__ void load_block(Raw<FMT>& r, const AttnParams& p, int
   } else if constexpr (!T::kFp8) {
     r.km = reinterpret_cast<const float4*>(p.k_meta + id * 256)[lane];
     r.vm = reinterpret_cast<const float4*>(p.v_meta + id * 256)[lane];
+  }
+  if constexpr (T::kOut) {
+    r.ko = reinterpret_cast<const uint2*>(p.k_out + id * kHeadDim)[lane];
+    r.vo = reinterpret_cast<const uint2*>(p.v_out + id * kHeadDim)[lane];
   }
 }
 
@@ -389,7 +395,7 @@ struct WaveState {
 };
 
 struct LaneInfo {
-  int lane, qd, head;
+  int lane, qd, head, nrep;
   bool is_lo;       // column carries the lo remainder
   bool writer;      // hi column of a real query head: writes the results
   uint32_t hmask;   // 0xFFFFFFFF in lo columns, 0 in hi columns
@@ -399,6 +405,7 @@ struct LaneInfo {
 __device__ __forceinline__ LaneInfo lane_info(int nrep) {
   LaneInfo li;
   li.lane = threadIdx.x & 63;
+  li.nrep = nrep;
   const int col = li.lane & 15;
   li.qd = li.lane >> 4;
   li.head = col & 7;
@@ -494,6 +501,8 @@ __device__ __forceinline__ float2 rope_cs(double pos, double freq) {
 // In-block offsets (cos, sin)(k * theta_i), k < 32, i < 64, shared by the
 // workgroup in LDS: entry 64 k + i.
 constexpr int kRopeTableBytes = 32 * 64 * 8;
+// Outliers: per-wavefront query pairs [64 lanes][8 heads] (32-bit each).
+constexpr int kOutQBytes = 64 * 8 * 4;
 
 // Query of this lane's column head (its quarter's 32 channels) from a KV
 // head's n_rep query rows ([n_rep][128] fp16): packed f16 pairs in Key
@@ -570,7 +579,11 @@ __device__ __forceinline__ void static_q(const QOp& q, float scale, f16x8* bk) {
 
 // Online softmax over one block's 32 tokens (this lane: 8 of them, logits
 // lg[tile][i] for tokens 16*tile + 4qd + i); returns p = 2^(lg - m).
-__device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, float pr[2][4], float slack) {
+// vacc (outliers only): the wavefront's Value outlier sums [8 heads][128
+// channels] in LDS, rescaled with the accumulators; lane (qd, col < 8)
+// rescales head col's channels 32qd .. 32qd + 31.
+__device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, float pr[2][4], float slack,
+                                              float* vacc = nullptr) {
   float mx = neg_inf();
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
@@ -586,6 +599,18 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
     ws.z[1] *= alpha;
     ws.l *= alpha;
     ws.m = m_new;
+    if (vacc) {
+      const int lane = threadIdx.x & 63;
+      if ((lane & 15) < 8) {
+        float4* a = reinterpret_cast<float4*>(vacc + (lane & 7) * kHeadDim + 32 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float4 x = a[i];
+          x.x *= alpha; x.y *= alpha; x.z *= alpha; x.w *= alpha;
+          a[i] = x;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
@@ -630,11 +655,24 @@ __device__ constexpr bool pair_first(int j) {
   return (kind_of(FMT) == KVQ_INT4 || kind_of(FMT) == KVQ_INT2) ? ((j & 2) == 0) : ((j & 1) == 0);
 }
 
+// Dense-and-sparse outliers: per-wavefront LDS areas and the query values
+// the corrections need.  A Key outlier x at (token t, channel c) adds
+// q_c (x - x_hat(0)) to the logit of t, x_hat(0) being what code 0 decodes
+// to; a Value outlier at (t, c) adds p_t (x - x_hat(0)) to output channel c.
+struct OutCtx {
+  float* kc;        // [8 heads][32 tokens] logit corrections of the block
+  float* pst;       // [8 heads][32 tokens] p of the block
+                    // (token-minor: the lanes of one atomic spread over the banks)
+  float* vacc;      // [8 heads][128 channels] Value corrections of the segment
+  uint32_t* qst;    // [64 lanes][8 heads]: channels 2 lane, 2 lane + 1 of each query head
+                    // (packed f16, zero past n_rep), written when a segment starts
+};
+
 // t0: position of the block's first token (pre-RoPE Keys only).
 template <int FMT>
 __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const QOp& q,
                                               const f16x8* bk_static, const LaneInfo& li, const RopeCtx& rc,
-                                              double t0) {
+                                              double t0, const OutCtx& oc) {
   using T = Traits<FMT>;
   const int qd = li.qd;
 
@@ -703,6 +741,26 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
                                                            acc[tile], 0, 0, 0);
   } else {
     stage_meta<FMT>(r, st, li.lane);
+    if constexpr (T::kOut) {
+      // Key outliers of channels 2 lane, 2 lane + 1 into the block's logit
+      // corrections (logit units: log2(e) / sqrt(D) included); staged
+      // [128 + slot] is that unit times s z (or -m), i.e. -x_hat(0)
+      reinterpret_cast<float4*>(oc.kc)[li.lane] = float4{0.f, 0.f, 0.f, 0.f};
+      const uint4 qa = reinterpret_cast<const uint4*>(oc.qst)[2 * li.lane];
+      const uint4 qb = reinterpret_cast<const uint4*>(oc.qst)[2 * li.lane + 1];
+      const uint32_t qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      const uint32_t ent[2] = {r.ko.x, r.ko.y};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * li.lane + u;
+        const int t = (int)(ent[u] & 31u);
+        const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)(ent[u] >> 16));
+        const float d = __builtin_fmaf(x, kQScale, st[128 + (c & ~31) + k_slot_of<FMT>(c & 31)]);
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (h < li.nrep) atomicAdd(oc.kc + h * 32 + t, (float)u2h(qv[h])[u] * d);
+      }
+    }
     // zero-point term sum_c q_c s_c z_c over this lane's 32 channels (in
     // slot order), then over the four quarters
     float bias0 = 0.f, bias1 = 0.f;
@@ -740,12 +798,47 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * (T::kRope ? 1.0f : T::kCodeScale);
+  if constexpr (T::kOut) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[tile][i] += oc.kc[(li.lane & 7) * 32 + 16 * tile + 4 * qd + i];
+  }
   float slack = kSlack;
   if constexpr (!T::kFp8) {
     const float2 sv = pair_scales<FMT>(r.vm);
     if (__any(sv.x > kLazyScaleMax || sv.y > kLazyScaleMax)) slack = 0.f;
   }
-  softmax_block(lg, ws, pr, slack);
+  softmax_block(lg, ws, pr, slack, T::kOut ? oc.vacc : nullptr);
+
+  if constexpr (T::kOut) {
+    // Value outliers: entries 2 lane, 2 lane + 1 ([group][token] order, as
+    // the staged V meta) add p_t (x - x_hat(0)) to the segment's sums;
+    // staged [384 + entry] is s z (or -m), i.e. -x_hat(0)
+    if ((li.lane & 15) < 8) {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oc.pst[(li.lane & 7) * 32 + 16 * tile + 4 * qd + i] = pr[tile][i];
+    }
+    const uint32_t ent[2] = {r.vo.x, r.vo.y};
+    float pv[2][8], dv[2];
+    int cv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {               // all reads first, then the atomics
+      const int e = 2 * li.lane + u;
+      const int t = e & 31;
+      cv[u] = 32 * (e >> 5) + (int)(ent[u] & 31u);
+      dv[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ent[u] >> 16)) + st[384 + e];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) pv[u][h] = oc.pst[h * 32 + t];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (h < li.nrep) atomicAdd(oc.vacc + h * kHeadDim + cv[u], pv[u][h] * dv[u]);
+  }
 
   // ---- PV: Value codes (rows = channels) x P' (columns)
   if constexpr (T::kFp8) {
@@ -797,7 +890,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 // Sums over quarters and hi + lo columns, then writes one partial slot:
 // m, l, o[128] per query head (o unnormalised).
 __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneInfo& li, float* slot, float oscale,
-                                               bool has_z) {
+                                               bool has_z, const float* vacc = nullptr) {
   const float l = rows_sum(ws.l);
   float zs[4] = {0.f, 0.f, 0.f, 0.f};
   if (has_z) {
@@ -813,6 +906,10 @@ __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneIn
     o.y = (ws.o[m][1] + ror8(ws.o[m][1])) * oscale - zs[m >> 1];
     o.z = (ws.o[m][2] + ror8(ws.o[m][2])) * oscale - zs[m >> 1];
     o.w = (ws.o[m][3] + ror8(ws.o[m][3])) * oscale - zs[m >> 1];
+    if (vacc && li.writer) {                  // Value outlier sums of channels 16m + 4qd .. + 3
+      const float4 a = *reinterpret_cast<const float4*>(vacc + li.head * kHeadDim + 16 * m + 4 * li.qd);
+      o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+    }
     if (li.writer) *reinterpret_cast<float4*>(dst + 4 + 16 * m + 4 * li.qd) = o;
   }
   if (li.writer && li.qd == 0) {
@@ -956,6 +1053,7 @@ constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : 
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
 static_assert(kWaveLds >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
+static_assert(kWaveLds >= 2176 * 4, "stage area holds the outlier sums after the block metadata");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
 // touching heads h0..h1.
@@ -1111,6 +1209,30 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     WaveState ws;
     reset(ws);
     int cur = -1;
+    // outliers: the stage area after the block metadata holds the segment's
+    // Value sums [640, 1664), the block's logit corrections [1664, 1920) and
+    // its p [1920, 2176) (floats)
+    OutCtx oc{};
+    if constexpr (T::kOut) {
+      oc.vacc = stage + 640;
+      oc.kc = stage + 1664;
+      oc.pst = stage + 1920;
+      oc.qst = reinterpret_cast<uint32_t*>(lds + kLdsBytes + v * kOutQBytes);
+    }
+    // A new segment clears the Value sums and stores the query pairs in LDS;
+    // the loads are consumed here, so their wait stays on this path
+    auto start_segment = [&](int64_t bh) {
+      if constexpr (T::kOut) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<float4*>(oc.vacc)[li.lane + 64 * i] = float4{0.f, 0.f, 0.f, 0.f};
+        uint32_t qv[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          qv[h] = h < p.nrep ? reinterpret_cast<const uint32_t*>(p.q + (bh * p.nrep + h) * kHeadDim)[li.lane] : 0u;
+        reinterpret_cast<uint4*>(oc.qst)[2 * li.lane] = uint4{qv[0], qv[1], qv[2], qv[3]};
+        reinterpret_cast<uint4*>(oc.qst)[2 * li.lane + 1] = uint4{qv[4], qv[5], qv[6], qv[7]};
+      }
+    };
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
@@ -1118,10 +1240,11 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         if (rid[d] < 0) goto done;           // blocks are taken in order: none left
         if (rbh[d] != cur) {
           if (cur >= 0) {
-            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8, T::kOut ? oc.vacc : nullptr);
             reset(ws);
           }
           cur = rbh[d];
+          start_segment(cur);
           if (cur != qhead) {
             load_query<FMT>(p, cur, li, qop);
             qhead = cur;
@@ -1129,11 +1252,11 @@ __device__ void group_main(const AttnParams& p, char* lds) {
           if constexpr (T::kFp8 || T::kRope) static_q(qop, T::kFp8 ? p.k_scale * kQScale : kQScale, bk_static);
         }
         process_block<FMT>(buf[d], stage, ws, qop, bk_static, li, rc,
-                           (double)p.sink_cap + (double)kBlock * rblk[d]);
+                           (double)p.sink_cap + (double)kBlock * rblk[d], oc);
       }
     }
   done:
-    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8, T::kOut ? oc.vacc : nullptr);
   }
   __syncthreads();                            // every wavefront's partials written
 
@@ -1198,7 +1321,8 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
 
 template <int FMT>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
+  __shared__ __attribute__((aligned(16)))
+  char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0) + (Traits<FMT>::kOut ? kGroupWaves * kOutQBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
   else group_main<FMT>(p, lds);
 }
@@ -1277,6 +1401,15 @@ hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
     case KVQ_INT2 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kRope>, grid, block, 0, s, p); break;
     case KVQ_FP8_E4M3 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E4M3 | kRope>, grid, block, 0, s, p); break;
     case KVQ_FP8_E5M2 | kRope: hipLaunchKernelGGL(attn_kernel<KVQ_FP8_E5M2 | kRope>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kOutliers: hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kOutliers: hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kOutliers: hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT8 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT4 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT4 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
+    case KVQ_INT2 | kMeta16 | kOutliers:
+      hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kMeta16 | kOutliers>, grid, block, 0, s, p); break;
     case KVQ_INT8 | kMeta16 | kRope:
       hipLaunchKernelGGL(attn_kernel<KVQ_INT8 | kMeta16 | kRope>, grid, block, 0, s, p); break;
     case KVQ_INT4 | kMeta16 | kRope:

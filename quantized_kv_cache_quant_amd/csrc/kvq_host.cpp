@@ -56,6 +56,8 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_V_RING] = sz[KVQ_PLANE_K_RING];
   sz[KVQ_PLANE_K_SINK] = bh * (uint64_t)L.sink_tokens * d * 2;
   sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
+  sz[KVQ_PLANE_K_OUT] = L.outliers ? recs * d * 4 : 0;                       // one entry per channel
+  sz[KVQ_PLANE_V_OUT] = L.outliers ? recs * (d / L.v_group_channels) * kBlock * 4 : 0;
 }
 
 // Compute units of the current device (256 when no device answers).
@@ -138,6 +140,8 @@ int32_t kvq_layout_validate(const kvq_layout* L) {
   if (L->sink_tokens > L->max_tokens) return KVQ_ERR_LAYOUT;
   if (L->page_blocks < 0 || (L->page_blocks > 0 && L->num_pages < 1)) return KVQ_ERR_LAYOUT;
   if (!std::isfinite(L->rope_theta) || L->rope_theta < 0.f) return KVQ_ERR_LAYOUT;
+  if (L->outliers != 0 && L->outliers != 1) return KVQ_ERR_LAYOUT;
+  if (L->outliers && fp8_of(L->format)) return KVQ_ERR_LAYOUT;           // FP8 has no groups
   // block records are 32-bit in the attention kernel
   if (L->page_blocks > 0 && (int64_t)L->num_pages * L->num_kv_heads * L->page_blocks > 0x7fffffffLL)
     return KVQ_ERR_UNSUPPORTED;
@@ -145,6 +149,7 @@ int32_t kvq_layout_validate(const kvq_layout* L) {
     return KVQ_ERR_UNSUPPORTED;
   const int nrep = L->num_q_heads / L->num_kv_heads;
   if (nrep != 1 && nrep != 2 && nrep != 4 && nrep != 8) return KVQ_ERR_UNSUPPORTED;
+  if (L->outliers && L->rope_theta > 0.f) return KVQ_ERR_UNSUPPORTED;
   // grid.y = Hkv and grid.z = B must fit the launch limits
   if (L->num_kv_heads > 65535 || L->batch > 65535) return KVQ_ERR_UNSUPPORTED;
   if ((int64_t)L->residual_tokens + kBlock > (int64_t)1 << 30) return KVQ_ERR_UNSUPPORTED;
@@ -256,6 +261,8 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
     p.v_codes = reinterpret_cast<uint8_t*>(plane(KVQ_PLANE_V_CODES));
     p.k_meta = reinterpret_cast<float*>(plane(KVQ_PLANE_K_META));
     p.v_meta = reinterpret_cast<float*>(plane(KVQ_PLANE_V_META));
+    p.k_out = reinterpret_cast<uint32_t*>(plane(KVQ_PLANE_K_OUT));
+    p.v_out = reinterpret_cast<uint32_t*>(plane(KVQ_PLANE_V_OUT));
     p.n_old = n_old;
     p.T = T;
     p.hkv = L.num_kv_heads;
@@ -339,6 +346,8 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.v_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_V_CODES));
   p.k_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_K_META));
   p.v_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_V_META));
+  p.k_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_K_OUT));
+  p.v_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_V_OUT));
   p.k_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_RING));
   p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
   p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));

@@ -29,14 +29,16 @@ constexpr int kMaxPagedRange = 4096;     // paged caches: blocks per workgroup r
 // fp16 (scale, offset) pairs and kRope when the Keys are stored before RoPE.
 constexpr int kMeta16 = 8;
 constexpr int kRope = 16;
+constexpr int kOutliers = 32;
 __host__ __device__ constexpr int kind_of(int variant) { return variant & 7; }
 __host__ __device__ constexpr bool meta16_of(int variant) { return (variant & kMeta16) != 0; }
 __host__ __device__ constexpr bool rope_of(int variant) { return (variant & kRope) != 0; }
+__host__ __device__ constexpr bool outliers_of(int variant) { return (variant & kOutliers) != 0; }
 __host__ __device__ constexpr bool fp8_of(int variant) {
   return kind_of(variant) == KVQ_FP8_E4M3 || kind_of(variant) == KVQ_FP8_E5M2;
 }
 inline int variant_of(const kvq_layout& L) {
-  return L.format | (L.meta_fp16 ? kMeta16 : 0) | (L.rope_theta > 0.f ? kRope : 0);
+  return L.format | (L.meta_fp16 ? kMeta16 : 0) | (L.rope_theta > 0.f ? kRope : 0) | (L.outliers ? kOutliers : 0);
 }
 
 // Stored position of channel c in a pre-RoPE Key row (pairs side by side)
@@ -55,6 +57,8 @@ struct FlushParams {
   uint8_t* v_codes;       // [B][Hkv][NB][32*D*b/8]
   float* k_meta;          // [B][Hkv][NB][D][2]       (s, z) per channel (fp16 (s, m) pairs: meta16)
   float* v_meta;          // [B][Hkv][NB][D/32][32][2] (s, z) per group and token
+  uint32_t* k_out;        // outliers: [B][Hkv][NB][D] entries (index | fp16 << 16)
+  uint32_t* v_out;        // outliers: [B][Hkv][NB][D/32][32] entries
   int64_t n_old;          // tokens per sequence before this append
   int32_t T;              // tokens appended
   int32_t hkv;
@@ -118,6 +122,8 @@ struct AttnParams {
   const uint8_t* v_codes;
   const float* k_meta;
   const float* v_meta;
+  const uint32_t* k_out;  // outliers (see FlushParams)
+  const uint32_t* v_out;
   const uint16_t* k_ring;
   const uint16_t* v_ring;
   const uint16_t* k_sink;

@@ -17,7 +17,7 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_LAYOUT", -3: "KVQ_ERR_UN
           -4: "KVQ_ERR_CAPACITY", -5: "KVQ_ERR_ALIGN", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP",
           -8: "KVQ_ERR_EMPTY"}
 FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3, "fp8_e5m2": 4}
-PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink")
+PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink", "k_out", "v_out")
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
            "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table")
@@ -36,7 +36,8 @@ class Layout(ctypes.Structure):
                 ("k_group_tokens", ctypes.c_int32), ("v_group_channels", ctypes.c_int32),
                 ("residual_tokens", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("meta_fp16", ctypes.c_int32),
-                ("page_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+                ("page_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("outliers", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -92,10 +93,10 @@ def check(status: int, where: str) -> None:
 
 def make_layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, fmt, *, k_group_tokens=32,
                 v_group_channels=32, residual_tokens=128, sink_tokens=0, k_scale=1.0, v_scale=1.0,
-                meta_fp16=False, page_blocks=0, num_pages=0, rope_theta=0.0) -> Layout:
+                meta_fp16=False, page_blocks=0, num_pages=0, rope_theta=0.0, outliers=False) -> Layout:
     return Layout(batch, num_kv_heads, num_q_heads, head_dim, max_tokens, FORMATS[fmt], k_group_tokens,
                   v_group_channels, residual_tokens, sink_tokens, float(k_scale), float(v_scale), int(meta_fp16),
-                  int(page_blocks), int(num_pages), float(rope_theta))
+                  int(page_blocks), int(num_pages), float(rope_theta), int(outliers))
 
 
 def cache_bytes(layout: Layout) -> int:

@@ -33,7 +33,8 @@ def olayout_of(lay_kw: dict) -> ocache.Layout:
     return ocache.Layout(k["batch"], k["num_kv_heads"], k["num_q_heads"], 128, k["max_tokens"], k["fmt"],
                          residual_tokens=k.get("residual_tokens", 128), sink_tokens=k.get("sink_tokens", 0),
                          k_scale=k.get("k_scale", 1.0), v_scale=k.get("v_scale", 1.0),
-                         meta_fp16=bool(k.get("meta_fp16", False)), rope_theta=float(k.get("rope_theta", 0.0)))
+                         meta_fp16=bool(k.get("meta_fp16", False)), rope_theta=float(k.get("rope_theta", 0.0)),
+                         outliers=bool(k.get("outliers", False)))
 
 
 def make_cache(lay_kw: dict) -> kvq.Cache:
@@ -97,6 +98,11 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
         vm = blocks("v_meta", mt, (4, 32, 2))
         s_k, z_k = olayout.unpack_k_meta(km, rope=rope)
         s_v, z_v = olayout.unpack_v_meta(vm)
+        if olay.outliers:
+            ko = blocks("k_out", np.uint32, (d,))
+            vo = blocks("v_out", np.uint32, (4, 32))
+            ko_i, ko_v = olayout.unpack_outliers(ko)
+            vo_i, vo_v = olayout.unpack_v_outliers(vo)
     ring_k = pl("k_ring", np.float16, (b, hkv, rs, d))
     ring_v = pl("v_ring", np.float16, (b, hkv, rs, d))
     slots = (np.arange(n_q, n_q + r) % rs).astype(np.int64)
@@ -108,6 +114,8 @@ def read_state(c: kvq.Cache, olay: ocache.Layout) -> ocache.CacheState:
         sk = sv = np.zeros((b, hkv, 0, d), np.float16)
     st = ocache.CacheState(olay, n, n_sink, n_q, r, sk.copy(), sv.copy(), codes_k, codes_v, s_k, z_k, s_v,
                            z_v, ring_k[:, :, slots].copy(), ring_v[:, :, slots].copy(), slots)
+    if olay.outliers and olay.fmt not in FP8:
+        st.ko_idx, st.ko_val, st.vo_idx, st.vo_val = ko_i, ko_v, vo_i, vo_v
     return st
 
 
@@ -137,6 +145,10 @@ def assert_states_equal(got: ocache.CacheState, exp: ocache.CacheState, heads=No
     eq(got.res_v, exp.res_v, "V residual")
     eq(got.sink_k, exp.sink_k, "K sinks")
     eq(got.sink_v, exp.sink_v, "V sinks")
+    eq(got.ko_idx, exp.ko_idx, "K outlier index")
+    eq(got.ko_val, exp.ko_val, "K outlier value")
+    eq(got.vo_idx, exp.vo_idx, "V outlier index")
+    eq(got.vo_val, exp.vo_val, "V outlier value")
 
 
 def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_group: int = 0,
@@ -156,7 +168,8 @@ def substate(st: ocache.CacheState, bi: int, gi: int) -> ocache.CacheState:
     lay = st.layout
     sub = ocache.Layout(1, 1, lay.n_rep, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
                         lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale,
-                        lay.meta_fp16, lay.rope_theta)
+                        lay.meta_fp16, lay.rope_theta, lay.outliers)
     return ocache.CacheState(sub, st.n, st.n_sink, st.n_q, st.r, cut(st.sink_k), cut(st.sink_v),
                              cut(st.codes_k), cut(st.codes_v), cut(st.s_k), cut(st.z_k), cut(st.s_v),
-                             cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots)
+                             cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots, cut(st.ko_idx),
+                             cut(st.ko_val), cut(st.vo_idx), cut(st.vo_val))

@@ -75,6 +75,11 @@ def _lay(**kw):
     ({"rope_theta": -1.0}, -2),
     ({"rope_theta": float("nan")}, -2),
     ({"rope_theta": float("inf")}, -2),
+    ({"outliers": 1}, 0),
+    ({"fmt": "int2", "meta_fp16": 1, "outliers": 1, "page_blocks": 2, "num_pages": 9}, 0),
+    ({"outliers": 2}, -2),
+    ({"fmt": "fp8", "outliers": 1}, -2),                  # FP8 has no groups
+    ({"outliers": 1, "rope_theta": 10000.0}, -3),
 ])
 def test_layout_validation(kw, status):
     lay = _lay(**kw)
@@ -105,6 +110,8 @@ def test_cache_bytes_and_planes(fmt, bits, m16, s, r, maxt):
         "v_ring": b * hkv * (r + 32) * d * 2,
         "k_sink": b * hkv * s * d * 2,
         "v_sink": b * hkv * s * d * 2,
+        "k_out": 0,
+        "v_out": 0,
     }
     h = kvq.CacheStruct()
     assert kvq.lib().kvq_cache_init(ctypes.byref(h), ctypes.byref(lay), ctypes.c_void_p(FAKE), total) == 0
@@ -230,7 +237,7 @@ def test_paged_planes_and_table_binding(fmt, bits, pb, pages):
     expect = {"k_codes": recs * 32 * d * bits // 8, "v_codes": recs * 32 * d * bits // 8,
               "k_meta": 0 if fp8 else recs * 2 * d * 4, "v_meta": 0 if fp8 else recs * 2 * 4 * 32 * 4,
               "k_ring": b * hkv * 64 * d * 2, "v_ring": b * hkv * 64 * d * 2,
-              "k_sink": b * hkv * 4 * d * 2, "v_sink": b * hkv * 4 * d * 2}
+              "k_sink": b * hkv * 4 * d * 2, "v_sink": b * hkv * 4 * d * 2, "k_out": 0, "v_out": 0}
     for i, name in enumerate(kvq.PLANES):
         assert h.plane_bytes[i] == expect[name], name
     assert h.block_table is None and h.n_blocks_cap == (1000 - 36) // 32
@@ -251,3 +258,17 @@ def test_paged_planes_and_table_binding(fmt, bits, pb, pages):
     lay2, h2 = _cache()
     assert L.kvq_cache_set_block_table(ctypes.byref(h2), P(FAKE), 100) == -2
     assert L.kvq_cache_set_block_table(None, P(FAKE), 100) == -1
+
+
+@pytest.mark.parametrize("fmt,bits", [("int4", 4), ("int2", 2), ("int8", 8)])
+def test_outlier_planes(fmt, bits):
+    b, hkv, d, maxt = 3, 2, 128, 1000
+    lay = _lay(batch=b, num_kv_heads=hkv, num_q_heads=hkv * 4, fmt=fmt, max_tokens=maxt, residual_tokens=32,
+               sink_tokens=4, outliers=1)
+    h = kvq.CacheStruct()
+    assert kvq.lib().kvq_cache_init(ctypes.byref(h), ctypes.byref(lay), ctypes.c_void_p(FAKE),
+                                    kvq.cache_bytes(lay)) == 0
+    nb = (maxt - 36) // 32
+    sizes = dict(zip(kvq.PLANES, list(h.plane_bytes)))
+    assert sizes["k_out"] == b * hkv * nb * d * 4 and sizes["v_out"] == b * hkv * nb * 4 * 32 * 4
+    assert sizes["k_codes"] == b * hkv * nb * 32 * d * bits // 8

@@ -1,0 +1,142 @@
+"""GPU parity of dense-and-sparse outliers: one exact fp16 outlier per quantization group.
+
+The library's codes, scales, zero-points (or offsets) and outlier entries
+must equal the oracle's bit for bit, and attention over the cache (dense
+codes plus exact outliers) must match fp64 attention within 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from oracle import cache as ocache
+from quantized_kv_cache_quant_amd import synth
+
+from kvq_testlib import (append_chunks, assert_states_equal, attention_gpu, make_cache, olayout_of, read_state,
+                         require_gpu, split_fmt, substate)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+W = synth.WORKLOADS
+FMTS = ["int8", "int4", "int2", "int8_m16", "int4_m16", "int2_m16"]
+
+
+def _kw(name, b, hkv, nrep, maxt, r, s, **extra):
+    fmt, m16 = split_fmt(name)
+    kw = dict(batch=b, num_kv_heads=hkv, num_q_heads=hkv * nrep, max_tokens=maxt, fmt=fmt,
+              residual_tokens=r, sink_tokens=s, meta_fp16=m16, outliers=True)
+    kw.update(extra)
+    return kw
+
+
+def _spiky(k, v, rng, frac=0.01, scale=40.0):
+    """Scattered large Key values (per-vector outliers) on top of the workload's channel outliers.
+
+    Values keep the workload's distribution: every group has an outlier (its largest value)
+    anyway, and large Values would push outputs to magnitudes where the fp16 output
+    rounding alone (2^-11 |out|) exceeds the 2e-3 bar."""
+    m = rng.random(k.shape) < frac
+    k[m] = (k[m].astype(np.float32) * scale).astype(np.float16)
+    return k, v
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_outlier_append_bit_exact(fmt):
+    require_gpu()
+    rng = np.random.default_rng(1)
+    b, hkv, r, s = 2, 2, 32, 3
+    n = 32 * 9 + r + s + 11
+    k, v = _spiky(*synth.kv_tokens(W["llama3_8b"], 90, 91, b, n, hkv, 128), rng)
+    k[0, 40:72, 1, 5] = np.float16(3.0)                  # a constant channel group with ties
+    kw = _kw(fmt, b, hkv, 2, n + 40, r, s)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [n - 25] + [1] * 25)
+    olay = olayout_of(kw)
+    assert_states_equal(read_state(c, olay), ocache.build_cache(k, v, olay))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("nrep", [1, 4, 8])
+def test_outlier_attention(fmt, nrep):
+    require_gpu()
+    rng = np.random.default_rng(nrep)
+    b, hkv, r, s = 2, 2, 32, 4
+    n = 32 * 45 + r + s + 13
+    k, v = _spiky(*synth.kv_tokens(W["llama3_8b"], 92 + nrep, 93, b, n, hkv, 128), rng)
+    kw = _kw(fmt, b, hkv, nrep, n + 64, r, s)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [n])
+    q = synth.queries(W["llama3_8b"], b, hkv * nrep, 128, seed_offset=nrep)
+    st = read_state(c, olayout_of(kw))
+    assert_states_equal(st, ocache.build_cache(k, v, olayout_of(kw)))
+    kh, vh = ocache.dequantize(st)
+    ref = oattn.attention(q, kh, vh)
+    outs = []
+    for bpg, det in ((0, False), (3, True), (0, True)):
+        out = attention_gpu(c, q, bpg, det)
+        assert np.max(np.abs(out.astype(np.float64) - ref)) <= TOL, (bpg, det)
+        outs.append(out)
+    again = attention_gpu(c, q, 0, True)
+    assert np.array_equal(again.view(np.uint16), outs[2].view(np.uint16))      # deterministic mode repeats
+
+
+def test_outliers_improve_a_spiky_cache():
+    """With large scattered values the outlier split lowers the attention error of INT2."""
+    require_gpu()
+    rng = np.random.default_rng(7)
+    b, hkv, nrep, r = 1, 2, 4, 32
+    n = 32 * 30 + r
+    k, v = _spiky(*synth.kv_tokens(W["llama3_8b"], 97, 98, b, n, hkv, 128), rng, frac=0.02, scale=60.0)
+    q = synth.queries(W["llama3_8b"], b, hkv * nrep, 128, seed_offset=2)
+    full = oattn.attention(q, np.transpose(k, (0, 2, 1, 3)).astype(np.float64),
+                           np.transpose(v, (0, 2, 1, 3)).astype(np.float64))
+    errs = {}
+    for out_flag in (False, True):
+        kw = _kw("int2", b, hkv, nrep, n, r, 0, outliers=out_flag)
+        c = make_cache(kw)
+        append_chunks(c, k, v, [n])
+        errs[out_flag] = float(np.max(np.abs(attention_gpu(c, q).astype(np.float64) - full)))
+    assert errs[True] < errs[False]
+
+
+def test_outliers_in_a_paged_cache():
+    require_gpu()
+    rng = np.random.default_rng(11)
+    b, hkv, nrep, r = 2, 2, 4, 32
+    n = 32 * 12 + r + 5
+    k, v = _spiky(*synth.kv_tokens(W["llama3_8b"], 99, 100, b, n, hkv, 128), rng)
+    pps = (n + 32 - r) // 32
+    table = rng.permutation(b * pps + 3)[:b * pps].reshape(b, pps).astype(np.int32)
+    kw = _kw("int4", b, hkv, nrep, n + 32, r, 0, page_blocks=1, num_pages=b * pps + 3)
+    c = make_cache(kw)
+    c.set_block_table(torch.from_numpy(table).cuda())
+    append_chunks(c, k, v, [n])
+    st = read_state(c, olayout_of(kw))
+    assert_states_equal(st, ocache.build_cache(k, v, olayout_of(kw)))
+    q = synth.queries(W["llama3_8b"], b, hkv * nrep, 128, seed_offset=4)
+    kh, vh = ocache.dequantize(st)
+    assert np.max(np.abs(attention_gpu(c, q).astype(np.float64) - oattn.attention(q, kh, vh))) <= TOL
+
+
+def test_full_size_outliers_int4():
+    """The 70B shape (batch 16, 8192 tokens, n_rep 8, 4 sinks) with outliers."""
+    require_gpu()
+    w = W["llama3_70b"]
+    k, v = synth.prefill(w)
+    kw = _kw("int4", w.batch, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.seq_len + 32,
+             w.residual_tokens, w.sink_tokens)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [w.seq_len])
+    q = synth.queries(w)
+    out = attention_gpu(c, q)
+    st = read_state(c, olayout_of(kw))
+    nrep = w.num_q_heads // w.num_kv_heads
+    rng = np.random.default_rng(3)
+    for bi, gi in rng.integers(0, [w.batch, w.num_kv_heads], size=(3, 2)):
+        one = substate(st, bi, gi)
+        exp = ocache.build_cache(k[bi:bi + 1, :, gi:gi + 1], v[bi:bi + 1, :, gi:gi + 1], one.layout)
+        assert_states_equal(one, exp)
+        hs = slice(gi * nrep, (gi + 1) * nrep)
+        kh, vh = ocache.dequantize(one)
+        assert np.max(np.abs(out[bi:bi + 1, hs].astype(np.float64) - oattn.attention(q[bi:bi + 1, hs], kh, vh))) <= TOL
