@@ -171,8 +171,10 @@ struct Traits {
   // per wavefront: INT8 10 KiB, FP8 16 KiB, INT4 18 KiB, INT2 16 KiB; the
   // counts keep every format at or under 256 VGPRs, two wavefronts per SIMD)
   static constexpr int kDepthBase = kFp8 ? KVQ_DEPTH_FP8 : (kBits == 8 ? KVQ_DEPTH_INT8 : (kBits == 4 ? KVQ_DEPTH_INT4 : KVQ_DEPTH_INT2));
-  // the rotation's temporaries leave room for at most two blocks in flight
-  static constexpr int kDepth = ((kRope || kOut) && kDepthBase > 2) ? 2 : kDepthBase;
+  // the rotation's temporaries leave room for at most two blocks in flight,
+  // the outlier corrections' for two (INT4) or three (INT2)
+  static constexpr int kDepthCap = kRope ? 2 : (kOut ? (kBits == 2 ? 3 : 2) : kDepthBase);
+  static constexpr int kDepth = kDepthBase < kDepthCap ? kDepthBase : kDepthCap;
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -299,7 +301,18 @@ constexpr float kLazyScaleMax = 255.0f;
 // LDS staging area of one wavefront for one block (floats):
 //   [0,128) K scale / slot divisor   [128,256) K s*z
 //   [256,384) V scale / divisor [g][t]   [384,512) V s*z [g][t]
+// and with outliers (see stage_meta)
+//   [512,640) K outlier corrections (slot order)   [640,768) V outlier corrections [g][t]
+//   [768,832) K outlier tokens (16-bit, slot order)   [832,896) V outlier channels (16-bit)
 constexpr int kStage = 512;
+constexpr int kOutKd = 512, kOutVd = 640, kOutKx = 768, kOutVx = 832;
+// Outlier corrections go through the matrix cores as (one-hot) x (q or p times
+// the correction): the one-hot operand holds 2^kOhShift * 2^-24 (an f16
+// subnormal, like the codes) and the staged corrections carry 2^-kOhShift,
+// which keeps p * correction inside the f16 range.  Staged indices carry the
+// same shift, so index ^ (token << kOhShift) is either 0 or >= 2^kOhShift.
+constexpr int kOhShift = 8;
+constexpr float kOhScale = 1.0f / 256.0f;
 
 // Slot (see k_slot) of within-quarter channel w, by formula.
 template <int FMT>
@@ -347,8 +360,16 @@ __device__ __forceinline__ float2 pair_scales(const float4& m) {
 // Pre-RoPE Keys are dequantized before the rotation instead: their staged
 // Key values are s * 2^24 / slot divisor and the offset -s * z (= m for
 // fp16 pairs), so that k_hat = operand value * [0] + [128].
+// Outliers: a Key outlier x at (token t, channel c) adds q_c (x - x_hat(0))
+// to the logit of t, x_hat(0) being what code 0 decodes to; a Value outlier
+// at (t, c) adds p_t (x - x_hat(0)) to output channel c.  The corrections
+// x - x_hat(0) (Keys: in logit units) times 2^-kOhShift go to [512 + slot]
+// and [640 + g * 32 + t]; the Key outlier tokens to 16-bit [slot], the Value
+// outlier channels to 16-bit [g * 32 + 2 (t % 16) + t / 16] (the Value
+// operand pairs tokens t and t + 16), all shifted up by kOhShift.  Returns
+// the largest |Value correction| of the lane's entries (0 without outliers).
 template <int FMT>
-__device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lane) {
+__device__ __forceinline__ float stage_meta(const Raw<FMT>& r, float* st, int lane) {
   const int c = 2 * lane;                 // K stored position; V index g * 32 + t
   const int t = c & 31;
   constexpr bool kRopeK = Traits<FMT>::kRope;
@@ -385,6 +406,31 @@ __device__ __forceinline__ void stage_meta(const Raw<FMT>& r, float* st, int lan
   }
   *reinterpret_cast<float2*>(st + 256 + c) = vs;
   *reinterpret_cast<float2*>(st + 384 + c) = vz;
+  if constexpr (Traits<FMT>::kOut) {
+    auto value = [](uint32_t e) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16)); };
+    uint16_t* kx = reinterpret_cast<uint16_t*>(st + kOutKx);
+    uint16_t* vx = reinterpret_cast<uint16_t*>(st + kOutVx);
+    st[kOutKd + q0] = __builtin_fmaf(value(r.ko.x), kQScale, kz0) * kOhScale;
+    st[kOutKd + q1] = __builtin_fmaf(value(r.ko.y), kQScale, kz1) * kOhScale;
+    kx[q0] = (uint16_t)((r.ko.x & 31u) << kOhShift);
+    kx[q1] = (uint16_t)((r.ko.y & 31u) << kOhShift);
+    const float d0 = value(r.vo.x) + vz.x, d1 = value(r.vo.y) + vz.y;
+    *reinterpret_cast<float2*>(st + kOutVd + c) = float2{d0 * kOhScale, d1 * kOhScale};
+    const int pv = (c & ~31) + 2 * (t & 15) + (t >> 4);    // token t + 1 lands at pv + 2
+    vx[pv] = (uint16_t)((r.vo.x & 31u) << kOhShift);
+    vx[pv + 2] = (uint16_t)((r.vo.y & 31u) << kOhShift);
+    return fmaxf(fabsf(d0), fabsf(d1));
+  }
+  return 0.f;
+}
+
+// One-hot operand word: for two slots, 2^kOhShift (as f16 bits) where the
+// staged index equals the row's own (both shifted by kOhShift), else 0.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t one_hot(uint32_t idx, uint32_t own) {
+  const u16x2 x = __builtin_bit_cast(u16x2, idx ^ own);
+  const u16x2 top = {1u << kOhShift, 1u << kOhShift};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(top, x));
 }
 
 struct WaveState {
@@ -501,8 +547,6 @@ __device__ __forceinline__ float2 rope_cs(double pos, double freq) {
 // In-block offsets (cos, sin)(k * theta_i), k < 32, i < 64, shared by the
 // workgroup in LDS: entry 64 k + i.
 constexpr int kRopeTableBytes = 32 * 64 * 8;
-// Outliers: per-wavefront query pairs [64 lanes][8 heads] (32-bit each).
-constexpr int kOutQBytes = 64 * 8 * 4;
 
 // Query of this lane's column head (its quarter's 32 channels) from a KV
 // head's n_rep query rows ([n_rep][128] fp16): packed f16 pairs in Key
@@ -579,11 +623,7 @@ __device__ __forceinline__ void static_q(const QOp& q, float scale, f16x8* bk) {
 
 // Online softmax over one block's 32 tokens (this lane: 8 of them, logits
 // lg[tile][i] for tokens 16*tile + 4qd + i); returns p = 2^(lg - m).
-// vacc (outliers only): the wavefront's Value outlier sums [8 heads][128
-// channels] in LDS, rescaled with the accumulators; lane (qd, col < 8)
-// rescales head col's channels 32qd .. 32qd + 31.
-__device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, float pr[2][4], float slack,
-                                              float* vacc = nullptr) {
+__device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, float pr[2][4], float slack) {
   float mx = neg_inf();
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
@@ -599,18 +639,6 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
     ws.z[1] *= alpha;
     ws.l *= alpha;
     ws.m = m_new;
-    if (vacc) {
-      const int lane = threadIdx.x & 63;
-      if ((lane & 15) < 8) {
-        float4* a = reinterpret_cast<float4*>(vacc + (lane & 7) * kHeadDim + 32 * (lane >> 4));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float4 x = a[i];
-          x.x *= alpha; x.y *= alpha; x.z *= alpha; x.w *= alpha;
-          a[i] = x;
-        }
-      }
-    }
   }
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
@@ -655,29 +683,17 @@ __device__ constexpr bool pair_first(int j) {
   return (kind_of(FMT) == KVQ_INT4 || kind_of(FMT) == KVQ_INT2) ? ((j & 2) == 0) : ((j & 1) == 0);
 }
 
-// Dense-and-sparse outliers: per-wavefront LDS areas and the query values
-// the corrections need.  A Key outlier x at (token t, channel c) adds
-// q_c (x - x_hat(0)) to the logit of t, x_hat(0) being what code 0 decodes
-// to; a Value outlier at (t, c) adds p_t (x - x_hat(0)) to output channel c.
-struct OutCtx {
-  float* kc;        // [8 heads][32 tokens] logit corrections of the block
-  float* pst;       // [8 heads][32 tokens] p of the block
-                    // (token-minor: the lanes of one atomic spread over the banks)
-  float* vacc;      // [8 heads][128 channels] Value corrections of the segment
-  uint32_t* qst;    // [64 lanes][8 heads]: channels 2 lane, 2 lane + 1 of each query head
-                    // (packed f16, zero past n_rep), written when a segment starts
-};
-
 // t0: position of the block's first token (pre-RoPE Keys only).
 template <int FMT>
 __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, WaveState& ws, const QOp& q,
                                               const f16x8* bk_static, const LaneInfo& li, const RopeCtx& rc,
-                                              double t0, const OutCtx& oc) {
+                                              double t0) {
   using T = Traits<FMT>;
   const int qd = li.qd;
 
   // ---- QK: Key codes (rows = tokens) x q' (columns)
   f32x4 acc[2];
+  float vbig = 0.f;          // outliers: largest |Value correction| of the lane's entries
   if constexpr (T::kRope) {
     // Keys are dequantized, rotated at their positions t0 + token and split
     // into hi / lo f16 operands; the query operand is static (q, hi / lo
@@ -740,27 +756,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bk_static[kb],
                                                            acc[tile], 0, 0, 0);
   } else {
-    stage_meta<FMT>(r, st, li.lane);
-    if constexpr (T::kOut) {
-      // Key outliers of channels 2 lane, 2 lane + 1 into the block's logit
-      // corrections (logit units: log2(e) / sqrt(D) included); staged
-      // [128 + slot] is that unit times s z (or -m), i.e. -x_hat(0)
-      reinterpret_cast<float4*>(oc.kc)[li.lane] = float4{0.f, 0.f, 0.f, 0.f};
-      const uint4 qa = reinterpret_cast<const uint4*>(oc.qst)[2 * li.lane];
-      const uint4 qb = reinterpret_cast<const uint4*>(oc.qst)[2 * li.lane + 1];
-      const uint32_t qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-      const uint32_t ent[2] = {r.ko.x, r.ko.y};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = 2 * li.lane + u;
-        const int t = (int)(ent[u] & 31u);
-        const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)(ent[u] >> 16));
-        const float d = __builtin_fmaf(x, kQScale, st[128 + (c & ~31) + k_slot_of<FMT>(c & 31)]);
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-          if (h < li.nrep) atomicAdd(oc.kc + h * 32 + t, (float)u2h(qv[h])[u] * d);
-      }
-    }
+    vbig = stage_meta<FMT>(r, st, li.lane);
     // zero-point term sum_c q_c s_c z_c over this lane's 32 channels (in
     // slot order), then over the four quarters
     float bias0 = 0.f, bias1 = 0.f;
@@ -790,6 +786,24 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bq, acc[tile], 0,
                                                            0, 0);
+      if constexpr (T::kOut) {
+        // Key outliers: one-hot (token row, channel slot) x q times the
+        // staged correction, into the same accumulators
+        const float4 da = *reinterpret_cast<const float4*>(st + kOutKd + 32 * qd + 8 * kb);
+        const float4 db = *reinterpret_cast<const float4*>(st + kOutKd + 32 * qd + 8 * kb + 4);
+        const uint32_t e0 = split_q<false>(q.z[4 * kb], q.h[4 * kb], da.x, da.y, 0u);
+        const uint32_t e1 = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], da.z, da.w, e0);
+        const uint32_t e2 = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], db.x, db.y, e1);
+        const uint32_t e3 = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], db.z, db.w, e2);
+        const f16x8 bd = cat(e0, e1, e2, e3);
+        const uint4 ix = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutKx) + 32 * qd + 8 * kb);
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          const uint32_t own = (uint32_t)(16 * tile + (li.lane & 15)) * (0x10001u << kOhShift);
+          const f16x8 oh = cat(one_hot(ix.x, own), one_hot(ix.y, own), one_hot(ix.z, own), one_hot(ix.w, own));
+          acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oh, bd, acc[tile], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -798,47 +812,13 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * (T::kRope ? 1.0f : T::kCodeScale);
-  if constexpr (T::kOut) {
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lg[tile][i] += oc.kc[(li.lane & 7) * 32 + 16 * tile + 4 * qd + i];
-  }
   float slack = kSlack;
   if constexpr (!T::kFp8) {
     const float2 sv = pair_scales<FMT>(r.vm);
-    if (__any(sv.x > kLazyScaleMax || sv.y > kLazyScaleMax)) slack = 0.f;
+    // (outliers: p times the staged correction, at most p * |correction| / 2^8)
+    if (__any(sv.x > kLazyScaleMax || sv.y > kLazyScaleMax || vbig > kLazyScaleMax * 256.0f)) slack = 0.f;
   }
-  softmax_block(lg, ws, pr, slack, T::kOut ? oc.vacc : nullptr);
-
-  if constexpr (T::kOut) {
-    // Value outliers: entries 2 lane, 2 lane + 1 ([group][token] order, as
-    // the staged V meta) add p_t (x - x_hat(0)) to the segment's sums;
-    // staged [384 + entry] is s z (or -m), i.e. -x_hat(0)
-    if ((li.lane & 15) < 8) {
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oc.pst[(li.lane & 7) * 32 + 16 * tile + 4 * qd + i] = pr[tile][i];
-    }
-    const uint32_t ent[2] = {r.vo.x, r.vo.y};
-    float pv[2][8], dv[2];
-    int cv[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {               // all reads first, then the atomics
-      const int e = 2 * li.lane + u;
-      const int t = e & 31;
-      cv[u] = 32 * (e >> 5) + (int)(ent[u] & 31u);
-      dv[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ent[u] >> 16)) + st[384 + e];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) pv[u][h] = oc.pst[h * 32 + t];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int h = 0; h < 8; ++h)
-        if (h < li.nrep) atomicAdd(oc.vacc + h * kHeadDim + cv[u], pv[u][h] * dv[u]);
-  }
+  softmax_block(lg, ws, pr, slack);
 
   // ---- PV: Value codes (rows = channels) x P' (columns)
   if constexpr (T::kFp8) {
@@ -883,6 +863,25 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
         const int m = 2 * g + mm;
         ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.v, m), bp, ws.o[m], 0, 0, 0);
       }
+      if constexpr (T::kOut) {
+        // Value outliers of group g: one-hot (channel row, token slot) x p
+        // times the staged correction
+        const float4 d0 = *reinterpret_cast<const float4*>(st + kOutVd + 32 * g + 4 * qd);
+        const float4 d1 = *reinterpret_cast<const float4*>(st + kOutVd + 32 * g + 16 + 4 * qd);
+        uint32_t cw[4];
+        cw[0] = split_p<false>(pr[0][0], pb[0][0], d0.x, pr[1][0], pb[1][0], d1.x, 0u);
+        cw[1] = split_p<false>(pr[0][1], pb[0][1], d0.y, pr[1][1], pb[1][1], d1.y, cw[0]);
+        cw[2] = split_p<false>(pr[0][2], pb[0][2], d0.z, pr[1][2], pb[1][2], d1.z, cw[1]);
+        cw[3] = split_p<true>(pr[0][3], pb[0][3], d0.w, pr[1][3], pb[1][3], d1.w, cw[2]);
+        const f16x8 bd = cat(cw[0], cw[1], cw[2], cw[3]);
+        const uint4 ix = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutVx) + 32 * g + 8 * qd);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const uint32_t own = (uint32_t)(16 * mm + (li.lane & 15)) * (0x10001u << kOhShift);
+          const f16x8 oh = cat(one_hot(ix.x, own), one_hot(ix.y, own), one_hot(ix.z, own), one_hot(ix.w, own));
+          ws.o[2 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oh, bd, ws.o[2 * g + mm], 0, 0, 0);
+        }
+      }
     }
   }
 }
@@ -890,7 +889,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 // Sums over quarters and hi + lo columns, then writes one partial slot:
 // m, l, o[128] per query head (o unnormalised).
 __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneInfo& li, float* slot, float oscale,
-                                               bool has_z, const float* vacc = nullptr) {
+                                               bool has_z) {
   const float l = rows_sum(ws.l);
   float zs[4] = {0.f, 0.f, 0.f, 0.f};
   if (has_z) {
@@ -906,10 +905,6 @@ __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneIn
     o.y = (ws.o[m][1] + ror8(ws.o[m][1])) * oscale - zs[m >> 1];
     o.z = (ws.o[m][2] + ror8(ws.o[m][2])) * oscale - zs[m >> 1];
     o.w = (ws.o[m][3] + ror8(ws.o[m][3])) * oscale - zs[m >> 1];
-    if (vacc && li.writer) {                  // Value outlier sums of channels 16m + 4qd .. + 3
-      const float4 a = *reinterpret_cast<const float4*>(vacc + li.head * kHeadDim + 16 * m + 4 * li.qd);
-      o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
-    }
     if (li.writer) *reinterpret_cast<float4*>(dst + 4 + 16 * m + 4 * li.qd) = o;
   }
   if (li.writer && li.qd == 0) {
@@ -1053,7 +1048,7 @@ constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : 
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
 static_assert(kWaveLds >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
-static_assert(kWaveLds >= 2176 * 4, "stage area holds the outlier sums after the block metadata");
+static_assert(kWaveLds >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
 // touching heads h0..h1.
@@ -1209,30 +1204,6 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     WaveState ws;
     reset(ws);
     int cur = -1;
-    // outliers: the stage area after the block metadata holds the segment's
-    // Value sums [640, 1664), the block's logit corrections [1664, 1920) and
-    // its p [1920, 2176) (floats)
-    OutCtx oc{};
-    if constexpr (T::kOut) {
-      oc.vacc = stage + 640;
-      oc.kc = stage + 1664;
-      oc.pst = stage + 1920;
-      oc.qst = reinterpret_cast<uint32_t*>(lds + kLdsBytes + v * kOutQBytes);
-    }
-    // A new segment clears the Value sums and stores the query pairs in LDS;
-    // the loads are consumed here, so their wait stays on this path
-    auto start_segment = [&](int64_t bh) {
-      if constexpr (T::kOut) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<float4*>(oc.vacc)[li.lane + 64 * i] = float4{0.f, 0.f, 0.f, 0.f};
-        uint32_t qv[8];
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-          qv[h] = h < p.nrep ? reinterpret_cast<const uint32_t*>(p.q + (bh * p.nrep + h) * kHeadDim)[li.lane] : 0u;
-        reinterpret_cast<uint4*>(oc.qst)[2 * li.lane] = uint4{qv[0], qv[1], qv[2], qv[3]};
-        reinterpret_cast<uint4*>(oc.qst)[2 * li.lane + 1] = uint4{qv[4], qv[5], qv[6], qv[7]};
-      }
-    };
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
@@ -1240,11 +1211,10 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         if (rid[d] < 0) goto done;           // blocks are taken in order: none left
         if (rbh[d] != cur) {
           if (cur >= 0) {
-            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8, T::kOut ? oc.vacc : nullptr);
+            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
             reset(ws);
           }
           cur = rbh[d];
-          start_segment(cur);
           if (cur != qhead) {
             load_query<FMT>(p, cur, li, qop);
             qhead = cur;
@@ -1252,11 +1222,11 @@ __device__ void group_main(const AttnParams& p, char* lds) {
           if constexpr (T::kFp8 || T::kRope) static_q(qop, T::kFp8 ? p.k_scale * kQScale : kQScale, bk_static);
         }
         process_block<FMT>(buf[d], stage, ws, qop, bk_static, li, rc,
-                           (double)p.sink_cap + (double)kBlock * rblk[d], oc);
+                           (double)p.sink_cap + (double)kBlock * rblk[d]);
       }
     }
   done:
-    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8, T::kOut ? oc.vacc : nullptr);
+    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
   }
   __syncthreads();                            // every wavefront's partials written
 
@@ -1322,7 +1292,7 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
 template <int FMT>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16)))
-  char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0) + (Traits<FMT>::kOut ? kGroupWaves * kOutQBytes : 0)];
+  char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
   else group_main<FMT>(p, lds);
 }
