@@ -476,42 +476,67 @@ __device__ __forceinline__ void reset(WaveState& ws) {
 // a * b - c once to f16; its operands may be fp32 or a half of a packed f16
 // register (op_sel / op_sel_hi), so one instruction forms each half.
 //
-// The four words of one operand feed a matrix-core instruction, and the
-// compiler does not count inline assembly as a vector write when it spaces a
+// One asm statement forms all four words of an operand (16 instructions, in
+// four independent waves of four).  The compiler pads between dependent asm
+// statements and does not count asm as a vector write when it spaces a
 // vector write from a matrix-core read of the same register (two wait
-// states).  So the four splits of an operand are chained (each one's first
-// instruction takes the previous result as an unused input, so they issue in
-// order) and the last one ends with s_nop 1: every word is then at least two
-// wait states old when the operand is read.
+// states), so the statement ends with s_nop 1: every word is then at least
+// two wait states old when the operand is read.
 
-// x = q * s for two channels: q from packed f16 (both halves of qh, and of
-// qz = qh in lo columns, 0 in hi columns), s0 / s1 fp32.  dep: the previous
-// split of the operand (ordering only).
-template <bool LAST>
-__device__ __forceinline__ uint32_t split_q(uint32_t qz, uint32_t qh, float s0, float s1, uint32_t dep) {
-  uint32_t hz, r;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(hz) : "v"(qz), "v"(s0), "v"(dep));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(hz) : "v"(qz), "v"(s1));
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(qh), "v"(s0), "v"(hz));
-  if constexpr (LAST)
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\ts_nop 1" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
-  else
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "+v"(r) : "v"(qh), "v"(s1), "v"(hz));
-  return r;
+// x = q * s for eight channels: q from packed f16 (both halves of qh[j], and
+// of qz[j] = qh[j] in lo columns, 0 in hi columns), s[2j], s[2j + 1] fp32.
+__device__ __forceinline__ f16x8 split_q4(const uint32_t* qz, const uint32_t* qh, float4 sa, float4 sb) {
+  uint32_t r0, r1, r2, r3, h0, h1, h2, h3;
+  asm("v_fma_mixlo_f16 %4, %8, %16, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %5, %9, %18, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %6, %10, %20, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %7, %11, %22, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %4, %8, %17, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %5, %9, %19, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %6, %10, %21, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %7, %11, %23, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %0, %12, %16, -%4 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %13, %18, -%5 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %14, %20, -%6 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %15, %22, -%7 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %12, %17, -%4 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %13, %19, -%5 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %14, %21, -%6 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %15, %23, -%7 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3)
+      : "v"(qz[0]), "v"(qz[1]), "v"(qz[2]), "v"(qz[3]), "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]),
+        "v"(sa.x), "v"(sa.y), "v"(sa.z), "v"(sa.w), "v"(sb.x), "v"(sb.y), "v"(sb.z), "v"(sb.w));
+  return cat(r0, r1, r2, r3);
 }
 
-// x = a * b for two values, all fp32; az = a in lo columns, 0 in hi columns.
-template <bool LAST>
-__device__ __forceinline__ uint32_t split_p(float a0, float az0, float b0, float a1, float az1, float b1, uint32_t dep) {
-  uint32_t hz, r;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(hz) : "v"(az0), "v"(b0), "v"(dep));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(hz) : "v"(az1), "v"(b1));
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a0), "v"(b0), "v"(hz));
-  if constexpr (LAST)
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\ts_nop 1" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
-  else
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(a1), "v"(b1), "v"(hz));
-  return r;
+// x = a * b for eight values, all fp32: word j holds (a0[j] b0[j], a1[j] b1[j]);
+// az = a in lo columns, 0 in hi columns.
+__device__ __forceinline__ f16x8 split_p4(const float* a0, const float* az0, const float* b0, const float* a1,
+                                          const float* az1, const float* b1) {
+  uint32_t r0, r1, r2, r3, h0, h1, h2, h3;
+  asm("v_fma_mixlo_f16 %4, %12, %16, 0\n\t"
+      "v_fma_mixlo_f16 %5, %13, %17, 0\n\t"
+      "v_fma_mixlo_f16 %6, %14, %18, 0\n\t"
+      "v_fma_mixlo_f16 %7, %15, %19, 0\n\t"
+      "v_fma_mixhi_f16 %4, %24, %28, 0\n\t"
+      "v_fma_mixhi_f16 %5, %25, %29, 0\n\t"
+      "v_fma_mixhi_f16 %6, %26, %30, 0\n\t"
+      "v_fma_mixhi_f16 %7, %27, %31, 0\n\t"
+      "v_fma_mixlo_f16 %0, %8, %16, -%4 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %9, %17, -%5 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %10, %18, -%6 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %11, %19, -%7 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %20, %28, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %21, %29, -%5 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %22, %30, -%6 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %23, %31, -%7 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3)
+      : "v"(a0[0]), "v"(a0[1]), "v"(a0[2]), "v"(a0[3]), "v"(az0[0]), "v"(az0[1]), "v"(az0[2]), "v"(az0[3]),
+        "v"(b0[0]), "v"(b0[1]), "v"(b0[2]), "v"(b0[3]), "v"(a1[0]), "v"(a1[1]), "v"(a1[2]), "v"(a1[3]),
+        "v"(az1[0]), "v"(az1[1]), "v"(az1[2]), "v"(az1[3]), "v"(b1[0]), "v"(b1[1]), "v"(b1[2]), "v"(b1[3]));
+  return cat(r0, r1, r2, r3);
 }
 
 // hi / lo pair of a fully fp32 operand (both parts in every lane):
@@ -612,12 +637,8 @@ __device__ __forceinline__ void load_query(const AttnParams& p, int64_t bh, cons
 __device__ __forceinline__ void static_q(const QOp& q, float scale, f16x8* bk) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    uint32_t bw[4];
-    bw[0] = split_q<false>(q.z[4 * kb], q.h[4 * kb], scale, scale, 0u);
-    bw[1] = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], scale, scale, bw[0]);
-    bw[2] = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], scale, scale, bw[1]);
-    bw[3] = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], scale, scale, bw[2]);
-    bk[kb] = cat(bw[0], bw[1], bw[2], bw[3]);
+    const float4 sc{scale, scale, scale, scale};
+    bk[kb] = split_q4(q.z + 4 * kb, q.h + 4 * kb, sc, sc);
   }
 }
 
@@ -658,11 +679,8 @@ __device__ __forceinline__ f16x8 p_operand(const float pr[2][4], const LaneInfo&
     z[0][v] = li.is_lo ? pr[0][v] : 0.f;
     z[1][v] = li.is_lo ? pr[1][v] : 0.f;
   }
-  const uint32_t b0 = split_p<false>(pr[0][0], z[0][0], 1.0f, pr[1][0], z[1][0], 1.0f, 0u);
-  const uint32_t b1 = split_p<false>(pr[0][1], z[0][1], 1.0f, pr[1][1], z[1][1], 1.0f, b0);
-  const uint32_t b2 = split_p<false>(pr[0][2], z[0][2], 1.0f, pr[1][2], z[1][2], 1.0f, b1);
-  const uint32_t b3 = split_p<true>(pr[0][3], z[0][3], 1.0f, pr[1][3], z[1][3], 1.0f, b2);
-  return cat(b0, b1, b2, b3);
+  const float one[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  return split_p4(pr[0], z[0], one, pr[1], z[1], one);
 }
 
 // Pre-RoPE Keys: this lane's RoPE frequency (theta_lane, for the block base
@@ -777,11 +795,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
     for (int kb = 0; kb < 4; ++kb) {
       const float4 sa = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb);
       const float4 sb = *reinterpret_cast<const float4*>(st + 32 * qd + 8 * kb + 4);
-      const uint32_t b0 = split_q<false>(q.z[4 * kb], q.h[4 * kb], sa.x, sa.y, 0u);
-      const uint32_t b1 = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], sa.z, sa.w, b0);
-      const uint32_t b2 = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], sb.x, sb.y, b1);
-      const uint32_t b3 = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], sb.z, sb.w, b2);
-      const f16x8 bq = cat(b0, b1, b2, b3);
+      const f16x8 bq = split_q4(q.z + 4 * kb, q.h + 4 * kb, sa, sb);
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(r.k[tile], kb), bq, acc[tile], 0,
@@ -791,11 +805,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
         // staged correction, into the same accumulators
         const float4 da = *reinterpret_cast<const float4*>(st + kOutKd + 32 * qd + 8 * kb);
         const float4 db = *reinterpret_cast<const float4*>(st + kOutKd + 32 * qd + 8 * kb + 4);
-        const uint32_t e0 = split_q<false>(q.z[4 * kb], q.h[4 * kb], da.x, da.y, 0u);
-        const uint32_t e1 = split_q<false>(q.z[4 * kb + 1], q.h[4 * kb + 1], da.z, da.w, e0);
-        const uint32_t e2 = split_q<false>(q.z[4 * kb + 2], q.h[4 * kb + 2], db.x, db.y, e1);
-        const uint32_t e3 = split_q<true>(q.z[4 * kb + 3], q.h[4 * kb + 3], db.z, db.w, e2);
-        const f16x8 bd = cat(e0, e1, e2, e3);
+        const f16x8 bd = split_q4(q.z + 4 * kb, q.h + 4 * kb, da, db);
         const uint4 ix = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutKx) + 32 * qd + 8 * kb);
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -852,12 +862,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       const float4 s1 = *reinterpret_cast<const float4*>(st + 256 + 32 * g + 16 + 4 * qd);
       const float sv0[4] = {s0.x, s0.y, s0.z, s0.w};
       const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
-      uint32_t bw[4];
-      bw[0] = split_p<false>(pr[0][0], pb[0][0], sv0[0], pr[1][0], pb[1][0], sv1[0], 0u);
-      bw[1] = split_p<false>(pr[0][1], pb[0][1], sv0[1], pr[1][1], pb[1][1], sv1[1], bw[0]);
-      bw[2] = split_p<false>(pr[0][2], pb[0][2], sv0[2], pr[1][2], pb[1][2], sv1[2], bw[1]);
-      bw[3] = split_p<true>(pr[0][3], pb[0][3], sv0[3], pr[1][3], pb[1][3], sv1[3], bw[2]);
-      const f16x8 bp = cat(bw[0], bw[1], bw[2], bw[3]);
+      const f16x8 bp = split_p4(pr[0], pb[0], sv0, pr[1], pb[1], sv1);
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const int m = 2 * g + mm;
@@ -868,12 +873,8 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
         // times the staged correction
         const float4 d0 = *reinterpret_cast<const float4*>(st + kOutVd + 32 * g + 4 * qd);
         const float4 d1 = *reinterpret_cast<const float4*>(st + kOutVd + 32 * g + 16 + 4 * qd);
-        uint32_t cw[4];
-        cw[0] = split_p<false>(pr[0][0], pb[0][0], d0.x, pr[1][0], pb[1][0], d1.x, 0u);
-        cw[1] = split_p<false>(pr[0][1], pb[0][1], d0.y, pr[1][1], pb[1][1], d1.y, cw[0]);
-        cw[2] = split_p<false>(pr[0][2], pb[0][2], d0.z, pr[1][2], pb[1][2], d1.z, cw[1]);
-        cw[3] = split_p<true>(pr[0][3], pb[0][3], d0.w, pr[1][3], pb[1][3], d1.w, cw[2]);
-        const f16x8 bd = cat(cw[0], cw[1], cw[2], cw[3]);
+        const float dv0[4] = {d0.x, d0.y, d0.z, d0.w}, dv1[4] = {d1.x, d1.y, d1.z, d1.w};
+        const f16x8 bd = split_p4(pr[0], pb[0], dv0, pr[1], pb[1], dv1);
         const uint4 ix = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutVx) + 32 * g + 8 * qd);
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
