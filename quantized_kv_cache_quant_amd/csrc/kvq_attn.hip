@@ -1078,6 +1078,11 @@ __device__ __forceinline__ int64_t covering_count(const AttnParams& p, int64_t h
 
 __device__ __forceinline__ int64_t slot_floats(const AttnParams& p) { return (int64_t)p.nrep * kPartStride; }
 
+// Head of flattened block j (j < 2^31): j / nblk by multiply and shift.
+__device__ __forceinline__ uint32_t head_of(const AttnParams& p, uint32_t j) {
+  return (uint32_t)(((uint64_t)j * p.nblk_magic) >> p.nblk_shift);
+}
+
 // The workgroup's wavefronts stream the blocks of its range: each keeps
 // kDepth blocks in flight beyond the one it processes and takes its next
 // block from a counter in LDS, so a wavefront that the memory system serves
@@ -1106,7 +1111,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   if (p.table) {
     for (int i = threadIdx.x; i < gr.len; i += kGroupThreads) {
       const int64_t j = gr.jb + i;
-      const int64_t bhj = j / nblk;
+      const int64_t bhj = head_of(p, (uint32_t)j);
       const int64_t r = block_record(p.table, p.table_stride, p.page_blocks, p.num_pages, p.hkv, p.nb_cap,
                                      bhj / p.hkv, bhj % p.hkv, j - bhj * nblk);
       recs[i] = r < 0 ? 0 : (int)r;
@@ -1132,7 +1137,8 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   // rid = block index within the range (-1 past its end), rbh = its head.
   // Loads past the end read block 0 of head 0 with ordinary loads: every
   // wavefront's surplus loads hit the same lines, which stay in the cache.
-  const uint32_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;
+  const uint64_t rot = ((uint32_t)g * 0x9E3779B9u) >> 12;     // a 20-bit fraction
+  const uint32_t jb = (uint32_t)gr.jb, je = (uint32_t)(gr.jb + gr.len);
   Raw<FMT> buf[D];
   int rid[D], rbh[D], rblk[D];
   int kst = 0;
@@ -1148,14 +1154,18 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     }
     if (idx < gr.len) {
       id = idx;
-      uint32_t j = (uint32_t)(gr.jb + idx);
-      const uint32_t bh = j / nblk;
-      // visit the blocks of each head's part of the range starting at a
-      // per-workgroup offset, so that the workgroups' streams sit at
-      // unrelated addresses rather than in step
-      const uint32_t ps = bh * nblk > (uint32_t)gr.jb ? bh * nblk : (uint32_t)gr.jb;
-      const uint32_t pe = (bh + 1) * nblk < (uint32_t)(gr.jb + gr.len) ? (bh + 1) * nblk : (uint32_t)(gr.jb + gr.len);
-      j = ps + (j - ps + rot) % (pe - ps);
+      uint32_t j = jb + (uint32_t)idx;
+      const uint32_t bh = head_of(p, j);
+      // visit the blocks of each head's part of the range (n blocks from ps)
+      // starting at a per-workgroup fraction of it, so that the workgroups'
+      // streams sit at unrelated addresses rather than in step:
+      // j -> ps + (j - ps + floor(rot n / 2^20)) mod n
+      const uint32_t ps = bh * nblk > jb ? bh * nblk : jb;
+      const uint32_t pe = (bh + 1) * nblk < je ? (bh + 1) * nblk : je;
+      const uint32_t n = pe - ps;
+      uint32_t x = j - ps + (uint32_t)((rot * n) >> 20);   // < 2n
+      x = x >= n ? x - n : x;
+      j = ps + x;
       bhout = (int)bh;
       blkout = (int)(j - bh * nblk);
       const int64_t rec = p.table ? (int64_t)__builtin_amdgcn_readfirstlane(recs[j - (uint32_t)gr.jb])

@@ -361,6 +361,16 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.nrep = L.num_q_heads / L.num_kv_heads;
   p.nb_cap = c->n_blocks_cap;
   p.nblk = (int32_t)nblk;
+  {
+    // multiply-shift division by d = nblk for dividends below 2^31: with
+    // 2^l >= d, m = ceil(2^(31+l) / d) < 2^32 and m d - 2^(31+l) < d, so
+    // floor(j m / 2^(31+l)) = floor(j / d) whenever j < 2^31
+    const uint64_t d = nblk > 0 ? (uint64_t)nblk : 1;
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    p.nblk_shift = 31 + l;
+    p.nblk_magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+  }
   p.ring_slots = c->ring_slots;
   p.sink_cap = L.sink_tokens;
   p.n_sink = (int32_t)w.n_sink;
