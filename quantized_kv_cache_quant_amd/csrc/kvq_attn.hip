@@ -299,7 +299,8 @@ constexpr float kSlack = 8.0f;
 constexpr float kLazyScaleMax = 255.0f;
 
 // LDS staging area of one wavefront for one block (floats):
-//   [0,128) K scale / slot divisor   [128,256) K s*z
+//   [0,128) K scale / slot divisor   [128,256) K s*z (pre-RoPE Keys: fp32;
+//   otherwise f16 hi / lo pairs, 16-bit [256 + slot] and [384 + slot])
 //   [256,384) V scale / divisor [g][t]   [384,512) V s*z [g][t]
 // and with outliers (see stage_meta)
 //   [512,640) K outlier corrections (slot order)   [640,768) V outlier corrections [g][t]
@@ -395,14 +396,36 @@ __device__ __forceinline__ float stage_meta(const Raw<FMT>& r, float* st, int la
   }
   const float ks0 = sq0 * (1.0f / slot_div<FMT>(c)), ks1 = sq1 * (1.0f / slot_div<FMT>(c + 1));
   const int q0 = (c & ~31) + k_slot_of<FMT>(c & 31), q1 = (c & ~31) + k_slot_of<FMT>((c + 1) & 31);
+  // Keys with a zero-point term: the term as an f16 hi / lo pair (hi at
+  // 16-bit [256 + slot], lo at [384 + slot]), so that the bias is formed
+  // with packed-f16 dot products against the query pairs
+  uint16_t* zst = reinterpret_cast<uint16_t*>(st);
+  auto zsplit = [](float x, uint16_t& h, uint16_t& l) {
+    const _Float16 xh = (_Float16)x;
+    h = __builtin_bit_cast(uint16_t, xh);
+    l = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)xh));
+  };
   if constexpr (kind_of(FMT) == KVQ_INT8) {
     *reinterpret_cast<float2*>(st + q0) = float2{ks0, ks1};
-    *reinterpret_cast<float2*>(st + 128 + q0) = float2{kz0, kz1};
+    if constexpr (kRopeK) {
+      *reinterpret_cast<float2*>(st + 128 + q0) = float2{kz0, kz1};
+    } else {
+      uint16_t h0, l0, h1, l1;
+      zsplit(kz0, h0, l0);
+      zsplit(kz1, h1, l1);
+      *reinterpret_cast<uint32_t*>(zst + 256 + q0) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      *reinterpret_cast<uint32_t*>(zst + 384 + q0) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
   } else {
     st[q0] = ks0;
     st[q1] = ks1;
-    st[128 + q0] = kz0;
-    st[128 + q1] = kz1;
+    if constexpr (kRopeK) {
+      st[128 + q0] = kz0;
+      st[128 + q1] = kz1;
+    } else {
+      zsplit(kz0, zst[256 + q0], zst[384 + q0]);
+      zsplit(kz1, zst[256 + q1], zst[384 + q1]);
+    }
   }
   *reinterpret_cast<float2*>(st + 256 + c) = vs;
   *reinterpret_cast<float2*>(st + 384 + c) = vz;
@@ -776,16 +799,20 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   } else {
     vbig = stage_meta<FMT>(r, st, li.lane);
     // zero-point term sum_c q_c s_c z_c over this lane's 32 channels (in
-    // slot order), then over the four quarters
+    // slot order; query pair k against the term's hi and lo pairs), then
+    // over the four quarters
     float bias0 = 0.f, bias1 = 0.f;
+    const uint4* zh = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st) + 256 + 32 * qd);
+    const uint4* zl = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st) + 384 + 32 * qd);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 z4 = *reinterpret_cast<const float4*>(st + 128 + 32 * qd + 4 * i);
-      const f16x2 qa = u2h(q.h[2 * i]), qb = u2h(q.h[2 * i + 1]);
-      bias0 = __builtin_fmaf((float)qa[0], z4.x, bias0);
-      bias1 = __builtin_fmaf((float)qa[1], z4.y, bias1);
-      bias0 = __builtin_fmaf((float)qb[0], z4.z, bias0);
-      bias1 = __builtin_fmaf((float)qb[1], z4.w, bias1);
+    for (int i = 0; i < 4; ++i) {
+      const uint4 h = zh[i], l = zl[i];
+      const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bias0 = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(hw[k]), bias0, false);
+        bias1 = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(lw[k]), bias1, false);
+      }
     }
     const float bias = rows_sum(bias0 + bias1);
     const float c0 = li.is_lo ? 0.f : -bias * kTwoM24;
