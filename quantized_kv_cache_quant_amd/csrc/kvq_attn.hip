@@ -58,7 +58,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQScale = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 constexpr float kTwo24 = 16777216.0f;
-constexpr float kTwoM24 = 1.0f / 16777216.0f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -735,6 +734,7 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   // ---- QK: Key codes (rows = tokens) x q' (columns)
   f32x4 acc[2];
   float vbig = 0.f;          // outliers: largest |Value correction| of the lane's entries
+  float kbias = 0.f;         // zero-point term of the logits (INT Keys)
   if constexpr (T::kRope) {
     // Keys are dequantized, rotated at their positions t0 + token and split
     // into hi / lo f16 operands; the query operand is static (q, hi / lo
@@ -799,9 +799,10 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   } else {
     vbig = stage_meta<FMT>(r, st, li.lane);
     // zero-point term sum_c q_c s_c z_c over this lane's 32 channels (in
-    // slot order; query pair k against the term's hi and lo pairs), then
-    // over the four quarters
-    float bias0 = 0.f, bias1 = 0.f;
+    // slot order; query pair k against the term's hi and lo pairs, four
+    // independent sums), then over the four quarters; it is subtracted from
+    // the logits, so the matrix-core products do not wait for it
+    float bz[4] = {0.f, 0.f, 0.f, 0.f};
     const uint4* zh = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st) + 256 + 32 * qd);
     const uint4* zl = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st) + 384 + 32 * qd);
 #pragma unroll
@@ -810,13 +811,12 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        bias0 = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(hw[k]), bias0, false);
-        bias1 = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(lw[k]), bias1, false);
+        bz[i & 1] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(hw[k]), bz[i & 1], false);
+        bz[2 + (i & 1)] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(lw[k]), bz[2 + (i & 1)], false);
       }
     }
-    const float bias = rows_sum(bias0 + bias1);
-    const float c0 = li.is_lo ? 0.f : -bias * kTwoM24;
-    acc[0] = f32x4{c0, c0, c0, c0};
+    kbias = rows_sum((bz[0] + bz[1]) + (bz[2] + bz[3]));
+    acc[0] = f32x4{0, 0, 0, 0};
     acc[1] = acc[0];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -848,7 +848,8 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[tile][i] = (acc[tile][i] + ror8(acc[tile][i])) * (T::kRope ? 1.0f : T::kCodeScale);
+    for (int i = 0; i < 4; ++i)
+      lg[tile][i] = __builtin_fmaf(acc[tile][i] + ror8(acc[tile][i]), T::kRope ? 1.0f : T::kCodeScale, -kbias);
   float slack = kSlack;
   if constexpr (!T::kFp8) {
     const float2 sv = pair_scales<FMT>(r.vm);
