@@ -2,7 +2,7 @@
 
 One step = for every layer of the model: append one new token's K / V to
 that layer's packed cache (quantize-on-append) and run fused-dequant decode
-attention for all query heads (split-K attention kernel + reduce).  Inputs
+attention for all query heads (one split-K attention kernel).  Inputs
 are synthetic and already resident in HBM when the timed region starts.
 Each layer owns its own cache buffer, so the timed loop streams every
 layer's packed cache from HBM (one layer's cache is larger than the 256 MB
@@ -380,7 +380,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(head["attn_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": counter_traffic(variants[0]),
-                     "kernel": "attn_kernel + reduce_kernel (one kv_decode_attention call)",
+                     "kernel": "attn_kernel (one kv_decode_attention call, split-K combine in the same kernel)",
                      "bytes_per_launch": head["bytes_per_attn_call"],
                      "call_us": round(head["attn_call_us"], 2)},
     }

@@ -17,8 +17,9 @@
  *    that returns a validation error (NULL, LAYOUT, UNSUPPORTED, CAPACITY,
  *    ALIGN, WORKSPACE, EMPTY) has changed nothing.  KVQ_ERR_HIP means a
  *    kernel launch failed; the cache contents are then undefined.
- *  - A cache must not be used from two streams at once; the host struct is
- *    not thread-safe.
+ *  - A cache must not be used from two streams at once, and two attention
+ *    calls on one cache must not overlap (they share the cache's sync
+ *    plane); the host struct is not thread-safe.
  *  - Inputs must be finite (no NaN / Inf); this is not checked.
  *
  * Cache layout (one cache per layer; all sequences of the batch hold the
@@ -74,6 +75,11 @@
  *            fp16 (s, m) pairs (half the bytes).
  *   K ring, V ring  [B][Hkv][R+32][D] fp16
  *   K sink, V sink  [B][Hkv][S][D] fp16
+ *   sync     [B][Hkv] int32 arrival counters of the attention call (the
+ *            workgroups that cover a head count themselves in; the last one
+ *            combines the head's partials and sets the counter back to 0).
+ *            Set to 0 by the cache's first kv_quant_append and 0 again
+ *            after every attention call; no other call touches it.
  * Each plane starts on a 256-byte boundary.
  *
  * FP8 E5M2 codes use the INT8 / FP8 byte layouts above.
@@ -177,7 +183,7 @@ typedef struct {
 enum {
   KVQ_PLANE_K_CODES = 0, KVQ_PLANE_V_CODES, KVQ_PLANE_K_META, KVQ_PLANE_V_META,
   KVQ_PLANE_K_RING, KVQ_PLANE_V_RING, KVQ_PLANE_K_SINK, KVQ_PLANE_V_SINK,
-  KVQ_PLANE_K_OUT, KVQ_PLANE_V_OUT,
+  KVQ_PLANE_K_OUT, KVQ_PLANE_V_OUT, KVQ_PLANE_SYNC,
   KVQ_NUM_PLANES
 };
 
@@ -255,9 +261,10 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, ui
  * For every sequence b and query head h:
  *   out[b][h] = sum_t softmax_t(q[b][h] . k_hat[b][g][t] / sqrt(D)) v_hat[b][g][t]
  * over all n_tokens cached tokens, g = h / (Hq/Hkv), with k_hat, v_hat the
- * dequantized (or fp16) cache entries.  Split-K: a first kernel writes
- * partials (max, sum, unnormalised output) into ws, merged per workgroup; a
- * second combines each head's partials into out.
+ * dequantized (or fp16) cache entries.  Split-K in one kernel: workgroups
+ * write partials (max, sum, unnormalised output) into ws, merged per
+ * workgroup; the last workgroup to finish a (sequence, KV head) combines
+ * that head's partials into out, in a fixed order.
  * ws: device scratch of >= kvq_workspace_bytes(cache, 0) bytes, 16-B
  * aligned, any contents, overwritten; calls that share a workspace must be
  * ordered on one stream.  Blocks are handed to wavefronts as the memory

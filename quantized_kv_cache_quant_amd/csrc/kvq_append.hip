@@ -18,6 +18,8 @@
 //  copy_kernel   copies new sink tokens and new residual tokens into their
 //                fp16 planes (ring slot u mod (R + 32)).  It runs after the
 //                flush because it may overwrite ring slots the flush read.
+//                On a cache's first append it also zeroes the attention
+//                arrival counters.
 //
 // Bit-exactness: every quantization step is one IEEE fp32 operation in the
 // order of the formula (true division, no contraction: this file is built
@@ -344,6 +346,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int b = blockIdx.y;
+  if (p.sync_zero && e < p.hkv) p.sync_zero[(int64_t)b * p.hkv + e] = 0;
   const int64_t total = (int64_t)p.T * p.hkv * 2 * 16;
   if (e >= total) return;
   const int chunk = (int)(e & 15);

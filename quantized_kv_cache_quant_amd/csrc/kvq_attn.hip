@@ -22,9 +22,10 @@
 //  * the fp16 segment (sinks + residual ring) of every head is cut into
 //    32-token blocks, spread one per wavefront over the grid and handled
 //    while the wavefront's first quantized blocks load;
-//  * at the end a workgroup merges its wavefronts' partials per head, and
-//    reduce_kernel combines each head's workgroup and fp16 partials in a
-//    fixed order.
+//  * at the end a workgroup merges its wavefronts' partials per head and
+//    counts itself in on each head's arrival counter (sync plane of the
+//    cache); the last workgroup to arrive on a head combines the head's
+//    workgroup and fp16 partials in a fixed order and writes its output.
 //
 // Per 32-token block a wavefront runs both products on the matrix cores with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate):
@@ -915,8 +916,21 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
   }
 }
 
+// A workgroup's merged slots are read by another workgroup (on another
+// compute unit, possibly another XCD): they are written and read with
+// device-coherent accesses (relaxed atomics at agent scope), which go past
+// the non-coherent caches without the L2-wide write-back and invalidate that
+// device-scope fences cost.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Sums over quarters and hi + lo columns, then writes one partial slot:
-// m, l, o[128] per query head (o unnormalised).
+// m, l, o[128] per query head (o unnormalised).  The slot is read only by
+// this workgroup, after a barrier.
 __device__ __forceinline__ void finish_segment(const WaveState& ws, const LaneInfo& li, float* slot, float oscale,
                                                bool has_z) {
   const float l = rows_sum(ws.l);
@@ -1111,6 +1125,99 @@ __device__ __forceinline__ uint32_t head_of(const AttnParams& p, uint32_t j) {
   return (uint32_t)(((uint64_t)j * p.nblk_magic) >> p.nblk_shift);
 }
 
+// Online-softmax combine of N partials (m, l, o) into (M, L, O), in order:
+// M = max, then every non-empty partial weighted by 2^(m - M) (an empty
+// partial, m = -inf, weighs 0 and its o is not read).
+template <int N>
+__device__ __forceinline__ void fold(float& M, float& L, float& O, const float* m, const float* l, const float* o) {
+  float Mn = M;
+#pragma unroll
+  for (int j = 0; j < N; ++j) Mn = fmaxf(Mn, m[j]);
+  if (Mn != neg_inf()) {                         // rescale what was summed before
+    const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
+    L *= a;
+    O *= a;
+  }
+  M = Mn;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (m[j] != neg_inf()) {
+      const float wt = exp2f(m[j] - M);
+      L = __builtin_fmaf(wt, l[j], L);
+      O = __builtin_fmaf(wt, o[j], O);
+    }
+  }
+}
+
+constexpr int kReduceBatch = 16;          // slots whose loads a thread issues together
+
+// out[b][h] of all n_rep query heads of (sequence, KV head) h:
+//   sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
+// (the exact regrouping of one softmax over all tokens), over the slots in
+// a fixed order.  SHARED: the head's merged workgroup slots, written by other
+// workgroups (device-coherent loads); otherwise its fp16 slots, written by
+// this workgroup before a barrier.  Every load of a batch of kReduceBatch
+// slots is issued before any is used (one memory round trip).
+template <bool SHARED>
+__device__ void reduce_head(const AttnParams& p, int64_t h) {
+  const int ns = SHARED ? (int)covering_count(p, h) : p.fp16_blocks;
+  const float* base = SHARED ? p.part_group + (covering_lo(p, h) + h) * slot_floats(p)
+                             : p.part_fp16 + h * p.fp16_blocks * slot_floats(p);
+  for (int idx = threadIdx.x; idx < p.nrep * kHeadDim; idx += kGroupThreads) {
+    const int hh = idx / kHeadDim, c = idx % kHeadDim;
+    float M = neg_inf(), L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += kReduceBatch) {
+      float m[kReduceBatch], l[kReduceBatch], o[kReduceBatch];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        if (s0 + j < ns) {
+          const float* sp = base + (s0 + j) * slot_floats(p) + hh * kPartStride;
+          m[j] = SHARED ? ld_dev(sp) : sp[0];
+          l[j] = SHARED ? ld_dev(sp + 1) : sp[1];
+          o[j] = SHARED ? ld_dev(sp + 4 + c) : sp[4 + c];
+        } else {
+          m[j] = neg_inf();
+          l[j] = 0.f;
+          o[j] = 0.f;
+        }
+      }
+      fold<kReduceBatch>(M, L, O, m, l, o);
+    }
+    const _Float16 r = (_Float16)(O / L);
+    p.out[(h * p.nrep + hh) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
+  }
+}
+
+// Called by the whole workgroup once its merged slots are written.  The workgroup counts itself in
+// on the counter of every head h0..h1 its range touches; the workgroup whose
+// arrival completes a head's count (covering_count workgroups) resets the
+// counter to 0 and combines that head.  The merged slots (the only data
+// another workgroup reads) were written with device-coherent stores, and each wavefront waits for its
+// stores to be acknowledged before the barrier that precedes the arrivals;
+// the combining workgroup reads the slots with device-coherent loads issued
+// after its arrival returned.  So the counter orders the hand-over without
+// device-scope fences.
+__device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* lds) {
+  int* last = reinterpret_cast<int*>(lds);       // the wavefront areas are free by now
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int64_t hb = h0; hb <= h1; hb += kGroupThreads) {
+    const int n = h1 - hb + 1 < kGroupThreads ? (int)(h1 - hb + 1) : kGroupThreads;
+    if ((int)threadIdx.x < n) {
+      const int64_t h = hb + threadIdx.x;
+      const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int is_last = prev == (int)covering_count(p, h) - 1;
+      if (is_last) __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last[threadIdx.x] = is_last;
+    }
+    __syncthreads();
+    for (int i = 0; i < n; ++i)
+      if (last[i]) reduce_head<true>(p, hb + i);
+    __syncthreads();                             // before last[] is rewritten
+  }
+}
+
+
 // The workgroup's wavefronts stream the blocks of its range: each keeps
 // kDepth blocks in flight beyond the one it processes and takes its next
 // block from a counter in LDS, so a wavefront that the memory system serves
@@ -1269,13 +1376,35 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   }
   __syncthreads();                            // every wavefront's partials written
 
-  // merge the wavefronts' partials of each head into the workgroup's slot:
-  // thread t takes (query head, channel) items t, t + threads, ...; all
-  // loads of a head are issued before any is used
+  // merge the wavefronts' partials of each head, then the fp16 blocks of the
+  // head that this workgroup handled (fb = g - g_lo(h) + k count(h)), into
+  // the workgroup's slot: thread t takes (query head, channel) items t,
+  // t + threads, ...; the loads of the wavefront slots and of the first
+  // kFoldFp16 fp16 slots are issued before any is used
   {
     constexpr int kItems = 8 * kHeadDim / kGroupThreads;     // items per thread at n_rep 8
+    constexpr int kFoldFp16 = 4;
+    const int nf = p.fp16_blocks;
     for (int h = gr.h0; h <= gr.h1; ++h) {
+      const int64_t nc = covering_count(p, h), fb0 = g - covering_lo(p, h);
       float m[kItems][kGroupWaves], l[kItems][kGroupWaves], o[kItems][kGroupWaves];
+      float fm[kItems][kFoldFp16], fl[kItems][kFoldFp16], fo[kItems][kFoldFp16];
+      auto load_fp16 = [&](int k, int64_t first, int hh, int c) {
+#pragma unroll
+        for (int j = 0; j < kFoldFp16; ++j) {
+          const int64_t fb = first + j * nc;
+          if (fb < nf) {
+            const float* sp = p.part_fp16 + ((int64_t)h * nf + fb) * slot_floats(p) + hh * kPartStride;
+            fm[k][j] = sp[0];
+            fl[k][j] = sp[1];
+            fo[k][j] = sp[4 + c];
+          } else {
+            fm[k][j] = neg_inf();
+            fl[k][j] = 0.f;
+            fo[k][j] = 0.f;
+          }
+        }
+      };
 #pragma unroll
       for (int k = 0; k < kItems; ++k) {
         const int idx = (int)threadIdx.x + k * kGroupThreads;
@@ -1287,6 +1416,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
             l[k][w] = sp[1];
             o[k][w] = sp[4 + idx % kHeadDim];
           }
+          load_fp16(k, fb0, idx / kHeadDim, idx % kHeadDim);
         }
       }
 #pragma unroll
@@ -1294,31 +1424,28 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         const int idx = (int)threadIdx.x + k * kGroupThreads;
         if (idx >= p.nrep * kHeadDim) continue;
         const int hh = idx / kHeadDim, c = idx % kHeadDim;
-        float M = neg_inf();
-#pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) M = fmaxf(M, m[k][w]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) {
-          if (m[k][w] != neg_inf()) {
-            const float wt = exp2f(m[k][w] - M);
-            L = __builtin_fmaf(wt, l[k][w], L);
-            O = __builtin_fmaf(wt, o[k][w], O);
-          }
+        float M = neg_inf(), L = 0.f, O = 0.f;
+        fold<kGroupWaves>(M, L, O, m[k], l[k], o[k]);
+        fold<kFoldFp16>(M, L, O, fm[k], fl[k], fo[k]);
+        for (int64_t first = fb0 + kFoldFp16 * nc; first < nf; first += kFoldFp16 * nc) {
+          load_fp16(k, first, hh, c);           // more than kFoldFp16 fp16 blocks here
+          fold<kFoldFp16>(M, L, O, fm[k], fl[k], fo[k]);
         }
         float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
         if (c == 0) {
-          dst[0] = M;
-          dst[1] = L;
+          st_dev(dst, M);
+          st_dev(dst + 1, L);
         }
-        dst[4 + c] = O;
+        st_dev(dst + 4 + c, O);
       }
     }
   }
+  finish_heads(p, gr.h0, gr.h1, lds);
 }
 
 
-// No quantized blocks yet: workgroup g takes the fp16 blocks of head g.
+// No quantized blocks yet: workgroup g takes the fp16 blocks of head g and
+// combines them.
 template <bool ROPE>
 __device__ void fp16_group(const AttnParams& p, char* lds) {
   const int g = blockIdx.x;
@@ -1326,6 +1453,8 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
   for (int fb = v; fb < p.fp16_blocks; fb += kGroupWaves)
     fp16_block<ROPE>(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
                p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
+  __syncthreads();                            // the head's partials, all written by this workgroup
+  reduce_head<false>(p, g);
 }
 
 template <int FMT>
@@ -1334,62 +1463,6 @@ __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2
   char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
   else group_main<FMT>(p, lds);
-}
-
-constexpr int kReduceThreads = 128;
-constexpr int kReduceRegSlots = 32;       // slots whose output this thread loads at once
-
-// out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s,
-// over the head's workgroup slots and fp16 slots (empty slots weigh 0 and
-// their output is not read).  All loads of a pass of up to kReduceRegSlots
-// slots are issued together (one memory round trip).
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnParams p) {
-  __shared__ float wts[kReduceRegSlots];
-  __shared__ float msh[kReduceRegSlots], lsh[kReduceRegSlots];
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int hh = hq % p.nrep;
-  const int64_t h = (int64_t)b * p.hkv + hq / p.nrep;
-  const int nf = p.fp16_blocks;
-  const int64_t g_lo = p.nblk > 0 ? covering_lo(p, h) : 0;
-  const int ng = p.nblk > 0 ? (int)covering_count(p, h) : 0;
-  const int ns = ng + nf;
-  auto slot_ptr = [&](int s) -> const float* {
-    const float* base = s < ng ? p.part_group + (g_lo + s + h) * slot_floats(p)
-                               : p.part_fp16 + (h * nf + (s - ng)) * slot_floats(p);
-    return base + hh * kPartStride;
-  };
-  float M = neg_inf(), L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kReduceRegSlots) {
-    const int cnt = ns - s0 < kReduceRegSlots ? ns - s0 : kReduceRegSlots;
-    float v[kReduceRegSlots];
-#pragma unroll
-    for (int j = 0; j < kReduceRegSlots; ++j) v[j] = j < cnt ? slot_ptr(s0 + j)[4 + c] : 0.f;
-    if (c < cnt) {
-      msh[c] = slot_ptr(s0 + c)[0];
-      lsh[c] = slot_ptr(s0 + c)[1];
-    }
-    __syncthreads();
-    float Mn = M;
-    for (int j = 0; j < cnt; ++j) Mn = fmaxf(Mn, msh[j]);
-    if (Mn != neg_inf()) {                       // rescale what earlier passes summed
-      const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
-      L *= a;
-      O *= a;
-    }
-    M = Mn;
-    if (c < cnt) wts[c] = msh[c] == neg_inf() ? 0.f : exp2f(msh[c] - M);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kReduceRegSlots; ++j) {
-      if (j < cnt && wts[j] != 0.f) {           // an empty slot's output is not read
-        L = __builtin_fmaf(wts[j], lsh[j], L);
-        O = __builtin_fmaf(wts[j], v[j], O);
-      }
-    }
-    __syncthreads();
-  }
-  const _Float16 r = (_Float16)(O / L);
-  p.out[(h * p.nrep + hh) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
 }
 
 }  // namespace
@@ -1427,8 +1500,6 @@ hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
       hipLaunchKernelGGL(attn_kernel<KVQ_INT2 | kMeta16 | kRope>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL(reduce_kernel, dim3(p.hkv * p.nrep, p.bh_count / p.hkv), dim3(kReduceThreads), 0, s, p);
   return hipGetLastError();
 }
 

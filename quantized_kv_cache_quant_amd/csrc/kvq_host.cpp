@@ -58,6 +58,7 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_V_SINK] = sz[KVQ_PLANE_K_SINK];
   sz[KVQ_PLANE_K_OUT] = L.outliers ? recs * d * 4 : 0;                       // one entry per channel
   sz[KVQ_PLANE_V_OUT] = L.outliers ? recs * (d / L.v_group_channels) * kBlock * 4 : 0;
+  sz[KVQ_PLANE_SYNC] = bh * 4;                                               // int32 per (sequence, KV head)
 }
 
 // Compute units of the current device (256 when no device answers).
@@ -294,6 +295,8 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
   cp.hkv = L.num_kv_heads;
   cp.sink = L.sink_tokens;
   cp.ring_slots = c->ring_slots;
+  // the first append of a cache also sets the attention arrival counters to 0
+  cp.sync_zero = n_old == 0 ? reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC)) : nullptr;
   if (launch_copy(cp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   c->n_tokens = n_new;
   return KVQ_OK;
@@ -352,6 +355,7 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
   p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
   p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));
   p.v_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_SINK));
+  p.sync = reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC));
   p.q = static_cast<const uint16_t*>(q);
   p.out = static_cast<uint16_t*>(out);
   p.part_fp16 = static_cast<float*>(ws);

@@ -97,6 +97,7 @@ struct CopyParams {
   int64_t n_old;
   int64_t n_q_new;        // quantized body tokens after the append
   int32_t T, hkv, sink, ring_slots;
+  int32_t* sync_zero;     // non-null on a cache's first append: [B][Hkv] counters set to 0
 };
 
 hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s);
@@ -130,6 +131,7 @@ struct AttnParams {
   const uint16_t* v_sink;
   const uint16_t* q;      // fp16 [B][Hq][D]
   uint16_t* out;          // fp16 [B][Hq][D]
+  int32_t* sync;          // [B][Hkv] arrival counters (0 between calls)
   float* part_fp16;
   float* part_wave;
   float* part_group;

@@ -17,7 +17,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_LAYOUT", -3: "KVQ_ERR_UN
           -4: "KVQ_ERR_CAPACITY", -5: "KVQ_ERR_ALIGN", -6: "KVQ_ERR_WORKSPACE", -7: "KVQ_ERR_HIP",
           -8: "KVQ_ERR_EMPTY"}
 FORMATS = {"int8": 0, "int4": 1, "int2": 2, "fp8": 3, "fp8_e5m2": 4}
-PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink", "k_out", "v_out")
+PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink", "v_sink", "k_out", "v_out",
+          "sync")
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
            "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table")

@@ -112,6 +112,7 @@ def test_cache_bytes_and_planes(fmt, bits, m16, s, r, maxt):
         "v_sink": b * hkv * s * d * 2,
         "k_out": 0,
         "v_out": 0,
+        "sync": b * hkv * 4,
     }
     h = kvq.CacheStruct()
     assert kvq.lib().kvq_cache_init(ctypes.byref(h), ctypes.byref(lay), ctypes.c_void_p(FAKE), total) == 0
@@ -237,7 +238,8 @@ def test_paged_planes_and_table_binding(fmt, bits, pb, pages):
     expect = {"k_codes": recs * 32 * d * bits // 8, "v_codes": recs * 32 * d * bits // 8,
               "k_meta": 0 if fp8 else recs * 2 * d * 4, "v_meta": 0 if fp8 else recs * 2 * 4 * 32 * 4,
               "k_ring": b * hkv * 64 * d * 2, "v_ring": b * hkv * 64 * d * 2,
-              "k_sink": b * hkv * 4 * d * 2, "v_sink": b * hkv * 4 * d * 2, "k_out": 0, "v_out": 0}
+              "k_sink": b * hkv * 4 * d * 2, "v_sink": b * hkv * 4 * d * 2, "k_out": 0, "v_out": 0,
+              "sync": b * hkv * 4}
     for i, name in enumerate(kvq.PLANES):
         assert h.plane_bytes[i] == expect[name], name
     assert h.block_table is None and h.n_blocks_cap == (1000 - 36) // 32

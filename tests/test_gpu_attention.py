@@ -131,6 +131,29 @@ def test_split_invariance_and_determinism(fmt):
         assert np.array_equal(again.astype(np.float64), outs[bpg, True]), bpg   # bitwise repeatable
 
 
+def test_arrival_counters_start_and_end_at_zero():
+    """The sync plane (one int32 arrival counter per sequence and KV head, through which the
+    last workgroup to finish a head takes over its combine) holds garbage before the first
+    append, is zeroed by it, and is zero again after every attention call whatever the split;
+    the outputs meet the bar each time.  Covers caches with quantized blocks and with the fp16
+    segment alone (one workgroup per head, no counters used)."""
+    require_gpu()
+    for n, r in ((32 * 70 + 40, 32), (40, 32)):
+        k, v = synth.kv_tokens(W["llama3_8b"], 21, 22, 2, n, 2, 128)
+        kw = _kw("int4", 2, 2, 4, n + 64, r, 0, k, v)
+        c = make_cache(kw)
+        c.plane("sync").fill_(0xA5)
+        append_chunks(c, k, v, [n])
+        assert not c.plane("sync").cpu().numpy().any(), n
+        q = synth.queries(W["llama3_8b"], 2, 8, 128, seed_offset=21)
+        ref = _oracle_out(c, kw, q)
+        for bpg in (1, 7, 0):
+            for det in (True, False):
+                o = attention_gpu(c, q, bpg, det).astype(np.float64)
+                assert np.max(np.abs(o - ref)) <= TOL, (n, bpg, det)
+                assert not c.plane("sync").cpu().numpy().any(), (n, bpg, det)
+
+
 def test_workspace_reuse_any_contents():
     """One workspace, filled with NaN to start with, serves repeated calls and caches of
     other shapes; the deterministic mode repeats bit for bit."""
