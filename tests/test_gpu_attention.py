@@ -154,6 +154,47 @@ def test_arrival_counters_start_and_end_at_zero():
                 assert not c.plane("sync").cpu().numpy().any(), (n, bpg, det)
 
 
+def test_graph_capture_replays_match_eager():
+    """kv_decode_attention captured in a HIP graph (torch.cuda.CUDAGraph on the capture stream)
+    and replayed several times, with eager work and a synchronization between replays: every
+    replay gives the eager result (bit for bit in deterministic mode, within one fp16 ulp
+    otherwise), the arrival counters are back at zero after each replay, and the result meets
+    the bar against the oracle.  The call allocates nothing and enqueues only its kernel."""
+    require_gpu()
+    c, kw, q = _build("int4", 2, 2, 4, 32 * 40 + 20, 32, 0, seed=31)
+    ref = _oracle_out(c, kw, q)
+    qd = to_dev(q)
+    out = torch.empty_like(qd)
+    ws = torch.empty(c.workspace_bytes(0) // 4 + 4, dtype=torch.float32, device="cuda")
+    counters = lambda: c.plane("sync").cpu().numpy().view(np.int32)
+    for det in (True, False):
+        c.attention(qd, out, ws, 0, det)
+        torch.cuda.synchronize()
+        eager = out.cpu().numpy().astype(np.float64)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):                 # warm-up on a side stream before capture
+            c.attention(qd, out, ws, 0, det)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            c.attention(qd, out, ws, 0, det)
+        for rep in range(4):
+            out.fill_(float("nan"))                   # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+            if det:
+                assert np.array_equal(got, eager), rep
+            else:
+                assert np.all(np.abs(got - eager) <= np.maximum(np.abs(eager), 1.0) * 2.0**-10), rep
+            assert np.max(np.abs(got - ref)) <= TOL, rep
+            assert not counters().any(), rep
+        del g
+
+
 def test_workspace_reuse_any_contents():
     """One workspace, filled with NaN to start with, serves repeated calls and caches of
     other shapes; the deterministic mode repeats bit for bit."""
