@@ -28,6 +28,9 @@ launches on (torch's current stream):
     by its own event pair -> the roofline entry (algorithmic bytes per call /
     mean call time).  The events sit outside the step loop because an event
     record between launches adds a few microseconds of idle time per call.
+read_gbps_measured is the best rate of the library's plain streaming-read
+kernel (kvq_read_probe) over 4 GiB; attn_frac_of_measured_read is the
+attention call's rate (roofline.achieved) over it.
 roofline.traffic comes from the FETCH_SIZE / WRITE_SIZE counter passes
 recorded in profiles/attn_counters.json, scaled by the plain-copy
 calibration stored there, and is null when the attention source has changed
@@ -69,6 +72,30 @@ def parse():
     ap.add_argument("--no-variants", action="store_true", help="skip the attention sweep of the other variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
+
+
+def read_peak(torch, kvq) -> dict:
+    """GB/s of the library's plain streaming-read kernel (kvq_read_probe) over 4 GiB, with one
+    and with four workgroups of 512 threads per compute unit (the first is the attention
+    kernel's launch shape), each timed with events on the stream it launches on."""
+    n = 4 << 30
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4 * cus * 512, dtype=torch.int32, device="cuda")
+    res = {}
+    for per_cu in (1, 4):
+        g = per_cu * cus
+        kvq.read_probe(x, sink, g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            kvq.read_probe(x, sink, g)
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{per_cu}_per_cu"] = round(n / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9, 1)
+    del x, sink
+    return res
 
 
 def copy_bandwidth(torch) -> float:
@@ -354,6 +381,9 @@ def main():
         vres = variant_sweep(torch, kvq, synth, accounting, w, VARIANTS, args)
     copy_gbps = copy_bandwidth(torch)
     log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
+    reads = read_peak(torch, kvq)
+    read_gbps = max(reads.values())
+    log(f"streaming read (kvq_read_probe, workgroups per compute unit: GB/s): {reads}")
     head = results[variants[0]]
     line = {
         "metric": METRIC,
@@ -377,6 +407,9 @@ def main():
         "attn_call_us": round(head["attn_call_us"], 2),
         "step_us_per_layer": round(head["step_us_per_layer"], 2),
         "copy_gbps_measured": round(copy_gbps, 1),
+        "read_gbps_measured": read_gbps,
+        "read_gbps_by_shape": reads,
+        "attn_frac_of_measured_read": round(head["attn_gbps"] / read_gbps, 4),
         "roofline": {"bound": "hbm", "achieved": round(head["attn_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": counter_traffic(variants[0]),

@@ -290,6 +290,20 @@ int32_t kv_decode_attention_split(const kvq_cache* cache, const void* q, void* o
                                   uint64_t ws_bytes, int32_t blocks_per_group, int32_t deterministic,
                                   void* stream);
 
+/* Diagnostic, not part of the method: a plain streaming read of a device
+ * buffer, which measures the HBM read rate this GPU delivers to a kernel of
+ * the attention call's shape (the benchmark reports attention calls against
+ * it as well as against the nominal peak).  groups workgroups of 512 threads
+ * (0 = one per compute unit) each read one contiguous part of buf (bytes, a
+ * multiple of 16) with 16-byte nontemporal loads, eight in flight per thread;
+ * each thread writes the XOR of the words it read to its uint32 of sink, so
+ * no load can be dropped.  buf and sink are device pointers, 16-B aligned;
+ * sink_bytes >= 4 * 512 * groups.  Errors: KVQ_ERR_NULL, KVQ_ERR_LAYOUT
+ * (bytes not a multiple of 16, groups < 0), KVQ_ERR_ALIGN, KVQ_ERR_WORKSPACE
+ * (sink too small), KVQ_ERR_HIP. */
+int32_t kvq_read_probe(const void* buf, uint64_t bytes, void* sink, uint64_t sink_bytes, int32_t groups,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

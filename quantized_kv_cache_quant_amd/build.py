@@ -29,6 +29,7 @@ SOURCES = {
     "kvq_host.cpp": [],
     "kvq_append.hip": ["-ffp-contract=off"],
     "kvq_attn.hip": [],
+    "kvq_probe.hip": [],
 }
 
 

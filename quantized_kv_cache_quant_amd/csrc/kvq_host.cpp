@@ -402,4 +402,19 @@ int32_t kv_decode_attention(const kvq_cache* c, const void* q, void* out, void* 
   return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, 0, stream);
 }
 
+int32_t kvq_read_probe(const void* buf, uint64_t bytes, void* sink, uint64_t sink_bytes, int32_t groups,
+                       void* stream) {
+  if (!buf || !sink) return KVQ_ERR_NULL;
+  if (bytes % 16 != 0 || groups < 0) return KVQ_ERR_LAYOUT;
+  if (!aligned(buf, 16) || !aligned(sink, 16)) return KVQ_ERR_ALIGN;
+  const int64_t g = groups > 0 ? groups : device_cus();
+  if (g > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  if ((uint64_t)g * kProbeThreads * 4 > sink_bytes) return KVQ_ERR_WORKSPACE;
+  if (bytes == 0) return KVQ_OK;
+  if (launch_read_probe(buf, bytes / 16, static_cast<uint32_t*>(sink), (int)g,
+                        reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
 }  // extern "C"

@@ -161,4 +161,8 @@ struct AttnParams {
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s);
 
+// ------------------------------------------------------------- read probe
+constexpr int kProbeThreads = 512;        // threads per workgroup, as the attention kernel
+hipError_t launch_read_probe(const void* buf, uint64_t units, uint32_t* sink, int groups, hipStream_t s);
+
 }  // namespace kvq

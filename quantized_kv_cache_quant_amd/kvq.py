@@ -21,7 +21,8 @@ PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink"
           "sync")
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
-           "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table")
+           "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table",
+           "kvq_read_probe")
 
 
 class KvqError(RuntimeError):
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "kv_decode_attention": (I32, [CP, P, P, P, U64, P]),
             "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, I32, P]),
             "kvq_cache_set_block_table": (I32, [CP, P, I32]),
+            "kvq_read_probe": (I32, [P, U64, P, U64, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -193,3 +195,12 @@ def _check_tensor(t, name: str) -> None:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != torch.float16 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float16 tensor")
+
+
+def read_probe(buf, sink, groups: int = 0, stream=None) -> None:
+    """Diagnostic streaming read of a device tensor (see kvq_read_probe): buf is read whole;
+    sink is a device tensor of at least 4 * 512 * groups bytes (groups 0: one workgroup per
+    compute unit)."""
+    check(lib().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                               ctypes.c_void_p(sink.data_ptr()), sink.numel() * sink.element_size(),
+                               int(groups), _stream(stream)), "kvq_read_probe")

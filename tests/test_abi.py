@@ -165,6 +165,21 @@ def test_append_errors_leave_cache_unchanged():
     assert L.kv_quant_append(None, P(FAKE), P(FAKE), 1, None) == -1
 
 
+def test_read_probe_validation():
+    """The diagnostic read probe validates before launching anything."""
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    sink = 4 * 512 * 256
+    assert L.kvq_read_probe(None, 1024, P(FAKE), sink, 0, None) == -1
+    assert L.kvq_read_probe(P(FAKE), 1024, None, sink, 0, None) == -1
+    assert L.kvq_read_probe(P(FAKE), 1000, P(FAKE), sink, 0, None) == -2        # not a multiple of 16
+    assert L.kvq_read_probe(P(FAKE), 1024, P(FAKE), sink, -1, None) == -2
+    assert L.kvq_read_probe(P(FAKE + 8), 1024, P(FAKE), sink, 0, None) == -5
+    assert L.kvq_read_probe(P(FAKE), 1024, P(FAKE + 4), sink, 0, None) == -5
+    assert L.kvq_read_probe(P(FAKE), 1024, P(FAKE), 4 * 512 * 3 - 1, 3, None) == -6
+    assert L.kvq_read_probe(P(FAKE), 0, P(FAKE), sink, 0, None) == 0            # nothing to read
+
+
 def test_attention_errors():
     L = kvq.lib()
     P = ctypes.c_void_p
