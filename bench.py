@@ -2,7 +2,10 @@
 
 One step = for every layer of the model: append one new token's K / V to
 that layer's packed cache (quantize-on-append) and run fused-dequant decode
-attention for all query heads (one split-K attention kernel).  Inputs
+attention for all query heads, through kv_append_decode_attention (one
+split-K attention kernel that also writes the new token into the fp16 ring;
+on every 32nd step, when a block leaves the window, the append's kernels
+run first).  Inputs
 are synthetic and already resident in HBM when the timed region starts.
 Each layer owns its own cache buffer, so the timed loop streams every
 layer's packed cache from HBM (one layer's cache is larger than the 256 MB
@@ -235,9 +238,14 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
                      dtype=torch.float32, device="cuda")
 
     def step(j):
+        # kv_append_decode_attention: append + attention, one launch unless a block leaves the
+        # window (every 32nd step); an explicit split takes the two separate calls
         for c in caches:
-            c.append(steps_k[j], steps_v[j])
-            c.attention(q, out, ws, args.blocks_per_group)
+            if args.blocks_per_group:
+                c.append(steps_k[j], steps_v[j])
+                c.attention(q, out, ws, args.blocks_per_group)
+            else:
+                c.append_attention(steps_k[j], steps_v[j], q, out, ws)
 
     for j in range(args.warmup):
         step(j)

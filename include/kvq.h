@@ -273,6 +273,20 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, ui
 int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream);
 
+/* One decode step of one layer: kv_quant_append of one token (K, V: device
+ * fp16 [B][1][Hkv][D]) followed by kv_decode_attention over the cache that
+ * includes it, with the results of those two calls (the same kernel, the
+ * library's own split).  When the token only enters the fp16
+ * residual ring (not the cache's first append, not a sink, no block leaves
+ * the window: 31 of every 32 decode steps) it is one kernel launch: the
+ * attention kernel reads the token from K, V and copies it to its ring slot;
+ * otherwise the two calls are enqueued in turn.  Every check of both calls
+ * runs before anything is enqueued, so an error leaves the cache unchanged;
+ * n_tokens advances by one on success.  Errors: those of kv_quant_append
+ * (T = 1) and kv_decode_attention. */
+int32_t kv_append_decode_attention(kvq_cache* cache, const void* K, const void* V, const void* q, void* out,
+                                   void* ws, uint64_t ws_bytes, void* stream);
+
 /* kv_decode_attention with an explicit split.  The quantized 32-token blocks
  * of all heads, flattened head-major, are cut into ranges of blocks_per_group
  * blocks (a range may cross from one head into the next), one per workgroup

@@ -968,8 +968,12 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // LDS area into the (channel, 8 tokens) operand order.
 constexpr int kSegVStride = 136;     // halves per staged Value row (16-byte aligned)
 
+// Row of segment token k: a sink, a ring slot, or (fused append, fresh != null)
+// for the newest token the input row, which fp16_block also copies to its
+// ring slot.
 __device__ __forceinline__ const uint16_t* seg_row(const AttnParams& p, const uint16_t* sink,
-                                                   const uint16_t* ring, int64_t bh, int k) {
+                                                   const uint16_t* ring, const uint16_t* fresh, int64_t bh, int k) {
+  if (fresh && k == p.n_sink + p.n_res - 1) return fresh + bh * kHeadDim;
   if (k < p.n_sink) return sink + (bh * p.sink_cap + k) * kHeadDim;
   const int slot = (p.ring_first + (k - p.n_sink)) % p.ring_slots;
   return ring + (bh * p.ring_slots + slot) * kHeadDim;
@@ -984,6 +988,16 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
   const LaneInfo li = lane_info(p.nrep);
   const int lane = li.lane;
   const int nt = p.n_sink + p.n_res;
+  // fused append: the block holding the newest token (a residual token) copies
+  // its Key and Value rows from the input to its ring slot, 16 bytes per lane;
+  // no other block of this call reads that slot
+  if (p.new_k && fb == (nt - 1) / kBlock && lane < 32) {
+    const int kv = lane >> 4, chunk = lane & 15;
+    const uint16_t* ring = kv ? p.v_ring : p.k_ring;
+    const uint16_t* dst = seg_row(p, nullptr, ring, nullptr, bh, nt - 1) + 8 * chunk;
+    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(dst)) =
+        *reinterpret_cast<const uint4*>((kv ? p.new_v : p.new_k) + bh * kHeadDim + 8 * chunk);
+  }
   QOp q;
   f16x8 bk[4];
   load_query<ROPE ? (KVQ_INT8 | kRope) : KVQ_INT8>(p, bh, li, q);   // scale 1
@@ -999,7 +1013,7 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
     int k = 32 * fb + 16 * tile + (lane & 15);
     k = k < nt ? k : nt - 1;                           // masked below; any valid row keeps values finite
     kpos[tile] = k < p.n_sink ? k : p.sink_cap + kBlock * p.nblk + (k - p.n_sink);
-    const uint16_t* row = seg_row(p, p.k_sink, p.k_ring, bh, k);
+    const uint16_t* row = seg_row(p, p.k_sink, p.k_ring, p.new_k, bh, k);
     if constexpr (ROPE) {
       const uint4* a = reinterpret_cast<const uint4*>(row + 16 * li.qd);
       const uint4* b = reinterpret_cast<const uint4*>(row + kHeadDim / 2 + 16 * li.qd);
@@ -1014,7 +1028,7 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
   {
     int k = 32 * fb + (lane & 31);
     k = k < nt ? k : nt - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.v_sink, p.v_ring, bh, k) + 64 * (lane >> 5));
+    const uint4* src = reinterpret_cast<const uint4*>(seg_row(p, p.v_sink, p.v_ring, p.new_v, bh, k) + 64 * (lane >> 5));
     uint4* dst = reinterpret_cast<uint4*>(vt + (lane & 31) * kSegVStride + 64 * (lane >> 5));
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = src[i];

@@ -106,6 +106,83 @@ uint64_t slot_bytes(const kvq_layout& L) {
 
 }  // namespace
 
+// Validation and kernel parameters of an attention call over the first
+// n_tokens tokens of the cache (every check before anything is enqueued).
+static int32_t prepare_attention(const kvq_cache* c, int64_t n_tokens, const void* q, void* out, void* ws,
+                                 uint64_t ws_bytes, int32_t bpg, int32_t deterministic, AttnParams& p) {
+  if (!c || !c->base || !q || !out) return KVQ_ERR_NULL;
+  const kvq_layout& L = c->layout;
+  int32_t st = kvq_layout_validate(&L);
+  if (st != KVQ_OK) return st;
+  if (bpg < 0 || bpg > kMaxBlocksPerGroup || (deterministic != 0 && deterministic != 1)) return KVQ_ERR_LAYOUT;
+  if (L.page_blocks > 0 && bpg > kMaxPagedRange) return KVQ_ERR_LAYOUT;
+  if (L.page_blocks > 0 && !c->block_table) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  if (n_tokens == 0) return KVQ_ERR_EMPTY;
+  const Window w = window(L, n_tokens);
+  const int64_t nblk = w.n_q / kBlock;
+  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
+  // workspace is checked before anything touches the device
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpg);
+  const uint64_t sb = slot_bytes(L);
+  if ((uint64_t)a.slots * sb > ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+
+  char* base = static_cast<char*>(c->base);
+  auto plane = [&](int i) { return base + c->plane_off[i]; };
+  p = AttnParams{};
+  p.k_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_K_CODES));
+  p.v_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_V_CODES));
+  p.k_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_K_META));
+  p.v_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_V_META));
+  p.k_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_K_OUT));
+  p.v_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_V_OUT));
+  p.k_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_RING));
+  p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
+  p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));
+  p.v_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_SINK));
+  p.sync = reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC));
+  p.q = static_cast<const uint16_t*>(q);
+  p.out = static_cast<uint16_t*>(out);
+  p.part_fp16 = static_cast<float*>(ws);
+  p.part_wave = p.part_fp16 + bh * a.fp16_blocks * (sb / sizeof(float));
+  p.part_group = p.part_wave + (nblk > 0 ? kGroupWaves * (a.groups + bh) : 0) * (int64_t)(sb / sizeof(float));
+  p.hkv = L.num_kv_heads;
+  p.nrep = L.num_q_heads / L.num_kv_heads;
+  p.nb_cap = c->n_blocks_cap;
+  p.nblk = (int32_t)nblk;
+  {
+    // multiply-shift division by d = nblk for dividends below 2^31: with
+    // 2^l >= d, m = ceil(2^(31+l) / d) < 2^32 and m d - 2^(31+l) < d, so
+    // floor(j m / 2^(31+l)) = floor(j / d) whenever j < 2^31
+    const uint64_t d = nblk > 0 ? (uint64_t)nblk : 1;
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    p.nblk_shift = 31 + l;
+    p.nblk_magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+  }
+  p.ring_slots = c->ring_slots;
+  p.sink_cap = L.sink_tokens;
+  p.n_sink = (int32_t)w.n_sink;
+  p.n_res = (int32_t)w.r;
+  p.ring_first = (int32_t)(w.n_q % c->ring_slots);
+  p.bh_count = (int32_t)bh;
+  p.group_blocks = (int32_t)a.group_blocks;
+  p.groups = (int32_t)a.groups;
+  p.fp16_blocks = (int32_t)a.fp16_blocks;
+  p.deterministic = deterministic;
+  p.k_scale = L.k_scale;
+  p.v_scale = L.v_scale;
+  p.table = c->block_table;
+  p.table_stride = c->table_stride;
+  p.page_blocks = L.page_blocks;
+  p.num_pages = L.num_pages;
+  p.rope_theta = L.rope_theta;
+  return KVQ_OK;
+}
+
 extern "C" {
 
 const char* kvq_status_string(int32_t s) {
@@ -322,76 +399,10 @@ int32_t kvq_workspace_bytes(const kvq_cache* c, int32_t bpg, uint64_t* bytes) {
 
 int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, void* ws,
                                   uint64_t ws_bytes, int32_t bpg, int32_t deterministic, void* stream) {
-  if (!c || !c->base || !q || !out) return KVQ_ERR_NULL;
-  const kvq_layout& L = c->layout;
-  int32_t st = kvq_layout_validate(&L);
+  AttnParams p;
+  const int32_t st = prepare_attention(c, c ? c->n_tokens : 0, q, out, ws, ws_bytes, bpg, deterministic, p);
   if (st != KVQ_OK) return st;
-  if (bpg < 0 || bpg > kMaxBlocksPerGroup || (deterministic != 0 && deterministic != 1)) return KVQ_ERR_LAYOUT;
-  if (L.page_blocks > 0 && bpg > kMaxPagedRange) return KVQ_ERR_LAYOUT;
-  if (L.page_blocks > 0 && !c->block_table) return KVQ_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
-  if (c->n_tokens == 0) return KVQ_ERR_EMPTY;
-  const Window w = window(L, c->n_tokens);
-  const int64_t nblk = w.n_q / kBlock;
-  const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
-  // workspace is checked before anything touches the device
-  if (!ws) return KVQ_ERR_WORKSPACE;
-  const AttnPlan a = plan(L, nblk, w.n_sink + w.r, bpg);
-  const uint64_t sb = slot_bytes(L);
-  if ((uint64_t)a.slots * sb > ws_bytes) return KVQ_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
-  if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
-
-  char* base = static_cast<char*>(c->base);
-  auto plane = [&](int i) { return base + c->plane_off[i]; };
-  AttnParams p{};
-  p.k_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_K_CODES));
-  p.v_codes = reinterpret_cast<const uint8_t*>(plane(KVQ_PLANE_V_CODES));
-  p.k_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_K_META));
-  p.v_meta = reinterpret_cast<const float*>(plane(KVQ_PLANE_V_META));
-  p.k_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_K_OUT));
-  p.v_out = reinterpret_cast<const uint32_t*>(plane(KVQ_PLANE_V_OUT));
-  p.k_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_RING));
-  p.v_ring = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_RING));
-  p.k_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_K_SINK));
-  p.v_sink = reinterpret_cast<const uint16_t*>(plane(KVQ_PLANE_V_SINK));
-  p.sync = reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC));
-  p.q = static_cast<const uint16_t*>(q);
-  p.out = static_cast<uint16_t*>(out);
-  p.part_fp16 = static_cast<float*>(ws);
-  p.part_wave = p.part_fp16 + bh * a.fp16_blocks * (sb / sizeof(float));
-  p.part_group = p.part_wave + (nblk > 0 ? kGroupWaves * (a.groups + bh) : 0) * (int64_t)(sb / sizeof(float));
-  p.hkv = L.num_kv_heads;
-  p.nrep = L.num_q_heads / L.num_kv_heads;
-  p.nb_cap = c->n_blocks_cap;
-  p.nblk = (int32_t)nblk;
-  {
-    // multiply-shift division by d = nblk for dividends below 2^31: with
-    // 2^l >= d, m = ceil(2^(31+l) / d) < 2^32 and m d - 2^(31+l) < d, so
-    // floor(j m / 2^(31+l)) = floor(j / d) whenever j < 2^31
-    const uint64_t d = nblk > 0 ? (uint64_t)nblk : 1;
-    int l = 0;
-    while ((1ull << l) < d) ++l;
-    p.nblk_shift = 31 + l;
-    p.nblk_magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
-  }
-  p.ring_slots = c->ring_slots;
-  p.sink_cap = L.sink_tokens;
-  p.n_sink = (int32_t)w.n_sink;
-  p.n_res = (int32_t)w.r;
-  p.ring_first = (int32_t)(w.n_q % c->ring_slots);
-  p.bh_count = (int32_t)bh;
-  p.group_blocks = (int32_t)a.group_blocks;
-  p.groups = (int32_t)a.groups;
-  p.fp16_blocks = (int32_t)a.fp16_blocks;
-  p.deterministic = deterministic;
-  p.k_scale = L.k_scale;
-  p.v_scale = L.v_scale;
-  p.table = c->block_table;
-  p.table_stride = c->table_stride;
-  p.page_blocks = L.page_blocks;
-  p.num_pages = L.num_pages;
-  p.rope_theta = L.rope_theta;
+  const kvq_layout& L = c->layout;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
@@ -400,6 +411,38 @@ int32_t kv_decode_attention_split(const kvq_cache* c, const void* q, void* out, 
 int32_t kv_decode_attention(const kvq_cache* c, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream) {
   return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, 0, stream);
+}
+
+int32_t kv_append_decode_attention(kvq_cache* c, const void* K, const void* V, const void* q, void* out,
+                                   void* ws, uint64_t ws_bytes, void* stream) {
+  if (!c || !c->base || !K || !V) return KVQ_ERR_NULL;
+  const kvq_layout& L = c->layout;
+  int32_t st = kvq_layout_validate(&L);
+  if (st != KVQ_OK) return st;
+  if (L.page_blocks > 0 && !c->block_table) return KVQ_ERR_NULL;
+  if (!aligned(K, 16) || !aligned(V, 16)) return KVQ_ERR_ALIGN;
+  const int64_t n_old = c->n_tokens;
+  if (n_old + 1 > (int64_t)L.max_tokens) return KVQ_ERR_CAPACITY;
+  AttnParams p;                                   // attention over the n_old + 1 tokens
+  st = prepare_attention(c, n_old + 1, q, out, ws, ws_bytes, 0, 0, p);
+  if (st != KVQ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Window w0 = window(L, n_old), w1 = window(L, n_old + 1);
+  // one launch when the token only enters the residual ring: not the cache's
+  // first append (which also zeroes the counters), not a sink, and no block
+  // leaves the window; the attention kernel reads the token from K, V and
+  // copies it to its ring slot
+  if (n_old > 0 && n_old >= L.sink_tokens && w1.n_q == w0.n_q) {
+    p.new_k = static_cast<const uint16_t*>(K);
+    p.new_v = static_cast<const uint16_t*>(V);
+    if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
+    c->n_tokens = n_old + 1;
+    return KVQ_OK;
+  }
+  st = kv_quant_append(c, K, V, 1, stream);       // every validation already passed above
+  if (st != KVQ_OK) return st;
+  if (launch_attention(variant_of(L), p, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
 }
 
 int32_t kvq_read_probe(const void* buf, uint64_t bytes, void* sink, uint64_t sink_bytes, int32_t groups,

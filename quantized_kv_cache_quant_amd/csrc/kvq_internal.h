@@ -132,6 +132,8 @@ struct AttnParams {
   const uint16_t* q;      // fp16 [B][Hq][D]
   uint16_t* out;          // fp16 [B][Hq][D]
   int32_t* sync;          // [B][Hkv] arrival counters (0 between calls)
+  const uint16_t* new_k;  // fused append: fp16 [B][1][Hkv][D] of the newest token, else null;
+  const uint16_t* new_v;  // it is read from here and copied to its ring slot
   float* part_fp16;
   float* part_wave;
   float* part_group;

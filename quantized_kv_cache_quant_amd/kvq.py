@@ -22,7 +22,7 @@ PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink"
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
            "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table",
-           "kvq_read_probe")
+           "kvq_read_probe", "kv_append_decode_attention")
 
 
 class KvqError(RuntimeError):
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, I32, P]),
             "kvq_cache_set_block_table": (I32, [CP, P, I32]),
             "kvq_read_probe": (I32, [P, U64, P, U64, I32, P]),
+            "kv_append_decode_attention": (I32, [CP, P, P, P, P, P, U64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -170,6 +171,17 @@ class Cache:
         t = k.shape[1]
         check(lib().kv_quant_append(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
                                     ctypes.c_void_p(v.data_ptr()), int(t), _stream(stream)), "kv_quant_append")
+
+    def append_attention(self, k, v, q, out, ws, stream=None) -> None:
+        """One decode step (kv_append_decode_attention): k, v fp16 [B][1][Hkv][D]; q, out fp16
+        [B][Hq][D]; ws: device scratch tensor."""
+        for t, name in ((k, "K"), (v, "V"), (q, "q"), (out, "out")):
+            _check_tensor(t, name)
+        check(lib().kv_append_decode_attention(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
+                                               ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+                                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                               ws.numel() * ws.element_size(), _stream(stream)),
+              "kv_append_decode_attention")
 
     def workspace_bytes(self, blocks_per_group: int = 0) -> int:
         n = ctypes.c_uint64()

@@ -14,7 +14,7 @@ from oracle import cache as ocache
 from oracle import quant
 from quantized_kv_cache_quant_amd import kvq, synth
 
-from kvq_testlib import (FP8, append_chunks, attention_gpu, make_cache, olayout_of, read_state,
+from kvq_testlib import (FP8, append_chunks, assert_states_equal, attention_gpu, make_cache, olayout_of, read_state,
                          require_gpu, split_fmt, substate, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -193,6 +193,50 @@ def test_graph_capture_replays_match_eager():
             assert np.max(np.abs(got - ref)) <= TOL, rep
             assert not counters().any(), rep
         del g
+
+
+@pytest.mark.parametrize("fmt,s,r,theta", [("int4", 0, 32, 0.0), ("int8", 4, 32, 0.0), ("fp8", 0, 64, 0.0),
+                                            ("int2_m16", 0, 32, 0.0), ("int4", 2, 32, 500000.0)])
+def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta):
+    """kv_append_decode_attention (one launch when the token only enters the fp16 ring) against
+    kv_quant_append + kv_decode_attention on a twin cache, over 70 one-token decode steps that
+    start with sink appends (when S > 0) and cross a block flush (which takes the two-call
+    path): every step's
+    output agrees within one fp16 ulp (the two runs may hand blocks to wavefronts in different
+    orders), some steps are checked against the oracle, and the two caches end bit-identical
+    (the fused path's ring copy is exact)."""
+    require_gpu()
+    b, hkv, nrep, n0, steps = 2, 2, 4, 1, 70
+    w = W["llama3_8b"]
+    k, v = synth.kv_tokens(w, 41, 42, b, n0 + steps, hkv, 128)
+    kw = _kw(fmt, b, hkv, nrep, n0 + steps + 8, r, s, k, v)
+    if theta:
+        kw.update(rope_theta=theta)
+    ca, cb = make_cache(kw), make_cache(kw)
+    append_chunks(ca, k[:, :n0], v[:, :n0], [n0])
+    append_chunks(cb, k[:, :n0], v[:, :n0], [n0])
+    ws_bytes = max(ca.workspace_bytes(0), cb.workspace_bytes(0))
+    wa = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+    wb = torch.empty_like(wa)
+    for i in range(steps):
+        kt, vt = to_dev(k[:, n0 + i:n0 + i + 1]), to_dev(v[:, n0 + i:n0 + i + 1])
+        q = synth.queries(w, b, hkv * nrep, 128, seed_offset=100 + i)
+        qd = to_dev(q)
+        oa, ob = torch.empty_like(qd), torch.empty_like(qd)
+        ca.append(kt, vt)
+        ca.attention(qd, oa, wa)
+        cb.append_attention(kt, vt, qd, ob, wb)
+        torch.cuda.synchronize()
+        a, bb = oa.cpu().numpy().astype(np.float64), ob.cpu().numpy().astype(np.float64)
+        assert cb.n_tokens == ca.n_tokens == n0 + i + 1
+        assert np.all(np.abs(bb - a) <= np.maximum(np.abs(a), 1.0) * 2.0**-10), i
+        if i % 17 == 5 or i == steps - 1:
+            st = read_state(cb, olayout_of(kw))
+            kh, vh = ocache.dequantize(st)
+            ref = oattn.attention(q, ocache.attention_keys(st, kh), vh)   # pre-RoPE Keys rotated
+            assert np.max(np.abs(bb - ref)) <= TOL, i
+    olay = olayout_of(kw)
+    assert_states_equal(read_state(cb, olay), read_state(ca, olay))
 
 
 def test_workspace_reuse_any_contents():
