@@ -195,16 +195,19 @@ def test_graph_capture_replays_match_eager():
         del g
 
 
-@pytest.mark.parametrize("fmt,s,r,theta", [("int4", 0, 32, 0.0), ("int8", 4, 32, 0.0), ("fp8", 0, 64, 0.0),
-                                            ("int2_m16", 0, 32, 0.0), ("int4", 2, 32, 500000.0)])
-def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta):
+@pytest.mark.parametrize("fmt,s,r,theta,extra", [("int4", 0, 32, 0.0, ""), ("int8", 4, 32, 0.0, ""),
+                                                  ("fp8", 0, 64, 0.0, ""), ("int2_m16", 0, 32, 0.0, ""),
+                                                  ("int4", 2, 32, 500000.0, ""), ("int4", 0, 32, 0.0, "outliers"),
+                                                  ("int8", 3, 32, 0.0, "paged")])
+def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta, extra):
     """kv_append_decode_attention (one launch when the token only enters the fp16 ring) against
     kv_quant_append + kv_decode_attention on a twin cache, over 70 one-token decode steps that
     start with sink appends (when S > 0) and cross a block flush (which takes the two-call
     path): every step's
     output agrees within one fp16 ulp (the two runs may hand blocks to wavefronts in different
     orders), some steps are checked against the oracle, and the two caches end bit-identical
-    (the fused path's ring copy is exact)."""
+    (the fused path's ring copy is exact).  Also with outliers, and for a paged pool (shuffled
+    one-block pages; there the whole buffers, pre-filled alike, are compared byte for byte)."""
     require_gpu()
     b, hkv, nrep, n0, steps = 2, 2, 4, 1, 70
     w = W["llama3_8b"]
@@ -212,7 +215,19 @@ def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta):
     kw = _kw(fmt, b, hkv, nrep, n0 + steps + 8, r, s, k, v)
     if theta:
         kw.update(rope_theta=theta)
+    if extra == "outliers":
+        kw.update(outliers=1)
+    paged = extra == "paged"
+    if paged:
+        nb = (n0 + steps + 8 - s - r) // 32
+        kw.update(page_blocks=1, num_pages=b * nb + 3)
     ca, cb = make_cache(kw), make_cache(kw)
+    if paged:
+        table = torch.from_numpy(np.random.default_rng(43).permutation(b * nb + 3)[:b * nb]
+                                 .reshape(b, nb).astype(np.int32)).cuda()
+        for c in (ca, cb):
+            c.buf.fill_(0x5A)
+            c.set_block_table(table)
     append_chunks(ca, k[:, :n0], v[:, :n0], [n0])
     append_chunks(cb, k[:, :n0], v[:, :n0], [n0])
     ws_bytes = max(ca.workspace_bytes(0), cb.workspace_bytes(0))
@@ -230,13 +245,16 @@ def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta):
         a, bb = oa.cpu().numpy().astype(np.float64), ob.cpu().numpy().astype(np.float64)
         assert cb.n_tokens == ca.n_tokens == n0 + i + 1
         assert np.all(np.abs(bb - a) <= np.maximum(np.abs(a), 1.0) * 2.0**-10), i
-        if i % 17 == 5 or i == steps - 1:
+        if not paged and (i % 17 == 5 or i == steps - 1):
             st = read_state(cb, olayout_of(kw))
             kh, vh = ocache.dequantize(st)
             ref = oattn.attention(q, ocache.attention_keys(st, kh), vh)   # pre-RoPE Keys rotated
             assert np.max(np.abs(bb - ref)) <= TOL, i
-    olay = olayout_of(kw)
-    assert_states_equal(read_state(cb, olay), read_state(ca, olay))
+    if paged:
+        assert torch.equal(ca.buf, cb.buf)
+    else:
+        olay = olayout_of(kw)
+        assert_states_equal(read_state(cb, olay), read_state(ca, olay))
 
 
 def test_workspace_reuse_any_contents():
