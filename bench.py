@@ -359,9 +359,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
-              "(the decode-attention path shards by KV head / token range without exchange, "
-              "see DESIGN.md)", file=sys.stderr)
+        print("bench.py: measures one GPU; the decode-attention path shards by KV head or by token "
+              "range with no exchange between GPUs, and runs on more than one GPU are not measured here",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -9,7 +9,7 @@ heads.  "KV Cache Quantization Analysis", sec. 5, has the cache dequantized
 before (or inside) attention, with the arithmetic itself done in high
 precision.
 
-Readings (listed in DESIGN.md): query head h reads KV head h // n_rep
+Readings: query head h reads KV head h // n_rep
 (contiguous blocks of query heads share a KV head); the scale is
 1/sqrt(head_dim); one decode query per sequence attends to every cached
 token (sinks, quantized body, fp16 residual) with no mask; the softmax

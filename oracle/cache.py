@@ -14,7 +14,7 @@ What the pages fix
   sensitivity: keeping the attention-sink tokens' K/V in FP16 recovers most
   of the quality.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
 
 * The first ``S`` absolute tokens are sinks, stored verbatim (fp16).
 * The other tokens form the body, indexed u = t - S.  Per-channel Keys need

@@ -10,7 +10,7 @@ to x_hat = s * (q - z), with s the scale and z the zero-point; an asymmetric
 z (non-zero) is preferred when the data is not centred on zero; per-channel /
 per-token granularity stores one (s, z) pair per row or column.
 
-Readings taken where the page is silent (each also listed in the design doc):
+Readings taken where the page is silent:
 
 * range estimator: s and z map the group minimum to code 0 and the group
   maximum to code 2^b - 1 (plain min/max, no clipping);
@@ -52,7 +52,7 @@ fp16 scale / offset metadata (INT formats)
 The 27B KL-divergence study's table of KV-cache sizes per token (34 : 32 : 18
 KiB for 8-bit block formats, FP8 and 4-bit block formats) works out to one
 16-bit scale per 32 values.  The fp16-metadata variant stores 16 bits per
-scale and per offset.  Readings (listed in the design doc):
+scale and per offset.  Readings:
 
 * an fp16 zero-point z = -min / s would lose the s/2 error bound whenever
   |z| is large (its rounding error is up to |z| * 2^-11 code steps), so the
@@ -72,7 +72,7 @@ Dense-and-sparse outliers (INT formats)
 the grid and cost every other value resolution) and sec. 4 (KVQuant, its
 fourth component: per-vector dense-and-sparse quantization keeps outliers
 apart from the quantized values).  The pages give no outlier count or
-selection rule.  Readings (listed in the design doc):
+selection rule.  Readings:
 
 * one outlier per quantization group (the vector: a Key channel's 32 tokens
   of a block, a Value token's 32-channel group), about 3 % of the values;

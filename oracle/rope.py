@@ -7,7 +7,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 Key outlier channels, so KVQuant quantizes the Keys per channel *before*
 RoPE; the rotation is then applied to the dequantized Keys.
 
-The pages do not write the rotation out.  Readings (listed in the design doc):
+The pages do not write the rotation out.  Readings:
 
 * the rotate-half convention of the Llama family: channel i and channel
   i + D/2 (i < D/2) form a pair rotated by the angle pos * theta_i, with
