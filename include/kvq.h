@@ -273,7 +273,10 @@ int32_t kvq_workspace_bytes(const kvq_cache* cache, int32_t blocks_per_group, ui
 int32_t kv_decode_attention(const kvq_cache* cache, const void* q, void* out, void* ws,
                             uint64_t ws_bytes, void* stream);
 
-/* One decode step of one layer: kv_quant_append of one token (K, V: device
+/* One decode step of one layer, the two hot calls back to back as the method
+ * integrates them ("KV Cache Quantization Analysis", sec. 5, system
+ * integration: quantize the new K, V right after they are produced, then
+ * dequantize inside attention): kv_quant_append of one token (K, V: device
  * fp16 [B][1][Hkv][D]) followed by kv_decode_attention over the cache that
  * includes it, with the results of those two calls (the same kernel, the
  * library's own split).  When the token only enters the fp16
