@@ -329,6 +329,40 @@ def test_full_size_workloads(name, fmt, steps):
     _full_size(name, fmt, steps=steps)
 
 
+@pytest.mark.parametrize("name,fmt,steps", [("llama3_8b_kivi2", "int2", 40), ("llama3_8b", "int8", 33)])
+def test_full_size_fused_decode_steps(name, fmt, steps):
+    """The decode step the benchmark times, at full size: after the 8192-token prefill, every
+    step goes through kv_append_decode_attention (one launch, or the append's kernels first on
+    the step where a block leaves the window); the last step's output is checked against the
+    oracle on sampled (sequence, KV head) pairs of the final cache."""
+    require_gpu()
+    w = W[name]
+    k, v = synth.prefill(w)
+    kw = _kw(fmt, w.batch, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.seq_len + 64,
+             w.residual_tokens, w.sink_tokens, k, v)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [w.seq_len])
+    q = synth.queries(w)
+    qd = to_dev(q)
+    out = torch.empty_like(qd)
+    ws = torch.empty(c.workspace_bytes(0) // 4 + 4, dtype=torch.float32, device="cuda")
+    for j in range(steps):
+        ks, vs = synth.append_step(w, j)
+        c.append_attention(to_dev(ks), to_dev(vs), qd, out, ws)
+    torch.cuda.synchronize()
+    assert c.n_tokens == w.seq_len + steps
+    got = out.cpu().numpy().astype(np.float64)
+    st = read_state(c, olayout_of(kw))
+    rng = np.random.default_rng(2)
+    nrep = w.num_q_heads // w.num_kv_heads
+    for bi, gi in rng.integers(0, [w.batch, w.num_kv_heads], size=(4, 2)):
+        hs = slice(gi * nrep, (gi + 1) * nrep)
+        kh, vh = ocache.dequantize(substate(st, bi, gi))
+        ref = oattn.attention(q[bi:bi + 1, hs], kh, vh)
+        err = np.max(np.abs(got[bi:bi + 1, hs] - ref))
+        assert err <= TOL, (bi, gi, err)
+
+
 @pytest.mark.parametrize("fmt", ["int8", "int4"])
 def test_long_context_layer(fmt):
     """batch 1, 131072 tokens: the two layer formats of the mixed-precision stack."""
