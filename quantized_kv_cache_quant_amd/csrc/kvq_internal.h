@@ -115,8 +115,10 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 //   part_wave   slot kGroupWaves * (g + bh) + w   wavefront w of workgroup g, head bh
 //   part_group  slot g + bh                      workgroup g, head bh (its wavefronts merged)
 // Workgroup g's range touches heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk),
-// so g + bh never collides between workgroups.  A second kernel combines each
-// head's workgroup and fp16 partials and writes the output rows.
+// so g + bh never collides between workgroups.  Each workgroup folds its
+// wavefront slots and the fp16 slots it produced into its merged slot; the
+// last workgroup to finish a head (arrival counter in the cache's sync plane)
+// combines the head's merged slots and writes the output rows.
 // With no quantized block (nblk == 0) workgroup g takes the fp16 blocks of head g.
 struct AttnParams {
   const uint8_t* k_codes;
