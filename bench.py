@@ -22,11 +22,14 @@ order; INT8 and INT4 with Keys stored before RoPE, rotated in attention
 with base 500000; INT4 and INT2 with one exact fp16 outlier per group),
 eight layer caches each.
 
-Timed regions, both bracketed by HIP events on the stream the library
+Timed regions, each bracketed by HIP events on the stream the library
 launches on (torch's current stream):
   * steps: `--steps` decode steps back to back -> value (effective KV GB/s =
     algorithmic attention bytes / wall time, appends included), ms_per_step,
     tokens/s;
+  * prefill: each layer cache's kv_quant_append of the prompt between its own
+    event pair -> prefill_quantize (fp16 K/V input GB/s; the first layer's
+    call, which pays one-off costs, is left out);
   * attention sweep: every layer's kv_decode_attention call, each bracketed
     by its own event pair -> the roofline entry (algorithmic bytes per call /
     mean call time).  The events sit outside the step loop because an event
@@ -220,11 +223,18 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     del kp, vp
     amax_k, amax_v = float(kd.abs().max().float().item()), float(vd.abs().max().float().item())
     caches = []
+    pre_ev = []                                 # prefill quantize-on-append, one event pair per layer
     for li, fmt in enumerate(fmt_list):
         c = make_cache(kvq, w, fmt, max_tokens, amax_k, amax_v)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         c.append(kd, vd)
+        e1.record()
+        pre_ev.append((e0, e1))
         caches.append(c)
     torch.cuda.synchronize()
+    pre_us = [a.elapsed_time(bb) * 1e3 for a, bb in (pre_ev[1:] or pre_ev)]   # the first pays one-off costs
+    pre_in = 2 * kd.numel() * kd.element_size()                               # fp16 K and V of the prompt
     del kd, vd
     log(f"{layers} layer caches prefilled ({sum(c.buf.numel() for c in caches) / 2**30:.2f} GiB)")
     steps_k, steps_v = [], []
@@ -291,6 +301,10 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         "step_us_per_layer": ms_step * 1e3 / layers,
         "bytes_per_attn_call": sweep_bytes,
         "attn_calls_timed": len(attn_ms),
+        "prefill_quantize": {"us_per_layer": round(float(np.mean(pre_us)), 1),
+                             "input_gbps": round(pre_in / (float(np.mean(pre_us)) * 1e-6) / 1e9, 1),
+                             "tokens_per_s": round(b * n0 / (float(np.mean(pre_us)) * 1e-6)),
+                             "layers_timed": len(pre_us)},
     }
     res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
     log(f"{'/'.join(res['formats'])}: {ms_step:.3f} ms/step, {res['tokens_per_s']:.0f} tok/s, "
@@ -353,6 +367,36 @@ def cpu_baseline(w, fmt, seconds):
             "sample": f"{done} x one (sequence, KV head) decode step of {fmt} ({n} tokens, {nrep} query heads): "
                       f"fp64 dequantize + attention, {dt:.1f} s, single thread",
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def cpu_quantize_baseline(w, fmt, seconds):
+    """The CPU oracle's quantize-on-append of the prompt for one (sequence, KV head), repeated for a
+    bounded time: GB/s of fp16 K and V input, beside the GPU's prefill_quantize."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cache as ocache
+    from oracle import quant
+    from quantized_kv_cache_quant_amd import synth
+
+    nrep = w.num_q_heads // w.num_kv_heads
+    n = w.seq_len
+    k, v = synth.kv_tokens(w, 1000 + w.index, 2000 + w.index, 1, n, 1, w.head_dim)
+    lay = ocache.Layout(1, 1, nrep, w.head_dim, n, fmt, residual_tokens=w.residual_tokens,
+                        sink_tokens=w.sink_tokens, k_scale=float(quant.fp8_scale(k)),
+                        v_scale=float(quant.fp8_scale(v)))
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            ocache.build_cache(k, v, lay)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    nbytes = 2 * n * w.head_dim * 2
+    return {"value": nbytes * done / dt / 1e9, "unit": "GB/s of fp16 K/V input", "cores": 1, "kind": "oracle",
+            "sample": f"{done} x the {n}-token prompt of one (sequence, KV head) quantized to {fmt} "
+                      f"(fp32 steps as specified), {dt:.1f} s, single thread"}
 
 
 def main():
@@ -418,6 +462,7 @@ def main():
         "read_gbps_measured": read_gbps,
         "read_gbps_by_shape": reads,
         "attn_frac_of_measured_read": round(head["attn_gbps"] / read_gbps, 4),
+        "prefill_quantize": head["prefill_quantize"],
         "roofline": {"bound": "hbm", "achieved": round(head["attn_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(head["attn_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": counter_traffic(variants[0]),
@@ -434,6 +479,8 @@ def main():
         fmt0 = variants[0] if variants[0] != "mixed" else "int4"
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(w, fmt0, args.cpu_seconds)
+        log("timing the CPU oracle's prefill quantization for ~5 s")
+        line["cpu_baseline_quantize"] = cpu_quantize_baseline(w, fmt0, 5.0)
     print(json.dumps(line), flush=True)
 
 
