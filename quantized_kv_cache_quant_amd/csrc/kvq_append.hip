@@ -21,10 +21,12 @@
 //                On a cache's first append it also zeroes the attention
 //                arrival counters.
 //
-// Bit-exactness: every quantization step is one IEEE fp32 operation in the
-// order of the formula (true division, no contraction: this file is built
-// with -ffp-contract=off and correctly rounded fp32 division), rint is
-// round-half-even, exactly like the CPU oracle.
+// Bit-exactness: every quantization step is one correctly rounded IEEE fp32
+// operation in the order of the formula, exactly like the CPU oracle: the
+// division x / s by the exact reciprocal-and-remainder sequence of div_rn
+// (FP8 by true division), no contraction (this file is built with
+// -ffp-contract=off and correctly rounded fp32 division), rint
+// round-half-even.
 #include "kvq_internal.h"
 
 #pragma clang fp contract(off)
@@ -36,18 +38,32 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Integer code of x in a group with scale s and zero-point z (fp32 pairs:
-// rint(x / s + z)) or, with fp16 metadata (OFFSET), offset z = m:
-// rint((x - m) / s).  One fp32 operation per step, clamped to the code range.
+// The correctly rounded quotient x / s from y = RN(1 / s) (one correctly
+// rounded division per group): q = RN(x y) lies within one ulp of x / s, the
+// remainder x - q s is then exact in one fused multiply-add, and RN(q + r y)
+// is RN(x / s) (Markstein's theorem on division by a correctly rounded
+// reciprocal; it holds without overflow or underflow, which is the case
+// here: x is an fp16 value or the difference of two, and s a group scale of
+// fp16 data, so |x / s| stays below 2^49 and above 2^-41 or is 0).
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  return __builtin_fmaf(r, y, q);
+}
+
+// Integer code of x in a group with scale s (reciprocal y = RN(1 / s)) and
+// zero-point z (fp32 pairs: rint(x / s + z)) or, with fp16 metadata
+// (OFFSET), offset z = m: rint((x - m) / s).  Each step is one correctly
+// rounded fp32 operation, clamped to the code range.
 template <int BITS, bool OFFSET>
-__device__ __forceinline__ uint32_t encode_int(float x, float s, float z) {
+__device__ __forceinline__ uint32_t encode_int(float x, float s, float z, float y) {
   constexpr float kQmax = (float)((1 << BITS) - 1);
   float v;
   if constexpr (OFFSET) {
     v = x - z;
-    v = v / s;
+    v = div_rn(v, s, y);
   } else {
-    v = x / s;
+    v = div_rn(x, s, y);
     v = v + z;
   }
   v = __builtin_rintf(v);
@@ -94,8 +110,8 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 
   __shared__ float ks[kBlock][kHeadDim + 1];
   __shared__ float vs[kBlock][kHeadDim + 1];
-  __shared__ float sk[kHeadDim], zk[kHeadDim];
-  __shared__ float sv[kBlock][kVGroups], zv[kBlock][kVGroups];
+  __shared__ float sk[kHeadDim], zk[kHeadDim], rk[kHeadDim];            // rk = RN(1 / sk)
+  __shared__ float sv[kBlock][kVGroups], zv[kBlock][kVGroups], rv[kBlock][kVGroups];
   __shared__ int ko[kHeadDim];               // outliers: token of each channel's outlier
   __shared__ int vo[kBlock][kVGroups];       // outliers: channel (in group) of each token's outlier
 
@@ -179,6 +195,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
         sk[c] = half_bits_to_float(sb);
         zk[c] = mn;
+        rk[c] = 1.0f / sk[c];
         const int sp = kRopeK ? rope_stored_pos(c) : c;   // stored position of channel c
         reinterpret_cast<uint32_t*>(p.k_meta)[rec * kHeadDim + sp] = sb | (mb << 16);
       } else {
@@ -187,6 +204,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const float z = (-mn) / s;
         sk[c] = s;
         zk[c] = z;
+        rk[c] = 1.0f / s;
         float* km = p.k_meta + rec * (2 * kHeadDim);   // [stored position][s, z]
         const int sp = kRopeK ? rope_stored_pos(c) : c;
         km[2 * sp] = s;
@@ -227,6 +245,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const uint32_t mb = __builtin_bit_cast(uint16_t, (_Float16)mn);
         sv[t][g] = half_bits_to_float(sb);
         zv[t][g] = mn;
+        rv[t][g] = 1.0f / sv[t][g];
         reinterpret_cast<uint32_t*>(p.v_meta)[rec * (kVGroups * kBlock) + g * kBlock + t] =
             sb | (mb << 16);
       } else {
@@ -235,6 +254,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const float z = (-mn) / s;
         sv[t][g] = s;
         zv[t][g] = z;
+        rv[t][g] = 1.0f / s;
         float* vm = p.v_meta + rec * (2 * kVGroups * kBlock);  // [group][token][s, z]
         vm[2 * (g * kBlock + t)] = s;
         vm[2 * (g * kBlock + t) + 1] = z;
@@ -275,7 +295,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int c = chan(wi * kPer + j);
-          uint32_t code = encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c]);
+          uint32_t code = encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c], rk[c]);
           if constexpr (kOut) code = ko[c] == t ? 0u : code;            // the outlier's code is 0
           word |= code << (j * kBits);
         }
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = record_token(qd, j);
-          word |= oz(encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g]), t, ch, g) << (4 * j);
+          word |= oz(encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (4 * j);
         }
       } else if constexpr (kBits == 8) {          // bytes 8m..8m+7 = T0 T4 T1 T5 T2 T6 T3 T7
         const int ch = 16 * (wi >> 1) + r;
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int t = record_token(qd, sel(base + k));
-            word |= oz(encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g]), t, ch, g) << (8 * k);
+            word |= oz(encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (8 * k);
           }
         }
       } else {                                    // INT2 word p: A = 32p + r, B = 32p + 16 + r
@@ -331,10 +351,10 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t0 = record_token(qd, j), t1 = record_token(qd, 4 + j);
-          word |= oz(encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga]), t0, cha, ga) << (2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb]), t0, chb, gb) << (8 + 2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga]), t1, cha, ga) << (16 + 2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb]), t1, chb, gb) << (24 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga], rv[t0][ga]), t0, cha, ga) << (2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb], rv[t0][gb]), t0, chb, gb) << (8 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga], rv[t1][ga]), t1, cha, ga) << (16 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb], rv[t1][gb]), t1, chb, gb) << (24 + 2 * j);
         }
       }
       dst[w] = word;
