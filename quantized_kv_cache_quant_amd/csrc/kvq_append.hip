@@ -39,9 +39,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 }
 
 // The correctly rounded quotient x / s from y = RN(1 / s) (one correctly
-// rounded division per group): q = RN(x y) lies within one ulp of x / s, the
-// remainder x - q s is then exact in one fused multiply-add, and RN(q + r y)
-// is RN(x / s) (Markstein's theorem on division by a correctly rounded
+// rounded division per group): q = RN(x y) lies within one ulp of x / s,
+// r = RN(x - q s) is one fused multiply-add, and RN(q + r y), another, is
+// RN(x / s) (Markstein's theorem on division by a correctly rounded
 // reciprocal; it holds without overflow or underflow, which is the case
 // here: x is an fp16 value or the difference of two, and s a group scale of
 // fp16 data, so |x / s| stays below 2^49 and above 2^-41 or is 0).
