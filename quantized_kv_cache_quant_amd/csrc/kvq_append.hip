@@ -108,8 +108,13 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   constexpr int kRowBytes = kHeadDim * kBits / 8;   // packed bytes per token
   constexpr float kQmax = (float)((1 << kBits) - 1);
 
-  __shared__ float ks[kBlock][kHeadDim + 1];
-  __shared__ float vs[kBlock][kHeadDim + 1];
+  // the block's K and V as their fp16 bits (exact; widened to fp32 where
+  // read): rows of kRowH halves, 16-byte aligned for the gather's stores
+  constexpr int kRowH = kHeadDim + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ksh[kBlock][kRowH];
+  __shared__ __attribute__((aligned(16))) uint16_t vsh[kBlock][kRowH];
+  auto ks_at = [&](int t, int c) { return half_bits_to_float(ksh[t][c]); };
+  auto vs_at = [&](int t, int c) { return half_bits_to_float(vsh[t][c]); };
   __shared__ float sk[kHeadDim], zk[kHeadDim], rk[kHeadDim];            // rk = RN(1 / sk)
   __shared__ float sv[kBlock][kVGroups], zv[kBlock][kVGroups], rv[kBlock][kVGroups];
   __shared__ int ko[kHeadDim];               // outliers: token of each channel's outlier
@@ -142,17 +147,8 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       ksrc = p.k_in + off;
       vsrc = p.v_in + off;
     }
-    const uint4 kk = *reinterpret_cast<const uint4*>(ksrc);
-    const uint4 vv = *reinterpret_cast<const uint4*>(vsrc);
-    const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ks[t][c8 + 2 * j] = half_bits_to_float(kw[j] & 0xFFFFu);
-      ks[t][c8 + 2 * j + 1] = half_bits_to_float(kw[j] >> 16);
-      vs[t][c8 + 2 * j] = half_bits_to_float(vw[j] & 0xFFFFu);
-      vs[t][c8 + 2 * j + 1] = half_bits_to_float(vw[j] >> 16);
-    }
+    *reinterpret_cast<uint4*>(&ksh[t][c8]) = *reinterpret_cast<const uint4*>(ksrc);
+    *reinterpret_cast<uint4*>(&vsh[t][c8]) = *reinterpret_cast<const uint4*>(vsrc);
   }
   __syncthreads();
 
@@ -166,26 +162,26 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         // the outlier: largest magnitude, lowest token index on ties; the
         // range comes from the other 31 values
         int oi = 0;
-        float oa = fabsf(ks[0][c]);
+        float oa = fabsf(ks_at(0, c));
         for (int t = 1; t < kBlock; ++t)
-          if (fabsf(ks[t][c]) > oa) { oa = fabsf(ks[t][c]); oi = t; }
+          if (fabsf(ks_at(t, c)) > oa) { oa = fabsf(ks_at(t, c)); oi = t; }
         const int first = oi == 0 ? 1 : 0;
-        mn = ks[first][c];
+        mn = ks_at(first, c);
         mx = mn;
         for (int t = 0; t < kBlock; ++t) {
           if (t == oi) continue;
-          mn = fminf(mn, ks[t][c]);
-          mx = fmaxf(mx, ks[t][c]);
+          mn = fminf(mn, ks_at(t, c));
+          mx = fmaxf(mx, ks_at(t, c));
         }
         ko[c] = oi;
-        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)ks[oi][c]);   // exact: an fp16 input
+        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)ks_at(oi, c));   // exact: an fp16 input
         p.k_out[rec * kHeadDim + (kRopeK ? rope_stored_pos(c) : c)] = (uint32_t)oi | (xb << 16);
       } else {
-        mn = ks[0][c];
-        mx = ks[0][c];
+        mn = ks_at(0, c);
+        mx = ks_at(0, c);
         for (int t = 1; t < kBlock; ++t) {
-          mn = fminf(mn, ks[t][c]);
-          mx = fmaxf(mx, ks[t][c]);
+          mn = fminf(mn, ks_at(t, c));
+          mx = fmaxf(mx, ks_at(t, c));
         }
       }
       mn = mn + 0.0f;                                 // a zero minimum is +0
@@ -216,26 +212,26 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       float mn, mx;
       if constexpr (kOut) {
         int oi = 0;
-        float oa = fabsf(vs[t][kVGroup * g]);
+        float oa = fabsf(vs_at(t, kVGroup * g));
         for (int c = 1; c < kVGroup; ++c)
-          if (fabsf(vs[t][kVGroup * g + c]) > oa) { oa = fabsf(vs[t][kVGroup * g + c]); oi = c; }
+          if (fabsf(vs_at(t, kVGroup * g + c)) > oa) { oa = fabsf(vs_at(t, kVGroup * g + c)); oi = c; }
         const int first = oi == 0 ? 1 : 0;
-        mn = vs[t][kVGroup * g + first];
+        mn = vs_at(t, kVGroup * g + first);
         mx = mn;
         for (int c = 0; c < kVGroup; ++c) {
           if (c == oi) continue;
-          mn = fminf(mn, vs[t][kVGroup * g + c]);
-          mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+          mn = fminf(mn, vs_at(t, kVGroup * g + c));
+          mx = fmaxf(mx, vs_at(t, kVGroup * g + c));
         }
         vo[t][g] = oi;
-        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)vs[t][kVGroup * g + oi]);
+        const uint32_t xb = __builtin_bit_cast(uint16_t, (_Float16)vs_at(t, kVGroup * g + oi));
         p.v_out[rec * (kVGroups * kBlock) + g * kBlock + t] = (uint32_t)oi | (xb << 16);
       } else {
-        mn = vs[t][kVGroup * g];
+        mn = vs_at(t, kVGroup * g);
         mx = mn;
         for (int c = 1; c < kVGroup; ++c) {
-          mn = fminf(mn, vs[t][kVGroup * g + c]);
-          mx = fmaxf(mx, vs[t][kVGroup * g + c]);
+          mn = fminf(mn, vs_at(t, kVGroup * g + c));
+          mx = fmaxf(mx, vs_at(t, kVGroup * g + c));
         }
       }
       mn = mn + 0.0f;
@@ -288,14 +284,14 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       auto chan = [](int sp) { return kRopeK ? rope_channel(sp) : sp; };
       if constexpr (kFp8) {
         const int c = wi * 4;
-        word = encode_fp8_pair<kE5M2>(ks[t][chan(c)], ks[t][chan(c + 1)], p.k_scale) |
-               (encode_fp8_pair<kE5M2>(ks[t][chan(c + 2)], ks[t][chan(c + 3)], p.k_scale) << 16);
+        word = encode_fp8_pair<kE5M2>(ks_at(t, chan(c)), ks_at(t, chan(c + 1)), p.k_scale) |
+               (encode_fp8_pair<kE5M2>(ks_at(t, chan(c + 2)), ks_at(t, chan(c + 3)), p.k_scale) << 16);
       } else {
         constexpr int kPer = 32 / kBits;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int c = chan(wi * kPer + j);
-          uint32_t code = encode_int<kBits, kM16>(ks[t][c], sk[c], zk[c], rk[c]);
+          uint32_t code = encode_int<kBits, kM16>(ks_at(t, c), sk[c], zk[c], rk[c]);
           if constexpr (kOut) code = ko[c] == t ? 0u : code;            // the outlier's code is 0
           word |= code << (j * kBits);
         }
@@ -324,7 +320,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = record_token(qd, j);
-          word |= oz(encode_int<4, kM16>(vs[t][ch], sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (4 * j);
+          word |= oz(encode_int<4, kM16>(vs_at(t, ch), sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (4 * j);
         }
       } else if constexpr (kBits == 8) {          // bytes 8m..8m+7 = T0 T4 T1 T5 T2 T6 T3 T7
         const int ch = 16 * (wi >> 1) + r;
@@ -333,16 +329,16 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         const int base = 4 * (wi & 1);
         auto sel = [](int k) { return (k >> 1) + 4 * (k & 1); };
         if constexpr (kFp8) {
-          const float x0 = vs[record_token(qd, sel(base + 0))][ch];
-          const float x1 = vs[record_token(qd, sel(base + 1))][ch];
-          const float x2 = vs[record_token(qd, sel(base + 2))][ch];
-          const float x3 = vs[record_token(qd, sel(base + 3))][ch];
+          const float x0 = vs_at(record_token(qd, sel(base + 0)), ch);
+          const float x1 = vs_at(record_token(qd, sel(base + 1)), ch);
+          const float x2 = vs_at(record_token(qd, sel(base + 2)), ch);
+          const float x3 = vs_at(record_token(qd, sel(base + 3)), ch);
           word = encode_fp8_pair<kE5M2>(x0, x1, p.v_scale) | (encode_fp8_pair<kE5M2>(x2, x3, p.v_scale) << 16);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int t = record_token(qd, sel(base + k));
-            word |= oz(encode_int<8, kM16>(vs[t][ch], sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (8 * k);
+            word |= oz(encode_int<8, kM16>(vs_at(t, ch), sv[t][g], zv[t][g], rv[t][g]), t, ch, g) << (8 * k);
           }
         }
       } else {                                    // INT2 word p: A = 32p + r, B = 32p + 16 + r
@@ -351,10 +347,10 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t0 = record_token(qd, j), t1 = record_token(qd, 4 + j);
-          word |= oz(encode_int<2, kM16>(vs[t0][cha], sv[t0][ga], zv[t0][ga], rv[t0][ga]), t0, cha, ga) << (2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t0][chb], sv[t0][gb], zv[t0][gb], rv[t0][gb]), t0, chb, gb) << (8 + 2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t1][cha], sv[t1][ga], zv[t1][ga], rv[t1][ga]), t1, cha, ga) << (16 + 2 * j);
-          word |= oz(encode_int<2, kM16>(vs[t1][chb], sv[t1][gb], zv[t1][gb], rv[t1][gb]), t1, chb, gb) << (24 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs_at(t0, cha), sv[t0][ga], zv[t0][ga], rv[t0][ga]), t0, cha, ga) << (2 * j);
+          word |= oz(encode_int<2, kM16>(vs_at(t0, chb), sv[t0][gb], zv[t0][gb], rv[t0][gb]), t0, chb, gb) << (8 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs_at(t1, cha), sv[t1][ga], zv[t1][ga], rv[t1][ga]), t1, cha, ga) << (16 + 2 * j);
+          word |= oz(encode_int<2, kM16>(vs_at(t1, chb), sv[t1][gb], zv[t1][gb], rv[t1][gb]), t1, chb, gb) << (24 + 2 * j);
         }
       }
       dst[w] = word;
