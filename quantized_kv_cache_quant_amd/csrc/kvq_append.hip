@@ -358,27 +358,29 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   }
 }
 
-// One thread per 16-byte chunk of one token row of K or V.
+// One thread per 16-byte chunk of one token row of K or V, over the tokens
+// that are copied (sinks, then residual tokens; a long prefill quantizes the
+// others straight from the input and launches no thread for them).
 __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int b = blockIdx.y;
   if (p.sync_zero && e < p.hkv) p.sync_zero[(int64_t)b * p.hkv + e] = 0;
-  const int64_t total = (int64_t)p.T * p.hkv * 2 * 16;
+  const int64_t total = p.n_copy * p.hkv * 2 * 16;
   if (e >= total) return;
   const int chunk = (int)(e & 15);
   int64_t rest = e >> 4;
   const int kv = (int)(rest & 1);
   rest >>= 1;
   const int h = (int)(rest % p.hkv);
-  const int64_t i = rest / p.hkv;                  // input token
-  const int64_t t = p.n_old + i;                   // absolute token
+  const int64_t k = rest / p.hkv;                  // copied token
+  const int64_t t = k < p.n_sink_copy ? p.n_old + k : p.ring_first_t + (k - p.n_sink_copy);   // absolute
+  const int64_t i = t - p.n_old;                   // input token
   uint16_t* dst;
   if (t < p.sink) {
     uint16_t* plane = kv ? p.v_sink : p.k_sink;
     dst = plane + (((int64_t)b * p.hkv + h) * p.sink + t) * kHeadDim + chunk * 8;
   } else {
-    const int64_t u = t - p.sink;
-    if (u < p.n_q_new) return;                     // quantized straight from the input
+    const int64_t u = t - p.sink;                  // u >= n_q_new: a residual token
     uint16_t* plane = kv ? p.v_ring : p.k_ring;
     dst = plane + (((int64_t)b * p.hkv + h) * p.ring_slots + (u % p.ring_slots)) * kHeadDim + chunk * 8;
   }
@@ -425,8 +427,10 @@ hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int bat
 }
 
 hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s) {
-  const int64_t total = (int64_t)p.T * p.hkv * 2 * 16;
-  const int64_t blocks = (total + 255) / 256;
+  const int64_t total = p.n_copy * p.hkv * 2 * 16;
+  int64_t blocks = (total + 255) / 256;
+  if (p.sync_zero) blocks = blocks > (p.hkv + 255) / 256 ? blocks : (p.hkv + 255) / 256;   // zeroing threads
+  if (blocks == 0) return hipSuccess;              // nothing to copy
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks, batch), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -372,6 +372,11 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
   cp.hkv = L.num_kv_heads;
   cp.sink = L.sink_tokens;
   cp.ring_slots = c->ring_slots;
+  // copied tokens: new sinks [n_old, min(n_new, S)), then new residual tokens
+  // [max(n_old, S + n_q_new), n_new)
+  cp.n_sink_copy = std::max<int64_t>(0, std::min<int64_t>(n_new, L.sink_tokens) - n_old);
+  cp.ring_first_t = std::max<int64_t>(n_old, (int64_t)L.sink_tokens + w1.n_q);
+  cp.n_copy = cp.n_sink_copy + std::max<int64_t>(0, n_new - cp.ring_first_t);
   // the first append of a cache also sets the attention arrival counters to 0
   cp.sync_zero = n_old == 0 ? reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC)) : nullptr;
   if (launch_copy(cp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;

@@ -98,6 +98,9 @@ struct CopyParams {
   int64_t n_q_new;        // quantized body tokens after the append
   int32_t T, hkv, sink, ring_slots;
   int32_t* sync_zero;     // non-null on a cache's first append: [B][Hkv] counters set to 0
+  int64_t n_sink_copy;    // appended tokens copied: n_sink_copy sinks from token n_old, then
+  int64_t n_copy;         // n_copy - n_sink_copy residual tokens from token ring_first_t
+  int64_t ring_first_t;   // (the tokens in between are quantized straight from the input)
 };
 
 hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s);
