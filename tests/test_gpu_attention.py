@@ -197,11 +197,12 @@ def test_graph_capture_replays_match_eager():
         del g
 
 
-@pytest.mark.parametrize("fmt,s,r,theta,extra", [("int4", 0, 32, 0.0, ""), ("int8", 4, 32, 0.0, ""),
-                                                  ("fp8", 0, 64, 0.0, ""), ("int2_m16", 0, 32, 0.0, ""),
-                                                  ("int4", 2, 32, 500000.0, ""), ("int4", 0, 32, 0.0, "outliers"),
-                                                  ("int8", 3, 32, 0.0, "paged")])
-def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta, extra):
+@pytest.mark.parametrize("fmt,s,r,theta,extra,nrep", [
+    ("int4", 0, 32, 0.0, "", 4), ("int8", 4, 32, 0.0, "", 4), ("fp8", 0, 64, 0.0, "", 4),
+    ("int2_m16", 0, 32, 0.0, "", 4), ("int4", 2, 32, 500000.0, "", 4), ("int4", 0, 32, 0.0, "outliers", 4),
+    ("int8", 3, 32, 0.0, "paged", 4), ("fp8_e5m2", 0, 32, 0.0, "", 8), ("int8_m16", 2, 13, 0.0, "", 1),
+    ("int2", 0, 0, 0.0, "", 2)])
+def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta, extra, nrep):
     """kv_append_decode_attention (one launch when the token only enters the fp16 ring) against
     kv_quant_append + kv_decode_attention on a twin cache, over 70 one-token decode steps that
     start with sink appends (when S > 0) and cross a block flush (which takes the two-call
@@ -209,9 +210,10 @@ def test_fused_append_attention_matches_separate_calls(fmt, s, r, theta, extra):
     output agrees within one fp16 ulp (the two runs may hand blocks to wavefronts in different
     orders), some steps are checked against the oracle, and the two caches end bit-identical
     (the fused path's ring copy is exact).  Also with outliers, and for a paged pool (shuffled
-    one-block pages; there the whole buffers, pre-filled alike, are compared byte for byte)."""
+    one-block pages; there the whole buffers, pre-filled alike, are compared byte for byte).
+    Grouped-query ratios 1, 2, 4 and 8; windows of 0, 13, 32 and 64 tokens."""
     require_gpu()
-    b, hkv, nrep, n0, steps = 2, 2, 4, 1, 70
+    b, hkv, n0, steps = 2, 2, 1, 70
     w = W["llama3_8b"]
     k, v = synth.kv_tokens(w, 41, 42, b, n0 + steps, hkv, 128)
     kw = _kw(fmt, b, hkv, nrep, n0 + steps + 8, r, s, k, v)
