@@ -212,12 +212,12 @@ def test_library_side_byte_count_agrees_with_oracle():
     from quantized_kv_cache_quant_amd import accounting
     for name in synth.WORKLOADS:
         w = synth.WORKLOADS[name]
-        for fmt, m16 in (("int8", 0), ("int4", 0), ("int2", 0), ("fp8", 0), ("fp8_e5m2", 0), ("int4", 1),
-                         ("int2", 1)):
+        for fmt, m16, out in (("int8", 0, 0), ("int4", 0, 0), ("int2", 0, 0), ("fp8", 0, 0), ("fp8_e5m2", 0, 0),
+                              ("int4", 1, 0), ("int2", 1, 0), ("int4", 0, 1), ("int2", 0, 1), ("int8", 1, 1)):
             for n in (1, 100, w.seq_len, w.seq_len + 37):
                 lay = cache.Layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
                                    residual_tokens=w.residual_tokens, sink_tokens=w.sink_tokens,
-                                   meta_fp16=bool(m16))
+                                   meta_fp16=bool(m16), outliers=bool(out))
                 assert accounting.attention_bytes(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt,
-                                                  w.sink_tokens, w.residual_tokens,
-                                                  meta_fp16=bool(m16)) == nbytes.step_bytes(lay, n)["total"]
+                                                  w.sink_tokens, w.residual_tokens, meta_fp16=bool(m16),
+                                                  outliers=bool(out)) == nbytes.step_bytes(lay, n)["total"]
