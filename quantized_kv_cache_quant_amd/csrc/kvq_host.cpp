@@ -2,6 +2,7 @@
 // plane placement, token routing and launch configuration.  Nothing here
 // touches device memory; kernels are enqueued on the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -61,17 +62,20 @@ void plane_sizes(const kvq_layout& L, uint64_t sz[KVQ_NUM_PLANES]) {
   sz[KVQ_PLANE_SYNC] = bh * 4;                                               // int32 per (sequence, KV head)
 }
 
-// Compute units of the current device (256 when no device answers).
+// Compute units of the current device (256 when no device answers), cached
+// per device id; concurrent first calls store the same value.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
 int64_t device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus = n;
-  }
-  return cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  int cached = dev < kMaxDevices ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cached > 0) return cached;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 struct AttnPlan {

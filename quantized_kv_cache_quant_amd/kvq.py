@@ -164,19 +164,45 @@ class Cache:
                                               int(table.shape[1])), "kvq_cache_set_block_table")
         self.table = table
 
-    def append(self, k, v, stream=None) -> None:
-        """k, v: contiguous fp16 device tensors [B][T][Hkv][D]."""
+    def _check_kv(self, k, v, t=None) -> int:
+        """k, v: fp16 device tensors of one shape [B][T][Hkv][D] matching the layout; returns T.
+        Shapes are checked first, then dtype, contiguity and device: a mistake raises ValueError
+        before anything reaches the library."""
+        L = self.layout
+        if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"K and V must both be [B][T][Hkv][D]; got {tuple(k.shape)} and {tuple(v.shape)}")
+        if (k.shape[0], k.shape[2], k.shape[3]) != (L.batch, L.num_kv_heads, L.head_dim):
+            raise ValueError(f"K / V shape {tuple(k.shape)} does not match the layout "
+                             f"[{L.batch}][T][{L.num_kv_heads}][{L.head_dim}]")
+        if t is not None and k.shape[1] != t:
+            raise ValueError(f"K / V must hold {t} token(s) per sequence; got {k.shape[1]}")
         _check_tensor(k, "K")
         _check_tensor(v, "V")
-        t = k.shape[1]
+        return int(k.shape[1])
+
+    def _check_q_out(self, q, out, ws) -> None:
+        """q, out: fp16 device tensors [B][Hq][D]; ws: a device tensor (shapes checked first)."""
+        L = self.layout
+        want = (L.batch, L.num_q_heads, L.head_dim)
+        for t, name in ((q, "q"), (out, "out")):
+            if tuple(t.shape) != want:
+                raise ValueError(f"{name} must be [{want[0]}][{want[1]}][{want[2]}]; got {tuple(t.shape)}")
+        _check_tensor(q, "q")
+        _check_tensor(out, "out")
+        if not getattr(ws, "is_cuda", False):
+            raise ValueError("ws must be a device tensor")
+
+    def append(self, k, v, stream=None) -> None:
+        """k, v: contiguous fp16 device tensors [B][T][Hkv][D]."""
+        t = self._check_kv(k, v)
         check(lib().kv_quant_append(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
                                     ctypes.c_void_p(v.data_ptr()), int(t), _stream(stream)), "kv_quant_append")
 
     def append_attention(self, k, v, q, out, ws, stream=None) -> None:
         """One decode step (kv_append_decode_attention): k, v fp16 [B][1][Hkv][D]; q, out fp16
         [B][Hq][D]; ws: device scratch tensor."""
-        for t, name in ((k, "K"), (v, "V"), (q, "q"), (out, "out")):
-            _check_tensor(t, name)
+        self._check_kv(k, v, 1)
+        self._check_q_out(q, out, ws)
         check(lib().kv_append_decode_attention(ctypes.byref(self.handle), ctypes.c_void_p(k.data_ptr()),
                                                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(q.data_ptr()),
                                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
@@ -192,8 +218,7 @@ class Cache:
     def attention(self, q, out, ws, blocks_per_group: int = 0, deterministic: bool = False,
                   stream=None) -> None:
         """q, out: contiguous fp16 device tensors [B][Hq][D]; ws: device scratch tensor."""
-        _check_tensor(q, "q")
-        _check_tensor(out, "out")
+        self._check_q_out(q, out, ws)
         check(lib().kv_decode_attention_split(ctypes.byref(self.handle), ctypes.c_void_p(q.data_ptr()),
                                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                               ws.numel() * ws.element_size(), int(blocks_per_group),

@@ -10,6 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import layout as olayout
 from quantized_kv_cache_quant_amd import kvq
@@ -161,15 +162,45 @@ def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_group: int = 0,
     return out.cpu().numpy()
 
 
-def substate(st: ocache.CacheState, bi: int, gi: int) -> ocache.CacheState:
-    """The (sequence bi, KV head gi) slice of a cache state, as a 1 x 1 state."""
+def substate(st: ocache.CacheState, bi: int, gi: int | None = None) -> ocache.CacheState:
+    """The (sequence bi, KV head gi) slice of a cache state, as a 1 x 1 state; with gi None,
+    sequence bi with all its KV heads."""
+    hs = slice(None) if gi is None else slice(gi, gi + 1)
+
     def cut(a):
-        return None if a is None else a[bi:bi + 1, gi:gi + 1]
+        return None if a is None else a[bi:bi + 1, hs]
     lay = st.layout
-    sub = ocache.Layout(1, 1, lay.n_rep, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
+    hkv = lay.num_kv_heads if gi is None else 1
+    sub = ocache.Layout(1, hkv, lay.n_rep * hkv, lay.head_dim, lay.max_tokens, lay.fmt, lay.k_group_tokens,
                         lay.v_group_channels, lay.residual_tokens, lay.sink_tokens, lay.k_scale, lay.v_scale,
                         lay.meta_fp16, lay.rope_theta, lay.outliers)
     return ocache.CacheState(sub, st.n, st.n_sink, st.n_q, st.r, cut(st.sink_k), cut(st.sink_v),
                              cut(st.codes_k), cut(st.codes_v), cut(st.s_k), cut(st.z_k), cut(st.s_v),
                              cut(st.z_v), cut(st.res_k), cut(st.res_v), st.res_slots, cut(st.ko_idx),
                              cut(st.ko_val), cut(st.vo_idx), cut(st.vo_val))
+
+
+def check_every_head(c: kvq.Cache, kw: dict, out: np.ndarray, q: np.ndarray, k: np.ndarray | None = None,
+                     v: np.ndarray | None = None, tol: float = 2e-3) -> float:
+    """Parity of a whole cache and one attention output, every (sequence, KV head) pair.
+
+    With the token history k, v [B][n][Hkv][D] the library's codes, scales, zero-points,
+    residual ring and sinks must equal the oracle's build of that history bit for bit;
+    then every element of ``out`` [B][Hq][D] must lie within ``tol`` of the fp64 oracle's
+    attention over the library's own cache (dequantized exactly, rotated for pre-RoPE
+    Keys).  Works one sequence at a time to bound host memory.  Returns the max-abs error.
+    """
+    olay = olayout_of(kw)
+    st = read_state(c, olay)
+    if k is not None:
+        assert_states_equal(st, ocache.build_cache(k, v, olay))
+    worst = 0.0
+    for bi in range(olay.batch):
+        one = substate(st, bi)
+        kh, vh = ocache.dequantize(one)
+        ref = oattn.attention(q[bi:bi + 1], ocache.attention_keys(one, kh), vh)
+        err = np.abs(out[bi:bi + 1].astype(np.float64) - ref)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= tol, (bi, np.unravel_index(int(err.argmax()), err.shape), float(err.max()))
+    assert np.all(np.isfinite(out))
+    return worst

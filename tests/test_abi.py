@@ -289,3 +289,40 @@ def test_outlier_planes(fmt, bits):
     sizes = dict(zip(kvq.PLANES, list(h.plane_bytes)))
     assert sizes["k_out"] == b * hkv * nb * d * 4 and sizes["v_out"] == b * hkv * nb * 4 * 32 * 4
     assert sizes["k_codes"] == b * hkv * nb * 32 * d * bits // 8
+
+
+def test_binding_rejects_mismatched_shapes_before_any_call():
+    """The Python binding checks every tensor's shape against the layout (then dtype, contiguity
+    and device) before it calls the library: a 3-D decode tensor, K and V of different shapes, or
+    q / out of the wrong head count raise ValueError, so no kernel is ever launched over the
+    wrong extent.  CPU tensors stand in; the checks run before the device check."""
+    import torch
+    lay = kvq.make_layout(2, 4, 8, 128, 256, "int4", residual_tokens=32)
+    c = kvq.Cache(lay, None, kvq.CacheStruct())          # never passed to the library here
+    f16 = torch.float16
+    good = torch.zeros(2, 3, 4, 128, dtype=f16)
+    bad_kv = [(torch.zeros(2, 4, 128, dtype=f16), torch.zeros(2, 4, 128, dtype=f16)),   # 3-D decode tensor
+              (good, torch.zeros(2, 2, 4, 128, dtype=f16)),                             # T differs
+              (torch.zeros(1, 3, 4, 128, dtype=f16),) * 2,                               # batch
+              (torch.zeros(2, 3, 2, 128, dtype=f16),) * 2,                               # KV heads
+              (torch.zeros(2, 3, 4, 64, dtype=f16),) * 2]                                # head_dim
+    for k, v in bad_kv:
+        with pytest.raises(ValueError):
+            c.append(k, v)
+    q = torch.zeros(2, 8, 128, dtype=f16)
+    ws = torch.zeros(16)
+    with pytest.raises(ValueError):                      # T = 3 in a one-token decode step
+        c.append_attention(good, good, q, q, ws)
+    for bad in (torch.zeros(2, 4, 128, dtype=f16), torch.zeros(8, 128, dtype=f16),
+                torch.zeros(2, 8, 64, dtype=f16)):
+        with pytest.raises(ValueError):
+            c.attention(bad, q, ws)
+        with pytest.raises(ValueError):
+            c.attention(q, bad, ws)
+    one = torch.zeros(2, 1, 4, 128, dtype=f16)
+    with pytest.raises(ValueError, match="device"):      # right shapes, host memory
+        c.append(good, good)
+    with pytest.raises(ValueError, match="device"):
+        c.attention(q, q, ws)
+    with pytest.raises(ValueError, match="device"):
+        c.append_attention(one, one, q, q, ws)

@@ -15,8 +15,8 @@ from oracle import layout as olayout
 from oracle import quant
 from quantized_kv_cache_quant_amd import synth
 
-from kvq_testlib import (FP8, append_chunks, assert_states_equal, attention_gpu, make_cache, olayout_of,
-                         read_state, require_gpu, split_fmt, substate)
+from kvq_testlib import (FP8, append_chunks, assert_states_equal, attention_gpu, check_every_head, make_cache,
+                         olayout_of, read_state, require_gpu, split_fmt)
 
 pytestmark = pytest.mark.gpu
 
@@ -201,12 +201,4 @@ def test_full_size_paged_int8():
     append_chunks(c, k, v, [w.seq_len])
     q = synth.queries(w)
     out = attention_gpu(c, q)
-    st = read_state(c, olayout_of(kw))
-    nrep = w.num_q_heads // w.num_kv_heads
-    for bi, gi in rng.integers(0, [w.batch, w.num_kv_heads], size=(3, 2)):
-        one = substate(st, bi, gi)
-        exp = ocache.build_cache(k[bi:bi + 1, :, gi:gi + 1], v[bi:bi + 1, :, gi:gi + 1], one.layout)
-        assert_states_equal(one, exp)
-        hs = slice(gi * nrep, (gi + 1) * nrep)
-        kh, vh = ocache.dequantize(one)
-        assert np.max(np.abs(out[bi:bi + 1, hs].astype(np.float64) - oattn.attention(q[bi:bi + 1, hs], kh, vh))) <= TOL
+    check_every_head(c, kw, out, q, k, v)
