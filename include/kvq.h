@@ -307,6 +307,21 @@ int32_t kv_decode_attention_split(const kvq_cache* cache, const void* q, void* o
                                   uint64_t ws_bytes, int32_t blocks_per_group, int32_t deterministic,
                                   void* stream);
 
+/* kv_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same kernel and the same results
+ * (the library's own split); the partials go to a workspace the library owns:
+ * a 32 MiB device array, one copy per GPU, held until the process ends.  The
+ * call allocates and frees nothing.  All calls on one GPU share that array,
+ * so two calls whose kernels may overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream do
+ * not.  Its address is looked up on the first call on each device.
+ * Errors: those of kv_decode_attention; KVQ_ERR_WORKSPACE when the call
+ * needs more than the 32 MiB (kvq_workspace_bytes(cache, 0) above 32 MiB;
+ * checked before any device call); KVQ_ERR_HIP if the array cannot be
+ * located on the current device. */
+int32_t kv_decode_attention_noalloc(const kvq_cache* cache, const void* q, void* out, void* stream);
+
 /* Diagnostic, not part of the method: a plain streaming read of a device
  * buffer, which measures the HBM read rate this GPU delivers to a kernel of
  * the attention call's shape (the benchmark reports attention calls against

@@ -47,6 +47,8 @@
 //    P' = p * s per token and channel group; the zero-point sums are
 //    accumulated on the VALU and subtracted at the end.
 // The softmax runs in base 2 (log2(e) / sqrt(D) folded into q).
+#include <atomic>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1480,6 +1482,33 @@ __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2
 }
 
 }  // namespace
+
+// Workspace of kv_decode_attention_noalloc (partials of the split-K combine,
+// which any contents may start from).  In host code `scratch` names a host
+// stand-in, not device memory: only the address from hipGetSymbolAddress is
+// ever handed to a kernel.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+}  // namespace
+
+hipError_t attention_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* a = g_scratch[dev].load(std::memory_order_acquire);
+  if (!a) {                                     // first call on this device: it is current
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(a, std::memory_order_release);   // racing first calls store the same address
+  }
+  *ptr = a;
+  return hipSuccess;
+}
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.groups), block(kGroupThreads);

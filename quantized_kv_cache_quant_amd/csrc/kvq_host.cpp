@@ -422,6 +422,24 @@ int32_t kv_decode_attention(const kvq_cache* c, const void* q, void* out, void* 
   return kv_decode_attention_split(c, q, out, ws, ws_bytes, 0, 0, stream);
 }
 
+int32_t kv_decode_attention_noalloc(const kvq_cache* c, const void* q, void* out, void* stream) {
+  // every check first, the workspace size against the library's scratch
+  // included, with a host stand-in address (alignment and arithmetic only;
+  // those parameters are discarded): nothing touches the device on an error
+  alignas(256) static const char stand_in[256] = {};
+  AttnParams p;
+  void* probe = const_cast<char*>(stand_in);
+  int32_t st = prepare_attention(c, c ? c->n_tokens : 0, q, out, probe, kScratchBytes, 0, 0, p);
+  if (st != KVQ_OK) return st;
+  void* ws = nullptr;
+  if (attention_scratch(&ws) != hipSuccess) return KVQ_ERR_HIP;
+  st = prepare_attention(c, c->n_tokens, q, out, ws, kScratchBytes, 0, 0, p);
+  if (st != KVQ_OK) return st;
+  if (launch_attention(variant_of(c->layout), p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
 int32_t kv_append_decode_attention(kvq_cache* c, const void* K, const void* V, const void* q, void* out,
                                    void* ws, uint64_t ws_bytes, void* stream) {
   if (!c || !c->base || !K || !V) return KVQ_ERR_NULL;

@@ -168,6 +168,13 @@ struct AttnParams {
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s);
 
+// Library-owned workspace of kv_decode_attention_noalloc: a file-scope device
+// array of kScratchBytes in kvq_attn.hip, one copy per GPU for the life of
+// the process.  attention_scratch returns the current device's copy (its
+// address is looked up once per device, with that device current).
+constexpr uint64_t kScratchBytes = 32ull << 20;
+hipError_t attention_scratch(void** ptr);
+
 // ------------------------------------------------------------- read probe
 constexpr int kProbeThreads = 512;        // threads per workgroup, as the attention kernel
 hipError_t launch_read_probe(const void* buf, uint64_t units, uint32_t* sink, int groups, hipStream_t s);

@@ -22,7 +22,7 @@ PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink"
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
            "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table",
-           "kvq_read_probe", "kv_append_decode_attention")
+           "kvq_read_probe", "kv_append_decode_attention", "kv_decode_attention_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "kvq_cache_set_block_table": (I32, [CP, P, I32]),
             "kvq_read_probe": (I32, [P, U64, P, U64, I32, P]),
             "kv_append_decode_attention": (I32, [CP, P, P, P, P, P, U64, P]),
+            "kv_decode_attention_noalloc": (I32, [CP, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -224,6 +225,21 @@ class Cache:
                                               ws.numel() * ws.element_size(), int(blocks_per_group),
                                               int(bool(deterministic)), _stream(stream)),
               "kv_decode_attention")
+
+
+    def attention_noalloc(self, q, out, stream=None) -> None:
+        """kv_decode_attention_noalloc: q, out contiguous fp16 device tensors [B][Hq][D]; the
+        partials go to the library's own per-GPU workspace (nothing is allocated)."""
+        L = self.layout
+        want = (L.batch, L.num_q_heads, L.head_dim)
+        for t, name in ((q, "q"), (out, "out")):
+            if tuple(t.shape) != want:
+                raise ValueError(f"{name} must be [{want[0]}][{want[1]}][{want[2]}]; got {tuple(t.shape)}")
+        _check_tensor(q, "q")
+        _check_tensor(out, "out")
+        check(lib().kv_decode_attention_noalloc(ctypes.byref(self.handle), ctypes.c_void_p(q.data_ptr()),
+                                                ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+              "kv_decode_attention_noalloc")
 
 
 def _check_tensor(t, name: str) -> None:

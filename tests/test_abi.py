@@ -326,3 +326,32 @@ def test_binding_rejects_mismatched_shapes_before_any_call():
         c.attention(q, q, ws)
     with pytest.raises(ValueError, match="device"):
         c.append_attention(one, one, q, q, ws)
+
+
+def test_noalloc_attention_rejects_before_touching_the_device():
+    """kv_decode_attention_noalloc validates like kv_decode_attention and refuses, before any
+    device call, a cache whose partials need more than the library's 32 MiB workspace."""
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    f = L.kv_decode_attention_noalloc
+    lay, h = _cache(max_tokens=2000)
+    assert f(ctypes.byref(h), P(FAKE), P(FAKE), None) == -8                   # empty cache
+    h.n_tokens = 1500
+    assert f(ctypes.byref(h), None, P(FAKE), None) == -1
+    assert f(ctypes.byref(h), P(FAKE + 2), P(FAKE), None) == -5
+    assert f(None, P(FAKE), P(FAKE), None) == -1
+    # 4096 sequences x 8 KV heads x 8 query heads each: ~160 MB of partials
+    big = kvq.make_layout(4096, 8, 64, 128, 2000, "int4", residual_tokens=32)
+    hb = kvq.CacheStruct()
+    assert L.kvq_cache_init(ctypes.byref(hb), ctypes.byref(big), P(FAKE), 1 << 50) == 0
+    hb.n_tokens = 1500
+    need = ctypes.c_uint64()
+    assert L.kvq_workspace_bytes(ctypes.byref(hb), 0, ctypes.byref(need)) == 0
+    assert need.value > 32 << 20
+    assert f(ctypes.byref(hb), P(FAKE), P(FAKE), None) == -6
+    # the benchmark's largest workload fits: the 70B layer (16 x 8 KV heads, 8 query heads each)
+    w70 = kvq.make_layout(16, 8, 64, 128, 8192 + 64, "int4", residual_tokens=128, sink_tokens=4)
+    h70 = kvq.CacheStruct()
+    assert L.kvq_cache_init(ctypes.byref(h70), ctypes.byref(w70), P(FAKE), 1 << 40) == 0
+    assert L.kvq_workspace_bytes(ctypes.byref(h70), 0, ctypes.byref(need)) == 0
+    assert need.value <= 32 << 20
