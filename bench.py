@@ -11,16 +11,24 @@ Each layer owns its own cache buffer, so the timed loop streams every
 layer's packed cache from HBM (one layer's cache is larger than the 256 MB
 last-level cache, and the 32 layers together are ~8 GB).
 
-Default workload: the Llama-3-8B layer shape (32 query / 8 KV heads,
-head_dim 128) at batch 16 and 8192 cached tokens, 32 layers, with the cache
-quantized to INT8 (headline) and to FP8 E4M3.  The single JSON line on
-stdout carries the INT8 numbers as "value" and the FP8 numbers under "fp8".
-Under "variants" it adds attention-only sweeps of the same shape for the
-other cache variants (FP8 E5M2; INT8 / INT4 / INT2 with fp16 scale and
-offset metadata; INT8 in a paged pool of 32-token pages in shuffled
-order; INT8 and INT4 with Keys stored before RoPE, rotated in attention
-with base 500000; INT4 and INT2 with one exact fp16 outlier per group),
-eight layer caches each.
+Default run (no --workload): the Llama-3-8B layer shape (32 query / 8 KV
+heads, head_dim 128) at batch 16 and 8192 cached tokens, 32 layers, with the
+cache quantized to INT8 (headline "value") and to FP8 E4M3 ("fp8"); then,
+under "workloads", each of the other decode workloads at its own shape and
+depth: KIVI-style INT2 on the 8B shape (fp32 scale / zero-point, 128-token
+window, one fused one-token append per layer and step, 32 layers), the
+Llama-3-70B layer shape in INT4 with 4 fp16 sink tokens (80 layers), and
+131072 tokens at batch 1 with INT8 on layers 0-3 and 28-31 and INT4 between
+(32 layers); under "tiny_latency" the call latency of the batch-1, 4-query-
+head, 256-token INT4 case.  Under "variants" it adds attention-only sweeps of
+the 8B shape for the other cache variants (FP8 E5M2; INT8 / INT4 / INT2 with
+fp16 scale and offset metadata; INT8 in a paged pool of 32-token pages in
+shuffled order; INT8 and INT4 with Keys stored before RoPE, rotated in
+attention with base 500000; INT4 and INT2 with one exact fp16 outlier per
+group), eight layer caches each.  "cpu_baseline" is the CPU oracle timed on
+one layer's decode step of the headline workload on all host cores, and
+"pages_context" holds the speed-ups and capacities the pages report, with the
+hardware they name, as context (none is this metric on this hardware).
 
 Timed regions, each bracketed by HIP events on the stream the library
 launches on (torch's current stream):
@@ -69,14 +77,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "llama3_8b_kivi2", "llama3_70b", "long_ctx"])
+    ap.add_argument("--workload", default=None,
+                    choices=["llama3_8b", "llama3_8b_kivi2", "llama3_70b", "long_ctx"],
+                    help="time one workload only (default: the 8B headline, then every other workload)")
     ap.add_argument("--formats", default=None, help="comma list overriding the workload's formats")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--blocks-per-group", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the attention sweep of the other variants")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="only time the plain streaming-read kernel over a range of sizes and print that")
     return ap.parse_args()
 
 
@@ -282,6 +293,14 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     torch.cuda.synchronize()
     attn_ms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
     n_final = n0 + total_steps
+    by_fmt = {}                                 # per layer format: mean call, bytes, fraction of peak
+    for fmt in sorted(set(fmt_list)):
+        ms_f = [e0.elapsed_time(e1) for row in evs for li, (e0, e1) in enumerate(row) if fmt_list[li] == fmt]
+        us_f = 1e3 * float(np.mean(ms_f))
+        nb_f = call_bytes(accounting, w, fmt, n_final)
+        by_fmt[fmt] = {"layers": fmt_list.count(fmt), "attn_call_us": round(us_f, 2), "bytes_per_attn_call": nb_f,
+                       "attn_gbps": round(nb_f / (us_f * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(nb_f / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     sweep_bytes = sum(call_bytes(accounting, w, fmt, n_final) for fmt in fmt_list) / layers
     nbytes = 0
     for s in range(args.steps):
@@ -301,6 +320,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         "step_us_per_layer": ms_step * 1e3 / layers,
         "bytes_per_attn_call": sweep_bytes,
         "attn_calls_timed": len(attn_ms),
+        "attn_by_format": by_fmt,
         "prefill_quantize": {"us_per_layer": round(float(np.mean(pre_us)), 1),
                              "input_gbps": round(pre_in / (float(np.mean(pre_us)) * 1e-6) / 1e9, 1),
                              "tokens_per_s": round(b * n0 / (float(np.mean(pre_us)) * 1e-6)),
@@ -335,68 +355,182 @@ def counter_traffic(fmt):
 
 
 def cpu_baseline(w, fmt, seconds):
-    """The CPU oracle's decode attention on a time-bounded sample of (sequence, KV head) pairs."""
-    from threadpoolctl import threadpool_limits
+    """The CPU oracle on one layer's decode step of workload w in format fmt, on all host cores.
+
+    Set-up: the oracle quantizes the prompt plus one appended token of every sequence
+    (one thread per sequence; timed as the CPU's prefill quantization).  Timed: the layer's
+    decode step as the oracle states it, fp64 dequantization of every (sequence, KV head)
+    and fp64 GQA attention of all query heads, one sequence per worker thread, repeated for
+    about `seconds`.  The oracle's own functions are called unchanged; the threads only split
+    the batch (numpy releases the interpreter lock inside its array operations).  Full-depth
+    figures are that one layer's time times the layer count, labelled as extrapolated.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_info
 
     from oracle import attention as oattn
     from oracle import cache as ocache
-    from oracle import nbytes as obytes
-    from quantized_kv_cache_quant_amd import synth
+    from oracle import quant
+    from quantized_kv_cache_quant_amd import accounting, synth
 
-    nrep = w.num_q_heads // w.num_kv_heads
+    cores = len(os.sched_getaffinity(0))
+    b = w.batch
     n = w.seq_len + 1
-    k, v = synth.kv_tokens(w, 1000 + w.index, 2000 + w.index, 1, n, 1, w.head_dim)
-    q = synth.queries(w, 1, nrep, w.head_dim)
-    from oracle import quant
-    lay = ocache.Layout(1, 1, nrep, w.head_dim, n, fmt, residual_tokens=w.residual_tokens,
-                        sink_tokens=w.sink_tokens, k_scale=float(quant.fp8_scale(k)),
-                        v_scale=float(quant.fp8_scale(v)))
-    st = ocache.build_cache(k, v, lay)           # set-up, not timed
-    per_head = obytes.step_bytes(lay, n)["total"]
-    done = 0
-    with threadpool_limits(limits=1):
+    k, v = synth.prefill(w)
+    k1, v1 = synth.append_step(w, 0)
+    k = np.concatenate([k, k1], axis=1)
+    v = np.concatenate([v, v1], axis=1)
+    q = synth.queries(w)
+    ks = float(quant.fp8_scale(k)) if fmt.startswith("fp8") else 1.0
+    vs = float(quant.fp8_scale(v)) if fmt.startswith("fp8") else 1.0
+    lay = ocache.Layout(1, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt, residual_tokens=w.residual_tokens,
+                        sink_tokens=w.sink_tokens, k_scale=ks, v_scale=vs)
+    with ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
+        states = list(ex.map(lambda i: ocache.build_cache(k[i:i + 1], v[i:i + 1], lay), range(b)))
+        t_quant = time.perf_counter() - t0
+        del k, v
+
+        def step(i):
+            kh, vh = ocache.dequantize(states[i])
+            return oattn.attention(q[i:i + 1], kh, vh)
+
+        reps = 0
         t0 = time.perf_counter()
         while True:
-            kh, vh = ocache.dequantize(st)
-            oattn.attention(q, kh, vh)
-            done += 1
+            list(ex.map(step, range(b)))
+            reps += 1
             if time.perf_counter() - t0 >= seconds:
                 break
         dt = time.perf_counter() - t0
-    return {"value": per_head * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} x one (sequence, KV head) decode step of {fmt} ({n} tokens, {nrep} query heads): "
-                      f"fp64 dequantize + attention, {dt:.1f} s, single thread",
-            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+    layer_s = dt / reps
+    nbytes = accounting.attention_bytes(b, w.num_kv_heads, w.num_q_heads, w.head_dim, n, fmt, w.sink_tokens,
+                                        w.residual_tokens)
+    blas = sorted({(t.get("internal_api"), t.get("num_threads")) for t in threadpool_info()})
+    return {"value": round(nbytes / layer_s / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x one layer's decode step of {w.name} in {fmt} (batch {b}, {n} tokens, "
+                      f"{w.num_q_heads}/{w.num_kv_heads} heads): fp64 dequantize + fp64 attention of every "
+                      f"(sequence, KV head), one sequence per thread on {cores} threads, {dt:.1f} s",
+            "layer_step_s": round(layer_s, 4),
+            "tokens_per_s_extrapolated": round(b / (layer_s * w.layers), 3),
+            "extrapolation": f"{w.layers} layers x the one-layer step time (not run at full depth)",
+            "prefill_quantize_s_per_layer": round(t_quant, 3),
+            "prefill_quantize_input_gbps": round(2 * b * w.seq_len * w.num_kv_heads * w.head_dim * 2 / t_quant / 1e9,
+                                                 3),
+            "os_cpu_count": os.cpu_count(), "affinity_cpus": cores,
+            "blas_threads": [{"api": a, "num_threads": t} for a, t in blas]}
 
 
-def cpu_quantize_baseline(w, fmt, seconds):
-    """The CPU oracle's quantize-on-append of the prompt for one (sequence, KV head), repeated for a
-    bounded time: GB/s of fp16 K and V input, beside the GPU's prefill_quantize."""
-    from threadpoolctl import threadpool_limits
+def tiny_latency(torch, kvq, synth, calls=200) -> dict:
+    """Call latency of the tiny workload (batch 1, 4 query heads on 1 KV head, 256 tokens, INT4,
+    32-token window): kv_decode_attention and kv_append_decode_attention, each call between its
+    own event pair, and back-to-back calls between one pair (launch-rate bound)."""
+    w = synth.WORKLOADS["tiny"]
+    k, v = synth.prefill(w)
+    lay = kvq.make_layout(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, w.seq_len + calls + 16, "int4",
+                          residual_tokens=w.residual_tokens)
+    c = kvq.Cache.create(lay)
+    c.append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    q = torch.from_numpy(synth.queries(w)).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty(c.workspace_bytes(0) // 4 + 4, dtype=torch.float32, device="cuda")
+    steps = [synth.append_step(w, j) for j in range(calls)]
+    ks = [torch.from_numpy(a).cuda() for a, _ in steps]
+    vs = [torch.from_numpy(b).cuda() for _, b in steps]
+    for _ in range(10):
+        c.attention(q, out, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in ev:
+        e0.record()
+        c.attention(q, out, ws)
+        e1.record()
+    torch.cuda.synchronize()
+    single = 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        c.attention(q, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    b2b = 1e3 * e0.elapsed_time(e1) / calls
+    for j, (e0, e1) in enumerate(ev):
+        e0.record()
+        c.append_attention(ks[j], vs[j], q, out, ws)
+        e1.record()
+    torch.cuda.synchronize()
+    step = 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+    return {"workload": f"tiny: {w.notes}", "attn_call_us": round(single, 2),
+            "attn_call_us_back_to_back": round(b2b, 2), "decode_step_us": round(step, 2),
+            "calls": calls, "note": "median of per-call event pairs; latency-bound, not a roofline figure"}
 
-    from oracle import cache as ocache
-    from oracle import quant
-    from quantized_kv_cache_quant_amd import synth
 
-    nrep = w.num_q_heads // w.num_kv_heads
-    n = w.seq_len
-    k, v = synth.kv_tokens(w, 1000 + w.index, 2000 + w.index, 1, n, 1, w.head_dim)
-    lay = ocache.Layout(1, 1, nrep, w.head_dim, n, fmt, residual_tokens=w.residual_tokens,
-                        sink_tokens=w.sink_tokens, k_scale=float(quant.fp8_scale(k)),
-                        v_scale=float(quant.fp8_scale(v)))
-    done = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            ocache.build_cache(k, v, lay)
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-    nbytes = 2 * n * w.head_dim * 2
-    return {"value": nbytes * done / dt / 1e9, "unit": "GB/s of fp16 K/V input", "cores": 1, "kind": "oracle",
-            "sample": f"{done} x the {n}-token prompt of one (sequence, KV head) quantized to {fmt} "
-                      f"(fp32 steps as specified), {dt:.1f} s, single thread"}
+def read_sweep(torch, kvq) -> dict:
+    """The plain streaming-read kernel (kvq_read_probe, one workgroup of 512 threads per compute
+    unit, the attention kernel's launch shape) over a range of sizes: each call reads a fresh
+    slice of an 11 GiB buffer (the 256 MB last-level cache cannot serve it) between its own
+    event pair."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    total = 11 << 30
+    x = torch.empty(total, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 512, dtype=torch.int32, device="cuda")
+    res = {}
+    for mib in (64, 128, 275, 342, 1024, 4096):
+        nb = mib << 20
+        slices = max(8, min(32, total // nb))
+        offs = [(i * nb) % (total - nb + 1) // 256 * 256 for i in range(slices)]
+        kvq.read_probe(x[offs[0]:offs[0] + nb], sink, cus)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in offs]
+        for (e0, e1), o in zip(ev, offs):
+            e0.record()
+            kvq.read_probe(x[o:o + nb], sink, cus)
+            e1.record()
+        torch.cuda.synchronize()
+        us = [1e3 * a.elapsed_time(b) for a, b in ev]
+        res[f"{mib}_MiB"] = {"mean_us": round(float(np.mean(us)), 2), "min_us": round(float(np.min(us)), 2),
+                             "gbps_mean": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1), "calls": len(us)}
+        log(f"read {mib} MiB: {res[f'{mib}_MiB']}")
+    del x, sink
+    return res
+
+
+PAGES_CONTEXT = {
+    "note": "figures the pages report for other kernels on other hardware; context, not this metric",
+    "kivi_throughput_speedup": {"value": "2.35-3.47x", "hardware": "not stated on the page",
+                                "what": "KIVI 2-bit KV cache (K per channel, V per token, fp16 residual), "
+                                        "throughput vs an fp16 cache",
+                                "source": "KV Cache Quantization Analysis, sec. 4 (KIVI)"},
+    "kvquant_kernel_speedup": {"value": "~1.7x", "hardware": "custom CUDA kernels; GPU not named for this figure",
+                               "what": "KVQuant sub-4-bit KV kernels vs fp16",
+                               "source": "KV Cache Quantization Analysis, sec. 4 (KVQuant)"},
+    "kvquant_context": {"value": "1M tokens on one GPU (10M on 8 GPUs)", "hardware": "one A100-80GB",
+                        "what": "KVQuant 3-bit KV cache, LLaMA-7B",
+                        "source": "KV Cache Quantization Analysis, sec. 4 (KVQuant)"},
+}
+
+# the decode workloads timed after the headline, each at its own shape and depth
+OTHER_WORKLOADS = (("kivi2_int2", "llama3_8b_kivi2", ["int2"]), ("llama3_70b_int4", "llama3_70b", ["int4"]),
+                   ("long_ctx_mixed", "long_ctx", ["mixed"]))
+
+
+def layer_formats(w, var, nl):
+    if var == "mixed":
+        return list(w.formats)[:nl] if nl <= len(w.formats) else (list(w.formats) * nl)[:nl]
+    return [var] * nl
+
+
+def summary(w, r) -> dict:
+    """The per-workload entry of the JSON line."""
+    return {"workload": f"{w.name}: {w.notes}", "batch": w.batch, "seq_len": w.seq_len,
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "residual_tokens": w.residual_tokens,
+            "sink_tokens": w.sink_tokens, "layers": r["layers"], "formats": r["formats"],
+            "attn_call_us": round(r["attn_call_us"], 2), "bytes_per_attn_call": r["bytes_per_attn_call"],
+            "attn_gbps": round(r["attn_gbps"], 1), "frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4),
+            "attn_by_format": r["attn_by_format"], "ms_per_step": round(r["ms_per_step"], 4),
+            "step_us_per_layer": round(r["step_us_per_layer"], 2), "tokens_per_s": round(r["tokens_per_s"], 1),
+            "effective_gbps": round(r["effective_gbps"], 1), "prefill_quantize": r["prefill_quantize"]}
 
 
 def main():
@@ -411,26 +545,34 @@ def main():
 
     from quantized_kv_cache_quant_amd import accounting, kvq, synth
     kvq.lib()
-    w = synth.WORKLOADS[args.workload]
+    if args.read_sweep:
+        print(json.dumps({"read_probe_sweep": read_sweep(torch, kvq)}), flush=True)
+        return
+    name = args.workload or "llama3_8b"
+    w = synth.WORKLOADS[name]
     if args.formats:
         variants = [f.strip() for f in args.formats.split(",")]
-    elif args.workload == "long_ctx":
+    elif name == "long_ctx":
         variants = ["mixed"]
+    elif name == "llama3_8b":
+        variants = ["int8", "fp8"]                   # INT8 is the headline line
     else:
         variants = list(w.formats)
-    if args.workload == "llama3_8b" and not args.formats:
-        variants = ["int8", "fp8"]                   # INT8 is the headline line
     nl = args.layers or w.layers
     results = {}
     for var in variants:
-        if var == "mixed":
-            fl = list(w.formats)[:nl] if nl <= len(w.formats) else (list(w.formats) * nl)[:nl]
-        else:
-            fl = [var] * nl
-        results[var] = run_format(torch, kvq, synth, accounting, w, fl, args)
+        results[var] = run_format(torch, kvq, synth, accounting, w, layer_formats(w, var, nl), args)
+    default_run = args.workload is None and not args.formats and not args.layers
+    others = {}
+    if default_run:
+        for key, wname, fl in OTHER_WORKLOADS:
+            wo = synth.WORKLOADS[wname]
+            r = run_format(torch, kvq, synth, accounting, wo, layer_formats(wo, fl[0], wo.layers), args)
+            others[key] = summary(wo, r)
     vres = None
-    if not args.no_variants and args.workload == "llama3_8b" and not args.formats:
+    if not args.no_variants and name == "llama3_8b" and not args.formats:
         vres = variant_sweep(torch, kvq, synth, accounting, w, VARIANTS, args)
+    tiny = tiny_latency(torch, kvq, synth) if default_run else None
     copy_gbps = copy_bandwidth(torch)
     log(f"device-to-device copy: {copy_gbps:.0f} GB/s")
     reads = read_peak(torch, kvq)
@@ -473,14 +615,17 @@ def main():
     for var in variants[1:]:
         r = results[var]
         line[var] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+    if others:
+        line["workloads"] = others
+    if tiny:
+        line["tiny_latency"] = tiny
     if vres:
         line["variants"] = vres
     if not args.no_cpu_baseline:
         fmt0 = variants[0] if variants[0] != "mixed" else "int4"
-        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        log(f"timing the CPU oracle on one layer's decode step for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(w, fmt0, args.cpu_seconds)
-        log("timing the CPU oracle's prefill quantization for ~5 s")
-        line["cpu_baseline_quantize"] = cpu_quantize_baseline(w, fmt0, 5.0)
+    line["pages_context"] = PAGES_CONTEXT
     print(json.dumps(line), flush=True)
 
 

@@ -48,6 +48,7 @@
 //    accumulated on the VALU and subtracted at the end.
 // The softmax runs in base 2 (log2(e) / sqrt(D) folded into q).
 #include <atomic>
+#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -157,6 +158,15 @@ __device__ __forceinline__ f16x8 cvt_fp8(uint32_t w0, uint32_t w1) {
 #define KVQ_DEPTH_INT2 4
 #endif
 
+// Ring sizes of the paired path (blocks, even): the pair being processed plus
+// (ring - 2) blocks in flight.
+#ifndef KVQ_PAIR_RING_INT4
+#define KVQ_PAIR_RING_INT4 4
+#endif
+#ifndef KVQ_PAIR_RING_INT2
+#define KVQ_PAIR_RING_INT2 6
+#endif
+
 // FMT is a kernel variant: the kvq_format, plus kMeta16 for fp16 metadata.
 template <int FMT>
 struct Traits {
@@ -177,6 +187,10 @@ struct Traits {
   // the outlier corrections' for two (INT4) or three (INT2)
   static constexpr int kDepthCap = kRope ? 2 : (kOut ? (kBits == 2 ? 3 : 2) : kDepthBase);
   static constexpr int kDepth = kDepthBase < kDepthCap ? kDepthBase : kDepthCap;
+  // paired processing (INT4 / INT2 at n_rep <= 4, see process_pair): two blocks per step, the
+  // ring holds the pair being processed and the next pairs' loads
+  static constexpr bool kPairable = !kFp8 && !kRope && !kOut && kBits < 8;
+  static constexpr int kPairRing = kBits == 2 ? KVQ_PAIR_RING_INT2 : KVQ_PAIR_RING_INT4;
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -471,6 +485,8 @@ struct LaneInfo {
   bool writer;      // hi column of a real query head: writes the results
   uint32_t hmask;   // 0xFFFFFFFF in lo columns, 0 in hi columns
   int zg;           // first Value channel group whose zero-point sum this lane keeps
+  int par;          // paired path: which block of the pair this column serves (0 or 1)
+  uint32_t amask;   // paired path: 0xFFFFFFFF in columns of the pair's first block, else 0
 };
 
 __device__ __forceinline__ LaneInfo lane_info(int nrep) {
@@ -484,6 +500,22 @@ __device__ __forceinline__ LaneInfo lane_info(int nrep) {
   li.writer = !li.is_lo && li.head < nrep;
   li.hmask = li.is_lo ? 0xFFFFFFFFu : 0u;
   li.zg = li.is_lo ? 2 : 0;
+  li.par = 0;
+  li.amask = 0xFFFFFFFFu;
+  return li;
+}
+
+// Paired path (n_rep <= 4): column col = 8 lo + 4 par + head, i.e. query head
+// col % 4 of the pair's block par, hi part in columns 0-7, lo in 8-15 (so
+// the hi / lo partner is still lane + 8).  Both parities hold the same head;
+// their softmax states are merged when the head's segment ends.
+__device__ __forceinline__ LaneInfo lane_info_pair(int nrep) {
+  LaneInfo li = lane_info(nrep);
+  const int col = li.lane & 15;
+  li.head = col & 3;
+  li.par = (col >> 2) & 1;
+  li.amask = li.par ? 0u : 0xFFFFFFFFu;
+  li.writer = !li.is_lo && li.par == 0 && li.head < nrep;
   return li;
 }
 
@@ -691,6 +723,37 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pr[tile][i] = __builtin_amdgcn_exp2f(lg[tile][i] - ws.m);
+      ws.l += pr[tile][i];
+    }
+}
+
+// softmax_block for a wavefront whose inactive lanes (active = false) take no
+// tokens: their state is left as it is and their p are 0.  Active lanes see at
+// least one finite logit, so their new running max is finite.
+__device__ __forceinline__ void softmax_block_some(float lg[2][4], WaveState& ws, float pr[2][4], float slack,
+                                                   bool active) {
+  float mx = neg_inf();
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[tile][i]);
+  mx = rows_max(mx);
+  if (!active) mx = neg_inf();
+  if (__any(mx > ws.m + slack)) {
+    const float m_new = fmaxf(ws.m, mx);
+    const float alpha = active ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
+    ws.z[0] *= alpha;
+    ws.z[1] *= alpha;
+    ws.l *= alpha;
+    ws.m = active ? m_new : ws.m;
+  }
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[tile][i] = active ? __builtin_amdgcn_exp2f(lg[tile][i] - ws.m) : 0.f;
       ws.l += pr[tile][i];
     }
 }
@@ -916,6 +979,122 @@ __device__ __forceinline__ void process_block(const Raw<FMT>& r, float* st, Wave
       }
     }
   }
+}
+
+// Two blocks of one KV head at once (INT4 / INT2, n_rep <= 4; see
+// lane_info_pair): the matrix-core columns that n_rep <= 4 leaves free carry
+// the second block.  Both blocks are staged; each lane forms q' and P' from
+// its own block's scales (so every split instruction serves two blocks), the
+// QK products of both blocks share the q' operands and each lane keeps the
+// logits of its block, one softmax pass runs for both, and each PV product
+// takes the P' columns of its own block (the other columns masked to zero).
+// b_on = false: only block ra counts (the second-block lanes are inactive).
+template <int FMT>
+__device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>& rb, bool b_on, float* st,
+                                             WaveState& ws, const QOp& q, const LaneInfo& li) {
+  using T = Traits<FMT>;
+  const int qd = li.qd;
+  stage_meta<FMT>(ra, st, li.lane);
+  stage_meta<FMT>(rb, st + kStage, li.lane);
+  const float* sp = st + (li.par ? kStage : 0);          // this lane's block
+
+  // zero-point term of this lane's block (see process_block)
+  float bz[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint4* zh = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sp) + 256 + 32 * qd);
+  const uint4* zl = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sp) + 384 + 32 * qd);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 h = zh[i], l = zl[i];
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bz[i & 1] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(hw[k]), bz[i & 1], false);
+      bz[2 + (i & 1)] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(lw[k]), bz[2 + (i & 1)], false);
+    }
+  }
+  const float kbias = rows_sum((bz[0] + bz[1]) + (bz[2] + bz[3]));
+
+  f32x4 acc_a[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  f32x4 acc_b[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float4 sa = *reinterpret_cast<const float4*>(sp + 32 * qd + 8 * kb);
+    const float4 sb = *reinterpret_cast<const float4*>(sp + 32 * qd + 8 * kb + 4);
+    const f16x8 bq = split_q4(q.z + 4 * kb, q.h + 4 * kb, sa, sb);
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      acc_a[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(ra.k[tile], kb), bq, acc_a[tile], 0, 0, 0);
+      acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(rb.k[tile], kb), bq, acc_b[tile], 0, 0, 0);
+    }
+  }
+  float lg[2][4], pr[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = li.par ? acc_b[tile][i] : acc_a[tile][i];
+      lg[tile][i] = __builtin_fmaf(x + ror8(x), T::kCodeScale, -kbias);
+    }
+  const float2 sva = pair_scales<FMT>(ra.vm), svb = pair_scales<FMT>(rb.vm);
+  const bool big = sva.x > kLazyScaleMax || sva.y > kLazyScaleMax || (b_on && (svb.x > kLazyScaleMax || svb.y > kLazyScaleMax));
+  const float slack = __any(big) ? 0.f : kSlack;
+  if (b_on) softmax_block(lg, ws, pr, slack);
+  else softmax_block_some(lg, ws, pr, slack, li.par == 0);
+
+  // Value zero-point sums (this lane's block), groups zg and zg + 1
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    const float* zs = sp + 384 + 32 * (li.zg + gg);
+    const float4 z0 = *reinterpret_cast<const float4*>(zs + 4 * qd);
+    const float4 z1 = *reinterpret_cast<const float4*>(zs + 16 + 4 * qd);
+    float za = ws.z[gg];
+    za = __builtin_fmaf(pr[0][0], z0.x, za); za = __builtin_fmaf(pr[0][1], z0.y, za);
+    za = __builtin_fmaf(pr[0][2], z0.z, za); za = __builtin_fmaf(pr[0][3], z0.w, za);
+    za = __builtin_fmaf(pr[1][0], z1.x, za); za = __builtin_fmaf(pr[1][1], z1.y, za);
+    za = __builtin_fmaf(pr[1][2], z1.z, za); za = __builtin_fmaf(pr[1][3], z1.w, za);
+    ws.z[gg] = za;
+  }
+  float pb[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[tile][i] = li.is_lo ? pr[tile][i] : 0.f;
+  const uint32_t am = li.amask, bm = ~li.amask;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 s0 = *reinterpret_cast<const float4*>(sp + 256 + 32 * g + 4 * qd);
+    const float4 s1 = *reinterpret_cast<const float4*>(sp + 256 + 32 * g + 16 + 4 * qd);
+    const float sv0[4] = {s0.x, s0.y, s0.z, s0.w};
+    const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
+    const f16x8 bp = split_p4(pr[0], pb[0], sv0, pr[1], pb[1], sv1);
+    const uint4 w = __builtin_bit_cast(uint4, bp);
+    const f16x8 bpa = cat(w.x & am, w.y & am, w.z & am, w.w & am);
+    const f16x8 bpb = cat(w.x & bm, w.y & bm, w.z & bm, w.w & bm);
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * g + mm;
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(ra.v, m), bpa, ws.o[m], 0, 0, 0);
+      if (b_on) ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(rb.v, m), bpb, ws.o[m], 0, 0, 0);
+    }
+  }
+}
+
+// Paired path: fold the second-block columns' softmax state (lane ^ 4: same
+// quarter, same hi / lo half, other parity) into the first's, so that every
+// lane holds its head's state over both.  An empty state (m = -inf) weighs 0.
+__device__ __forceinline__ void merge_parity(WaveState& ws) {
+  const float mo = __shfl_xor(ws.m, 4);
+  const float mn = fmaxf(ws.m, mo);
+  const float a = ws.m == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ws.m - mn);
+  const float b = mo == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+  ws.l = __builtin_fmaf(a, ws.l, b * __shfl_xor(ws.l, 4));
+  ws.z[0] = __builtin_fmaf(a, ws.z[0], b * __shfl_xor(ws.z[0], 4));
+  ws.z[1] = __builtin_fmaf(a, ws.z[1], b * __shfl_xor(ws.z[1], 4));
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.o[m][i] = __builtin_fmaf(a, ws.o[m][i], b * __shfl_xor(ws.o[m][i], 4));
+  ws.m = mn;
 }
 
 // A workgroup's merged slots are read by another workgroup (on another
@@ -1243,13 +1422,16 @@ __device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* 
 // slot per head of the range.  Before its first block it handles its share of
 // the workgroup's fp16 blocks, while its first blocks load.  At the end the
 // workgroup merges its wavefronts' partials into one slot per head.
-template <int FMT>
+// PAIR: blocks are processed two at a time (process_pair; INT4 / INT2 at
+// n_rep <= 4), with a ring of kPairRing blocks.
+template <int FMT, bool PAIR>
 __device__ void group_main(const AttnParams& p, char* lds) {
   using T = Traits<FMT>;
-  constexpr int D = T::kDepth + 1;
+  constexpr int D = PAIR ? T::kPairRing : T::kDepth + 1;
+  static_assert(!PAIR || (T::kPairable && D % 2 == 0 && D >= 4), "paired ring");
   const int g = blockIdx.x;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront index, uniform
-  const LaneInfo li = lane_info(p.nrep);
+  const LaneInfo li = PAIR ? lane_info_pair(p.nrep) : lane_info(p.nrep);
   const GroupRange gr = group_range(p, g);
   if (!gr.len) return;                        // (never: every workgroup has a range)
   const uint32_t nblk = (uint32_t)p.nblk;
@@ -1329,8 +1511,71 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       load_block<FMT, false>(r, p, 0, li.lane);
     }
   };
+  // Paired path: the range's blocks are handed out as units of two
+  // consecutive blocks of one head (a head part of odd length ends with a
+  // single block).  Units of the first head part come first, then ceil(nblk
+  // / 2) units per whole head, then those of the last part; like single
+  // blocks, each part's units are visited from a per-workgroup rotation.
+  const uint32_t e0 = (uint32_t)gr.h0 * nblk + nblk < je ? (uint32_t)gr.h0 * nblk + nblk : je;
+  const uint32_t u0 = (e0 - jb + 1) / 2;
+  const uint32_t hn = (nblk + 1) / 2;
+  const uint32_t units = gr.h1 > gr.h0 ? u0 + (uint32_t)(gr.h1 - gr.h0 - 1) * hn + (je - (uint32_t)gr.h1 * nblk + 1) / 2
+                                       : u0;
+  bool two[D / 2 > 0 ? D / 2 : 1];
+  auto fetch_pair = [&](Raw<FMT>& ra, Raw<FMT>& rb, int& id, int& bhout, bool& has2) {
+    int idx;
+    if (p.deterministic) {
+      idx = v + kGroupWaves * kst;
+      ++kst;
+    } else {
+      idx = 0;
+      if (li.lane == 0) idx = atomicAdd(ctr, 1);
+      idx = __builtin_amdgcn_readfirstlane(idx);
+    }
+    if ((uint32_t)idx < units) {
+      id = idx;
+      uint32_t bh, ps, pe, r;
+      if ((uint32_t)idx < u0) {
+        bh = (uint32_t)gr.h0;
+        ps = jb;
+        pe = e0;
+        r = (uint32_t)idx;
+      } else {
+        const uint32_t t = (uint32_t)idx - u0;
+        const uint32_t k = (uint32_t)(((uint64_t)t * p.half_magic) >> p.half_shift);   // t / hn
+        bh = (uint32_t)gr.h0 + 1 + k;
+        r = t - k * hn;
+        ps = bh * nblk;
+        pe = ps + nblk < je ? ps + nblk : je;
+      }
+      const uint32_t nu = (pe - ps + 1) / 2;
+      uint32_t x = r + (uint32_t)((rot * nu) >> 20);        // < 2 nu
+      x = x >= nu ? x - nu : x;
+      const uint32_t ja = ps + 2 * x;
+      has2 = ja + 1 < pe;
+      bhout = (int)bh;
+      auto rec = [&](uint32_t j) {
+        return p.table ? (int64_t)__builtin_amdgcn_readfirstlane(recs[j - jb])
+                       : (int64_t)bh * p.nb_cap + (j - bh * nblk);
+      };
+      load_block<FMT>(ra, p, rec(ja), li.lane);
+      if (has2) load_block<FMT>(rb, p, rec(ja + 1), li.lane);
+      else load_block<FMT, false>(rb, p, 0, li.lane);
+    } else {
+      id = -1;
+      bhout = 0;
+      has2 = false;
+      load_block<FMT, false>(ra, p, 0, li.lane);
+      load_block<FMT, false>(rb, p, 0, li.lane);
+    }
+  };
+  if constexpr (PAIR) {
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], rblk[d]);
+    for (int d = 0; d < D - 2; d += 2) fetch_pair(buf[d], buf[d + 1], rid[d], rbh[d], two[d / 2]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], rblk[d]);
+  }
 
   // fp16 block fb of head h belongs to covering workgroup g_lo(h) + fb mod
   // count(h); the workgroup's fp16 blocks go round robin to its wavefronts
@@ -1366,29 +1611,69 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     WaveState ws;
     reset(ws);
     int cur = -1;
-    for (;;) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], rblk[(d + D - 1) % D]);
-        if (rid[d] < 0) goto done;           // blocks are taken in order: none left
-        if (rbh[d] != cur) {
-          if (cur >= 0) {
-            finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
-            reset(ws);
-          }
-          cur = rbh[d];
-          if (cur != qhead) {
-            load_query<FMT>(p, cur, li, qop);
-            qhead = cur;
-          }
-          if constexpr (T::kFp8 || T::kRope) static_q(qop, T::kFp8 ? p.k_scale * kQScale : kQScale, bk_static);
+    if constexpr (PAIR) {
+      // the segment of head h starts: close the previous one (both parities merged)
+      auto begin_head = [&](int h) {
+        if (h == cur) return;
+        if (cur >= 0) {
+          merge_parity(ws);
+          finish_segment(ws, li, wave_slot(cur, v), oscale, true);
+          reset(ws);
         }
-        process_block<FMT>(buf[d], stage, ws, qop, bk_static, li, rc,
-                           (double)p.sink_cap + (double)kBlock * rblk[d]);
+        cur = h;
+        if (cur != qhead) {
+          load_query<FMT>(p, cur, li, qop);
+          qhead = cur;
+        }
+      };
+      // one step per ring position d (a compile-time constant, so the ring
+      // stays in registers); false once no unit is left
+      auto step = [&](auto dc) -> bool {
+        constexpr int d = decltype(dc)::value;
+        constexpr int f = (d + D - 2) % D;
+        fetch_pair(buf[f], buf[f + 1], rid[f], rbh[f], two[f / 2]);
+        if (rid[d] < 0) return false;        // units are taken in order: none left
+        begin_head(rbh[d]);
+        process_pair<FMT>(buf[d], buf[d + 1], two[d / 2], stage, ws, qop, li);
+        return true;
+      };
+      static_assert(D <= 8, "paired ring of at most 8 blocks");
+      for (;;) {
+        if (!step(std::integral_constant<int, 0>{})) break;
+        if (!step(std::integral_constant<int, 2>{})) break;
+        if constexpr (D > 4)
+          if (!step(std::integral_constant<int, (D > 4 ? 4 : 0)>{})) break;
+        if constexpr (D > 6)
+          if (!step(std::integral_constant<int, (D > 6 ? 6 : 0)>{})) break;
+      }
+    } else {
+      for (;;) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          fetch(buf[(d + D - 1) % D], rid[(d + D - 1) % D], rbh[(d + D - 1) % D], rblk[(d + D - 1) % D]);
+          if (rid[d] < 0) goto done;           // blocks are taken in order: none left
+          if (rbh[d] != cur) {
+            if (cur >= 0) {
+              finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+              reset(ws);
+            }
+            cur = rbh[d];
+            if (cur != qhead) {
+              load_query<FMT>(p, cur, li, qop);
+              qhead = cur;
+            }
+            if constexpr (T::kFp8 || T::kRope) static_q(qop, T::kFp8 ? p.k_scale * kQScale : kQScale, bk_static);
+          }
+          process_block<FMT>(buf[d], stage, ws, qop, bk_static, li, rc,
+                             (double)p.sink_cap + (double)kBlock * rblk[d]);
+        }
       }
     }
   done:
-    if (cur >= 0) finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+    if (cur >= 0) {
+      if constexpr (PAIR) merge_parity(ws);
+      finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+    }
   }
   __syncthreads();                            // every wavefront's partials written
 
@@ -1473,12 +1758,12 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
   reduce_head<false>(p, g);
 }
 
-template <int FMT>
+template <int FMT, bool PAIR = false>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16)))
   char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
-  else group_main<FMT>(p, lds);
+  else group_main<FMT, PAIR>(p, lds);
 }
 
 }  // namespace
@@ -1512,6 +1797,17 @@ hipError_t attention_scratch(void** ptr) {
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.groups), block(kGroupThreads);
+  if (p.nrep <= 4) {                    // INT4 / INT2: two blocks per step (process_pair)
+    switch (variant) {
+      case KVQ_INT4: hipLaunchKernelGGL((attn_kernel<KVQ_INT4, true>), grid, block, 0, s, p); return hipGetLastError();
+      case KVQ_INT2: hipLaunchKernelGGL((attn_kernel<KVQ_INT2, true>), grid, block, 0, s, p); return hipGetLastError();
+      case KVQ_INT4 | kMeta16:
+        hipLaunchKernelGGL((attn_kernel<KVQ_INT4 | kMeta16, true>), grid, block, 0, s, p); return hipGetLastError();
+      case KVQ_INT2 | kMeta16:
+        hipLaunchKernelGGL((attn_kernel<KVQ_INT2 | kMeta16, true>), grid, block, 0, s, p); return hipGetLastError();
+      default: break;
+    }
+  }
   switch (variant) {
     case KVQ_INT8: hipLaunchKernelGGL(attn_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(attn_kernel<KVQ_INT4>, grid, block, 0, s, p); break;

@@ -166,6 +166,12 @@ static int32_t prepare_attention(const kvq_cache* c, int64_t n_tokens, const voi
     while ((1ull << l) < d) ++l;
     p.nblk_shift = 31 + l;
     p.nblk_magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+    // the same for d = ceil(nblk / 2), the block pairs of a whole head
+    const uint64_t d2 = (d + 1) / 2;
+    l = 0;
+    while ((1ull << l) < d2) ++l;
+    p.half_shift = 31 + l;
+    p.half_magic = (uint32_t)(((1ull << (31 + l)) + d2 - 1) / d2);
   }
   p.ring_slots = c->ring_slots;
   p.sink_cap = L.sink_tokens;

@@ -148,6 +148,8 @@ struct AttnParams {
   int32_t nblk;           // quantized blocks currently held per head (n_q / 32)
   uint32_t nblk_magic;    // j / nblk == (j * nblk_magic) >> nblk_shift for 0 <= j < 2^31
   int32_t nblk_shift;
+  uint32_t half_magic;    // the same for the divisor ceil(nblk / 2)
+  int32_t half_shift;
   int32_t ring_slots;
   int32_t sink_cap;       // S of the layout (row stride of the sink planes)
   int32_t n_sink;         // sink tokens held
