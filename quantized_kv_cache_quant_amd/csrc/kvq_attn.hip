@@ -476,7 +476,7 @@ struct WaveState {
   float m;          // running max (base-2 logits) of this lane's column
   float l;          // this lane's partial softmax denominator
   f32x4 o[8];       // PV accumulator: rows 16m + 4qd + i, column col
-  float z[2];       // Value zero-point sums of channel groups zg, zg + 1
+  float z[4];       // Value zero-point sums of channel groups zg, zg + 1 (slot path: groups 0-3)
 };
 
 struct LaneInfo {
@@ -505,6 +505,22 @@ __device__ __forceinline__ LaneInfo lane_info(int nrep) {
   return li;
 }
 
+// Slot path (n_rep 8): column col = 8 slot + head, query head col % 8 of
+// the pair's block slot; hi and lo operand parts go through separate
+// matrix-core products into one accumulator, so no column carries a lo part.
+__device__ __forceinline__ LaneInfo lane_info_slot(int nrep) {
+  LaneInfo li = lane_info(nrep);
+  const int col = li.lane & 15;
+  li.head = col & 7;
+  li.par = col >> 3;
+  li.is_lo = false;
+  li.hmask = 0u;
+  li.zg = 0;
+  li.amask = li.par ? 0u : 0xFFFFFFFFu;
+  li.writer = li.par == 0 && li.head < nrep;
+  return li;
+}
+
 // Paired path (n_rep <= 4): column col = 8 lo + 4 par + head, i.e. query head
 // col % 4 of the pair's block par, hi part in columns 0-7, lo in 8-15 (so
 // the hi / lo partner is still lane + 8).  Both parities hold the same head;
@@ -524,7 +540,7 @@ __device__ __forceinline__ void reset(WaveState& ws) {
   ws.l = 0.f;
 #pragma unroll
   for (int m = 0; m < 8; ++m) ws.o[m] = f32x4{0, 0, 0, 0};
-  ws.z[0] = ws.z[1] = 0.f;
+  ws.z[0] = ws.z[1] = ws.z[2] = ws.z[3] = 0.f;
 }
 
 // hi / lo operand pairs.  A column's operand is hi = f16(x) in hi columns and
@@ -594,6 +610,64 @@ __device__ __forceinline__ f16x8 split_p4(const float* a0, const float* az0, con
         "v"(b0[0]), "v"(b0[1]), "v"(b0[2]), "v"(b0[3]), "v"(a1[0]), "v"(a1[1]), "v"(a1[2]), "v"(a1[3]),
         "v"(az1[0]), "v"(az1[1]), "v"(az1[2]), "v"(az1[3]), "v"(b1[0]), "v"(b1[1]), "v"(b1[2]), "v"(b1[3]));
   return cat(r0, r1, r2, r3);
+}
+
+// hi and lo parts of x = q * s for eight channels in every lane (slot path):
+// split_q4 with qz = qh gives hi = f16(x) as its first words and lo =
+// f16(x - hi) as the result.
+struct HiLo {
+  f16x8 hi, lo;
+};
+__device__ __forceinline__ HiLo split_q4_both(const uint32_t* qh, float4 sa, float4 sb) {
+  uint32_t r0, r1, r2, r3, h0, h1, h2, h3;
+  asm("v_fma_mixlo_f16 %4, %8, %12, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %5, %9, %14, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %6, %10, %16, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %7, %11, %18, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %4, %8, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %5, %9, %15, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %6, %10, %17, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %7, %11, %19, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %0, %8, %12, -%4 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %9, %14, -%5 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %10, %16, -%6 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %11, %18, -%7 op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %8, %13, -%4 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %9, %15, -%5 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %10, %17, -%6 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %11, %19, -%7 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3)
+      : "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]),
+        "v"(sa.x), "v"(sa.y), "v"(sa.z), "v"(sa.w), "v"(sb.x), "v"(sb.y), "v"(sb.z), "v"(sb.w));
+  return HiLo{cat(h0, h1, h2, h3), cat(r0, r1, r2, r3)};
+}
+
+// The same for x = a * b with fp32 a, b (eight values: word j holds
+// (a0[j] b0[j], a1[j] b1[j])).
+__device__ __forceinline__ HiLo split_p4_both(const float* a0, const float* b0, const float* a1, const float* b1) {
+  uint32_t r0, r1, r2, r3, h0, h1, h2, h3;
+  asm("v_fma_mixlo_f16 %4, %8, %12, 0\n\t"
+      "v_fma_mixlo_f16 %5, %9, %13, 0\n\t"
+      "v_fma_mixlo_f16 %6, %10, %14, 0\n\t"
+      "v_fma_mixlo_f16 %7, %11, %15, 0\n\t"
+      "v_fma_mixhi_f16 %4, %16, %20, 0\n\t"
+      "v_fma_mixhi_f16 %5, %17, %21, 0\n\t"
+      "v_fma_mixhi_f16 %6, %18, %22, 0\n\t"
+      "v_fma_mixhi_f16 %7, %19, %23, 0\n\t"
+      "v_fma_mixlo_f16 %0, %8, %12, -%4 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %9, %13, -%5 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %10, %14, -%6 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %11, %15, -%7 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %16, %20, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %17, %21, -%5 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %18, %22, -%6 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %19, %23, -%7 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3)
+      : "v"(a0[0]), "v"(a0[1]), "v"(a0[2]), "v"(a0[3]), "v"(b0[0]), "v"(b0[1]), "v"(b0[2]), "v"(b0[3]),
+        "v"(a1[0]), "v"(a1[1]), "v"(a1[2]), "v"(a1[3]), "v"(b1[0]), "v"(b1[1]), "v"(b1[2]), "v"(b1[3]));
+  return HiLo{cat(h0, h1, h2, h3), cat(r0, r1, r2, r3)};
 }
 
 // hi / lo pair of a fully fp32 operand (both parts in every lane):
@@ -713,8 +787,8 @@ __device__ __forceinline__ void softmax_block(float lg[2][4], WaveState& ws, flo
     const float alpha = __builtin_amdgcn_exp2f(ws.m - m_new);
 #pragma unroll
     for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
-    ws.z[0] *= alpha;
-    ws.z[1] *= alpha;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ws.z[g] *= alpha;
     ws.l *= alpha;
     ws.m = m_new;
   }
@@ -744,8 +818,8 @@ __device__ __forceinline__ void softmax_block_some(float lg[2][4], WaveState& ws
     const float alpha = active ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) ws.o[m] *= alpha;
-    ws.z[0] *= alpha;
-    ws.z[1] *= alpha;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ws.z[g] *= alpha;
     ws.l *= alpha;
     ws.m = active ? m_new : ws.m;
   }
@@ -1079,6 +1153,147 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
   }
 }
 
+// Two blocks of one KV head at once at n_rep 8 (INT4 / INT2; see
+// lane_info_slot): column col = 8 slot + head holds the pair's block slot,
+// and the hi and lo parts of q' and P' are separate operands, each with its
+// own matrix-core product into the same accumulator.  Every lane forms both
+// parts of its own block's q' and P' (two split instructions give two
+// operand halves), so each split instruction, each zero-point term and the
+// softmax serve one (head, block) column, none a lo column.  The PV products
+// take the P' columns of their block (the other slot's columns masked to
+// zero).  b_on = false: only block ra counts.
+template <int FMT>
+__device__ __forceinline__ void process_slots(const Raw<FMT>& ra, const Raw<FMT>& rb, bool b_on, float* st,
+                                              WaveState& ws, const QOp& q, const LaneInfo& li) {
+  using T = Traits<FMT>;
+  const int qd = li.qd;
+  stage_meta<FMT>(ra, st, li.lane);
+  stage_meta<FMT>(rb, st + kStage, li.lane);
+  const float* sp = st + (li.par ? kStage : 0);          // this lane's block
+
+  float bz[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint4* zh = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sp) + 256 + 32 * qd);
+  const uint4* zl = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sp) + 384 + 32 * qd);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 h = zh[i], l = zl[i];
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bz[i & 1] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(hw[k]), bz[i & 1], false);
+      bz[2 + (i & 1)] = __builtin_amdgcn_fdot2(u2h(q.h[4 * i + k]), u2h(lw[k]), bz[2 + (i & 1)], false);
+    }
+  }
+  const float kbias = rows_sum((bz[0] + bz[1]) + (bz[2] + bz[3]));
+
+  f32x4 acc_a[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  f32x4 acc_b[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float4 sa = *reinterpret_cast<const float4*>(sp + 32 * qd + 8 * kb);
+    const float4 sb = *reinterpret_cast<const float4*>(sp + 32 * qd + 8 * kb + 4);
+    const HiLo bq = split_q4_both(q.h + 4 * kb, sa, sb);
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const f16x8 ka = operand<FMT>(ra.k[tile], kb), kbo = operand<FMT>(rb.k[tile], kb);
+      acc_a[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq.hi, acc_a[tile], 0, 0, 0);
+      acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbo, bq.hi, acc_b[tile], 0, 0, 0);
+      acc_a[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq.lo, acc_a[tile], 0, 0, 0);
+      acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbo, bq.lo, acc_b[tile], 0, 0, 0);
+    }
+  }
+  float lg[2][4], pr[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lg[tile][i] = __builtin_fmaf(li.par ? acc_b[tile][i] : acc_a[tile][i], T::kCodeScale, -kbias);
+  const float2 sva = pair_scales<FMT>(ra.vm), svb = pair_scales<FMT>(rb.vm);
+  const bool big = sva.x > kLazyScaleMax || sva.y > kLazyScaleMax || (b_on && (svb.x > kLazyScaleMax || svb.y > kLazyScaleMax));
+  const float slack = __any(big) ? 0.f : kSlack;
+  if (b_on) softmax_block(lg, ws, pr, slack);
+  else softmax_block_some(lg, ws, pr, slack, li.par == 0);
+
+  // Value zero-point sums of all four groups (this lane's block)
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float* zs = sp + 384 + 32 * g;
+    const float4 z0 = *reinterpret_cast<const float4*>(zs + 4 * qd);
+    const float4 z1 = *reinterpret_cast<const float4*>(zs + 16 + 4 * qd);
+    float za = ws.z[g];
+    za = __builtin_fmaf(pr[0][0], z0.x, za); za = __builtin_fmaf(pr[0][1], z0.y, za);
+    za = __builtin_fmaf(pr[0][2], z0.z, za); za = __builtin_fmaf(pr[0][3], z0.w, za);
+    za = __builtin_fmaf(pr[1][0], z1.x, za); za = __builtin_fmaf(pr[1][1], z1.y, za);
+    za = __builtin_fmaf(pr[1][2], z1.z, za); za = __builtin_fmaf(pr[1][3], z1.w, za);
+    ws.z[g] = za;
+  }
+  const uint32_t am = li.amask, bm = ~li.amask;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 s0 = *reinterpret_cast<const float4*>(sp + 256 + 32 * g + 4 * qd);
+    const float4 s1 = *reinterpret_cast<const float4*>(sp + 256 + 32 * g + 16 + 4 * qd);
+    const float sv0[4] = {s0.x, s0.y, s0.z, s0.w};
+    const float sv1[4] = {s1.x, s1.y, s1.z, s1.w};
+    const HiLo bp = split_p4_both(pr[0], sv0, pr[1], sv1);
+    const uint4 wh = __builtin_bit_cast(uint4, bp.hi), wl = __builtin_bit_cast(uint4, bp.lo);
+    const f16x8 ha = cat(wh.x & am, wh.y & am, wh.z & am, wh.w & am);
+    const f16x8 la = cat(wl.x & am, wl.y & am, wl.z & am, wl.w & am);
+    const f16x8 hb = cat(wh.x & bm, wh.y & bm, wh.z & bm, wh.w & bm);
+    const f16x8 lb = cat(wl.x & bm, wl.y & bm, wl.z & bm, wl.w & bm);
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * g + mm;
+      const f16x8 va = operand<FMT>(ra.v, m), vb = operand<FMT>(rb.v, m);
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ha, ws.o[m], 0, 0, 0);
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, hb, ws.o[m], 0, 0, 0);
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, la, ws.o[m], 0, 0, 0);
+      ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, lb, ws.o[m], 0, 0, 0);
+    }
+  }
+}
+
+// Slot path: fold the other slot's state (lane + 8 in the row: same quarter,
+// same head, other block slot) into this lane's, so both slots' lanes hold
+// the head's state over both.  An empty state (m = -inf) weighs 0.
+__device__ __forceinline__ void merge_slots(WaveState& ws) {
+  const float mo = ror8(ws.m);
+  const float mn = fmaxf(ws.m, mo);
+  const float a = ws.m == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ws.m - mn);
+  const float b = mo == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+  ws.l = __builtin_fmaf(a, ws.l, b * ror8(ws.l));
+#pragma unroll
+  for (int g = 0; g < 4; ++g) ws.z[g] = __builtin_fmaf(a, ws.z[g], b * ror8(ws.z[g]));
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.o[m][i] = __builtin_fmaf(a, ws.o[m][i], b * ror8(ws.o[m][i]));
+  ws.m = mn;
+}
+
+// Slot path counterpart of finish_segment (after merge_slots): the lane's
+// column already holds whole values, so only the four quarters are summed.
+__device__ __forceinline__ void finish_slot_segment(const WaveState& ws, const LaneInfo& li, float* slot,
+                                                    float oscale) {
+  const float l = rows_sum(ws.l);
+  float zs[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) zs[g] = rows_sum(ws.z[g]);
+  float* dst = slot + li.head * kPartStride;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    float4 o;
+    o.x = ws.o[m][0] * oscale - zs[m >> 1];
+    o.y = ws.o[m][1] * oscale - zs[m >> 1];
+    o.z = ws.o[m][2] * oscale - zs[m >> 1];
+    o.w = ws.o[m][3] * oscale - zs[m >> 1];
+    if (li.writer) *reinterpret_cast<float4*>(dst + 4 + 16 * m + 4 * li.qd) = o;
+  }
+  if (li.writer && li.qd == 0) {
+    dst[0] = ws.m;
+    dst[1] = l;
+  }
+}
+
 // Paired path: fold the second-block columns' softmax state (lane ^ 4: same
 // quarter, same hi / lo half, other parity) into the first's, so that every
 // lane holds its head's state over both.  An empty state (m = -inf) weighs 0.
@@ -1284,8 +1499,11 @@ constexpr int kGroupThreads = 64 * kGroupWaves;
 constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
 // workgroup LDS: the wavefronts' areas, the block counter, the record ids of
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
-constexpr int kLdsBytes = kGroupWaves * kWaveLds + 16 + 4 * kMaxPagedRange;
+constexpr int kLdsHeader = 16 + 4 * kGroupWaves;    // block counter, then each wavefront's final head
+constexpr int kLdsBytes = kGroupWaves * kWaveLds + kLdsHeader + 4 * kMaxPagedRange;
 static_assert(kWaveLds >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
+static_assert(kWaveLds >= 8 * kPartStride * 4, "a wavefront's area holds its last segment's partial at n_rep 8");
+static_assert(kWaveLds >= 2 * kStage * 4, "a wavefront's area stages two blocks (paired and slot paths)");
 static_assert(kWaveLds >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
@@ -1344,42 +1562,124 @@ __device__ __forceinline__ void fold(float& M, float& L, float& O, const float* 
   }
 }
 
-constexpr int kReduceBatch = 16;          // slots whose loads a thread issues together
+// fold for four channels that share their partials' (m, l).
+template <int N>
+__device__ __forceinline__ void fold4(float& M, float& L, float4& O, const float* m, const float* l,
+                                      const float4* o) {
+  float Mn = M;
+#pragma unroll
+  for (int j = 0; j < N; ++j) Mn = fmaxf(Mn, m[j]);
+  if (Mn != neg_inf()) {
+    const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
+    L *= a;
+    O.x *= a; O.y *= a; O.z *= a; O.w *= a;
+  }
+  M = Mn;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (m[j] != neg_inf()) {
+      const float wt = exp2f(m[j] - M);
+      L = __builtin_fmaf(wt, l[j], L);
+      O.x = __builtin_fmaf(wt, o[j].x, O.x);
+      O.y = __builtin_fmaf(wt, o[j].y, O.y);
+      O.z = __builtin_fmaf(wt, o[j].z, O.z);
+      O.w = __builtin_fmaf(wt, o[j].w, O.w);
+    }
+  }
+}
+
+// Four consecutive floats of a merged slot, device-coherent (two 64-bit
+// relaxed atomics at agent scope).
+__device__ __forceinline__ void st_dev4(float* p, float4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, ((uint64_t)__builtin_bit_cast(uint32_t, v.y) << 32) | __builtin_bit_cast(uint32_t, v.x),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, ((uint64_t)__builtin_bit_cast(uint32_t, v.w) << 32) | __builtin_bit_cast(uint32_t, v.z),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_dev4(const float* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float4{__builtin_bit_cast(float, (uint32_t)a), __builtin_bit_cast(float, (uint32_t)(a >> 32)),
+                __builtin_bit_cast(float, (uint32_t)b), __builtin_bit_cast(float, (uint32_t)(b >> 32))};
+}
+
+constexpr int kReduceItems = 4;           // items per thread and pass of the combine
+constexpr int kReduceBatch = 4;           // slots per item whose loads are issued together
 
 // out[b][h] of all n_rep query heads of (sequence, KV head) h:
 //   sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
 // (the exact regrouping of one softmax over all tokens), over the slots in
-// a fixed order.  SHARED: the head's merged workgroup slots, written by other
-// workgroups (device-coherent loads); otherwise its fp16 slots, written by
-// this workgroup before a barrier.  Every load of a batch of kReduceBatch
-// slots is issued before any is used (one memory round trip).
+// a fixed order, for every head heads[0 .. nh-1] (heads == nullptr: the
+// single head `single`).  SHARED: the head's merged workgroup slots, written
+// by other workgroups (device-coherent loads); otherwise its fp16 slots,
+// written by this workgroup before a barrier.  Items are (head, query head,
+// four channels), kReduceItems per thread and pass; the loads of
+// kReduceBatch slots of all of a thread's items are issued before any is
+// used (one memory round trip per batch).
 template <bool SHARED>
-__device__ void reduce_head(const AttnParams& p, int64_t h) {
-  const int ns = SHARED ? (int)covering_count(p, h) : p.fp16_blocks;
-  const float* base = SHARED ? p.part_group + (covering_lo(p, h) + h) * slot_floats(p)
-                             : p.part_fp16 + h * p.fp16_blocks * slot_floats(p);
-  for (int idx = threadIdx.x; idx < p.nrep * kHeadDim; idx += kGroupThreads) {
-    const int hh = idx / kHeadDim, c = idx % kHeadDim;
-    float M = neg_inf(), L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += kReduceBatch) {
-      float m[kReduceBatch], l[kReduceBatch], o[kReduceBatch];
+__device__ void reduce_heads(const AttnParams& p, const int* heads, int nh, int single = 0) {
+  const int per = p.nrep * (kHeadDim / 4);
+  const int total = nh * per;
+  int max_ns = 0;
+  for (int i = 0; i < nh; ++i) {
+    const int ns = SHARED ? (int)covering_count(p, heads ? heads[i] : single) : p.fp16_blocks;
+    max_ns = ns > max_ns ? ns : max_ns;
+  }
+  for (int base = 0; base < total; base += kReduceItems * kGroupThreads) {
+    float M[kReduceItems], L[kReduceItems];
+    float4 O[kReduceItems];
+    int ns[kReduceItems], off[kReduceItems];
+    const float* sb[kReduceItems];
 #pragma unroll
-      for (int j = 0; j < kReduceBatch; ++j) {
-        if (s0 + j < ns) {
-          const float* sp = base + (s0 + j) * slot_floats(p) + hh * kPartStride;
-          m[j] = SHARED ? ld_dev(sp) : sp[0];
-          l[j] = SHARED ? ld_dev(sp + 1) : sp[1];
-          o[j] = SHARED ? ld_dev(sp + 4 + c) : sp[4 + c];
-        } else {
-          m[j] = neg_inf();
-          l[j] = 0.f;
-          o[j] = 0.f;
+    for (int k = 0; k < kReduceItems; ++k) {
+      M[k] = neg_inf();
+      L[k] = 0.f;
+      O[k] = float4{0.f, 0.f, 0.f, 0.f};
+      const int idx = base + (int)threadIdx.x + k * kGroupThreads;
+      const int hi = idx < total ? idx / per : 0, r = idx % per;
+      const int64_t h = heads ? heads[hi] : single;
+      off[k] = (r >> 5) * kPartStride;                 // query head r / 32
+      ns[k] = idx < total ? (SHARED ? (int)covering_count(p, h) : p.fp16_blocks) : 0;
+      sb[k] = SHARED ? p.part_group + (covering_lo(p, h) + h) * slot_floats(p)
+                     : p.part_fp16 + h * p.fp16_blocks * slot_floats(p);
+    }
+    for (int s0 = 0; s0 < max_ns; s0 += kReduceBatch) {
+      float m[kReduceItems][kReduceBatch], l[kReduceItems][kReduceBatch];
+      float4 o[kReduceItems][kReduceBatch];
+#pragma unroll
+      for (int k = 0; k < kReduceItems; ++k) {
+        const int c4 = ((base + (int)threadIdx.x + k * kGroupThreads) % per) & 31;
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j) {
+          if (s0 + j < ns[k]) {
+            const float* sp = sb[k] + (s0 + j) * slot_floats(p) + off[k];
+            m[k][j] = SHARED ? ld_dev(sp) : sp[0];
+            l[k][j] = SHARED ? ld_dev(sp + 1) : sp[1];
+            o[k][j] = SHARED ? ld_dev4(sp + 4 + 4 * c4) : *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+          } else {
+            m[k][j] = neg_inf();
+            l[k][j] = 0.f;
+            o[k][j] = float4{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
-      fold<kReduceBatch>(M, L, O, m, l, o);
+#pragma unroll
+      for (int k = 0; k < kReduceItems; ++k) fold4<kReduceBatch>(M[k], L[k], O[k], m[k], l[k], o[k]);
     }
-    const _Float16 r = (_Float16)(O / L);
-    p.out[(h * p.nrep + hh) * kHeadDim + c] = __builtin_bit_cast(uint16_t, r);
+#pragma unroll
+    for (int k = 0; k < kReduceItems; ++k) {
+      const int idx = base + (int)threadIdx.x + k * kGroupThreads;
+      if (idx < total) {
+        const int r = idx % per;
+        const int64_t h = heads ? heads[idx / per] : single;
+        const f16x2 lo = {(_Float16)(O[k].x / L[k]), (_Float16)(O[k].y / L[k])};
+        const f16x2 hi = {(_Float16)(O[k].z / L[k]), (_Float16)(O[k].w / L[k])};
+        *reinterpret_cast<uint2*>(p.out + (h * p.nrep + (r >> 5)) * kHeadDim + 4 * (r & 31)) =
+            uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+    }
   }
 }
 
@@ -1394,20 +1694,23 @@ __device__ void reduce_head(const AttnParams& p, int64_t h) {
 // device-scope fences.
 __device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* lds) {
   int* last = reinterpret_cast<int*>(lds);       // the wavefront areas are free by now
+  int* nlast = last + kGroupThreads;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int64_t hb = h0; hb <= h1; hb += kGroupThreads) {
     const int n = h1 - hb + 1 < kGroupThreads ? (int)(h1 - hb + 1) : kGroupThreads;
+    if (threadIdx.x == 0) *nlast = 0;
+    __syncthreads();
     if ((int)threadIdx.x < n) {
       const int64_t h = hb + threadIdx.x;
       const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int is_last = prev == (int)covering_count(p, h) - 1;
-      if (is_last) __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last[threadIdx.x] = is_last;
+      if (prev == (int)covering_count(p, h) - 1) {
+        __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last[atomicAdd(nlast, 1)] = (int)h;       // LDS list of the heads to combine
+      }
     }
     __syncthreads();
-    for (int i = 0; i < n; ++i)
-      if (last[i]) reduce_head<true>(p, hb + i);
+    if (*nlast > 0) reduce_heads<true>(p, last, *nlast);
     __syncthreads();                             // before last[] is rewritten
   }
 }
@@ -1422,22 +1725,27 @@ __device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* 
 // slot per head of the range.  Before its first block it handles its share of
 // the workgroup's fp16 blocks, while its first blocks load.  At the end the
 // workgroup merges its wavefronts' partials into one slot per head.
-// PAIR: blocks are processed two at a time (process_pair; INT4 / INT2 at
-// n_rep <= 4), with a ring of kPairRing blocks.
-template <int FMT, bool PAIR>
+// MODE: kSingle (process_block), kPairs (process_pair; INT4 / INT2 at
+// n_rep <= 4) or kSlots (process_slots; INT4 / INT2 at n_rep 8); the last
+// two take blocks two at a time, with a ring of kPairRing blocks.
+constexpr int kSingle = 0, kPairs = 1, kSlots = 2;
+template <int FMT, int MODE>
 __device__ void group_main(const AttnParams& p, char* lds) {
   using T = Traits<FMT>;
+  constexpr bool PAIR = MODE != kSingle;
   constexpr int D = PAIR ? T::kPairRing : T::kDepth + 1;
   static_assert(!PAIR || (T::kPairable && D % 2 == 0 && D >= 4), "paired ring");
   const int g = blockIdx.x;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront index, uniform
-  const LaneInfo li = PAIR ? lane_info_pair(p.nrep) : lane_info(p.nrep);
+  const LaneInfo li = MODE == kPairs ? lane_info_pair(p.nrep) : (MODE == kSlots ? lane_info_slot(p.nrep)
+                                                                                 : lane_info(p.nrep));
   const GroupRange gr = group_range(p, g);
   if (!gr.len) return;                        // (never: every workgroup has a range)
   const uint32_t nblk = (uint32_t)p.nblk;
   float* stage = reinterpret_cast<float*>(lds + v * kWaveLds);
   int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
-  int* recs = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + 16);
+  int* fin_head = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + 16);
+  int* recs = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + kLdsHeader);
 
   // paged caches: the record ids of the range's blocks, read from the block
   // table once (a page id outside the pool reads record 0 instead)
@@ -1616,8 +1924,13 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       auto begin_head = [&](int h) {
         if (h == cur) return;
         if (cur >= 0) {
-          merge_parity(ws);
-          finish_segment(ws, li, wave_slot(cur, v), oscale, true);
+          if constexpr (MODE == kSlots) {
+            merge_slots(ws);
+            finish_slot_segment(ws, li, wave_slot(cur, v), oscale);
+          } else {
+            merge_parity(ws);
+            finish_segment(ws, li, wave_slot(cur, v), oscale, true);
+          }
           reset(ws);
         }
         cur = h;
@@ -1634,7 +1947,8 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         fetch_pair(buf[f], buf[f + 1], rid[f], rbh[f], two[f / 2]);
         if (rid[d] < 0) return false;        // units are taken in order: none left
         begin_head(rbh[d]);
-        process_pair<FMT>(buf[d], buf[d + 1], two[d / 2], stage, ws, qop, li);
+        if constexpr (MODE == kSlots) process_slots<FMT>(buf[d], buf[d + 1], two[d / 2], stage, ws, qop, li);
+        else process_pair<FMT>(buf[d], buf[d + 1], two[d / 2], stage, ws, qop, li);
         return true;
       };
       static_assert(D <= 8, "paired ring of at most 8 blocks");
@@ -1670,75 +1984,82 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       }
     }
   done:
+    // the wavefront's last segment goes to its own LDS area (free now), the
+    // earlier ones went to global memory
     if (cur >= 0) {
-      if constexpr (PAIR) merge_parity(ws);
-      finish_segment(ws, li, wave_slot(cur, v), oscale, !T::kFp8);
+      if constexpr (MODE == kSlots) {
+        merge_slots(ws);
+        finish_slot_segment(ws, li, stage, oscale);
+      } else {
+        if constexpr (MODE == kPairs) merge_parity(ws);
+        finish_segment(ws, li, stage, oscale, !T::kFp8);
+      }
     }
+    if (li.lane == 0) fin_head[v] = cur;
   }
   __syncthreads();                            // every wavefront's partials written
 
   // merge the wavefronts' partials of each head, then the fp16 blocks of the
   // head that this workgroup handled (fb = g - g_lo(h) + k count(h)), into
-  // the workgroup's slot: thread t takes (query head, channel) items t,
-  // t + threads, ...; the loads of the wavefront slots and of the first
-  // kFoldFp16 fp16 slots are issued before any is used
+  // the workgroup's slot.  Items are (head, query head, four channels) of
+  // all the range's heads, one per thread and pass; a pass issues the loads
+  // of the wavefront slots and of the first kFoldFp16 fp16 slots of its
+  // items before it uses any.
   {
-    constexpr int kItems = 8 * kHeadDim / kGroupThreads;     // items per thread at n_rep 8
     constexpr int kFoldFp16 = 4;
     const int nf = p.fp16_blocks;
-    for (int h = gr.h0; h <= gr.h1; ++h) {
+    const int per = p.nrep * (kHeadDim / 4);
+    const int total = (gr.h1 - gr.h0 + 1) * per;
+    for (int idx = threadIdx.x; idx < total; idx += kGroupThreads) {
+      const int h = gr.h0 + idx / per, r = idx % per, hh = r >> 5, c4 = r & 31;
       const int64_t nc = covering_count(p, h), fb0 = g - covering_lo(p, h);
-      float m[kItems][kGroupWaves], l[kItems][kGroupWaves], o[kItems][kGroupWaves];
-      float fm[kItems][kFoldFp16], fl[kItems][kFoldFp16], fo[kItems][kFoldFp16];
-      auto load_fp16 = [&](int k, int64_t first, int hh, int c) {
+      float m[kGroupWaves], l[kGroupWaves], fm[kFoldFp16], fl[kFoldFp16];
+      float4 o[kGroupWaves], fo[kFoldFp16];
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) {
+        if (fin_head[w] == h) {                   // the wavefront's last segment, in LDS
+          const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds) + hh * kPartStride;
+          m[w] = sp[0];
+          l[w] = sp[1];
+          o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+        } else {
+          const float* sp = wave_slot(h, w) + hh * kPartStride;
+          m[w] = sp[0];
+          l[w] = sp[1];
+          o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+        }
+      }
+      auto load_fp16 = [&](int64_t first) {
 #pragma unroll
         for (int j = 0; j < kFoldFp16; ++j) {
           const int64_t fb = first + j * nc;
           if (fb < nf) {
             const float* sp = p.part_fp16 + ((int64_t)h * nf + fb) * slot_floats(p) + hh * kPartStride;
-            fm[k][j] = sp[0];
-            fl[k][j] = sp[1];
-            fo[k][j] = sp[4 + c];
+            fm[j] = sp[0];
+            fl[j] = sp[1];
+            fo[j] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
           } else {
-            fm[k][j] = neg_inf();
-            fl[k][j] = 0.f;
-            fo[k][j] = 0.f;
+            fm[j] = neg_inf();
+            fl[j] = 0.f;
+            fo[j] = float4{0.f, 0.f, 0.f, 0.f};
           }
         }
       };
-#pragma unroll
-      for (int k = 0; k < kItems; ++k) {
-        const int idx = (int)threadIdx.x + k * kGroupThreads;
-        if (idx < p.nrep * kHeadDim) {
-#pragma unroll
-          for (int w = 0; w < kGroupWaves; ++w) {
-            const float* sp = wave_slot(h, w) + (idx / kHeadDim) * kPartStride;
-            m[k][w] = sp[0];
-            l[k][w] = sp[1];
-            o[k][w] = sp[4 + idx % kHeadDim];
-          }
-          load_fp16(k, fb0, idx / kHeadDim, idx % kHeadDim);
-        }
+      load_fp16(fb0);
+      float M = neg_inf(), L = 0.f;
+      float4 O = {0.f, 0.f, 0.f, 0.f};
+      fold4<kGroupWaves>(M, L, O, m, l, o);
+      fold4<kFoldFp16>(M, L, O, fm, fl, fo);
+      for (int64_t first = fb0 + kFoldFp16 * nc; first < nf; first += kFoldFp16 * nc) {
+        load_fp16(first);                         // more than kFoldFp16 fp16 blocks here
+        fold4<kFoldFp16>(M, L, O, fm, fl, fo);
       }
-#pragma unroll
-      for (int k = 0; k < kItems; ++k) {
-        const int idx = (int)threadIdx.x + k * kGroupThreads;
-        if (idx >= p.nrep * kHeadDim) continue;
-        const int hh = idx / kHeadDim, c = idx % kHeadDim;
-        float M = neg_inf(), L = 0.f, O = 0.f;
-        fold<kGroupWaves>(M, L, O, m[k], l[k], o[k]);
-        fold<kFoldFp16>(M, L, O, fm[k], fl[k], fo[k]);
-        for (int64_t first = fb0 + kFoldFp16 * nc; first < nf; first += kFoldFp16 * nc) {
-          load_fp16(k, first, hh, c);           // more than kFoldFp16 fp16 blocks here
-          fold<kFoldFp16>(M, L, O, fm[k], fl[k], fo[k]);
-        }
-        float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
-        if (c == 0) {
-          st_dev(dst, M);
-          st_dev(dst + 1, L);
-        }
-        st_dev(dst + 4 + c, O);
+      float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
+      if (c4 == 0) {
+        st_dev(dst, M);
+        st_dev(dst + 1, L);
       }
+      st_dev4(dst + 4 + 4 * c4, O);
     }
   }
   finish_heads(p, gr.h0, gr.h1, lds);
@@ -1755,15 +2076,15 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
     fp16_block<ROPE>(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
                p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
   __syncthreads();                            // the head's partials, all written by this workgroup
-  reduce_head<false>(p, g);
+  reduce_heads<false>(p, nullptr, 1, g);
 }
 
-template <int FMT, bool PAIR = false>
+template <int FMT, int MODE = kSingle>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16)))
   char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
-  else group_main<FMT, PAIR>(p, lds);
+  else group_main<FMT, MODE>(p, lds);
 }
 
 }  // namespace
@@ -1797,17 +2118,26 @@ hipError_t attention_scratch(void** ptr) {
 
 hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.groups), block(kGroupThreads);
-  if (p.nrep <= 4) {                    // INT4 / INT2: two blocks per step (process_pair)
+  // INT4 / INT2: two blocks per step, process_pair at n_rep <= 4, process_slots at n_rep 8
+#define KVQ_LAUNCH2(V, M) hipLaunchKernelGGL((attn_kernel<V, M>), grid, block, 0, s, p); return hipGetLastError()
+  if (p.nrep <= 4) {
     switch (variant) {
-      case KVQ_INT4: hipLaunchKernelGGL((attn_kernel<KVQ_INT4, true>), grid, block, 0, s, p); return hipGetLastError();
-      case KVQ_INT2: hipLaunchKernelGGL((attn_kernel<KVQ_INT2, true>), grid, block, 0, s, p); return hipGetLastError();
-      case KVQ_INT4 | kMeta16:
-        hipLaunchKernelGGL((attn_kernel<KVQ_INT4 | kMeta16, true>), grid, block, 0, s, p); return hipGetLastError();
-      case KVQ_INT2 | kMeta16:
-        hipLaunchKernelGGL((attn_kernel<KVQ_INT2 | kMeta16, true>), grid, block, 0, s, p); return hipGetLastError();
+      case KVQ_INT4: KVQ_LAUNCH2(KVQ_INT4, kPairs);
+      case KVQ_INT2: KVQ_LAUNCH2(KVQ_INT2, kPairs);
+      case KVQ_INT4 | kMeta16: KVQ_LAUNCH2(KVQ_INT4 | kMeta16, kPairs);
+      case KVQ_INT2 | kMeta16: KVQ_LAUNCH2(KVQ_INT2 | kMeta16, kPairs);
+      default: break;
+    }
+  } else {
+    switch (variant) {
+      case KVQ_INT4: KVQ_LAUNCH2(KVQ_INT4, kSlots);
+      case KVQ_INT2: KVQ_LAUNCH2(KVQ_INT2, kSlots);
+      case KVQ_INT4 | kMeta16: KVQ_LAUNCH2(KVQ_INT4 | kMeta16, kSlots);
+      case KVQ_INT2 | kMeta16: KVQ_LAUNCH2(KVQ_INT2 | kMeta16, kSlots);
       default: break;
     }
   }
+#undef KVQ_LAUNCH2
   switch (variant) {
     case KVQ_INT8: hipLaunchKernelGGL(attn_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(attn_kernel<KVQ_INT4>, grid, block, 0, s, p); break;
