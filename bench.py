@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--formats", default=None, help="comma list overriding the workload's formats")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count")
     ap.add_argument("--blocks-per-group", type=int, default=0)
+    ap.add_argument("--deterministic", action="store_true",
+                    help="time the deterministic hand-out (kv_decode_attention_split, deterministic = 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the attention sweep of the other variants")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -262,9 +264,9 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         # kv_append_decode_attention: append + attention, one launch unless a block leaves the
         # window (every 32nd step); an explicit split takes the two separate calls
         for c in caches:
-            if args.blocks_per_group:
+            if args.blocks_per_group or args.deterministic:
                 c.append(steps_k[j], steps_v[j])
-                c.attention(q, out, ws, args.blocks_per_group)
+                c.attention(q, out, ws, args.blocks_per_group, args.deterministic)
             else:
                 c.append_attention(steps_k[j], steps_v[j], q, out, ws)
 
@@ -288,7 +290,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     for r in range(rounds):
         for li, c in enumerate(caches):
             evs[r][li][0].record()
-            c.attention(q, out, ws, args.blocks_per_group)
+            c.attention(q, out, ws, args.blocks_per_group, args.deterministic)
             evs[r][li][1].record()
     torch.cuda.synchronize()
     attn_ms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]

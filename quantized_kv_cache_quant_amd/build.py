@@ -62,5 +62,51 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+def sanitizer_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (preloaded by a host process that loads
+    the sanitizer build)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for pat in (os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"),
+                "/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+        hits = sorted(glob.glob(pat))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """A copy of the library whose host code (the C ABI: validation, sizing, routing, launch
+    set-up) is built with AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests of
+    the ABI.  The kernels' objects come from the regular build (compiled first if missing);
+    the sanitizers apply to host code only.  Written to _build/sanitized/libkvq.so."""
+    cc = hipcc()
+    bdir = os.path.join(ROOT, "_build")
+    sdir = os.path.join(bdir, "sanitized")
+    os.makedirs(sdir, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(bdir, src + ".o")
+        if src.endswith(".hip"):
+            if not os.path.exists(obj):
+                subprocess.run([cc, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], check=True)
+        else:
+            obj = os.path.join(sdir, src + ".o")
+            san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+            cmd = [cc, *COMMON, *extra, *san, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+        objs.append(obj)
+    out = os.path.join(sdir, "libkvq.so")
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

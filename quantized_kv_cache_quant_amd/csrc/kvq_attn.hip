@@ -52,6 +52,14 @@
 
 #include "kvq_internal.h"
 
+// 1: the arrival counter is a release fetch-add and the last arriver takes an
+// agent-scope acquire fence (the language memory model's hand-over); 0: the
+// hardware ordering of coherent stores, their acknowledgement, the barrier
+// and the arrival (see finish_heads).
+#ifndef KVQ_FORMAL_ORDERING
+#define KVQ_FORMAL_ORDERING 0
+#endif
+
 namespace kvq {
 namespace {
 
@@ -1703,7 +1711,14 @@ __device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* 
     __syncthreads();
     if ((int)threadIdx.x < n) {
       const int64_t h = hb + threadIdx.x;
+#if KVQ_FORMAL_ORDERING
+      // release: this workgroup's slot stores happen before its arrival;
+      // acquire (last arriver): the other workgroups' slots are visible
+      const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (int)covering_count(p, h) - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#else
       const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
       if (prev == (int)covering_count(p, h) - 1) {
         __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last[atomicAdd(nlast, 1)] = (int)h;       // LDS list of the heads to combine

@@ -10,7 +10,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIBRARY overrides the path (e.g. the host-sanitizer build that the CPU ABI tests load)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 KVQ_OK = 0
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_LAYOUT", -3: "KVQ_ERR_UNSUPPORTED",

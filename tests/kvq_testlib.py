@@ -7,6 +7,8 @@ computed by ``oracle.cache.build_cache``.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -38,11 +40,51 @@ def olayout_of(lay_kw: dict) -> ocache.Layout:
                          outliers=bool(k.get("outliers", False)))
 
 
+CANARY = 0xC5          # guard byte pattern
+GUARD = 256            # guard bytes after the cache buffer, the workspace and the output
+
+
 def make_cache(lay_kw: dict) -> kvq.Cache:
+    """A cache whose device buffer is followed by GUARD canary bytes (and pre-filled with the
+    canary, so the alignment gaps between planes hold it too); see check_guards."""
     k = dict(lay_kw)
     lay = kvq.make_layout(k.pop("batch"), k.pop("num_kv_heads"), k.pop("num_q_heads"), 128,
                           k.pop("max_tokens"), k.pop("fmt"), **k)
-    return kvq.Cache.create(lay)
+    nbytes = kvq.cache_bytes(lay)
+    full = torch.full((nbytes + GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+    buf = full[:nbytes]                      # torch's allocations are 512-byte aligned
+    h = kvq.CacheStruct()
+    kvq.check(kvq.lib().kvq_cache_init(ctypes.byref(h), ctypes.byref(lay), ctypes.c_void_p(buf.data_ptr()), nbytes),
+              "kvq_cache_init")
+    c = kvq.Cache(lay, buf, h)
+    c.guard = full[nbytes:]
+    return c
+
+
+def plane_gaps(c: kvq.Cache):
+    """Byte ranges of the cache buffer that belong to no plane (alignment padding)."""
+    spans = sorted((c.handle.plane_off[i], c.handle.plane_off[i] + c.handle.plane_bytes[i])
+                   for i in range(len(kvq.PLANES)))
+    gaps, end = [], 0
+    for a, b in spans:
+        if a > end:
+            gaps.append((end, a))
+        end = max(end, b)
+    if end < c.buf.numel():
+        gaps.append((end, c.buf.numel()))
+    return gaps
+
+
+def check_guards(c: kvq.Cache) -> None:
+    """No write past the cache buffer (the trailing canary bytes) and none into the padding
+    between planes (every padding byte still holds the one value it was filled with)."""
+    g = getattr(c, "guard", None)
+    if g is not None:
+        assert bool((g == CANARY).all()), "a kernel wrote past the end of the cache buffer"
+    gaps = plane_gaps(c)
+    if gaps:
+        pad = torch.cat([c.buf[a:b] for a, b in gaps])
+        assert bool((pad == pad[0]).all()), "a kernel wrote into the padding between planes"
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:
@@ -57,6 +99,7 @@ def append_chunks(c: kvq.Cache, k: np.ndarray, v: np.ndarray, chunks) -> None:
         t0 += t
     assert t0 == k.shape[1]
     torch.cuda.synchronize()
+    check_guards(c)
 
 
 def plane_np(c: kvq.Cache, name: str) -> np.ndarray:
@@ -154,11 +197,26 @@ def assert_states_equal(got: ocache.CacheState, exp: ocache.CacheState, heads=No
 
 def attention_gpu(c: kvq.Cache, q: np.ndarray, blocks_per_group: int = 0,
                   deterministic: bool = False) -> np.ndarray:
+    """One attention call with guard bytes after the output and the workspace; the cache itself
+    must come out unchanged apart from its sync plane (attention only reads it)."""
     qd = to_dev(q)
-    out = torch.empty_like(qd)
-    ws = torch.empty(c.workspace_bytes(blocks_per_group) // 4 + 4, dtype=torch.float32, device="cuda")
+    n_out = qd.numel()
+    out_full = torch.full((n_out + GUARD // 2,), float("nan"), dtype=torch.float16, device="cuda")
+    out = out_full[:n_out].view(qd.shape)
+    need = c.workspace_bytes(blocks_per_group)
+    ws_full = torch.full((need + GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+    ws = ws_full[:need]
+    so, sb = c.handle.plane_off[kvq.PLANES.index("sync")], c.handle.plane_bytes[kvq.PLANES.index("sync")]
+    before = c.buf.clone()
     c.attention(qd, out, ws, blocks_per_group, deterministic)
     torch.cuda.synchronize()
+    assert torch.isnan(out_full[n_out:]).all(), "attention wrote past its output"
+    assert bool((ws_full[need:] == CANARY).all()), "attention wrote past its workspace"
+    after = c.buf
+    assert torch.equal(before[:so], after[:so]) and torch.equal(before[so + sb:], after[so + sb:]), \
+        "attention changed the cache outside its sync plane"
+    check_guards(c)
+    del before
     return out.cpu().numpy()
 
 
