@@ -1504,15 +1504,16 @@ __device__ void fp16_block(const AttnParams& p, int64_t bh, int fb, uint16_t* vt
 constexpr int kGroupThreads = 64 * kGroupWaves;
 // per-wavefront LDS area: the block staging of process_block, or the Value
 // rows of an fp16 block (never both at once)
-constexpr int kWaveLds = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
+constexpr int kStageBytes = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4 : kBlock * kSegVStride * 2;
+// then the wavefront's last segment partial (n_rep <= 8 query heads)
+constexpr int kWaveLds = kStageBytes + 8 * kPartStride * 4;
 // workgroup LDS: the wavefronts' areas, the block counter, the record ids of
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
 constexpr int kLdsHeader = 16 + 4 * kGroupWaves;    // block counter, then each wavefront's final head
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + kLdsHeader + 4 * kMaxPagedRange;
-static_assert(kWaveLds >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
-static_assert(kWaveLds >= 8 * kPartStride * 4, "a wavefront's area holds its last segment's partial at n_rep 8");
-static_assert(kWaveLds >= 2 * kStage * 4, "a wavefront's area stages two blocks (paired and slot paths)");
-static_assert(kWaveLds >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
+static_assert(kStageBytes >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
+static_assert(kStageBytes >= 2 * kStage * 4, "the stage area holds two blocks (paired and slot paths)");
+static_assert(kStageBytes >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
 // touching heads h0..h1.
@@ -1783,7 +1784,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   if constexpr (T::kRope) rc = RopeCtx{rope_freq(p.rope_theta, li.lane), rtab};
   // the block counter starts at zero; the barrier comes before any block
   // load is issued, so no wavefront waits on another's loads
-  if (threadIdx.x == 0) *ctr = 0;
+  if (threadIdx.x == 0) ctr[0] = ctr[1] = 0;     // quantized units, fp16 blocks
   __syncthreads();
 
   // query rows of the range's first head, loaded before the blocks
@@ -1900,21 +1901,23 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     for (int d = 0; d < D - 1; ++d) fetch(buf[d], rid[d], rbh[d], rblk[d]);
   }
 
-  // fp16 block fb of head h belongs to covering workgroup g_lo(h) + fb mod
-  // count(h); the workgroup's fp16 blocks go round robin to its wavefronts
-  {
-    int k = 0;
-    for (int h = gr.h0; h <= gr.h1; ++h) {
-      const int64_t glo = covering_lo(p, h), nc = covering_count(p, h);
-      for (int fb = 0; fb < p.fp16_blocks; ++fb) {
-        if (glo + fb % nc != g) continue;
-        if ((k & (kGroupWaves - 1)) == v)
-          fp16_block<T::kRope>(p, h, fb, reinterpret_cast<uint16_t*>(stage),
-                     p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p));
-        ++k;
+  // The fp16 blocks (sinks + residual ring) of the range's heads, each into
+  // its own partial slot: fp16 block fb of head h belongs to covering
+  // workgroup g_lo(h) + fb mod count(h); fp16_of maps the workgroup's k-th to
+  // (h, fb).  They are processed at the end (see below).
+  auto fp16_of = [&](int k, int& h, int& fb) -> bool {
+    for (int hh = gr.h0; hh <= gr.h1; ++hh) {
+      const int64_t nc = covering_count(p, hh), fb0 = g - covering_lo(p, hh);
+      const int cnt = fb0 < p.fp16_blocks ? (int)((p.fp16_blocks - fb0 + nc - 1) / nc) : 0;
+      if (k < cnt) {
+        h = hh;
+        fb = (int)(fb0 + k * nc);
+        return true;
       }
+      k -= cnt;
     }
-  }
+    return false;
+  };
 
   auto wave_slot = [&](int h, int w) { return p.part_wave + ((int64_t)kGroupWaves * (g + h) + w) * slot_floats(p); };
   if (li.writer && li.qd == 0) {
@@ -1999,18 +2002,35 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       }
     }
   done:
-    // the wavefront's last segment goes to its own LDS area (free now), the
+    // the wavefront's last segment goes to its own LDS partial area, the
     // earlier ones went to global memory
+    float* part = reinterpret_cast<float*>(lds + v * kWaveLds + kStageBytes);
     if (cur >= 0) {
       if constexpr (MODE == kSlots) {
         merge_slots(ws);
-        finish_slot_segment(ws, li, stage, oscale);
+        finish_slot_segment(ws, li, part, oscale);
       } else {
         if constexpr (MODE == kPairs) merge_parity(ws);
-        finish_segment(ws, li, stage, oscale, !T::kFp8);
+        finish_segment(ws, li, part, oscale, !T::kFp8);
       }
     }
     if (li.lane == 0) fin_head[v] = cur;
+  }
+
+  // The fp16 blocks are taken from a second LDS counter by the wavefronts as
+  // they run out of quantized blocks, so this work fills the wait for the
+  // workgroup's slowest one (measured faster than doing them at the start,
+  // under the first block loads, for every workload).
+  {
+    for (;;) {
+      int idx = 0;
+      if (li.lane == 0) idx = atomicAdd(ctr + 1, 1);
+      idx = __builtin_amdgcn_readfirstlane(idx);
+      int h, fb;
+      if (!fp16_of(idx, h, fb)) break;
+      fp16_block<T::kRope>(p, h, fb, reinterpret_cast<uint16_t*>(stage),
+                           p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p));
+    }
   }
   __syncthreads();                            // every wavefront's partials written
 
@@ -2033,7 +2053,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
 #pragma unroll
       for (int w = 0; w < kGroupWaves; ++w) {
         if (fin_head[w] == h) {                   // the wavefront's last segment, in LDS
-          const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds) + hh * kPartStride;
+          const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds + kStageBytes) + hh * kPartStride;
           m[w] = sp[0];
           l[w] = sp[1];
           o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
