@@ -52,10 +52,10 @@
 
 #include "kvq_internal.h"
 
-// 1: the arrival counter is a release fetch-add and the last arriver takes an
-// agent-scope acquire fence (the language memory model's hand-over); 0: the
-// hardware ordering of coherent stores, their acknowledgement, the barrier
-// and the arrival (see finish_heads).
+// 1: the "slot written" mark is a release fetch-add and the combining
+// workgroup's polls are acquire loads (the language memory model's
+// hand-over); 0: the hardware ordering of device-coherent stores, their
+// acknowledgement, the barrier and the mark (see the end of group_main).
 #ifndef KVQ_FORMAL_ORDERING
 #define KVQ_FORMAL_ORDERING 0
 #endif
@@ -1692,45 +1692,82 @@ __device__ void reduce_heads(const AttnParams& p, const int* heads, int nh, int 
   }
 }
 
-// Called by the whole workgroup once its merged slots are written.  The workgroup counts itself in
-// on the counter of every head h0..h1 its range touches; the workgroup whose
-// arrival completes a head's count (covering_count workgroups) resets the
-// counter to 0 and combines that head.  The merged slots (the only data
-// another workgroup reads) were written with device-coherent stores, and each wavefront waits for its
-// stores to be acknowledged before the barrier that precedes the arrivals;
-// the combining workgroup reads the slots with device-coherent loads issued
-// after its arrival returned.  So the counter orders the hand-over without
-// device-scope fences.
-__device__ void finish_heads(const AttnParams& p, int64_t h0, int64_t h1, char* lds) {
-  int* last = reinterpret_cast<int*>(lds);       // the wavefront areas are free by now
-  int* nlast = last + kGroupThreads;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int64_t hb = h0; hb <= h1; hb += kGroupThreads) {
-    const int n = h1 - hb + 1 < kGroupThreads ? (int)(h1 - hb + 1) : kGroupThreads;
-    if (threadIdx.x == 0) *nlast = 0;
-    __syncthreads();
-    if ((int)threadIdx.x < n) {
-      const int64_t h = hb + threadIdx.x;
-#if KVQ_FORMAL_ORDERING
-      // release: this workgroup's slot stores happen before its arrival;
-      // acquire (last arriver): the other workgroups' slots are visible
-      const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == (int)covering_count(p, h) - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#else
-      const int prev = __hip_atomic_fetch_add(p.sync + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
-      if (prev == (int)covering_count(p, h) - 1) {
-        __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last[atomicAdd(nlast, 1)] = (int)h;       // LDS list of the heads to combine
+// Bound on the polls of a head's counter while the other covering
+// workgroups finish writing their slots.  They have all arrived, so they are
+// running and write without waiting on anything; the bound only guarantees
+// that every wavefront exits.
+constexpr int kSpinLimit = 1 << 22;
+
+// The combine of the shared heads h0 (last0) and / or h1 (last1) that this
+// workgroup's arrival completed: once every other covering workgroup's
+// "written" mark is in the counter, the counter is set back to 0 and each
+// output row is
+//   sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
+// over the covering workgroups' merged partials in covering order (the
+// exact regrouping of one softmax over all tokens), this workgroup's own
+// from LDS, the others' by device-coherent loads issued after the marks
+// were seen, kCombineBatch slots per round trip.
+constexpr int kCombineBatch = 8;
+
+__device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool last0, bool last1, int nc0, int nc1,
+                               const float* own0, const float* own1) {
+  if (threadIdx.x == 0) {
+    for (int s = 0; s < 2; ++s) {
+      const bool on = s == 0 ? last0 : last1;
+      if (!on) continue;
+      const int h = s == 0 ? h0 : h1, nc = s == 0 ? nc0 : nc1;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        const int c = __hip_atomic_load(p.sync + h, KVQ_FORMAL_ORDERING ? __ATOMIC_ACQUIRE : __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        if ((c >> 16) >= nc - 1) break;
+        __builtin_amdgcn_s_sleep(2);
       }
+      __hip_atomic_store(p.sync + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    if (*nlast > 0) reduce_heads<true>(p, last, *nlast);
-    __syncthreads();                             // before last[] is rewritten
+  }
+  __syncthreads();
+  const int per = p.nrep * (kHeadDim / 4);
+  const int n0 = last0 ? per : 0;
+  const int total = n0 + (last1 ? per : 0);
+  for (int idx = threadIdx.x; idx < total; idx += kGroupThreads) {
+    const bool first = idx < n0;
+    const int h = first ? h0 : h1, nc = first ? nc0 : nc1, r = first ? idx : idx - n0;
+    const int hq = r >> 5, c4 = r & 31;
+    const float* own = (first ? own0 : own1) + hq * kPartStride;
+    const int64_t glo = covering_lo(p, h);
+    const int me = g - (int)glo;                 // this workgroup's place among the covering ones
+    const float* base = p.part_group + (glo + h) * slot_floats(p) + hq * kPartStride;
+    float M = neg_inf(), L = 0.f;
+    float4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nc; s0 += kCombineBatch) {
+      float m[kCombineBatch], l[kCombineBatch];
+      float4 o[kCombineBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        const int s = s0 + j;
+        if (s >= nc) {
+          m[j] = neg_inf();
+          l[j] = 0.f;
+          o[j] = float4{0.f, 0.f, 0.f, 0.f};
+        } else if (s == me) {
+          m[j] = own[0];
+          l[j] = own[1];
+          o[j] = *reinterpret_cast<const float4*>(own + 4 + 4 * c4);
+        } else {
+          const float* sp = base + s * slot_floats(p);
+          m[j] = ld_dev(sp);
+          l[j] = ld_dev(sp + 1);
+          o[j] = ld_dev4(sp + 4 + 4 * c4);
+        }
+      }
+      fold4<kCombineBatch>(M, L, O, m, l, o);
+    }
+    const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
+    const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
+    *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hq) * kHeadDim + 4 * c4) =
+        uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
   }
 }
-
 
 // The workgroup's wavefronts stream the blocks of its range: each keeps
 // kDepth blocks in flight beyond the one it processes and takes its next
@@ -2034,70 +2071,134 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   }
   __syncthreads();                            // every wavefront's partials written
 
-  // merge the wavefronts' partials of each head, then the fp16 blocks of the
-  // head that this workgroup handled (fb = g - g_lo(h) + k count(h)), into
-  // the workgroup's slot.  Items are (head, query head, four channels) of
-  // all the range's heads, one per thread and pass; a pass issues the loads
-  // of the wavefront slots and of the first kFoldFp16 fp16 slots of its
-  // items before it uses any.
+  // ---- end of the call.  Heads in the middle of the range are covered by
+  // this workgroup alone; the first and the last head may be shared with
+  // neighbouring workgroups.  A shared head's counter (sync plane) takes
+  // each covering workgroup's arrival in its low 16 bits; the workgroup
+  // whose arrival completes the count combines the head, every other one
+  // writes its merged slot and then adds its "written" mark (bit 16).
+  const int nc0 = (int)covering_count(p, gr.h0), nc1 = (int)covering_count(p, gr.h1);
+  const bool sh0 = nc0 > 1, sh1 = gr.h1 != gr.h0 && nc1 > 1;
+  int prev0 = 0, prev1 = 0;
+  if (threadIdx.x == 0) {                     // arrivals first: their round trips overlap the merge
+    if (sh0) prev0 = __hip_atomic_fetch_add(p.sync + gr.h0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sh1) prev1 = __hip_atomic_fetch_add(p.sync + gr.h1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bool last0 = false, last1 = false;
+  // own merged partials of a shared head this workgroup combines, in the
+  // (free) stage areas of wavefronts 0 and 1
+  auto own_slot = [&](int s) { return reinterpret_cast<float*>(lds + s * kWaveLds); };
+
+  // Merge the wavefronts' partials of each head, then the fp16 blocks of
+  // the head that this workgroup handled (fb = g - g_lo(h) + k count(h)).
+  // Items are (head, query head, four channels) of all the range's heads,
+  // one per thread and pass; a pass issues its loads (the wavefront slots,
+  // the first kFoldFp16 fp16 slots) before it uses any.  The result goes to
+  // the output (a head of this workgroup alone), to LDS (a shared head this
+  // workgroup combines) or to the workgroup's slot (device-coherent stores).
   {
     constexpr int kFoldFp16 = 4;
     const int nf = p.fp16_blocks;
     const int per = p.nrep * (kHeadDim / 4);
     const int total = (gr.h1 - gr.h0 + 1) * per;
-    for (int idx = threadIdx.x; idx < total; idx += kGroupThreads) {
-      const int h = gr.h0 + idx / per, r = idx % per, hh = r >> 5, c4 = r & 31;
-      const int64_t nc = covering_count(p, h), fb0 = g - covering_lo(p, h);
-      float m[kGroupWaves], l[kGroupWaves], fm[kFoldFp16], fl[kFoldFp16];
-      float4 o[kGroupWaves], fo[kFoldFp16];
-#pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) {
-        if (fin_head[w] == h) {                   // the wavefront's last segment, in LDS
-          const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds + kStageBytes) + hh * kPartStride;
-          m[w] = sp[0];
-          l[w] = sp[1];
-          o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
-        } else {
-          const float* sp = wave_slot(h, w) + hh * kPartStride;
-          m[w] = sp[0];
-          l[w] = sp[1];
-          o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
-        }
-      }
-      auto load_fp16 = [&](int64_t first) {
-#pragma unroll
-        for (int j = 0; j < kFoldFp16; ++j) {
-          const int64_t fb = first + j * nc;
-          if (fb < nf) {
-            const float* sp = p.part_fp16 + ((int64_t)h * nf + fb) * slot_floats(p) + hh * kPartStride;
-            fm[j] = sp[0];
-            fl[j] = sp[1];
-            fo[j] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
-          } else {
-            fm[j] = neg_inf();
-            fl[j] = 0.f;
-            fo[j] = float4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-      };
-      load_fp16(fb0);
+    for (int base = 0; base < total; base += kGroupThreads) {
+      const int idx = base + (int)threadIdx.x;
+      const int h = gr.h0 + (idx < total ? idx / per : 0), r = idx % per, hh = r >> 5, c4 = r & 31;
       float M = neg_inf(), L = 0.f;
       float4 O = {0.f, 0.f, 0.f, 0.f};
-      fold4<kGroupWaves>(M, L, O, m, l, o);
-      fold4<kFoldFp16>(M, L, O, fm, fl, fo);
-      for (int64_t first = fb0 + kFoldFp16 * nc; first < nf; first += kFoldFp16 * nc) {
-        load_fp16(first);                         // more than kFoldFp16 fp16 blocks here
+      if (idx < total) {
+        const int64_t nc = covering_count(p, h), fb0 = g - covering_lo(p, h);
+        float m[kGroupWaves], l[kGroupWaves], fm[kFoldFp16], fl[kFoldFp16];
+        float4 o[kGroupWaves], fo[kFoldFp16];
+#pragma unroll
+        for (int w = 0; w < kGroupWaves; ++w) {
+          if (fin_head[w] == h) {                 // the wavefront's last segment, in LDS
+            const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds + kStageBytes) + hh * kPartStride;
+            m[w] = sp[0];
+            l[w] = sp[1];
+            o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+          } else {
+            const float* sp = wave_slot(h, w) + hh * kPartStride;
+            m[w] = sp[0];
+            l[w] = sp[1];
+            o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+          }
+        }
+        auto load_fp16 = [&](int64_t first) {
+#pragma unroll
+          for (int j = 0; j < kFoldFp16; ++j) {
+            const int64_t fb = first + j * nc;
+            if (fb < nf) {
+              const float* sp = p.part_fp16 + ((int64_t)h * nf + fb) * slot_floats(p) + hh * kPartStride;
+              fm[j] = sp[0];
+              fl[j] = sp[1];
+              fo[j] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+            } else {
+              fm[j] = neg_inf();
+              fl[j] = 0.f;
+              fo[j] = float4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        };
+        load_fp16(fb0);
+        fold4<kGroupWaves>(M, L, O, m, l, o);
         fold4<kFoldFp16>(M, L, O, fm, fl, fo);
+        for (int64_t first = fb0 + kFoldFp16 * nc; first < nf; first += kFoldFp16 * nc) {
+          load_fp16(first);                       // more than kFoldFp16 fp16 blocks here
+          fold4<kFoldFp16>(M, L, O, fm, fl, fo);
+        }
       }
-      float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
-      if (c4 == 0) {
-        st_dev(dst, M);
-        st_dev(dst + 1, L);
+      if (base == 0) {                            // which shared heads this workgroup combines
+        int* lf = ctr + 2;                        // the block counters are done with
+        if (threadIdx.x == 0) {
+          lf[0] = sh0 && (prev0 & 0xFFFF) == nc0 - 1;
+          lf[1] = sh1 && (prev1 & 0xFFFF) == nc1 - 1;
+        }
+        __syncthreads();
+        last0 = lf[0] != 0;
+        last1 = lf[1] != 0;
       }
-      st_dev4(dst + 4 + 4 * c4, O);
+      if (idx < total) {
+        const bool shared = (h == gr.h0 && sh0) || (h == gr.h1 && sh1);
+        if (!shared) {                            // this workgroup's head alone: the output row
+          const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
+          const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
+          *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hh) * kHeadDim + 4 * c4) =
+              uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        } else {
+          const bool mine = h == gr.h0 ? last0 : last1;
+          float* dst = mine ? own_slot(h == gr.h0 ? 0 : 1) + hh * kPartStride
+                            : p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
+          if (mine) {
+            if (c4 == 0) {
+              dst[0] = M;
+              dst[1] = L;
+            }
+            *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = O;
+          } else {
+            if (c4 == 0) {
+              st_dev(dst, M);
+              st_dev(dst + 1, L);
+            }
+            st_dev4(dst + 4 + 4 * c4, O);
+          }
+        }
+      }
     }
   }
-  finish_heads(p, gr.h0, gr.h1, lds);
+  // Shared heads combined elsewhere: the merged slot is written (each store
+  // acknowledged), then the "written" mark.  The stores are device-coherent
+  // (write-through past the compute unit's caches) and acknowledged before
+  // the mark is added, so a combining workgroup that has seen the mark and
+  // then loads the slot device-coherently reads these values.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    constexpr int kMarkOrder = KVQ_FORMAL_ORDERING ? __ATOMIC_RELEASE : __ATOMIC_RELAXED;
+    if (sh0 && !last0) __hip_atomic_fetch_add(p.sync + gr.h0, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
+    if (sh1 && !last1) __hip_atomic_fetch_add(p.sync + gr.h1, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (last0 || last1) combine_shared(p, g, gr.h0, gr.h1, last0, last1, nc0, nc1, own_slot(0), own_slot(1));
 }
 
 

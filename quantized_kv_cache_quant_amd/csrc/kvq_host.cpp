@@ -133,6 +133,9 @@ static int32_t prepare_attention(const kvq_cache* c, int64_t n_tokens, const voi
   if ((uint64_t)a.slots * sb > ws_bytes) return KVQ_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  // a head's arrival counter holds up to 65535 arrivals and 32767 "written"
+  // marks: at most 32767 workgroups may cover one head
+  if (nblk > 0 && (nblk + a.group_blocks - 1) / a.group_blocks + 1 > 32767) return KVQ_ERR_UNSUPPORTED;
 
   char* base = static_cast<char*>(c->base);
   auto plane = [&](int i) { return base + c->plane_off[i]; };
