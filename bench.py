@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--read-sweep", action="store_true",
                     help="only time the plain streaming-read kernel over a range of sizes and print that")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="no GPU work: write profiles/attn_counters.json from the rocprofv3 --pmc runs "
+                         "DIR/<key>_FETCH_SIZE and DIR/<key>_WRITE_SIZE (see COUNTER_RUNS)")
     return ap.parse_args()
 
 
@@ -337,23 +340,97 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     return res
 
 
-def counter_traffic(fmt):
-    """Per-call HBM bytes of the attention kernels from profiles/attn_counters.json, or None
-    when the file is absent, has no entry for fmt, or was taken on another attention source."""
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "attn_counters.json")
+ATTN_SRC = os.path.join(ROOT, "quantized_kv_cache_quant_amd", "csrc", "kvq_attn.hip")
+# rocprofv3 --pmc runs read by --ingest-counters: run key -> (bench.py arguments, {entry: kernel
+# name filter}); an entry averages the run's attention dispatches whose name holds the filter
+COUNTER_RUNS = {
+    "llama3_8b": ("--workload llama3_8b --no-variants --no-cpu-baseline --steps 8 --warmup 2",
+                  {"int8": "attn_kernel<0", "fp8": "attn_kernel<3"}),
+    "kivi2_int2": ("--workload llama3_8b_kivi2 --no-variants --no-cpu-baseline --steps 8 --warmup 2",
+                   {"kivi2_int2": "attn_kernel<"}),
+    "llama3_70b_int4": ("--workload llama3_70b --no-variants --no-cpu-baseline --steps 8 --warmup 2",
+                        {"llama3_70b_int4": "attn_kernel<"}),
+    "long_ctx_mixed": ("--workload long_ctx --no-variants --no-cpu-baseline --steps 8 --warmup 2",
+                       {"long_ctx_mixed": "attn_kernel<"}),
+}
+
+
+def attn_digest() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attn_counters.json")
-    src = os.path.join(ROOT, "quantized_kv_cache_quant_amd", "csrc", "kvq_attn.hip")
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+
+
+def counter_traffic(key):
+    """Per-call HBM bytes of the attention kernel from profiles/attn_counters.json (entry key:
+    a format of the 8B headline or a workload key), or None when the file is absent, has no
+    such entry, or was taken on another attention source."""
     try:
-        rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        rec = json.load(open(COUNTERS_JSON))
+        digest = attn_digest()
     except (OSError, ValueError):
         return None
-    if rec.get("kvq_attn_hip_sha256") != digest or fmt not in rec.get("per_call", {}):
+    if rec.get("kvq_attn_hip_sha256") != digest or key not in rec.get("per_call", {}):
         return None
-    c = rec["per_call"][fmt]
+    c = rec["per_call"][key]
     cal = rec["calibration"]
-    kib = 1024.0
-    return (c["fetch_kib"] * cal["fetch_factor"] + c["write_kib"] * cal["write_factor"]) * kib
+    return round((c["fetch_kib"] * cal["fetch_factor"] + c["write_kib"] * cal["write_factor"]) * 1024.0)
+
+
+def read_counter_csv(path):
+    """{dispatch id: (kernel name, {counter: value})} of a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            d = out.setdefault(int(row["Dispatch_Id"]), (row["Kernel_Name"], {}))
+            d[1][row["Counter_Name"]] = d[1].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def ingest_counters(root) -> dict:
+    """Averages the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of every run in
+    COUNTER_RUNS over its attention dispatches, calibrates both against the run's largest
+    plain copy (the 2 GiB device-to-device copy of copy_bandwidth: bytes read, bytes written),
+    and writes the record, tied to the attention source's sha256, to profiles/attn_counters.json."""
+    import glob
+    copy_bytes = float(2 << 30)
+    per_call, cal = {}, {"fetch": [], "write": []}
+    for key, (_, entries) in COUNTER_RUNS.items():
+        vals = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            files = glob.glob(os.path.join(root, f"{key}_{counter}", "**", "*counter_collection.csv"),
+                              recursive=True)
+            if len(files) != 1:
+                raise SystemExit(f"--ingest-counters: expected one counter file for {key} {counter}, "
+                                 f"found {files}")
+            rows = read_counter_csv(files[0])
+            copies = [c.get(counter, 0.0) for name, c in rows.values() if "copyBuffer" in name]
+            if not copies:
+                raise SystemExit(f"--ingest-counters: no copyBuffer dispatch in {files[0]}")
+            cal["fetch" if counter == "FETCH_SIZE" else "write"].append(copy_bytes / (max(copies) * 1024.0))
+            for entry, pat in entries.items():
+                xs = [c[counter] for name, c in rows.values() if pat in name and counter in c]
+                if not xs:
+                    raise SystemExit(f"--ingest-counters: no '{pat}' dispatch in {files[0]}")
+                vals.setdefault(entry, {})[counter] = (sum(xs) / len(xs), len(xs))
+        for entry, v in vals.items():
+            per_call[entry] = {"fetch_kib": round(v["FETCH_SIZE"][0], 1), "write_kib": round(v["WRITE_SIZE"][0], 1),
+                               "dispatches": v["FETCH_SIZE"][1]}
+    # the copy reads and writes 2 GiB: FETCH_SIZE reads half of that on this part (factor 2)
+    factors = {k: round(sum(v) / len(v), 3) for k, v in cal.items()}
+    rec = {"kvq_attn_hip_sha256": attn_digest(),
+           "commands": {k: f"rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> --output-format csv -d "
+                           f"{root}/{k}_<counter> -o run -- python3 -u bench.py {a}"
+                        for k, (a, _) in COUNTER_RUNS.items()},
+           "calibration": {"fetch_factor": factors["fetch"], "write_factor": factors["write"],
+                           "source": "the largest __amd_rocclr_copyBuffer dispatch of each run: 2 GiB read, "
+                                     "2 GiB written"},
+           "per_call": per_call}
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def cpu_baseline(w, fmt, seconds):
@@ -523,8 +600,8 @@ def layer_formats(w, var, nl):
     return [var] * nl
 
 
-def summary(w, r) -> dict:
-    """The per-workload entry of the JSON line."""
+def summary(w, r, traffic=None) -> dict:
+    """The per-workload entry of the JSON line (traffic: counter HBM bytes per call, or None)."""
     return {"workload": f"{w.name}: {w.notes}", "batch": w.batch, "seq_len": w.seq_len,
             "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "residual_tokens": w.residual_tokens,
             "sink_tokens": w.sink_tokens, "layers": r["layers"], "formats": r["formats"],
@@ -532,11 +609,16 @@ def summary(w, r) -> dict:
             "attn_gbps": round(r["attn_gbps"], 1), "frac_of_hbm_peak": round(r["attn_gbps"] / HBM_PEAK_GBPS, 4),
             "attn_by_format": r["attn_by_format"], "ms_per_step": round(r["ms_per_step"], 4),
             "step_us_per_layer": round(r["step_us_per_layer"], 2), "tokens_per_s": round(r["tokens_per_s"], 1),
-            "effective_gbps": round(r["effective_gbps"], 1), "prefill_quantize": r["prefill_quantize"]}
+            "effective_gbps": round(r["effective_gbps"], 1), "prefill_quantize": r["prefill_quantize"],
+            "traffic": traffic}
 
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        rec = ingest_counters(args.ingest_counters)
+        print(json.dumps(rec["per_call"]), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py: measures one GPU; the decode-attention path shards by KV head or by token "
@@ -570,7 +652,7 @@ def main():
         for key, wname, fl in OTHER_WORKLOADS:
             wo = synth.WORKLOADS[wname]
             r = run_format(torch, kvq, synth, accounting, wo, layer_formats(wo, fl[0], wo.layers), args)
-            others[key] = summary(wo, r)
+            others[key] = summary(wo, r, counter_traffic(key))
     vres = None
     if not args.no_variants and name == "llama3_8b" and not args.formats:
         vres = variant_sweep(torch, kvq, synth, accounting, w, VARIANTS, args)
@@ -617,6 +699,7 @@ def main():
     for var in variants[1:]:
         r = results[var]
         line[var] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+        line[var]["traffic"] = counter_traffic(var)
     if others:
         line["workloads"] = others
     if tiny:

@@ -75,9 +75,14 @@
  *            fp16 (s, m) pairs (half the bytes).
  *   K ring, V ring  [B][Hkv][R+32][D] fp16
  *   K sink, V sink  [B][Hkv][S][D] fp16
- *   sync     [B][Hkv] int32 arrival counters of the attention call (the
- *            workgroups that cover a head count themselves in; the last one
- *            combines the head's partials and sets the counter back to 0).
+ *   sync     [B][Hkv] int32 counters of the attention call.  For a head
+ *            whose blocks are split over several workgroups, each of them
+ *            adds 1 on arrival (low 16 bits) and, unless its arrival
+ *            completed the count, 1 << 16 once its partial is written; the
+ *            one that completed the count waits for the others' marks,
+ *            combines the head's partials and sets the counter back to 0.
+ *            At most 32767 workgroups may share a head (checked by the
+ *            host: larger splits return KVQ_ERR_UNSUPPORTED).
  *            Set to 0 by the cache's first kv_quant_append and 0 again
  *            after every attention call; no other call touches it.
  * Each plane starts on a 256-byte boundary.

@@ -19,13 +19,19 @@
 //    an online softmax for all n_rep query heads of that KV head (GQA: every
 //    KV byte is read once per step) and writes one partial (max, sum,
 //    unnormalised output);
+//  * INT4 / INT2 take two blocks per step: at n_rep <= 4 the two blocks
+//    share the matrix columns (one block per column parity), at n_rep 8 they
+//    take separate products into one accumulator (column slots);
 //  * the fp16 segment (sinks + residual ring) of every head is cut into
-//    32-token blocks, spread one per wavefront over the grid and handled
-//    while the wavefront's first quantized blocks load;
-//  * at the end a workgroup merges its wavefronts' partials per head and
-//    counts itself in on each head's arrival counter (sync plane of the
-//    cache); the last workgroup to arrive on a head combines the head's
-//    workgroup and fp16 partials in a fixed order and writes its output.
+//    32-token blocks, dealt to the workgroups that cover the head and taken
+//    from a second LDS counter by wavefronts that have run out of quantized
+//    blocks, so they fill the wait for the workgroup's slowest wavefront;
+//  * at the end a workgroup merges, per head, its wavefronts' partials
+//    (the last one from LDS) and its fp16 partials.  A head that it covers
+//    alone goes straight to the output; a head shared with neighbouring
+//    workgroups is counted on the head's counter (sync plane of the cache):
+//    the workgroup whose arrival completes the count combines the head in
+//    covering order once the others have written their merged slots.
 //
 // Per 32-token block a wavefront runs both products on the matrix cores with
 // v_mfma_f32_16x16x32_f16 (fp32 accumulate):
@@ -1775,9 +1781,9 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
 // faster processes more blocks and all finish together (in deterministic
 // mode wavefront w takes blocks w, w + 8, w + 16, ... instead).  Every
 // wavefront keeps one online softmax per head it meets and writes one partial
-// slot per head of the range.  Before its first block it handles its share of
-// the workgroup's fp16 blocks, while its first blocks load.  At the end the
-// workgroup merges its wavefronts' partials into one slot per head.
+// per head of the range (the last one into its LDS area).  Then the
+// wavefronts take the workgroup's fp16 blocks from a second LDS counter, and
+// the workgroup merges, per head, its wavefronts' and fp16 partials.
 // MODE: kSingle (process_block), kPairs (process_pair; INT4 / INT2 at
 // n_rep <= 4) or kSlots (process_slots; INT4 / INT2 at n_rep 8); the last
 // two take blocks two at a time, with a ring of kPairRing blocks.

@@ -119,9 +119,14 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 //   part_group  slot g + bh                      workgroup g, head bh (its wavefronts merged)
 // Workgroup g's range touches heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk),
 // so g + bh never collides between workgroups.  Each workgroup folds its
-// wavefront slots and the fp16 slots it produced into its merged slot; the
-// last workgroup to finish a head (arrival counter in the cache's sync plane)
-// combines the head's merged slots and writes the output rows.
+// wavefront partials and the fp16 slots it produced per head.  A head the
+// workgroup covers alone is written to the output.  A head shared with other
+// workgroups is counted on its sync counter: arrivals in the low 16 bits,
+// "slot written" marks in bit 16 and up.  The workgroup whose arrival
+// completes the count combines the head (its own merged partial from LDS,
+// the others' part_group slots once all their marks are in) and sets the
+// counter back to 0; every other covering workgroup writes its part_group
+// slot and then adds its mark.
 // With no quantized block (nblk == 0) workgroup g takes the fp16 blocks of head g.
 struct AttnParams {
   const uint8_t* k_codes;
@@ -136,7 +141,7 @@ struct AttnParams {
   const uint16_t* v_sink;
   const uint16_t* q;      // fp16 [B][Hq][D]
   uint16_t* out;          // fp16 [B][Hq][D]
-  int32_t* sync;          // [B][Hkv] arrival counters (0 between calls)
+  int32_t* sync;          // [B][Hkv] counters of shared heads (0 between calls)
   const uint16_t* new_k;  // fused append: fp16 [B][1][Hkv][D] of the newest token, else null;
   const uint16_t* new_v;  // it is read from here and copied to its ring slot
   float* part_fp16;
