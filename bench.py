@@ -38,10 +38,11 @@ launches on (torch's current stream):
   * prefill: each layer cache's kv_quant_append of the prompt between its own
     event pair -> prefill_quantize (fp16 K/V input GB/s; the first layer's
     call, which pays one-off costs, is left out);
-  * attention sweep: every layer's kv_decode_attention call, each bracketed
-    by its own event pair -> the roofline entry (algorithmic bytes per call /
-    mean call time).  The events sit outside the step loop because an event
-    record between launches adds a few microseconds of idle time per call.
+  * attention sweep: the kv_decode_attention calls of every layer of one
+    format, several rounds back to back between one event pair -> the
+    roofline entry (algorithmic bytes per call / mean call time, launch gaps
+    included, so the mean is at least the kernel's own duration).  No event
+    sits between two calls: each record adds idle time on the stream.
 read_gbps_measured is the best rate of the library's plain streaming-read
 kernel (kvq_read_probe) over 4 GiB; attn_frac_of_measured_read is the
 attention call's rate (roofline.achieved) over it.
@@ -182,8 +183,25 @@ def call_bytes(accounting, w, spec, n):
                                       w.sink_tokens, w.residual_tokens, meta_fp16=m16, outliers=out)
 
 
+def back_to_back_us(torch, caches, call, rounds) -> float:
+    """Mean µs per call of `rounds` passes of call(c) over the caches, launched back to back
+    between one event pair on the launch stream (the launch gaps count; no event record sits
+    between two calls, since each record adds idle time on the stream)."""
+    for c in caches:                            # one untimed pass
+        call(c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for c in caches:
+            call(c)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (rounds * len(caches))
+
+
 def variant_sweep(torch, kvq, synth, accounting, w, specs, args, layers=8, rounds=8):
-    """Attention-only timing of each variant: `layers` caches, each call between its own events."""
+    """Attention-only timing of each variant: `layers` caches, calls back to back."""
     log(f"variant sweep: generating synthetic prefill for {', '.join(specs)}")
     kp, vp = synth.prefill(w)
     kd = torch.from_numpy(kp).cuda()
@@ -201,18 +219,7 @@ def variant_sweep(torch, kvq, synth, accounting, w, specs, args, layers=8, round
             caches.append(c)
         ws = torch.empty(caches[0].workspace_bytes(args.blocks_per_group) // 4 + 4, dtype=torch.float32,
                          device="cuda")
-        for c in caches:
-            c.attention(q, out, ws, args.blocks_per_group)
-        torch.cuda.synchronize()
-        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in caches]
-               for _ in range(rounds)]
-        for r in range(rounds):
-            for li, c in enumerate(caches):
-                evs[r][li][0].record()
-                c.attention(q, out, ws, args.blocks_per_group)
-                evs[r][li][1].record()
-        torch.cuda.synchronize()
-        us = 1e3 * float(np.mean([e0.elapsed_time(e1) for row in evs for (e0, e1) in row]))
+        us = back_to_back_us(torch, caches, lambda c: c.attention(q, out, ws, args.blocks_per_group), rounds)
         nb = call_bytes(accounting, w, spec, w.seq_len)
         res[spec] = {"attn_call_us": round(us, 2), "bytes_per_attn_call": nb,
                      "attn_gbps": round(nb / (us * 1e-6) / 1e9, 1),
@@ -286,22 +293,14 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
 
-    # attention sweep: each call between its own pair of events
+    # attention sweep: the layers of each format, kv_decode_attention calls back to back
     rounds = max(2, args.steps // 8)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in caches]
-           for _ in range(rounds)]
-    for r in range(rounds):
-        for li, c in enumerate(caches):
-            evs[r][li][0].record()
-            c.attention(q, out, ws, args.blocks_per_group, args.deterministic)
-            evs[r][li][1].record()
-    torch.cuda.synchronize()
-    attn_ms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
     n_final = n0 + total_steps
     by_fmt = {}                                 # per layer format: mean call, bytes, fraction of peak
     for fmt in sorted(set(fmt_list)):
-        ms_f = [e0.elapsed_time(e1) for row in evs for li, (e0, e1) in enumerate(row) if fmt_list[li] == fmt]
-        us_f = 1e3 * float(np.mean(ms_f))
+        cf = [c for li, c in enumerate(caches) if fmt_list[li] == fmt]
+        us_f = back_to_back_us(torch, cf, lambda c: c.attention(q, out, ws, args.blocks_per_group,
+                                                                args.deterministic), rounds)
         nb_f = call_bytes(accounting, w, fmt, n_final)
         by_fmt[fmt] = {"layers": fmt_list.count(fmt), "attn_call_us": round(us_f, 2), "bytes_per_attn_call": nb_f,
                        "attn_gbps": round(nb_f / (us_f * 1e-6) / 1e9, 1),
@@ -313,7 +312,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         for fmt in fmt_list:
             nbytes += call_bytes(accounting, w, fmt, n)
     ms_step = total_ms / args.steps
-    attn_avg_ms = float(np.mean(attn_ms))
+    attn_avg_ms = sum(by_fmt[f]["attn_call_us"] for f in fmt_list) / layers / 1e3   # mean over the layers
     res = {
         "formats": sorted(set(fmt_list)),
         "layers": layers,
@@ -324,7 +323,7 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         "attn_gbps": sweep_bytes / (attn_avg_ms * 1e-3) / 1e9,
         "step_us_per_layer": ms_step * 1e3 / layers,
         "bytes_per_attn_call": sweep_bytes,
-        "attn_calls_timed": len(attn_ms),
+        "attn_calls_timed": rounds * layers,
         "attn_by_format": by_fmt,
         "prefill_quantize": {"us_per_layer": round(float(np.mean(pre_us)), 1),
                              "input_gbps": round(pre_in / (float(np.mean(pre_us)) * 1e-6) / 1e9, 1),
