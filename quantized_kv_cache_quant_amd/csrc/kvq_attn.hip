@@ -1515,7 +1515,7 @@ constexpr int kStageBytes = (kStage * 4 > kBlock * kSegVStride * 2) ? kStage * 4
 constexpr int kWaveLds = kStageBytes + 8 * kPartStride * 4;
 // workgroup LDS: the wavefronts' areas, the block counter, the record ids of
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
-constexpr int kLdsHeader = 16 + 4 * kGroupWaves;    // block counter, then each wavefront's final head
+constexpr int kLdsHeader = 32 + 4 * kGroupWaves;    // counters, each wavefront's final head, covering info
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + kLdsHeader + 4 * kMaxPagedRange;
 static_assert(kStageBytes >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
 static_assert(kStageBytes >= 2 * kStage * 4, "the stage area holds two blocks (paired and slot paths)");
@@ -1528,22 +1528,52 @@ struct GroupRange {
   int len, h0, h1;
 };
 
+// The flattened blocks are cut into stretches of range_len blocks, each
+// stretch into range_parts consecutive ranges: part p of a stretch starts at
+// floor(p L / k) + (p odd ? d : 0) (L = range_len, k = range_parts, d =
+// group_skew), so odd-numbered workgroups take d fewer blocks than their
+// even neighbours.  Following heads: L = nblk, k ranges per head; equal
+// ranges of R blocks across head boundaries: L = 2 R, k = 2.  The host keeps
+// k L < 2^31, so every quotient below is a 32-bit multiply-shift.
+// range_start(g) is the first block of workgroup g's range and range_of(x)
+// the workgroup whose range holds flattened block x.
+__device__ __forceinline__ uint32_t div_len(const AttnParams& p, uint32_t x) {     // x / L, x < 2^31
+  return (uint32_t)(((uint64_t)x * p.len_magic) >> p.len_shift);
+}
+__device__ __forceinline__ uint32_t div_parts(const AttnParams& p, uint32_t x) {   // x / k, x < 2^31
+  return (uint32_t)(((uint64_t)x * p.parts_magic) >> p.parts_shift);
+}
+__device__ __forceinline__ int64_t part_start(const AttnParams& p, uint32_t part) {
+  return (int64_t)div_parts(p, part * (uint32_t)p.range_len) + ((part & 1) ? p.group_skew : 0);
+}
+__device__ __forceinline__ int64_t range_start(const AttnParams& p, int64_t g) {
+  const uint32_t s = div_parts(p, (uint32_t)g);
+  return (int64_t)s * p.range_len + part_start(p, (uint32_t)g - s * (uint32_t)p.range_parts);
+}
+__device__ __forceinline__ int64_t range_of(const AttnParams& p, int64_t x) {
+  const uint32_t s = div_len(p, (uint32_t)x), r = (uint32_t)x - s * (uint32_t)p.range_len;
+  uint32_t part = div_len(p, (r + 1) * (uint32_t)p.range_parts - 1);   // last part starting at or before r,
+  if (part_start(p, part) > r) --part;                                 // skew aside (an odd part starts d later)
+  return (int64_t)s * p.range_parts + part;
+}
+
 __device__ __forceinline__ GroupRange group_range(const AttnParams& p, int g) {
   GroupRange r;
   const int64_t total = (int64_t)p.bh_count * p.nblk;
-  r.jb = (int64_t)g * p.group_blocks;
-  r.len = r.jb < total ? (int)(total - r.jb < p.group_blocks ? total - r.jb : p.group_blocks) : 0;
-  r.h0 = r.len ? (int)(r.jb / p.nblk) : 0;
-  r.h1 = r.len ? (int)((r.jb + r.len - 1) / p.nblk) : -1;
+  r.jb = range_start(p, g);
+  const int64_t e = range_start(p, g + 1);
+  r.len = r.jb < total ? (int)((e < total ? e : total) - r.jb) : 0;
+  r.h0 = r.len ? (int)((uint32_t)r.jb / (uint32_t)p.nblk) : 0;             // jb < 2^31
+  r.h1 = r.len ? (int)((uint32_t)(r.jb + r.len - 1) / (uint32_t)p.nblk) : -1;
   return r;
 }
 
 // Workgroups whose range touches head h: g_lo .. g_lo + count - 1.
 __device__ __forceinline__ int64_t covering_lo(const AttnParams& p, int64_t h) {
-  return h * p.nblk / p.group_blocks;
+  return range_of(p, h * p.nblk);
 }
 __device__ __forceinline__ int64_t covering_count(const AttnParams& p, int64_t h) {
-  return ((h + 1) * p.nblk - 1) / p.group_blocks - covering_lo(p, h) + 1;
+  return range_of(p, (h + 1) * p.nblk - 1) - covering_lo(p, h) + 1;
 }
 
 __device__ __forceinline__ int64_t slot_floats(const AttnParams& p) { return (int64_t)p.nrep * kPartStride; }
@@ -1620,59 +1650,42 @@ __device__ __forceinline__ float4 ld_dev4(const float* p) {
                 __builtin_bit_cast(float, (uint32_t)b), __builtin_bit_cast(float, (uint32_t)(b >> 32))};
 }
 
-constexpr int kReduceItems = 4;           // items per thread and pass of the combine
+constexpr int kReduceItems = 4;           // items per thread and pass of reduce_fp16_head
 constexpr int kReduceBatch = 4;           // slots per item whose loads are issued together
 
-// out[b][h] of all n_rep query heads of (sequence, KV head) h:
+// out[b][h] of all n_rep query heads of (sequence, KV head) h, from the
+// head's fp16-block slots (written by this workgroup before a barrier):
 //   sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s
 // (the exact regrouping of one softmax over all tokens), over the slots in
-// a fixed order, for every head heads[0 .. nh-1] (heads == nullptr: the
-// single head `single`).  SHARED: the head's merged workgroup slots, written
-// by other workgroups (device-coherent loads); otherwise its fp16 slots,
-// written by this workgroup before a barrier.  Items are (head, query head,
-// four channels), kReduceItems per thread and pass; the loads of
-// kReduceBatch slots of all of a thread's items are issued before any is
-// used (one memory round trip per batch).
-template <bool SHARED>
-__device__ void reduce_heads(const AttnParams& p, const int* heads, int nh, int single = 0) {
-  const int per = p.nrep * (kHeadDim / 4);
-  const int total = nh * per;
-  int max_ns = 0;
-  for (int i = 0; i < nh; ++i) {
-    const int ns = SHARED ? (int)covering_count(p, heads ? heads[i] : single) : p.fp16_blocks;
-    max_ns = ns > max_ns ? ns : max_ns;
-  }
+// order.  Items are (query head, four channels), kReduceItems per thread and
+// pass; the loads of kReduceBatch slots of all of a thread's items are issued
+// before any is used (one memory round trip per batch).
+__device__ void reduce_fp16_head(const AttnParams& p, int64_t h) {
+  const int total = p.nrep * (kHeadDim / 4);
+  const int ns = p.fp16_blocks;
+  const float* sb = p.part_fp16 + h * p.fp16_blocks * slot_floats(p);
   for (int base = 0; base < total; base += kReduceItems * kGroupThreads) {
     float M[kReduceItems], L[kReduceItems];
     float4 O[kReduceItems];
-    int ns[kReduceItems], off[kReduceItems];
-    const float* sb[kReduceItems];
 #pragma unroll
     for (int k = 0; k < kReduceItems; ++k) {
       M[k] = neg_inf();
       L[k] = 0.f;
       O[k] = float4{0.f, 0.f, 0.f, 0.f};
-      const int idx = base + (int)threadIdx.x + k * kGroupThreads;
-      const int hi = idx < total ? idx / per : 0, r = idx % per;
-      const int64_t h = heads ? heads[hi] : single;
-      off[k] = (r >> 5) * kPartStride;                 // query head r / 32
-      ns[k] = idx < total ? (SHARED ? (int)covering_count(p, h) : p.fp16_blocks) : 0;
-      sb[k] = SHARED ? p.part_group + (covering_lo(p, h) + h) * slot_floats(p)
-                     : p.part_fp16 + h * p.fp16_blocks * slot_floats(p);
     }
-    for (int s0 = 0; s0 < max_ns; s0 += kReduceBatch) {
+    for (int s0 = 0; s0 < ns; s0 += kReduceBatch) {
       float m[kReduceItems][kReduceBatch], l[kReduceItems][kReduceBatch];
       float4 o[kReduceItems][kReduceBatch];
 #pragma unroll
       for (int k = 0; k < kReduceItems; ++k) {
-        const int c4 = ((base + (int)threadIdx.x + k * kGroupThreads) % per) & 31;
+        const int r = base + (int)threadIdx.x + k * kGroupThreads;
 #pragma unroll
         for (int j = 0; j < kReduceBatch; ++j) {
-          if (s0 + j < ns[k]) {
-            const float* sp = sb[k] + (s0 + j) * slot_floats(p) + off[k];
-            m[k][j] = SHARED ? ld_dev(sp) : sp[0];
-            l[k][j] = SHARED ? ld_dev(sp + 1) : sp[1];
-            o[k][j] = SHARED ? ld_dev4(sp + 4 + 4 * c4) : *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+          if (r < total && s0 + j < ns) {
+            const float* sp = sb + (s0 + j) * slot_floats(p) + (r >> 5) * kPartStride;
+            m[k][j] = sp[0];
+            l[k][j] = sp[1];
+            o[k][j] = *reinterpret_cast<const float4*>(sp + 4 + 4 * (r & 31));
           } else {
             m[k][j] = neg_inf();
             l[k][j] = 0.f;
@@ -1685,10 +1698,8 @@ __device__ void reduce_heads(const AttnParams& p, const int* heads, int nh, int 
     }
 #pragma unroll
     for (int k = 0; k < kReduceItems; ++k) {
-      const int idx = base + (int)threadIdx.x + k * kGroupThreads;
-      if (idx < total) {
-        const int r = idx % per;
-        const int64_t h = heads ? heads[idx / per] : single;
+      const int r = base + (int)threadIdx.x + k * kGroupThreads;
+      if (r < total) {
         const f16x2 lo = {(_Float16)(O[k].x / L[k]), (_Float16)(O[k].y / L[k])};
         const f16x2 hi = {(_Float16)(O[k].z / L[k]), (_Float16)(O[k].w / L[k])};
         *reinterpret_cast<uint2*>(p.out + (h * p.nrep + (r >> 5)) * kHeadDim + 4 * (r & 31)) =
@@ -1715,8 +1726,8 @@ constexpr int kSpinLimit = 1 << 22;
 // were seen, kCombineBatch slots per round trip.
 constexpr int kCombineBatch = 8;
 
-__device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool last0, bool last1, int nc0, int nc1,
-                               const float* own0, const float* own1) {
+__device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool last0, bool last1, int lo0, int lo1,
+                               int nc0, int nc1, const float* own0, const float* own1) {
   if (threadIdx.x == 0) {
     for (int s = 0; s < 2; ++s) {
       const bool on = s == 0 ? last0 : last1;
@@ -1740,7 +1751,7 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
     const int h = first ? h0 : h1, nc = first ? nc0 : nc1, r = first ? idx : idx - n0;
     const int hq = r >> 5, c4 = r & 31;
     const float* own = (first ? own0 : own1) + hq * kPartStride;
-    const int64_t glo = covering_lo(p, h);
+    const int64_t glo = first ? lo0 : lo1;
     const int me = g - (int)glo;                 // this workgroup's place among the covering ones
     const float* base = p.part_group + (glo + h) * slot_floats(p) + hq * kPartStride;
     float M = neg_inf(), L = 0.f;
@@ -1805,6 +1816,14 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   int* ctr = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds);
   int* fin_head = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + 16);
   int* recs = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + kLdsHeader);
+  // the workgroups covering the range's first and last heads: cov[0] / cov[2]
+  // the first of them, cov[1] / cov[3] how many (a head strictly between is
+  // this workgroup's alone); kept in LDS, read at the end of the call
+  int* cov = reinterpret_cast<int*>(lds + kGroupWaves * kWaveLds + 16 + 4 * kGroupWaves);
+  auto cover = [&](int h, int& lo, int& nc) {
+    lo = h == gr.h0 ? cov[0] : (h == gr.h1 ? cov[2] : g);
+    nc = h == gr.h0 ? cov[1] : (h == gr.h1 ? cov[3] : 1);
+  };
 
   // paged caches: the record ids of the range's blocks, read from the block
   // table once (a page id outside the pool reads record 0 instead)
@@ -1827,7 +1846,13 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   if constexpr (T::kRope) rc = RopeCtx{rope_freq(p.rope_theta, li.lane), rtab};
   // the block counter starts at zero; the barrier comes before any block
   // load is issued, so no wavefront waits on another's loads
-  if (threadIdx.x == 0) ctr[0] = ctr[1] = 0;     // quantized units, fp16 blocks
+  if (threadIdx.x == 0) {
+    ctr[0] = ctr[1] = 0;                         // quantized units, fp16 blocks
+    cov[0] = (int)covering_lo(p, gr.h0);
+    cov[1] = (int)covering_count(p, gr.h0);
+    cov[2] = gr.h1 == gr.h0 ? cov[0] : g;        // a later head starts inside this range
+    cov[3] = gr.h1 == gr.h0 ? cov[1] : (int)(range_of(p, (int64_t)(gr.h1 + 1) * p.nblk - 1) - g + 1);
+  }
   __syncthreads();
 
   // query rows of the range's first head, loaded before the blocks
@@ -1950,7 +1975,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   // (h, fb).  They are processed at the end (see below).
   auto fp16_of = [&](int k, int& h, int& fb) -> bool {
     for (int hh = gr.h0; hh <= gr.h1; ++hh) {
-      const int64_t nc = covering_count(p, hh), fb0 = g - covering_lo(p, hh);
+      int lo_h, nc_h;
+      cover(hh, lo_h, nc_h);
+      const int64_t nc = nc_h, fb0 = g - lo_h;
       const int cnt = fb0 < p.fp16_blocks ? (int)((p.fp16_blocks - fb0 + nc - 1) / nc) : 0;
       if (k < cnt) {
         h = hh;
@@ -2083,7 +2110,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   // each covering workgroup's arrival in its low 16 bits; the workgroup
   // whose arrival completes the count combines the head, every other one
   // writes its merged slot and then adds its "written" mark (bit 16).
-  const int nc0 = (int)covering_count(p, gr.h0), nc1 = (int)covering_count(p, gr.h1);
+  const int lo0 = cov[0], nc0 = cov[1], lo1 = cov[2], nc1 = cov[3];
   const bool sh0 = nc0 > 1, sh1 = gr.h1 != gr.h0 && nc1 > 1;
   int prev0 = 0, prev1 = 0;
   if (threadIdx.x == 0) {                     // arrivals first: their round trips overlap the merge
@@ -2113,7 +2140,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       float M = neg_inf(), L = 0.f;
       float4 O = {0.f, 0.f, 0.f, 0.f};
       if (idx < total) {
-        const int64_t nc = covering_count(p, h), fb0 = g - covering_lo(p, h);
+        int lo_h, nc_h;
+        cover(h, lo_h, nc_h);
+        const int64_t nc = nc_h, fb0 = g - lo_h;
         float m[kGroupWaves], l[kGroupWaves], fm[kFoldFp16], fl[kFoldFp16];
         float4 o[kGroupWaves], fo[kFoldFp16];
 #pragma unroll
@@ -2204,7 +2233,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     if (sh0 && !last0) __hip_atomic_fetch_add(p.sync + gr.h0, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
     if (sh1 && !last1) __hip_atomic_fetch_add(p.sync + gr.h1, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (last0 || last1) combine_shared(p, g, gr.h0, gr.h1, last0, last1, nc0, nc1, own_slot(0), own_slot(1));
+  if (last0 || last1) combine_shared(p, g, gr.h0, gr.h1, last0, last1, lo0, lo1, nc0, nc1, own_slot(0), own_slot(1));
 }
 
 
@@ -2218,7 +2247,7 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
     fp16_block<ROPE>(p, g, fb, reinterpret_cast<uint16_t*>(lds + v * kWaveLds),
                p.part_fp16 + ((int64_t)g * p.fp16_blocks + fb) * slot_floats(p));
   __syncthreads();                            // the head's partials, all written by this workgroup
-  reduce_heads<false>(p, nullptr, 1, g);
+  reduce_fp16_head(p, g);
 }
 
 template <int FMT, int MODE = kSingle>

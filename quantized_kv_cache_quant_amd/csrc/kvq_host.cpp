@@ -79,15 +79,36 @@ int64_t device_cus() {
 }
 
 struct AttnPlan {
-  int64_t group_blocks, groups, fp16_blocks, slots;
+  int64_t range_len, range_parts, group_skew;   // see AttnParams
+  int64_t max_range, min_range;                 // longest and shortest workgroup range
+  int64_t groups, fp16_blocks, slots;
 };
 
-// Split the work: the quantized blocks of all heads into ranges of
-// group_blocks blocks, one per workgroup (by default one range per compute
-// unit); the fp16 segment of each head into 32-token blocks handled by the
-// workgroups whose range touches the head (one workgroup per head when no
-// block is quantized yet).  Partial slots: one per fp16 block, plus, for the
-// quantized blocks, kGroupWaves + 1 per (workgroup, head) index g + bh.
+// The library's own split gives the workgroups on odd-numbered XCDs (odd
+// workgroup index: workgroup g runs on XCD g mod 8) kOddSkewPermille / 1000
+// of a range fewer blocks than their even neighbours: on MI355X the odd XCDs
+// stream measurably slower, so equal ranges finish unequally.
+#ifndef KVQ_ODD_SKEW_PERMILLE
+#define KVQ_ODD_SKEW_PERMILLE 40
+#endif
+constexpr int64_t kOddSkewPermille = KVQ_ODD_SKEW_PERMILLE;
+
+// Split the work: the quantized blocks of all heads into one range per
+// workgroup; the fp16 segment of each head into 32-token blocks handled by
+// the workgroups whose range touches the head (one workgroup per head when
+// no block is quantized yet).  Partial slots: one per fp16 block, plus, for
+// the quantized blocks, kGroupWaves + 1 per (workgroup, head) index g + bh.
+// Ranges: stretches of range_len blocks, each cut into range_parts parts
+// (part p from floor(p L / k) + (p odd ? d : 0), see range_start in
+// kvq_attn.hip):
+//  * bpg > 0: ranges of exactly bpg blocks (L = bpg, k = 1);
+//  * bpg = 0 (the library's split, one range per compute unit): when the
+//    compute units divide among the heads evenly (k = CUs / heads ranges per
+//    head are as long as an even cut of all blocks over the CUs, to within
+//    1/32), every head is cut into k parts (L = nblk), so no range straddles
+//    two heads and each head is shared by exactly k workgroups; otherwise
+//    all blocks are cut into equal ranges of R blocks across head boundaries
+//    (L = 2 R, k = 2).
 // Paged caches stage a range's record ids in LDS, so their ranges hold at
 // most kMaxPagedRange blocks.
 AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t bpg) {
@@ -95,13 +116,57 @@ AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t 
   const int64_t bh = (int64_t)L.batch * L.num_kv_heads;
   a.fp16_blocks = (n_fp16_tokens + kBlock - 1) / kBlock;
   const int64_t total = bh * nblk;
-  const int64_t target = device_cus() * kGroupsPerCu;
-  if (bpg > 0) a.group_blocks = bpg;
-  else a.group_blocks = total > 0 ? (total + target - 1) / target : 1;
-  if (L.page_blocks > 0 && a.group_blocks > kMaxPagedRange) a.group_blocks = kMaxPagedRange;
-  a.groups = total > 0 ? (total + a.group_blocks - 1) / a.group_blocks : bh;
-  a.slots = bh * a.fp16_blocks + (total > 0 ? (kGroupWaves + 1) * (a.groups + bh) : 0);
+  a.range_len = 1;
+  a.range_parts = 1;
+  a.group_skew = 0;
+  if (total == 0) {
+    a.groups = bh;
+    a.slots = bh * a.fp16_blocks;
+    return a;
+  }
+  const int64_t cap = L.page_blocks > 0 ? kMaxPagedRange : (int64_t(1) << 29);
+  if (bpg > 0) {                                    // exact ranges of bpg blocks
+    a.range_len = bpg;
+    a.range_parts = 1;
+  } else {
+    const int64_t target = device_cus() * kGroupsPerCu;
+    const int64_t even = std::min((total + target - 1) / target, cap);
+    const int64_t k = bh <= target ? target / bh : 0;
+    const int64_t per = k > 0 ? (nblk + k - 1) / k : 0;
+    if (k > 0 && nblk >= k && per <= even + even / 32 && per <= cap && k * nblk < (int64_t(1) << 31)) {
+      a.range_len = nblk;                           // k parts of every head
+      a.range_parts = k;
+    } else {
+      a.range_len = 2 * even;                       // equal ranges of `even` blocks
+      a.range_parts = 2;
+    }
+    const int64_t lo = a.range_len / a.range_parts, hi = (a.range_len + a.range_parts - 1) / a.range_parts;
+    a.group_skew = std::min(lo * kOddSkewPermille / 1000, lo - 1);
+    a.group_skew = std::max<int64_t>(0, std::min(a.group_skew, cap - hi));
+  }
+  const int64_t lo = a.range_len / a.range_parts, hi = (a.range_len + a.range_parts - 1) / a.range_parts;
+  a.max_range = hi + a.group_skew;
+  a.min_range = lo - a.group_skew;
+  // workgroups: every part that starts before the end
+  auto start = [&](int64_t g) {
+    const int64_t s = g / a.range_parts, part = g - s * a.range_parts;
+    return s * a.range_len + part * a.range_len / a.range_parts + ((part & 1) ? a.group_skew : 0);
+  };
+  a.groups = (total + a.range_len - 1) / a.range_len * a.range_parts;
+  while (a.groups > 1 && start(a.groups - 1) >= total) --a.groups;
+  a.slots = bh * a.fp16_blocks + (kGroupWaves + 1) * (a.groups + bh);
   return a;
+}
+
+// Multiply-shift division by d for dividends below 2^31: with 2^l >= d,
+// m = ceil(2^(31+l) / d) < 2^32 and m d - 2^(31+l) < d, so
+// floor(j m / 2^(31+l)) = floor(j / d) whenever j < 2^31.
+void div_magic(uint64_t d, uint32_t& magic, int32_t& shift) {
+  if (d == 0) d = 1;
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  shift = 31 + l;
+  magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
 }
 
 uint64_t slot_bytes(const kvq_layout& L) {
@@ -135,7 +200,9 @@ static int32_t prepare_attention(const kvq_cache* c, int64_t n_tokens, const voi
   if (bh * nblk > 0x7fffffffLL || a.groups > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
   // a head's arrival counter holds up to 65535 arrivals and 32767 "written"
   // marks: at most 32767 workgroups may cover one head
-  if (nblk > 0 && (nblk + a.group_blocks - 1) / a.group_blocks + 1 > 32767) return KVQ_ERR_UNSUPPORTED;
+  if (nblk > 0 && (nblk + a.min_range - 1) / a.min_range + 1 > 32767) return KVQ_ERR_UNSUPPORTED;
+  // the kernels' range arithmetic is 32-bit: range_len * range_parts < 2^31
+  if (nblk > 0 && a.range_len * a.range_parts >= (int64_t(1) << 31)) return KVQ_ERR_UNSUPPORTED;
 
   char* base = static_cast<char*>(c->base);
   auto plane = [&](int i) { return base + c->plane_off[i]; };
@@ -160,29 +227,19 @@ static int32_t prepare_attention(const kvq_cache* c, int64_t n_tokens, const voi
   p.nrep = L.num_q_heads / L.num_kv_heads;
   p.nb_cap = c->n_blocks_cap;
   p.nblk = (int32_t)nblk;
-  {
-    // multiply-shift division by d = nblk for dividends below 2^31: with
-    // 2^l >= d, m = ceil(2^(31+l) / d) < 2^32 and m d - 2^(31+l) < d, so
-    // floor(j m / 2^(31+l)) = floor(j / d) whenever j < 2^31
-    const uint64_t d = nblk > 0 ? (uint64_t)nblk : 1;
-    int l = 0;
-    while ((1ull << l) < d) ++l;
-    p.nblk_shift = 31 + l;
-    p.nblk_magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
-    // the same for d = ceil(nblk / 2), the block pairs of a whole head
-    const uint64_t d2 = (d + 1) / 2;
-    l = 0;
-    while ((1ull << l) < d2) ++l;
-    p.half_shift = 31 + l;
-    p.half_magic = (uint32_t)(((1ull << (31 + l)) + d2 - 1) / d2);
-  }
+  div_magic((uint64_t)nblk, p.nblk_magic, p.nblk_shift);
+  div_magic(((uint64_t)nblk + 1) / 2, p.half_magic, p.half_shift);   // the block pairs of a whole head
   p.ring_slots = c->ring_slots;
   p.sink_cap = L.sink_tokens;
   p.n_sink = (int32_t)w.n_sink;
   p.n_res = (int32_t)w.r;
   p.ring_first = (int32_t)(w.n_q % c->ring_slots);
   p.bh_count = (int32_t)bh;
-  p.group_blocks = (int32_t)a.group_blocks;
+  p.range_len = (int32_t)a.range_len;
+  p.range_parts = (int32_t)a.range_parts;
+  p.group_skew = (int32_t)a.group_skew;
+  div_magic((uint64_t)a.range_len, p.len_magic, p.len_shift);
+  div_magic((uint64_t)a.range_parts, p.parts_magic, p.parts_shift);
   p.groups = (int32_t)a.groups;
   p.fp16_blocks = (int32_t)a.fp16_blocks;
   p.deterministic = deterministic;

@@ -108,8 +108,10 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 
 // ------------------------------------------------------------- attention
 // Work: the quantized blocks of all heads, flattened head-major (block j is
-// block j mod nblk of head j / nblk), are cut into ranges of group_blocks
-// blocks, one per workgroup of kGroupWaves wavefronts; the wavefronts of a
+// block j mod nblk of head j / nblk), are cut into ranges, one per workgroup
+// of kGroupWaves wavefronts (whole heads cut into equal parts when the
+// workgroups divide among the heads evenly, else equal ranges across head
+// boundaries); the wavefronts of a
 // workgroup take the blocks of its range in turn.  The fp16 segment of every
 // head (sinks, then residual ring) is cut into 32-token blocks, dealt round
 // robin to the workgroups whose range touches the head.
@@ -117,8 +119,10 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 //   part_fp16   slot bh * fp16_blocks + fb       fp16 block fb of head bh
 //   part_wave   slot kGroupWaves * (g + bh) + w   wavefront w of workgroup g, head bh
 //   part_group  slot g + bh                      workgroup g, head bh (its wavefronts merged)
-// Workgroup g's range touches heads floor(g*R/nblk) .. floor(((g+1)*R - 1)/nblk),
-// so g + bh never collides between workgroups.  Each workgroup folds its
+// Workgroup g's range [start(g), start(g + 1)) (start: range_start in
+// kvq_attn.hip, increasing in g) touches heads floor(start(g) / nblk) ..
+// floor((start(g + 1) - 1) / nblk), so g + bh never collides between
+// workgroups.  Each workgroup folds its
 // wavefront partials and the fp16 slots it produced per head.  A head the
 // workgroup covers alone is written to the output.  A head shared with other
 // workgroups is counted on its sync counter: arrivals in the low 16 bits,
@@ -161,7 +165,13 @@ struct AttnParams {
   int32_t n_res;          // residual tokens held
   int32_t ring_first;     // ring slot of the oldest residual token (n_q mod RS)
   int32_t bh_count;       // B * Hkv
-  int32_t group_blocks;   // R: quantized blocks per workgroup range
+  int32_t range_len;      // L: blocks per stretch (nblk: ranges follow heads; 2 R: equal ranges of R)
+  int32_t range_parts;    // k: workgroup ranges per stretch (k L < 2^31)
+  int32_t group_skew;     // d: odd parts start d blocks later (0 <= d < floor(L / k))
+  uint32_t len_magic;     // x / L == (x * len_magic) >> len_shift for 0 <= x < 2^31
+  int32_t len_shift;
+  uint32_t parts_magic;   // the same for the divisor k
+  int32_t parts_shift;
   int32_t groups;         // workgroups in the grid
   int32_t fp16_blocks;    // ceil((n_sink + n_res) / 32) per head
   int32_t deterministic;  // 1: wavefront w takes blocks w, w + 8, ... of its range
