@@ -1867,6 +1867,24 @@ __device__ void group_main(const AttnParams& p, char* lds) {
   Raw<FMT> buf[D];
   int rid[D], rbh[D], rblk[D];
   int kst = 0;
+  // Heads of the range shared with neighbouring workgroups count this
+  // workgroup's arrival on their counters (sync plane).  The arrival is made
+  // by the one wavefront whose claim is the first past the range (claims are
+  // numbered, so exactly one gets index len), while the workgroup still has
+  // its last blocks in flight: the arrival order then follows the order in
+  // which the workgroups run out of blocks, and the atomics' round trips are
+  // hidden behind those blocks.  The returned counts go to LDS once the
+  // wavefront's loop is over.
+  int arr0 = 0, arr1 = 0;
+  bool arrived = false;
+  auto arrive = [&]() {
+    arrived = true;
+    if (li.lane == 0) {
+      if (cov[1] > 1) arr0 = __hip_atomic_fetch_add(p.sync + gr.h0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (gr.h1 != gr.h0 && cov[3] > 1)
+        arr1 = __hip_atomic_fetch_add(p.sync + gr.h1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
   auto fetch = [&](Raw<FMT>& r, int& id, int& bhout, int& blkout) {
     int idx;
     if (p.deterministic) {
@@ -1900,6 +1918,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       id = -1;
       bhout = 0;
       blkout = 0;
+      if (idx == gr.len) arrive();
       load_block<FMT, false>(r, p, 0, li.lane);
     }
   };
@@ -1957,6 +1976,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       id = -1;
       bhout = 0;
       has2 = false;
+      if (idx == (int)units) arrive();
       load_block<FMT, false>(ra, p, 0, li.lane);
       load_block<FMT, false>(rb, p, 0, li.lane);
     }
@@ -2085,6 +2105,10 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       }
     }
     if (li.lane == 0) fin_head[v] = cur;
+    if (arrived && li.lane == 0) {             // the arrival's returned counts
+      ctr[2] = arr0;
+      ctr[3] = arr1;
+    }
   }
 
   // The fp16 blocks are taken from a second LDS counter by the wavefronts as
@@ -2106,16 +2130,17 @@ __device__ void group_main(const AttnParams& p, char* lds) {
 
   // ---- end of the call.  Heads in the middle of the range are covered by
   // this workgroup alone; the first and the last head may be shared with
-  // neighbouring workgroups.  A shared head's counter (sync plane) takes
-  // each covering workgroup's arrival in its low 16 bits; the workgroup
-  // whose arrival completes the count combines the head, every other one
-  // writes its merged slot and then adds its "written" mark (bit 16).
+  // neighbouring workgroups.  A shared head's counter (sync plane) has taken
+  // each covering workgroup's arrival in its low 16 bits (see arrive); the
+  // workgroup whose arrival completed the count combines the head, every
+  // other one writes its merged slot and then adds its "written" mark (bit
+  // 16).
   const int lo0 = cov[0], nc0 = cov[1], lo1 = cov[2], nc1 = cov[3];
   const bool sh0 = nc0 > 1, sh1 = gr.h1 != gr.h0 && nc1 > 1;
   int prev0 = 0, prev1 = 0;
-  if (threadIdx.x == 0) {                     // arrivals first: their round trips overlap the merge
-    if (sh0) prev0 = __hip_atomic_fetch_add(p.sync + gr.h0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (sh1) prev1 = __hip_atomic_fetch_add(p.sync + gr.h1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    prev0 = ctr[2];
+    prev1 = ctr[3];
   }
   bool last0 = false, last1 = false;
   // own merged partials of a shared head this workgroup combines, in the
@@ -2184,7 +2209,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         }
       }
       if (base == 0) {                            // which shared heads this workgroup combines
-        int* lf = ctr + 2;                        // the block counters are done with
+        int* lf = ctr + 2;                        // the arrival's counts are in prev0 / prev1 now
         if (threadIdx.x == 0) {
           lf[0] = sh0 && (prev0 & 0xFFFF) == nc0 - 1;
           lf[1] = sh1 && (prev1 & 0xFFFF) == nc1 - 1;
