@@ -131,6 +131,26 @@ def test_split_invariance_and_determinism(fmt):
         assert np.array_equal(again.astype(np.float64), outs[bpg, True]), bpg   # bitwise repeatable
 
 
+@pytest.mark.parametrize("fmt", ["int8", "int2"])
+def test_repeated_calls_default_and_deterministic(fmt):
+    """Repeatability of the library's own split at a size where every workgroup's wavefronts
+    take many blocks: the deterministic mode (static hand-out) repeats bit for bit; the default
+    (dynamic hand-out) changes only the fp32 summation order, so repeats stay within one fp16
+    ulp of each other and within the bound of the oracle."""
+    require_gpu()
+    c, kw, q = _build(fmt, 4, 4, 4, 32 * 260 + 45, 128, 0, seed=21)
+    ref = _oracle_out(c, kw, q)
+    det = [attention_gpu(c, q, 0, True) for _ in range(4)]
+    for o in det[1:]:
+        assert np.array_equal(o.view(np.uint16), det[0].view(np.uint16))
+    base = det[0].astype(np.float64)
+    assert np.max(np.abs(base - ref)) <= TOL
+    for _ in range(4):
+        o = attention_gpu(c, q, 0, False).astype(np.float64)
+        assert np.max(np.abs(o - ref)) <= TOL
+        assert np.all(np.abs(o - base) <= np.maximum(np.abs(base), 1.0) * 2.0**-10)
+
+
 def test_arrival_counters_start_and_end_at_zero():
     """The sync plane (one int32 arrival counter per sequence and KV head, through which the
     last workgroup to finish a head takes over its combine) holds garbage before the first
