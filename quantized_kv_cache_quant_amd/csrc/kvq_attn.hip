@@ -72,6 +72,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQScale = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
@@ -1592,7 +1593,7 @@ __device__ __forceinline__ void fold(float& M, float& L, float& O, const float* 
 #pragma unroll
   for (int j = 0; j < N; ++j) Mn = fmaxf(Mn, m[j]);
   if (Mn != neg_inf()) {                         // rescale what was summed before
-    const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
+    const float a = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     L *= a;
     O *= a;
   }
@@ -1600,7 +1601,7 @@ __device__ __forceinline__ void fold(float& M, float& L, float& O, const float* 
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     if (m[j] != neg_inf()) {
-      const float wt = exp2f(m[j] - M);
+      const float wt = __builtin_amdgcn_exp2f(m[j] - M);
       L = __builtin_fmaf(wt, l[j], L);
       O = __builtin_fmaf(wt, o[j], O);
     }
@@ -1615,7 +1616,7 @@ __device__ __forceinline__ void fold4(float& M, float& L, float4& O, const float
 #pragma unroll
   for (int j = 0; j < N; ++j) Mn = fmaxf(Mn, m[j]);
   if (Mn != neg_inf()) {
-    const float a = M == neg_inf() ? 0.f : exp2f(M - Mn);
+    const float a = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     L *= a;
     O.x *= a; O.y *= a; O.z *= a; O.w *= a;
   }
@@ -1623,7 +1624,7 @@ __device__ __forceinline__ void fold4(float& M, float& L, float4& O, const float
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     if (m[j] != neg_inf()) {
-      const float wt = exp2f(m[j] - M);
+      const float wt = __builtin_amdgcn_exp2f(m[j] - M);
       L = __builtin_fmaf(wt, l[j], L);
       O.x = __builtin_fmaf(wt, o[j].x, O.x);
       O.y = __builtin_fmaf(wt, o[j].y, O.y);
@@ -2172,16 +2173,20 @@ __device__ void group_main(const AttnParams& p, char* lds) {
         float4 o[kGroupWaves], fo[kFoldFp16];
 #pragma unroll
         for (int w = 0; w < kGroupWaves; ++w) {
-          if (fin_head[w] == h) {                 // the wavefront's last segment, in LDS
-            const float* sp = reinterpret_cast<const float*>(lds + w * kWaveLds + kStageBytes) + hh * kPartStride;
-            m[w] = sp[0];
-            l[w] = sp[1];
-            o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
-          } else {
-            const float* sp = wave_slot(h, w) + hh * kPartStride;
-            m[w] = sp[0];
-            l[w] = sp[1];
-            o[w] = *reinterpret_cast<const float4*>(sp + 4 + 4 * c4);
+          // the wavefront's last segment is in its LDS area (read as LDS, not
+          // through a generic pointer); an earlier one in its workspace slot
+          const float* lp = reinterpret_cast<const float*>(lds + w * kWaveLds + kStageBytes) + hh * kPartStride;
+          const float2 ml = *reinterpret_cast<const float2*>(lp);
+          m[w] = ml.x;
+          l[w] = ml.y;
+          o[w] = *reinterpret_cast<const float4*>(lp + 4 + 4 * c4);
+          if (fin_head[w] != h) {                 // (nontemporal: a load of another kind than
+            const float* sp = wave_slot(h, w) + hh * kPartStride;   // the LDS one, never merged with it)
+            const f32x2 a = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(sp));
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + 4 + 4 * c4));
+            m[w] = a.x;
+            l[w] = a.y;
+            o[w] = float4{t.x, t.y, t.z, t.w};
           }
         }
         auto load_fp16 = [&](int64_t first) {
@@ -2227,15 +2232,15 @@ __device__ void group_main(const AttnParams& p, char* lds) {
               uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         } else {
           const bool mine = h == gr.h0 ? last0 : last1;
-          float* dst = mine ? own_slot(h == gr.h0 ? 0 : 1) + hh * kPartStride
-                            : p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
-          if (mine) {
+          if (mine) {                             // (LDS and workspace addresses kept apart, so
+            float* dst = own_slot(h == gr.h0 ? 0 : 1) + hh * kPartStride;   // that neither goes generic)
             if (c4 == 0) {
               dst[0] = M;
               dst[1] = L;
             }
             *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = O;
           } else {
+            float* dst = p.part_group + ((int64_t)g + h) * slot_floats(p) + hh * kPartStride;
             if (c4 == 0) {
               st_dev(dst, M);
               st_dev(dst + 1, L);
