@@ -547,15 +547,18 @@ def tiny_latency(torch, kvq, synth, calls=200) -> dict:
 def read_sweep(torch, kvq) -> dict:
     """The plain streaming-read kernel (kvq_read_probe, one workgroup of 512 threads per compute
     unit, the attention kernel's launch shape) over a range of sizes: each call reads a fresh
-    slice of an 11 GiB buffer (the 256 MB last-level cache cannot serve it) between its own
-    event pair."""
+    slice of an 11 GiB buffer (the 256 MB last-level cache cannot serve it), once with each call
+    between its own event pair and once with the calls back to back between one pair (the way
+    the attention sweep is timed)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     total = 11 << 30
     x = torch.empty(total, dtype=torch.uint8, device="cuda")
     sink = torch.empty(cus * 512, dtype=torch.int32, device="cuda")
     res = {}
-    for mib in (64, 128, 275, 342, 1024, 4096):
-        nb = mib << 20
+    # the attention calls' own sizes (8B INT8 342 MB, FP8 275 MB, KIVI INT2 142 MB, 70B INT4 209 MB,
+    # 131k mixed 235 MB mean) among others
+    for mb in (64, 128, 142, 209, 235, 275, 342, 1074, 4295):
+        nb = mb * 1000000 // 256 * 256
         slices = max(8, min(32, total // nb))
         offs = [(i * nb) % (total - nb + 1) // 256 * 256 for i in range(slices)]
         kvq.read_probe(x[offs[0]:offs[0] + nb], sink, cus)
@@ -567,9 +570,18 @@ def read_sweep(torch, kvq) -> dict:
             e1.record()
         torch.cuda.synchronize()
         us = [1e3 * a.elapsed_time(b) for a, b in ev]
-        res[f"{mib}_MiB"] = {"mean_us": round(float(np.mean(us)), 2), "min_us": round(float(np.min(us)), 2),
-                             "gbps_mean": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1), "calls": len(us)}
-        log(f"read {mib} MiB: {res[f'{mib}_MiB']}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for o in offs:
+            kvq.read_probe(x[o:o + nb], sink, cus)
+        e1.record()
+        torch.cuda.synchronize()
+        b2b = 1e3 * e0.elapsed_time(e1) / len(offs)
+        res[f"{mb}_MB"] = {"mean_us": round(float(np.mean(us)), 2), "min_us": round(float(np.min(us)), 2),
+                             "gbps_mean": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+                             "back_to_back_us": round(b2b, 2), "gbps_back_to_back": round(nb / (b2b * 1e-6) / 1e9, 1),
+                             "calls": len(us)}
+        log(f"read {mb} MB: {res[f'{mb}_MB']}")
     del x, sink
     return res
 
