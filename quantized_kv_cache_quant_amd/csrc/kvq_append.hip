@@ -24,7 +24,8 @@
 // Bit-exactness: every quantization step is one correctly rounded IEEE fp32
 // operation in the order of the formula, exactly like the CPU oracle: the
 // division x / s by the exact reciprocal-and-remainder sequence of div_rn
-// (FP8 by true division), no contraction (this file is built with
+// (FP8: div_rn_any while the per-tensor scale lies in [2^-60, 2^60], true
+// division outside), no contraction (this file is built with
 // -ffp-contract=off and correctly rounded fp32 division), rint
 // round-half-even.
 #include "kvq_internal.h"
@@ -71,6 +72,16 @@ __device__ __forceinline__ uint32_t encode_int(float x, float s, float z, float 
   return (uint32_t)v;
 }
 
+// div_rn for every fp16 dividend, signed zeros and infinities included (an
+// FP8 code keeps the sign of zero): a zero remainder means q * s = x exactly,
+// so q (with its sign) is the quotient; a NaN remainder comes from x = +-inf,
+// where q = x * y is already +-inf
+__device__ __forceinline__ float div_rn_any(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  return fabsf(r) > 0.0f ? __builtin_fmaf(r, y, q) : q;
+}
+
 // Smallest fp16 >= x, for finite 0 <= x <= 65504 (bit pattern; -0 gives -0).
 __device__ __forceinline__ uint32_t f16_round_up(float x) {
   const _Float16 h = (_Float16)x;                  // round to nearest even
@@ -83,10 +94,10 @@ __device__ __forceinline__ uint32_t f16_round_up(float x) {
 // explicit clamp to the format's largest finite value; the hardware
 // conversion rounds to nearest even.  E4M3: +-448; E5M2: +-57344.
 template <bool E5M2>
-__device__ __forceinline__ uint32_t encode_fp8_pair(float a, float b, float s) {
+__device__ __forceinline__ uint32_t encode_fp8_pair(float a, float b, float s, float y, bool fast) {
   constexpr float kMax = E5M2 ? 57344.0f : 448.0f;
-  float va = fminf(fmaxf(a / s, -kMax), kMax);
-  float vb = fminf(fmaxf(b / s, -kMax), kMax);
+  float va = fminf(fmaxf(fast ? div_rn_any(a, s, y) : a / s, -kMax), kMax);
+  float vb = fminf(fmaxf(fast ? div_rn_any(b, s, y) : b / s, -kMax), kMax);
   if constexpr (E5M2) return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(va, vb, 0, false) & 0xFFFFu;
   else return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
 }
@@ -129,26 +140,54 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   // table); a page id outside the pool leaves the block unwritten
   const int64_t rec = block_record(p.table, p.table_stride, p.page_blocks, p.num_pages, p.hkv, p.nb_cap, b, h, blk);
   if (rec < 0) return;                                // uniform over the workgroup, before any barrier
+  // FP8: x / s by div_rn from y = RN(1 / s) when s lies in [2^-60, 2^60] (no
+  // overflow or underflow for fp16 x), else by true division
+  const float ky = 1.0f / p.k_scale, vy = 1.0f / p.v_scale;
+  const bool kfast = p.k_scale >= 0x1p-60f && p.k_scale <= 0x1p60f;
+  const bool vfast = p.v_scale >= 0x1p-60f && p.v_scale <= 0x1p60f;
 
-  // 1) gather the block's 32 tokens (16-byte chunks, 16 per token row)
-  for (int e = tid; e < kBlock * 16; e += 256) {
-    const int t = e >> 4;
-    const int c8 = (e & 15) * 8;
-    const int64_t u = blk * kBlock + t;               // body index
-    const uint16_t* ksrc;
-    const uint16_t* vsrc;
-    if (u < p.n_body_old) {                           // still in the residual ring
-      const int64_t off = (bh * p.ring_slots + (u % p.ring_slots)) * kHeadDim + c8;
-      ksrc = p.k_ring + off;
-      vsrc = p.v_ring + off;
-    } else {                                          // arrives with this append
-      const int64_t i = u + p.sink - p.n_old;
-      const int64_t off = (((int64_t)b * p.T + i) * p.hkv + h) * kHeadDim + c8;
-      ksrc = p.k_in + off;
-      vsrc = p.v_in + off;
+  // 1) gather the block's 32 tokens: 512 16-byte chunks per tensor, two of K
+  //    and two of V per thread, all four loads issued before the LDS stores
+  //    (a workgroup per block: the hardware's dispatch keeps eight resident
+  //    per compute unit; a persistent loop prefetching the next block into
+  //    registers measured slower).
+  //    Ring slot of body index u: (u0 + t) mod (R + 32) with u0 the block's
+  //    first index reduced once (t < 32 <= R + 32: one subtraction).
+  {
+    int64_t ring0 = 0;
+    if (blk * kBlock < p.n_body_old) ring0 = (blk * kBlock) % p.ring_slots;
+    uint4 kc[2], vc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      const int t = e >> 4;
+      const int c8 = (e & 15) * 8;
+      const int64_t u = blk * kBlock + t;             // body index
+      const uint16_t* ksrc;
+      const uint16_t* vsrc;
+      if (u < p.n_body_old) {                         // still in the residual ring
+        int64_t slot = ring0 + t;
+        if (slot >= p.ring_slots) slot -= p.ring_slots;
+        const int64_t off = (bh * p.ring_slots + slot) * kHeadDim + c8;
+        ksrc = p.k_ring + off;
+        vsrc = p.v_ring + off;
+      } else {                                        // arrives with this append
+        const int64_t i_in = u + p.sink - p.n_old;
+        const int64_t off = (((int64_t)b * p.T + i_in) * p.hkv + h) * kHeadDim + c8;
+        ksrc = p.k_in + off;
+        vsrc = p.v_in + off;
+      }
+      kc[i] = *reinterpret_cast<const uint4*>(ksrc);
+      vc[i] = *reinterpret_cast<const uint4*>(vsrc);
     }
-    *reinterpret_cast<uint4*>(&ksh[t][c8]) = *reinterpret_cast<const uint4*>(ksrc);
-    *reinterpret_cast<uint4*>(&vsh[t][c8]) = *reinterpret_cast<const uint4*>(vsrc);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      const int t = e >> 4;
+      const int c8 = (e & 15) * 8;
+      *reinterpret_cast<uint4*>(&ksh[t][c8]) = kc[i];
+      *reinterpret_cast<uint4*>(&vsh[t][c8]) = vc[i];
+    }
   }
   __syncthreads();
 
@@ -203,8 +242,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         rk[c] = 1.0f / s;
         float* km = p.k_meta + rec * (2 * kHeadDim);   // [stored position][s, z]
         const int sp = kRopeK ? rope_stored_pos(c) : c;
-        km[2 * sp] = s;
-        km[2 * sp + 1] = z;
+        *reinterpret_cast<float2*>(km + 2 * sp) = make_float2(s, z);
       }
     } else {
       const int e = tid - kHeadDim;
@@ -252,8 +290,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
         zv[t][g] = z;
         rv[t][g] = 1.0f / s;
         float* vm = p.v_meta + rec * (2 * kVGroups * kBlock);  // [group][token][s, z]
-        vm[2 * (g * kBlock + t)] = s;
-        vm[2 * (g * kBlock + t) + 1] = z;
+        *reinterpret_cast<float2*>(vm + 2 * (g * kBlock + t)) = make_float2(s, z);
       }
     }
     __syncthreads();
@@ -284,8 +321,8 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
       auto chan = [](int sp) { return kRopeK ? rope_channel(sp) : sp; };
       if constexpr (kFp8) {
         const int c = wi * 4;
-        word = encode_fp8_pair<kE5M2>(ks_at(t, chan(c)), ks_at(t, chan(c + 1)), p.k_scale) |
-               (encode_fp8_pair<kE5M2>(ks_at(t, chan(c + 2)), ks_at(t, chan(c + 3)), p.k_scale) << 16);
+        word = encode_fp8_pair<kE5M2>(ks_at(t, chan(c)), ks_at(t, chan(c + 1)), p.k_scale, ky, kfast) |
+               (encode_fp8_pair<kE5M2>(ks_at(t, chan(c + 2)), ks_at(t, chan(c + 3)), p.k_scale, ky, kfast) << 16);
       } else {
         constexpr int kPer = 32 / kBits;
 #pragma unroll
@@ -333,7 +370,7 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
           const float x1 = vs_at(record_token(qd, sel(base + 1)), ch);
           const float x2 = vs_at(record_token(qd, sel(base + 2)), ch);
           const float x3 = vs_at(record_token(qd, sel(base + 3)), ch);
-          word = encode_fp8_pair<kE5M2>(x0, x1, p.v_scale) | (encode_fp8_pair<kE5M2>(x2, x3, p.v_scale) << 16);
+          word = encode_fp8_pair<kE5M2>(x0, x1, p.v_scale, vy, vfast) | (encode_fp8_pair<kE5M2>(x2, x3, p.v_scale, vy, vfast) << 16);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {

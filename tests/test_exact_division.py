@@ -65,3 +65,36 @@ def test_zero_and_scale_one():
             r = np.float32(np.float64(x) - np.float64(q) * np.float64(s))
             got = _rn32(Fraction(float(q)) + Fraction(float(r)) * Fraction(float(y)))
             assert got == np.float32(x / s)
+
+
+def _fast_fp8_quotient(x: np.float32, s: np.float32, y: np.float32) -> np.float32:
+    """The FP8 encoder's division with the kernel's roundings: q = RN(x y), r = RN(x - q s)
+    (fused), then q itself when r is 0 or NaN, else RN(q + r y) (fused)."""
+    q = np.float32(x * y)
+    with np.errstate(invalid="ignore"):
+        r = np.float32(np.float64(x) - np.float64(q) * np.float64(s))
+    if not abs(r) > 0:
+        return q
+    return _rn32(Fraction(float(q)) + Fraction(float(r)) * Fraction(float(y)))
+
+
+@pytest.mark.parametrize("s", [2.0**-60, 2.0**-60 * 1.3711, 3.1 / 448, 11.3 / 57344,
+                               float(np.nextafter(np.float32(2.0**60), np.float32(0)))])
+def test_fp8_division_every_fp16_value(s):
+    """FP8 per-tensor scales inside [2^-60, 2^60] take the reciprocal-and-remainder division:
+    every positive finite fp16 x gives the correctly rounded fp32 quotient at the range's ends
+    and at calibrated scales; -0, +-inf and negative values give exactly x / s, sign included
+    (an FP8 code keeps the sign of zero)."""
+    s = np.float32(s)
+    y = np.float32(1.0) / s
+    q = (X * y).astype(np.float32)
+    r = (X.astype(np.float64) - q.astype(np.float64) * np.float64(s)).astype(np.float32)
+    want = X / s
+    fy = Fraction(float(y))
+    for i in range(X.size):
+        got = q[i] if not abs(r[i]) > 0 else _rn32(Fraction(float(q[i])) + Fraction(float(r[i])) * fy)
+        assert got == want[i], (float(X[i]), float(s))
+    special = np.array([0.0, -0.0, np.inf, -np.inf, -65504.0, -2.0**-24, -1.5, -3.0e-5], np.float32)
+    for x in special:
+        got, ref = _fast_fp8_quotient(x, s, y), np.float32(x / s)
+        assert got.view(np.uint32) == ref.view(np.uint32), (float(x), float(s))

@@ -78,7 +78,8 @@ def test_chunking_invariance(fmt):
 
 @pytest.mark.parametrize("fmt,scale", [("fp8", 1.0), ("fp8", 0.0078125), ("fp8", 0.013671875), ("fp8", 3.7),
                                        ("fp8", 146.28571), ("fp8_e5m2", 1.0), ("fp8_e5m2", 2.0**-20),
-                                       ("fp8_e5m2", 1.1428571), ("fp8_e5m2", 0.013671875)])
+                                       ("fp8_e5m2", 1.1428571), ("fp8_e5m2", 0.013671875),
+                                       ("fp8", 2.0**-60 * 1.3711), ("fp8", 2.0**-62), ("fp8_e5m2", 2.0**61)])
 def test_fp8_encoder_every_fp16_value(fmt, scale):
     require_gpu()
     x = np.arange(65536, dtype=np.uint16).view(np.float16)
@@ -90,6 +91,26 @@ def test_fp8_encoder_every_fp16_value(fmt, scale):
               sink_tokens=0, k_scale=scale, v_scale=scale)
     c = make_cache(kw)
     append_chunks(c, k, v, [512])
+    olay = olayout_of(kw)
+    assert_states_equal(read_state(c, olay), ocache.build_cache(k, v, olay))
+
+
+@pytest.mark.parametrize("fmt,scale", [("fp8", 0.0078125), ("fp8", 2.0**-62), ("fp8_e5m2", 3.3)])
+def test_fp8_infinities_and_signed_zeros(fmt, scale):
+    """+-inf clamps to the largest finite code and -0 keeps its sign, on both division paths
+    (scale inside and outside [2^-60, 2^60])."""
+    require_gpu()
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((1, 64, 1, 128)).astype(np.float16)
+    v = rng.standard_normal((1, 64, 1, 128)).astype(np.float16)
+    k[0, 3, 0, :4] = [np.inf, -np.inf, -0.0, 0.0]
+    k[0, 40, 0, 100:104] = [-0.0, np.inf, -np.inf, -0.0]
+    v[0, 7, 0, 60:64] = [np.inf, -0.0, -np.inf, 0.0]
+    v[0, 33, 0, :2] = [-np.inf, -0.0]
+    kw = dict(batch=1, num_kv_heads=1, num_q_heads=1, max_tokens=64, fmt=fmt, residual_tokens=0,
+              sink_tokens=0, k_scale=scale, v_scale=scale)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [64])
     olay = olayout_of(kw)
     assert_states_equal(read_state(c, olay), ocache.build_cache(k, v, olay))
 
