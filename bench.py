@@ -37,7 +37,10 @@ launches on (torch's current stream):
     tokens/s;
   * prefill: each layer cache's kv_quant_append of the prompt between its own
     event pair -> prefill_quantize (fp16 K/V input GB/s; the first layer's
-    call, which pays one-off costs, is left out);
+    call, which pays one-off costs, is left out); flush_traffic_floor_us is
+    the library's read-then-write probe (kvq_rw_probe) moving the same
+    blocks' bytes with no compute, and frac_of_floor is that time over the
+    call's;
   * attention sweep: the kv_decode_attention calls of every layer of one
     format, several rounds back to back between one event pair -> the
     roofline entry (algorithmic bytes per call / mean call time, launch gaps
@@ -145,6 +148,35 @@ VARIANTS = ("fp8_e5m2", "int8_m16", "int4_m16", "int2_m16", "int8_paged", "int8_
 ROPE_THETA = 500000.0
 
 
+def flush_floor_us(torch, kvq, accounting, w, spec, reps=5) -> float:
+    """µs of the library's read-then-write probe (kvq_rw_probe) moving the bytes of the prompt's
+    flush in format spec: 32-token blocks of fp16 K and V read whole, then each block's codes and
+    metadata written; the same block count as the prompt's kv_quant_append quantizes.  Timed like
+    the prefill: one source read by every call, a newly allocated destination per call, one
+    event pair per call."""
+    fmt, m16, _, _, out = split_spec(spec)
+    d = w.head_dim
+    read_b = 2 * 32 * d * 2
+    pair = 0 if fmt.startswith("fp8") else (4 if m16 else 8) + (4 if out else 0)
+    write_b = 2 * 32 * d * accounting.BITS[fmt] // 8 + d * pair + (d // 32) * 32 * pair
+    _, nq, _ = accounting.routed(w.seq_len, w.sink_tokens, w.residual_tokens)
+    blocks = w.batch * w.num_kv_heads * (nq // 32)
+    src = torch.empty(blocks * read_b, dtype=torch.uint8, device="cuda")
+    dsts = [torch.empty(blocks * write_b, dtype=torch.uint8, device="cuda") for _ in range(reps + 1)]
+    ev = []
+    for dst in dsts:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.rw_probe(src, dst, read_b, write_b)
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [1e3 * a.elapsed_time(b) for a, b in ev[1:]]       # the first pays one-off costs
+    del src, dsts
+    torch.cuda.empty_cache()
+    return float(np.mean(us))
+
+
 def split_spec(spec: str):
     """Format spec -> (kvq format, fp16 metadata, paged, pre-RoPE Keys, outliers): suffix "_m16"
     selects fp16 (s, m) pairs, "_paged" a pool of 32-token pages, "_rope" Keys stored before RoPE,
@@ -245,19 +277,22 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
     vd = torch.from_numpy(vp).cuda()
     del kp, vp
     amax_k, amax_v = float(kd.abs().max().float().item()), float(vd.abs().max().float().item())
-    caches = []
+    # every layer's cache is allocated before the first append is timed (an allocation while a
+    # kernel runs remaps device memory under it)
+    caches = [make_cache(kvq, w, fmt, max_tokens, amax_k, amax_v) for fmt in fmt_list]
+    torch.cuda.synchronize()
     pre_ev = []                                 # prefill quantize-on-append, one event pair per layer
-    for li, fmt in enumerate(fmt_list):
-        c = make_cache(kvq, w, fmt, max_tokens, amax_k, amax_v)
+    for c in caches:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         c.append(kd, vd)
         e1.record()
         pre_ev.append((e0, e1))
-        caches.append(c)
     torch.cuda.synchronize()
     pre_us = [a.elapsed_time(bb) * 1e3 for a, bb in (pre_ev[1:] or pre_ev)]   # the first pays one-off costs
     pre_in = 2 * kd.numel() * kd.element_size()                               # fp16 K and V of the prompt
+    floors = {f: flush_floor_us(torch, kvq, accounting, w, f) for f in sorted(set(fmt_list))}
+    floor_us = float(np.mean([floors[f] for f in (fmt_list[1:] or fmt_list)]))
     del kd, vd
     log(f"{layers} layer caches prefilled ({sum(c.buf.numel() for c in caches) / 2**30:.2f} GiB)")
     steps_k, steps_v = [], []
@@ -328,7 +363,9 @@ def run_format(torch, kvq, synth, accounting, w, fmt_list, args):
         "prefill_quantize": {"us_per_layer": round(float(np.mean(pre_us)), 1),
                              "input_gbps": round(pre_in / (float(np.mean(pre_us)) * 1e-6) / 1e9, 1),
                              "tokens_per_s": round(b * n0 / (float(np.mean(pre_us)) * 1e-6)),
-                             "layers_timed": len(pre_us)},
+                             "layers_timed": len(pre_us),
+                             "flush_traffic_floor_us": round(floor_us, 1),
+                             "frac_of_floor": round(floor_us / float(np.mean(pre_us)), 3)},
     }
     res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
     log(f"{'/'.join(res['formats'])}: {ms_step:.3f} ms/step, {res['tokens_per_s']:.0f} tok/s, "

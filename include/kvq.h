@@ -341,6 +341,24 @@ int32_t kv_decode_attention_noalloc(const kvq_cache* cache, const void* q, void*
 int32_t kvq_read_probe(const void* buf, uint64_t bytes, void* sink, uint64_t sink_bytes, int32_t groups,
                        void* stream);
 
+/* Diagnostic, not part of the method: the traffic of a flush and nothing
+ * else, which measures the ceiling of kv_quant_append's quantization kernel
+ * on this GPU (the benchmark reports the prompt's quantization against it).
+ * One workgroup of 256 threads per unit of read_bytes of src (src_bytes /
+ * read_bytes units): it reads the unit whole (16-byte loads, all in flight
+ * together; thread t the unit's 16-byte words t, t + 256, ...), folds what
+ * each thread read by XOR into one 16-byte word w (four uint32 lanes), then
+ * writes the unit's write_bytes of dst, thread t the words j = t, t + 256,
+ * ... as w + j (uint32 lanes, wrapping).  A flush of head_dim 128 reads
+ * 16384 bytes per 32-token block and writes its codes and metadata.  src and
+ * dst are device pointers, 16-B aligned; read_bytes a multiple of 4096 up to
+ * 32768; write_bytes a multiple of 16 up to 65536; src_bytes a multiple of
+ * read_bytes; dst_bytes >= units * write_bytes.  Errors: KVQ_ERR_NULL,
+ * KVQ_ERR_LAYOUT (sizes), KVQ_ERR_ALIGN, KVQ_ERR_WORKSPACE (dst too small),
+ * KVQ_ERR_UNSUPPORTED (more than 2^31 - 1 units), KVQ_ERR_HIP. */
+int32_t kvq_rw_probe(const void* src, uint64_t src_bytes, void* dst, uint64_t dst_bytes, uint32_t read_bytes,
+                     uint32_t write_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

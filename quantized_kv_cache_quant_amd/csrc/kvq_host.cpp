@@ -553,4 +553,21 @@ int32_t kvq_read_probe(const void* buf, uint64_t bytes, void* sink, uint64_t sin
   return KVQ_OK;
 }
 
+int32_t kvq_rw_probe(const void* src, uint64_t src_bytes, void* dst, uint64_t dst_bytes, uint32_t read_bytes,
+                     uint32_t write_bytes, void* stream) {
+  if (!src || !dst) return KVQ_ERR_NULL;
+  if (read_bytes == 0 || read_bytes % 4096 != 0 || read_bytes > 32768 || write_bytes % 16 != 0 ||
+      write_bytes > 65536 || src_bytes % read_bytes != 0)
+    return KVQ_ERR_LAYOUT;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return KVQ_ERR_ALIGN;
+  const uint64_t units = src_bytes / read_bytes;
+  if (units > 0x7fffffffULL) return KVQ_ERR_UNSUPPORTED;
+  if (units * write_bytes > dst_bytes) return KVQ_ERR_WORKSPACE;
+  if (units == 0) return KVQ_OK;
+  if (launch_rw_probe(src, dst, units, (int)(read_bytes / 16), (int)(write_bytes / 16),
+                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
 }  // extern "C"

@@ -195,5 +195,7 @@ hipError_t attention_scratch(void** ptr);
 // ------------------------------------------------------------- read probe
 constexpr int kProbeThreads = 512;        // threads per workgroup, as the attention kernel
 hipError_t launch_read_probe(const void* buf, uint64_t units, uint32_t* sink, int groups, hipStream_t s);
+// units workgroups; read16 / write16: 16-byte words read / written per unit
+hipError_t launch_rw_probe(const void* src, void* dst, uint64_t units, int read16, int write16, hipStream_t s);
 
 }  // namespace kvq

@@ -23,7 +23,7 @@ PLANES = ("k_codes", "v_codes", "k_meta", "v_meta", "k_ring", "v_ring", "k_sink"
 EXPORTS = ("kvq_status_string", "kvq_layout_validate", "kvq_cache_bytes", "kvq_cache_init",
            "kvq_cache_plane", "kvq_cache_window", "kv_quant_append", "kvq_workspace_bytes",
            "kv_decode_attention", "kv_decode_attention_split", "kvq_cache_set_block_table",
-           "kvq_read_probe", "kv_append_decode_attention", "kv_decode_attention_noalloc")
+           "kvq_read_probe", "kvq_rw_probe", "kv_append_decode_attention", "kv_decode_attention_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "kv_decode_attention_split": (I32, [CP, P, P, P, U64, I32, I32, P]),
             "kvq_cache_set_block_table": (I32, [CP, P, I32]),
             "kvq_read_probe": (I32, [P, U64, P, U64, I32, P]),
+            "kvq_rw_probe": (I32, [P, U64, P, U64, ctypes.c_uint32, ctypes.c_uint32, P]),
             "kv_append_decode_attention": (I32, [CP, P, P, P, P, P, U64, P]),
             "kv_decode_attention_noalloc": (I32, [CP, P, P, P]),
         }
@@ -258,3 +259,11 @@ def read_probe(buf, sink, groups: int = 0, stream=None) -> None:
     check(lib().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                                ctypes.c_void_p(sink.data_ptr()), sink.numel() * sink.element_size(),
                                int(groups), _stream(stream)), "kvq_read_probe")
+
+
+def rw_probe(src, dst, read_bytes: int, write_bytes: int, stream=None) -> None:
+    """Diagnostic read-then-write traffic of a flush (see kvq_rw_probe): src (device tensor)
+    is read whole in units of read_bytes; dst receives write_bytes per unit."""
+    check(lib().kvq_rw_probe(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                             ctypes.c_void_p(dst.data_ptr()), dst.numel() * dst.element_size(),
+                             int(read_bytes), int(write_bytes), _stream(stream)), "kvq_rw_probe")

@@ -180,6 +180,25 @@ def test_read_probe_validation():
     assert L.kvq_read_probe(P(FAKE), 0, P(FAKE), sink, 0, None) == 0            # nothing to read
 
 
+def test_rw_probe_validation():
+    """The diagnostic read-then-write probe validates before launching anything."""
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    assert L.kvq_rw_probe(None, 16384, P(FAKE), 10240, 16384, 10240, None) == -1
+    assert L.kvq_rw_probe(P(FAKE), 16384, None, 10240, 16384, 10240, None) == -1
+    assert L.kvq_rw_probe(P(FAKE), 16384, P(FAKE), 10240, 0, 10240, None) == -2           # no read size
+    assert L.kvq_rw_probe(P(FAKE), 16384, P(FAKE), 10240, 12288 + 16, 10240, None) == -2  # not 4096-multiple
+    assert L.kvq_rw_probe(P(FAKE), 65536, P(FAKE), 10240, 65536, 10240, None) == -2       # over 32768
+    assert L.kvq_rw_probe(P(FAKE), 16384, P(FAKE), 10240, 16384, 10248, None) == -2       # not 16-multiple
+    assert L.kvq_rw_probe(P(FAKE), 16384, P(FAKE), 1 << 20, 16384, 65552, None) == -2     # over 65536
+    assert L.kvq_rw_probe(P(FAKE), 20480, P(FAKE), 10240, 16384, 10240, None) == -2       # ragged source
+    assert L.kvq_rw_probe(P(FAKE + 8), 16384, P(FAKE), 10240, 16384, 10240, None) == -5
+    assert L.kvq_rw_probe(P(FAKE), 16384, P(FAKE + 4), 10240, 16384, 10240, None) == -5
+    assert L.kvq_rw_probe(P(FAKE), 2 * 16384, P(FAKE), 2 * 10240 - 16, 16384, 10240, None) == -6
+    assert L.kvq_rw_probe(P(FAKE), 4096 * (1 << 31), P(FAKE), 1 << 62, 4096, 16, None) == -3   # 2^31 units
+    assert L.kvq_rw_probe(P(FAKE), 0, P(FAKE), 0, 16384, 10240, None) == 0            # nothing to move
+
+
 def test_attention_errors():
     L = kvq.lib()
     P = ctypes.c_void_p
