@@ -20,6 +20,9 @@
 //                flush because it may overwrite ring slots the flush read.
 //                On a cache's first append it also zeroes the attention
 //                arrival counters.
+// A flush that reads no ring slot (no body token was in the ring before the
+// append, as on a cache's first append) does the copy itself, in extra
+// workgroups of its launch, and copy_kernel is not launched.
 //
 // Bit-exactness: every quantization step is one correctly rounded IEEE fp32
 // operation in the order of the formula, exactly like the CPU oracle: the
@@ -107,6 +110,25 @@ __device__ __forceinline__ int record_token(int qd, int j) {
   return (j < 4) ? (4 * qd + j) : (16 + 4 * qd + (j - 4));
 }
 
+// 16-byte chunk `chunk` of copied token k (sinks first, then residual
+// tokens) of K (kv = 0) or V (kv = 1) of (sequence b, KV head h): from the
+// input to the sink plane or to the token's ring slot u mod (R + 32).
+__device__ __forceinline__ void copy_chunk(const CopyParams& p, int b, int h, int64_t k, int kv, int chunk) {
+  const int64_t t = k < p.n_sink_copy ? p.n_old + k : p.ring_first_t + (k - p.n_sink_copy);   // absolute
+  const int64_t i = t - p.n_old;                   // input token
+  uint16_t* dst;
+  if (t < p.sink) {
+    uint16_t* plane = kv ? p.v_sink : p.k_sink;
+    dst = plane + (((int64_t)b * p.hkv + h) * p.sink + t) * kHeadDim + chunk * 8;
+  } else {
+    const int64_t u = t - p.sink;                  // u >= n_q_new: a residual token
+    uint16_t* plane = kv ? p.v_ring : p.k_ring;
+    dst = plane + (((int64_t)b * p.hkv + h) * p.ring_slots + (u % p.ring_slots)) * kHeadDim + chunk * 8;
+  }
+  const uint16_t* src = (kv ? p.v_in : p.k_in) + (((int64_t)b * p.T + i) * p.hkv + h) * kHeadDim + chunk * 8;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
 template <int VAR>
 __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   constexpr int kKind = kind_of(VAR);
@@ -132,9 +154,17 @@ __global__ __launch_bounds__(256) void flush_kernel(FlushParams p) {
   __shared__ int vo[kBlock][kVGroups];       // outliers: channel (in group) of each token's outlier
 
   const int tid = threadIdx.x;
-  const int64_t blk = (int64_t)p.first_block + blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
+  if ((int)blockIdx.x >= p.flush_x) {               // fused copy: chunks of (b, h) in this workgroup's 256
+    const int64_t xc = (int64_t)blockIdx.x - p.flush_x;
+    if (xc == 0 && h == 0 && p.cp.sync_zero)
+      for (int e = tid; e < p.hkv; e += 256) p.cp.sync_zero[(int64_t)b * p.hkv + e] = 0;
+    const int64_t e = xc * 256 + tid;
+    if (e < p.cp.n_copy * 32) copy_chunk(p.cp, b, h, e >> 5, (int)((e >> 4) & 1), (int)(e & 15));
+    return;                                         // uniform over the workgroup, before any barrier
+  }
+  const int64_t blk = (int64_t)p.first_block + blockIdx.x;
   const int64_t bh = (int64_t)b * p.hkv + h;
   // record of this block in the code / meta planes (paged: through the block
   // table); a page id outside the pool leaves the block unwritten
@@ -409,26 +439,14 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   const int kv = (int)(rest & 1);
   rest >>= 1;
   const int h = (int)(rest % p.hkv);
-  const int64_t k = rest / p.hkv;                  // copied token
-  const int64_t t = k < p.n_sink_copy ? p.n_old + k : p.ring_first_t + (k - p.n_sink_copy);   // absolute
-  const int64_t i = t - p.n_old;                   // input token
-  uint16_t* dst;
-  if (t < p.sink) {
-    uint16_t* plane = kv ? p.v_sink : p.k_sink;
-    dst = plane + (((int64_t)b * p.hkv + h) * p.sink + t) * kHeadDim + chunk * 8;
-  } else {
-    const int64_t u = t - p.sink;                  // u >= n_q_new: a residual token
-    uint16_t* plane = kv ? p.v_ring : p.k_ring;
-    dst = plane + (((int64_t)b * p.hkv + h) * p.ring_slots + (u % p.ring_slots)) * kHeadDim + chunk * 8;
-  }
-  const uint16_t* src = (kv ? p.v_in : p.k_in) + (((int64_t)b * p.T + i) * p.hkv + h) * kHeadDim + chunk * 8;
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  copy_chunk(p, b, h, rest / p.hkv, kv, chunk);
 }
 
 }  // namespace
 
-hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s) {
-  const dim3 grid(n_blocks, p.hkv, batch), block(256);
+hipError_t launch_flush(int variant, const FlushParams& p, int batch, hipStream_t s) {
+  if (p.flush_x <= 0 || p.copy_x < 0 || (int64_t)p.flush_x + p.copy_x > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.flush_x + p.copy_x), p.hkv, batch), block(256);
   switch (variant) {
     case KVQ_INT8: hipLaunchKernelGGL(flush_kernel<KVQ_INT8>, grid, block, 0, s, p); break;
     case KVQ_INT4: hipLaunchKernelGGL(flush_kernel<KVQ_INT4>, grid, block, 0, s, p); break;

@@ -396,6 +396,29 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
   char* base = static_cast<char*>(c->base);
   auto plane = [&](int i) { return base + c->plane_off[i]; };
 
+  // copy of new sink tokens and new residual tokens to their fp16 planes
+  bool fused = false;
+  CopyParams cp{};
+  cp.k_in = static_cast<const uint16_t*>(K);
+  cp.v_in = static_cast<const uint16_t*>(V);
+  cp.k_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_RING));
+  cp.v_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_RING));
+  cp.k_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_SINK));
+  cp.v_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_SINK));
+  cp.n_old = n_old;
+  cp.n_q_new = w1.n_q;
+  cp.T = T;
+  cp.hkv = L.num_kv_heads;
+  cp.sink = L.sink_tokens;
+  cp.ring_slots = c->ring_slots;
+  // copied tokens: new sinks [n_old, min(n_new, S)), then new residual tokens
+  // [max(n_old, S + n_q_new), n_new)
+  cp.n_sink_copy = std::max<int64_t>(0, std::min<int64_t>(n_new, L.sink_tokens) - n_old);
+  cp.ring_first_t = std::max<int64_t>(n_old, (int64_t)L.sink_tokens + w1.n_q);
+  cp.n_copy = cp.n_sink_copy + std::max<int64_t>(0, n_new - cp.ring_first_t);
+  // the first append of a cache also sets the attention arrival counters to 0
+  cp.sync_zero = n_old == 0 ? reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC)) : nullptr;
+
   // 1) quantize the blocks that leave the residual window (reads ring slots
   //    of old tokens, so it runs before the copy below overwrites any slot)
   const int64_t n_flush = (w1.n_q - w0.n_q) / kBlock;
@@ -426,30 +449,22 @@ int32_t kv_quant_append(kvq_cache* c, const void* K, const void* V, int32_t T, v
     p.page_blocks = L.page_blocks;
     p.num_pages = L.num_pages;
     if (n_flush > 0x7fffffff) return KVQ_ERR_UNSUPPORTED;
-    if (launch_flush(variant_of(L), p, (int)n_flush, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+    p.flush_x = (int32_t)n_flush;
+    // a flush that reads no ring slot (nothing of the body was in the ring
+    // before this append) takes the copy as extra workgroups of its launch:
+    // the two touch disjoint planes, so they may run together
+    if (p.n_body_old == 0) {
+      const int64_t cx = std::max<int64_t>((cp.n_copy * 32 + 255) / 256, cp.sync_zero ? 1 : 0);
+      if (n_flush + cx <= 0x7fffffff) {
+        p.copy_x = (int32_t)cx;
+        p.cp = cp;
+        fused = true;
+      }
+    }
+    if (launch_flush(variant_of(L), p, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   }
-  // 2) copy new sink tokens and new residual tokens to their fp16 planes
-  CopyParams cp{};
-  cp.k_in = static_cast<const uint16_t*>(K);
-  cp.v_in = static_cast<const uint16_t*>(V);
-  cp.k_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_RING));
-  cp.v_ring = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_RING));
-  cp.k_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_K_SINK));
-  cp.v_sink = reinterpret_cast<uint16_t*>(plane(KVQ_PLANE_V_SINK));
-  cp.n_old = n_old;
-  cp.n_q_new = w1.n_q;
-  cp.T = T;
-  cp.hkv = L.num_kv_heads;
-  cp.sink = L.sink_tokens;
-  cp.ring_slots = c->ring_slots;
-  // copied tokens: new sinks [n_old, min(n_new, S)), then new residual tokens
-  // [max(n_old, S + n_q_new), n_new)
-  cp.n_sink_copy = std::max<int64_t>(0, std::min<int64_t>(n_new, L.sink_tokens) - n_old);
-  cp.ring_first_t = std::max<int64_t>(n_old, (int64_t)L.sink_tokens + w1.n_q);
-  cp.n_copy = cp.n_sink_copy + std::max<int64_t>(0, n_new - cp.ring_first_t);
-  // the first append of a cache also sets the attention arrival counters to 0
-  cp.sync_zero = n_old == 0 ? reinterpret_cast<int32_t*>(plane(KVQ_PLANE_SYNC)) : nullptr;
-  if (launch_copy(cp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
+  // 2) the copy, after the flush: it may overwrite ring slots the flush read
+  if (!fused && launch_copy(cp, L.batch, s) != hipSuccess) return KVQ_ERR_HIP;
   c->n_tokens = n_new;
   return KVQ_OK;
 }

@@ -48,6 +48,22 @@ __host__ __device__ constexpr int rope_channel(int p) { return (p >> 1) + (kHead
 inline int format_bits(int fmt) { return fmt == KVQ_INT4 ? 4 : (fmt == KVQ_INT2 ? 2 : 8); }
 
 // ---------------------------------------------------------------- append
+struct CopyParams {
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  uint16_t* k_ring;
+  uint16_t* v_ring;
+  uint16_t* k_sink;
+  uint16_t* v_sink;
+  int64_t n_old;
+  int64_t n_q_new;        // quantized body tokens after the append
+  int32_t T, hkv, sink, ring_slots;
+  int32_t* sync_zero;     // non-null on a cache's first append: [B][Hkv] counters set to 0
+  int64_t n_sink_copy;    // appended tokens copied: n_sink_copy sinks from token n_old, then
+  int64_t n_copy;         // n_copy - n_sink_copy residual tokens from token ring_first_t
+  int64_t ring_first_t;   // (the tokens in between are quantized straight from the input)
+};
+
 struct FlushParams {
   const uint16_t* k_in;   // fp16 [B][T][Hkv][D]
   const uint16_t* v_in;
@@ -72,6 +88,12 @@ struct FlushParams {
   int32_t table_stride;
   int32_t page_blocks;    // P
   int32_t num_pages;
+  // Fused copy (a flush that reads no ring slot, such as a cache's first
+  // append): workgroups x >= flush_x of each (KV head, sequence) copy that
+  // pair's tokens of cp, 256 16-byte chunks per workgroup; copy_x of them.
+  int32_t flush_x;        // blocks flushed per (sequence, KV head): the flush's workgroups in x
+  int32_t copy_x;         // 0: no fused copy (copy_kernel runs after the flush)
+  CopyParams cp;
 };
 
 // Record index of logical block blk of (sequence b, head h) in the code and
@@ -87,23 +109,8 @@ __host__ __device__ inline int64_t block_record(const int32_t* table, int32_t st
   return ((int64_t)page * hkv + h) * page_blocks + blk % page_blocks;
 }
 
-struct CopyParams {
-  const uint16_t* k_in;
-  const uint16_t* v_in;
-  uint16_t* k_ring;
-  uint16_t* v_ring;
-  uint16_t* k_sink;
-  uint16_t* v_sink;
-  int64_t n_old;
-  int64_t n_q_new;        // quantized body tokens after the append
-  int32_t T, hkv, sink, ring_slots;
-  int32_t* sync_zero;     // non-null on a cache's first append: [B][Hkv] counters set to 0
-  int64_t n_sink_copy;    // appended tokens copied: n_sink_copy sinks from token n_old, then
-  int64_t n_copy;         // n_copy - n_sink_copy residual tokens from token ring_first_t
-  int64_t ring_first_t;   // (the tokens in between are quantized straight from the input)
-};
 
-hipError_t launch_flush(int variant, const FlushParams& p, int n_blocks, int batch, hipStream_t s);
+hipError_t launch_flush(int variant, const FlushParams& p, int batch, hipStream_t s);
 hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 
 // ------------------------------------------------------------- attention
