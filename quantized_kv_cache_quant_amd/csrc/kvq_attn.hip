@@ -11,7 +11,7 @@
 // Work decomposition (workgroups of eight wavefronts, one per compute unit
 // by default):
 //  * the quantized 32-token blocks of all heads, flattened head-major, are
-//    cut into equal ranges, one per workgroup.  The wavefronts of a
+//    cut into ranges, one per workgroup (see AttnParams).  The wavefronts of a
 //    workgroup take the blocks of its range from a shared counter in LDS,
 //    each keeping its next kDepth blocks' loads in flight, so wavefronts the
 //    memory system serves faster take more blocks and the workgroup's

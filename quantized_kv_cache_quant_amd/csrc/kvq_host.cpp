@@ -133,7 +133,15 @@ AttnPlan plan(const kvq_layout& L, int64_t nblk, int64_t n_fp16_tokens, int32_t 
     const int64_t even = std::min((total + target - 1) / target, cap);
     const int64_t k = bh <= target ? target / bh : 0;
     const int64_t per = k > 0 ? (nblk + k - 1) / k : 0;
-    if (k > 0 && nblk >= k && per <= even + even / 32 && per <= cap && k * nblk < (int64_t(1) << 31)) {
+    // a small call: every head in parts of at most one block per wavefront,
+    // as long as they fit one workgroup per compute unit (a workgroup's merge
+    // and a shared head's combine cost the same whatever its share, so fewer,
+    // fuller workgroups finish sooner than one block each)
+    const int64_t ks = (nblk + kGroupWaves - 1) / kGroupWaves;
+    if (bh * ks <= target && kGroupWaves <= cap && ks * nblk < (int64_t(1) << 31)) {
+      a.range_len = nblk;                           // ks parts of every head
+      a.range_parts = ks;
+    } else if (k > 0 && nblk >= k && per <= even + even / 32 && per <= cap && k * nblk < (int64_t(1) << 31)) {
       a.range_len = nblk;                           // k parts of every head
       a.range_parts = k;
     } else {

@@ -116,9 +116,10 @@ hipError_t launch_copy(const CopyParams& p, int batch, hipStream_t s);
 // ------------------------------------------------------------- attention
 // Work: the quantized blocks of all heads, flattened head-major (block j is
 // block j mod nblk of head j / nblk), are cut into ranges, one per workgroup
-// of kGroupWaves wavefronts (whole heads cut into equal parts when the
-// workgroups divide among the heads evenly, else equal ranges across head
-// boundaries); the wavefronts of a
+// of kGroupWaves wavefronts (whole heads cut into equal parts of at most
+// kGroupWaves blocks when those fit one workgroup per compute unit, else into
+// equal parts when the workgroups divide among the heads evenly, else equal
+// ranges across head boundaries); the wavefronts of a
 // workgroup take the blocks of its range in turn.  The fp16 segment of every
 // head (sinks, then residual ring) is cut into 32-token blocks, dealt round
 // robin to the workgroups whose range touches the head.
