@@ -1728,7 +1728,7 @@ constexpr int kSpinLimit = 1 << 22;
 constexpr int kCombineBatch = 8;
 
 __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool last0, bool last1, int lo0, int lo1,
-                               int nc0, int nc1, const float* own0, const float* own1) {
+                               int nc0, int nc1, const float* own0, const float* own1, float* red) {
   if (threadIdx.x == 0) {
     for (int s = 0; s < 2; ++s) {
       const bool on = s == 0 ? last0 : last1;
@@ -1747,17 +1747,42 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
   const int per = p.nrep * (kHeadDim / 4);
   const int n0 = last0 ? per : 0;
   const int total = n0 + (last1 ? per : 0);
-  for (int idx = threadIdx.x; idx < total; idx += kGroupThreads) {
-    const bool first = idx < n0;
-    const int h = first ? h0 : h1, nc = first ? nc0 : nc1, r = first ? idx : idx - n0;
-    const int hq = r >> 5, c4 = r & 31;
+  // Items are (head, query head, four channels); each folds its head's
+  // slots in batches of kCombineBatch.  With threads to spare, G groups of
+  // `total` threads take every G-th batch each, and their results are folded
+  // once more through LDS (red: 8 floats per group and item).
+  const int nmax = (last0 && nc0 > (last1 ? nc1 : 0)) ? nc0 : (last1 ? nc1 : nc0);
+  const int nbat = (nmax + kCombineBatch - 1) / kCombineBatch;
+  int G = kGroupThreads / total;
+  G = G < nbat ? G : nbat;
+  G = G > 1 ? G : 1;
+  auto item = [&](int idx, int& h, int& nc, int& hq, int& c4, bool& first) {
+    first = idx < n0;
+    h = first ? h0 : h1;
+    nc = first ? nc0 : nc1;
+    const int r = first ? idx : idx - n0;
+    hq = r >> 5;
+    c4 = r & 31;
+  };
+  auto write_out = [&](int h, int hq, int c4, float L, float4 O) {
+    const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
+    const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
+    *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hq) * kHeadDim + 4 * c4) =
+        uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  };
+  const int gi = (int)threadIdx.x / total;
+  if (gi < G) {
+    const int idx = (int)threadIdx.x - gi * total;
+    int h, nc, hq, c4;
+    bool first;
+    item(idx, h, nc, hq, c4, first);
     const float* own = (first ? own0 : own1) + hq * kPartStride;
     const int64_t glo = first ? lo0 : lo1;
     const int me = g - (int)glo;                 // this workgroup's place among the covering ones
     const float* base = p.part_group + (glo + h) * slot_floats(p) + hq * kPartStride;
     float M = neg_inf(), L = 0.f;
     float4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nc; s0 += kCombineBatch) {
+    for (int s0 = gi * kCombineBatch; s0 < nc; s0 += G * kCombineBatch) {
       float m[kCombineBatch], l[kCombineBatch];
       float4 o[kCombineBatch];
 #pragma unroll
@@ -1780,10 +1805,44 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
       }
       fold4<kCombineBatch>(M, L, O, m, l, o);
     }
-    const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
-    const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
-    *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hq) * kHeadDim + 4 * c4) =
-        uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    if (G == 1) {
+      write_out(h, hq, c4, L, O);
+    } else {
+      float* r = red + 8 * (gi * total + idx);
+      r[0] = M;
+      r[1] = L;
+      *reinterpret_cast<float4*>(r + 4) = O;
+    }
+  }
+  if (G > 1) {                                  // uniform over the workgroup
+    __syncthreads();
+    if ((int)threadIdx.x < total) {
+      const int idx = threadIdx.x;
+      int h, nc, hq, c4;
+      bool first;
+      item(idx, h, nc, hq, c4, first);
+      float M = neg_inf(), L = 0.f;
+      float4 O = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < G; j0 += 4) {
+        float m[4], l[4];
+        float4 o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j0 + j < G) {
+            const float* r = red + 8 * ((j0 + j) * total + idx);
+            m[j] = r[0];
+            l[j] = r[1];
+            o[j] = *reinterpret_cast<const float4*>(r + 4);
+          } else {
+            m[j] = neg_inf();
+            l[j] = 0.f;
+            o[j] = float4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        fold4<4>(M, L, O, m, l, o);
+      }
+      write_out(h, hq, c4, L, O);
+    }
   }
 }
 
@@ -2286,7 +2345,9 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     if (sh0 && !last0) __hip_atomic_fetch_add(p.sync + gr.h0, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
     if (sh1 && !last1) __hip_atomic_fetch_add(p.sync + gr.h1, 1 << 16, kMarkOrder, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (last0 || last1) combine_shared(p, g, gr.h0, gr.h1, last0, last1, lo0, lo1, nc0, nc1, own_slot(0), own_slot(1));
+  if (last0 || last1)                          // (partials of the slot groups in wavefronts 2.. 's areas)
+    combine_shared(p, g, gr.h0, gr.h1, last0, last1, lo0, lo1, nc0, nc1, own_slot(0), own_slot(1),
+                   reinterpret_cast<float*>(lds + 2 * kWaveLds));
 }
 
 
