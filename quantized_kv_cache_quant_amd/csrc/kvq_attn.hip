@@ -204,8 +204,8 @@ struct Traits {
   static constexpr int kDepth = kDepthBase < kDepthCap ? kDepthBase : kDepthCap;
   // paired processing (INT4 / INT2 at n_rep <= 4, see process_pair): two blocks per step, the
   // ring holds the pair being processed and the next pairs' loads
-  static constexpr bool kPairable = !kFp8 && !kRope && !kOut && kBits < 8;
-  static constexpr int kPairRing = kBits == 2 ? KVQ_PAIR_RING_INT2 : KVQ_PAIR_RING_INT4;
+  static constexpr bool kPairable = !kFp8 && !kRope && kBits < 8;   // (the slot path: also !kOut)
+  static constexpr int kPairRing = kOut ? 4 : (kBits == 2 ? KVQ_PAIR_RING_INT2 : KVQ_PAIR_RING_INT4);
   static constexpr float kCodeScale = kFp8 ? 1.0f : kTwo24;   // undoes the subnormal placement
 };
 
@@ -336,6 +336,8 @@ constexpr float kLazyScaleMax = 255.0f;
 // and with outliers (see stage_meta)
 //   [512,640) K outlier corrections (slot order)   [640,768) V outlier corrections [g][t]
 //   [768,832) K outlier tokens (16-bit, slot order)   [832,896) V outlier channels (16-bit)
+// The paired and slot paths stage their second block from kStage on, or with
+// outliers from 896 on.
 constexpr int kStage = 512;
 constexpr int kOutKd = 512, kOutVd = 640, kOutKx = 768, kOutVx = 832;
 // Outlier corrections go through the matrix cores as (one-hot) x (q or p times
@@ -1083,9 +1085,11 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
                                              WaveState& ws, const QOp& q, const LaneInfo& li) {
   using T = Traits<FMT>;
   const int qd = li.qd;
-  stage_meta<FMT>(ra, st, li.lane);
-  stage_meta<FMT>(rb, st + kStage, li.lane);
-  const float* sp = st + (li.par ? kStage : 0);          // this lane's block
+  // block b's staging follows block a's (with outliers, after its corrections)
+  constexpr int kB = T::kOut ? kOutVx + 64 : kStage;
+  const float vba = stage_meta<FMT>(ra, st, li.lane);     // (outliers: largest |Value correction|)
+  const float vbb = stage_meta<FMT>(rb, st + kB, li.lane);
+  const float* sp = st + (li.par ? kB : 0);              // this lane's block
 
   // zero-point term of this lane's block (see process_block)
   float bz[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1115,6 +1119,24 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
       acc_a[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(ra.k[tile], kb), bq, acc_a[tile], 0, 0, 0);
       acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(rb.k[tile], kb), bq, acc_b[tile], 0, 0, 0);
     }
+    if constexpr (T::kOut) {
+      // Key outliers (see process_block): q times this lane's block's staged
+      // corrections, against each block's one-hot (token row, channel slot)
+      const float4 da = *reinterpret_cast<const float4*>(sp + kOutKd + 32 * qd + 8 * kb);
+      const float4 db = *reinterpret_cast<const float4*>(sp + kOutKd + 32 * qd + 8 * kb + 4);
+      const f16x8 bd = split_q4(q.z + 4 * kb, q.h + 4 * kb, da, db);
+      const uint4 ia = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutKx) + 32 * qd + 8 * kb);
+      const uint4 ib =
+          *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kB + kOutKx) + 32 * qd + 8 * kb);
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const uint32_t own = (uint32_t)(16 * tile + (li.lane & 15)) * (0x10001u << kOhShift);
+        const f16x8 oha = cat(one_hot(ia.x, own), one_hot(ia.y, own), one_hot(ia.z, own), one_hot(ia.w, own));
+        const f16x8 ohb = cat(one_hot(ib.x, own), one_hot(ib.y, own), one_hot(ib.z, own), one_hot(ib.w, own));
+        acc_a[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oha, bd, acc_a[tile], 0, 0, 0);
+        acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ohb, bd, acc_b[tile], 0, 0, 0);
+      }
+    }
   }
   float lg[2][4], pr[2][4];
 #pragma unroll
@@ -1125,7 +1147,9 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
       lg[tile][i] = __builtin_fmaf(x + ror8(x), T::kCodeScale, -kbias);
     }
   const float2 sva = pair_scales<FMT>(ra.vm), svb = pair_scales<FMT>(rb.vm);
-  const bool big = sva.x > kLazyScaleMax || sva.y > kLazyScaleMax || (b_on && (svb.x > kLazyScaleMax || svb.y > kLazyScaleMax));
+  // (outliers: p times a staged correction, at most p * |correction| / 2^8)
+  const bool big = sva.x > kLazyScaleMax || sva.y > kLazyScaleMax || vba > kLazyScaleMax * 256.0f ||
+                   (b_on && (svb.x > kLazyScaleMax || svb.y > kLazyScaleMax || vbb > kLazyScaleMax * 256.0f));
   const float slack = __any(big) ? 0.f : kSlack;
   if (b_on) softmax_block(lg, ws, pr, slack);
   else softmax_block_some(lg, ws, pr, slack, li.par == 0);
@@ -1164,6 +1188,30 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
       const int m = 2 * g + mm;
       ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(ra.v, m), bpa, ws.o[m], 0, 0, 0);
       if (b_on) ws.o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand<FMT>(rb.v, m), bpb, ws.o[m], 0, 0, 0);
+    }
+    if constexpr (T::kOut) {
+      // Value outliers of group g (see process_block): p times this lane's
+      // block's staged corrections, masked to each block's columns, against
+      // that block's one-hot (channel row, token slot)
+      const float4 d0 = *reinterpret_cast<const float4*>(sp + kOutVd + 32 * g + 4 * qd);
+      const float4 d1 = *reinterpret_cast<const float4*>(sp + kOutVd + 32 * g + 16 + 4 * qd);
+      const float dv0[4] = {d0.x, d0.y, d0.z, d0.w}, dv1[4] = {d1.x, d1.y, d1.z, d1.w};
+      const uint4 wd = __builtin_bit_cast(uint4, split_p4(pr[0], pb[0], dv0, pr[1], pb[1], dv1));
+      const f16x8 bda = cat(wd.x & am, wd.y & am, wd.z & am, wd.w & am);
+      const f16x8 bdb = cat(wd.x & bm, wd.y & bm, wd.z & bm, wd.w & bm);
+      const uint4 ia = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kOutVx) + 32 * g + 8 * qd);
+      const uint4 ib =
+          *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(st + kB + kOutVx) + 32 * g + 8 * qd);
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const uint32_t own = (uint32_t)(16 * mm + (li.lane & 15)) * (0x10001u << kOhShift);
+        const f16x8 oha = cat(one_hot(ia.x, own), one_hot(ia.y, own), one_hot(ia.z, own), one_hot(ia.w, own));
+        ws.o[2 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oha, bda, ws.o[2 * g + mm], 0, 0, 0);
+        if (b_on) {
+          const f16x8 ohb = cat(one_hot(ib.x, own), one_hot(ib.y, own), one_hot(ib.z, own), one_hot(ib.w, own));
+          ws.o[2 * g + mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ohb, bdb, ws.o[2 * g + mm], 0, 0, 0);
+        }
+      }
     }
   }
 }
@@ -1521,6 +1569,7 @@ constexpr int kLdsBytes = kGroupWaves * kWaveLds + kLdsHeader + 4 * kMaxPagedRan
 static_assert(kStageBytes >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
 static_assert(kStageBytes >= 2 * kStage * 4, "the stage area holds two blocks (paired and slot paths)");
 static_assert(kStageBytes >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
+static_assert(kStageBytes >= 2 * (kOutVx + 64) * 4, "stage area holds two blocks with outliers (paired path)");
 
 // One workgroup: range [jb, jb + len) of the flattened quantized blocks,
 // touching heads h0..h1.
@@ -1726,6 +1775,8 @@ constexpr int kSpinLimit = 1 << 22;
 // from LDS, the others' by device-coherent loads issued after the marks
 // were seen, kCombineBatch slots per round trip.
 constexpr int kCombineBatch = 8;
+// floats of the combine's batch results in LDS (the stage areas of wavefronts 2 on)
+constexpr int kRedFloats = (kGroupWaves - 2) * kWaveLds / 4;
 
 __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool last0, bool last1, int lo0, int lo1,
                                int nc0, int nc1, const float* own0, const float* own1, float* red) {
@@ -1747,14 +1798,18 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
   const int per = p.nrep * (kHeadDim / 4);
   const int n0 = last0 ? per : 0;
   const int total = n0 + (last1 ? per : 0);
-  // Items are (head, query head, four channels); each folds its head's
-  // slots in batches of kCombineBatch.  With threads to spare, G groups of
-  // `total` threads take every G-th batch each, and their results are folded
-  // once more through LDS (red: 8 floats per group and item).
+  // Items are (head, query head, four channels).  An item's slots are cut
+  // into batches of kCombineBatch; each batch is folded on its own, and the
+  // batch results are folded in batch order, so the result does not depend
+  // on how the work is spread.  With threads to spare, G groups of `total`
+  // threads fold every G-th batch each into LDS (red: 8 floats per batch and
+  // item) and one thread per item folds them; otherwise one thread per item
+  // does both in turn.
   const int nmax = (last0 && nc0 > (last1 ? nc1 : 0)) ? nc0 : (last1 ? nc1 : nc0);
   const int nbat = (nmax + kCombineBatch - 1) / kCombineBatch;
   int G = kGroupThreads / total;
   G = G < nbat ? G : nbat;
+  if ((int64_t)nbat * total * 8 > kRedFloats) G = 1;
   G = G > 1 ? G : 1;
   auto item = [&](int idx, int& h, int& nc, int& hq, int& c4, bool& first) {
     first = idx < n0;
@@ -1764,15 +1819,8 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
     hq = r >> 5;
     c4 = r & 31;
   };
-  auto write_out = [&](int h, int hq, int c4, float L, float4 O) {
-    const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
-    const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
-    *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hq) * kHeadDim + 4 * c4) =
-        uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-  };
-  const int gi = (int)threadIdx.x / total;
-  if (gi < G) {
-    const int idx = (int)threadIdx.x - gi * total;
+  // the fold of slots s0 .. s0 + kCombineBatch - 1 (those below nc) of an item
+  auto batch = [&](int idx, int s0, float& M, float& L, float4& O) {
     int h, nc, hq, c4;
     bool first;
     item(idx, h, nc, hq, c4, first);
@@ -1780,69 +1828,78 @@ __device__ void combine_shared(const AttnParams& p, int g, int h0, int h1, bool 
     const int64_t glo = first ? lo0 : lo1;
     const int me = g - (int)glo;                 // this workgroup's place among the covering ones
     const float* base = p.part_group + (glo + h) * slot_floats(p) + hq * kPartStride;
+    float m[kCombineBatch], l[kCombineBatch];
+    float4 o[kCombineBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const int s = s0 + j;
+      if (s >= nc) {
+        m[j] = neg_inf();
+        l[j] = 0.f;
+        o[j] = float4{0.f, 0.f, 0.f, 0.f};
+      } else if (s == me) {
+        m[j] = own[0];
+        l[j] = own[1];
+        o[j] = *reinterpret_cast<const float4*>(own + 4 + 4 * c4);
+      } else {
+        const float* sp = base + s * slot_floats(p);
+        m[j] = ld_dev(sp);
+        l[j] = ld_dev(sp + 1);
+        o[j] = ld_dev4(sp + 4 + 4 * c4);
+      }
+    }
+    M = neg_inf();
+    L = 0.f;
+    O = float4{0.f, 0.f, 0.f, 0.f};
+    fold4<kCombineBatch>(M, L, O, m, l, o);
+  };
+  auto write_out = [&](int idx, float L, float4 O) {
+    int h, nc, hq, c4;
+    bool first;
+    item(idx, h, nc, hq, c4, first);
+    const f16x2 lo = {(_Float16)(O.x / L), (_Float16)(O.y / L)};
+    const f16x2 hi = {(_Float16)(O.z / L), (_Float16)(O.w / L)};
+    *reinterpret_cast<uint2*>(p.out + ((int64_t)h * p.nrep + hq) * kHeadDim + 4 * c4) =
+        uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  };
+  auto nbat_of = [&](int idx) {
+    const int nc = idx < n0 ? nc0 : nc1;
+    return (nc + kCombineBatch - 1) / kCombineBatch;
+  };
+  {
+    const int gi = G > 1 ? (int)threadIdx.x / total : 0;
+    const int idx = (int)threadIdx.x - gi * total;
     float M = neg_inf(), L = 0.f;
     float4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = gi * kCombineBatch; s0 < nc; s0 += G * kCombineBatch) {
-      float m[kCombineBatch], l[kCombineBatch];
-      float4 o[kCombineBatch];
-#pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j) {
-        const int s = s0 + j;
-        if (s >= nc) {
-          m[j] = neg_inf();
-          l[j] = 0.f;
-          o[j] = float4{0.f, 0.f, 0.f, 0.f};
-        } else if (s == me) {
-          m[j] = own[0];
-          l[j] = own[1];
-          o[j] = *reinterpret_cast<const float4*>(own + 4 + 4 * c4);
+    if (gi < G && idx < total) {
+      const int nb = nbat_of(idx);
+      for (int b = gi; b < nb; b += G) {
+        float bm, bl;
+        float4 bo;
+        batch(idx, b * kCombineBatch, bm, bl, bo);
+        if (G > 1) {
+          float* r = red + 8 * (b * total + idx);
+          r[0] = bm;
+          r[1] = bl;
+          *reinterpret_cast<float4*>(r + 4) = bo;
         } else {
-          const float* sp = base + s * slot_floats(p);
-          m[j] = ld_dev(sp);
-          l[j] = ld_dev(sp + 1);
-          o[j] = ld_dev4(sp + 4 + 4 * c4);
+          fold4<1>(M, L, O, &bm, &bl, &bo);
         }
       }
-      fold4<kCombineBatch>(M, L, O, m, l, o);
     }
-    if (G == 1) {
-      write_out(h, hq, c4, L, O);
-    } else {
-      float* r = red + 8 * (gi * total + idx);
-      r[0] = M;
-      r[1] = L;
-      *reinterpret_cast<float4*>(r + 4) = O;
-    }
-  }
-  if (G > 1) {                                  // uniform over the workgroup
-    __syncthreads();
-    if ((int)threadIdx.x < total) {
-      const int idx = threadIdx.x;
-      int h, nc, hq, c4;
-      bool first;
-      item(idx, h, nc, hq, c4, first);
-      float M = neg_inf(), L = 0.f;
-      float4 O = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < G; j0 += 4) {
-        float m[4], l[4];
-        float4 o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j0 + j < G) {
-            const float* r = red + 8 * ((j0 + j) * total + idx);
-            m[j] = r[0];
-            l[j] = r[1];
-            o[j] = *reinterpret_cast<const float4*>(r + 4);
-          } else {
-            m[j] = neg_inf();
-            l[j] = 0.f;
-            o[j] = float4{0.f, 0.f, 0.f, 0.f};
-          }
+    if (G > 1) {                                // uniform over the workgroup
+      __syncthreads();
+      if ((int)threadIdx.x < total) {
+        const int nb = nbat_of(threadIdx.x);
+        for (int b = 0; b < nb; ++b) {
+          const float* r = red + 8 * (b * total + (int)threadIdx.x);
+          const float bm = r[0], bl = r[1];
+          const float4 bo = *reinterpret_cast<const float4*>(r + 4);
+          fold4<1>(M, L, O, &bm, &bl, &bo);
         }
-        fold4<4>(M, L, O, m, l, o);
       }
-      write_out(h, hq, c4, L, O);
     }
+    if ((int)threadIdx.x < total) write_out(threadIdx.x, L, O);
   }
 }
 
@@ -2411,6 +2468,10 @@ hipError_t launch_attention(int variant, const AttnParams& p, hipStream_t s) {
       case KVQ_INT2: KVQ_LAUNCH2(KVQ_INT2, kPairs);
       case KVQ_INT4 | kMeta16: KVQ_LAUNCH2(KVQ_INT4 | kMeta16, kPairs);
       case KVQ_INT2 | kMeta16: KVQ_LAUNCH2(KVQ_INT2 | kMeta16, kPairs);
+      case KVQ_INT4 | kOutliers: KVQ_LAUNCH2(KVQ_INT4 | kOutliers, kPairs);
+      case KVQ_INT2 | kOutliers: KVQ_LAUNCH2(KVQ_INT2 | kOutliers, kPairs);
+      case KVQ_INT4 | kMeta16 | kOutliers: KVQ_LAUNCH2(KVQ_INT4 | kMeta16 | kOutliers, kPairs);
+      case KVQ_INT2 | kMeta16 | kOutliers: KVQ_LAUNCH2(KVQ_INT2 | kMeta16 | kOutliers, kPairs);
       default: break;
     }
   } else {

@@ -131,3 +131,18 @@ def test_full_size_outliers_int4():
     q = synth.queries(w)
     out = attention_gpu(c, q)
     check_every_head(c, kw, out, q, k, v)
+
+
+def test_full_size_outliers_int2_pairs():
+    """The 8B shape (batch 16, 8192 tokens, n_rep 4) in INT2 with outliers: the paired path,
+    two blocks per step, every (sequence, KV head) pair against the oracle."""
+    require_gpu()
+    w = W["llama3_8b"]
+    k, v = synth.prefill(w)
+    kw = _kw("int2", w.batch, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.seq_len + 32,
+             w.residual_tokens, w.sink_tokens)
+    c = make_cache(kw)
+    append_chunks(c, k, v, [w.seq_len])
+    q = synth.queries(w)
+    out = attention_gpu(c, q)
+    check_every_head(c, kw, out, q, k, v)
