@@ -1137,6 +1137,8 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
         acc_b[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ohb, bd, acc_b[tile], 0, 0, 0);
       }
     }
+    // (with outliers, one k-block's temporaries live at a time)
+    if constexpr (T::kOut) __builtin_amdgcn_sched_barrier(0);
   }
   float lg[2][4], pr[2][4];
 #pragma unroll
@@ -1213,6 +1215,7 @@ __device__ __forceinline__ void process_pair(const Raw<FMT>& ra, const Raw<FMT>&
         }
       }
     }
+    if constexpr (T::kOut) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
