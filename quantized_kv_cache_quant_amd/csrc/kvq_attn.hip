@@ -1569,6 +1569,11 @@ constexpr int kWaveLds = kStageBytes + 8 * kPartStride * 4;
 // a paged range (then, for pre-RoPE Keys, the in-block offset table)
 constexpr int kLdsHeader = 32 + 4 * kGroupWaves;    // counters, each wavefront's final head, covering info
 constexpr int kLdsBytes = kGroupWaves * kWaveLds + kLdsHeader + 4 * kMaxPagedRange;
+// The first kFp16Lds fp16 partials of a workgroup's first head are kept in
+// LDS after kLdsBytes (the merge reads them as LDS instead of from the
+// workspace), the RoPE table after them.
+constexpr int kFp16Lds = 4;
+constexpr int kFp16LdsBytes = kFp16Lds * 8 * kPartStride * 4;
 static_assert(kStageBytes >= (kStage + 128) * 4, "stage area holds the RoPE base angles after the block metadata");
 static_assert(kStageBytes >= 2 * kStage * 4, "the stage area holds two blocks (paired and slot paths)");
 static_assert(kStageBytes >= (kOutVx + 64) * 4, "stage area holds the outlier corrections after the block metadata");
@@ -1957,7 +1962,7 @@ __device__ void group_main(const AttnParams& p, char* lds) {
     }
   }
   // pre-RoPE Keys: the in-block offsets (cos, sin)(k theta_i), k < 32, i < 64
-  float2* rtab = reinterpret_cast<float2*>(lds + kLdsBytes);
+  float2* rtab = reinterpret_cast<float2*>(lds + kLdsBytes + kFp16LdsBytes);
   if constexpr (T::kRope) {
     for (int e = threadIdx.x; e < 32 * 64; e += kGroupThreads)
       rtab[e] = rope_cs((double)(e >> 6), rope_freq(p.rope_theta, e & 63));
@@ -2265,8 +2270,11 @@ __device__ void group_main(const AttnParams& p, char* lds) {
       idx = __builtin_amdgcn_readfirstlane(idx);
       int h, fb;
       if (!fp16_of(idx, h, fb)) break;
-      fp16_block<T::kRope>(p, h, fb, reinterpret_cast<uint16_t*>(stage),
-                           p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p));
+      // (the first kFp16Lds of the first head's: idx is then their place among that head's)
+      float* dst = h == gr.h0 && idx < kFp16Lds
+                       ? reinterpret_cast<float*>(lds + kLdsBytes) + idx * slot_floats(p)
+                       : p.part_fp16 + ((int64_t)h * p.fp16_blocks + fb) * slot_floats(p);
+      fp16_block<T::kRope>(p, h, fb, reinterpret_cast<uint16_t*>(stage), dst);
     }
   }
   __syncthreads();                            // every wavefront's partials written
@@ -2331,11 +2339,20 @@ __device__ void group_main(const AttnParams& p, char* lds) {
             o[w] = float4{t.x, t.y, t.z, t.w};
           }
         }
+        // the first kFp16Lds of the first head's are in LDS (read as LDS)
+        const bool in_lds = h == gr.h0;
+        static_assert(kFoldFp16 == kFp16Lds, "one pass reads the LDS fp16 partials");
         auto load_fp16 = [&](int64_t first) {
 #pragma unroll
           for (int j = 0; j < kFoldFp16; ++j) {
             const int64_t fb = first + j * nc;
-            if (fb < nf) {
+            if (fb < nf && in_lds && first == fb0) {
+              const float* lp = reinterpret_cast<const float*>(lds + kLdsBytes) + j * slot_floats(p) + hh * kPartStride;
+              const float2 ml = *reinterpret_cast<const float2*>(lp);
+              fm[j] = ml.x;
+              fl[j] = ml.y;
+              fo[j] = *reinterpret_cast<const float4*>(lp + 4 + 4 * c4);
+            } else if (fb < nf) {
               const float* sp = p.part_fp16 + ((int64_t)h * nf + fb) * slot_floats(p) + hh * kPartStride;
               fm[j] = sp[0];
               fl[j] = sp[1];
@@ -2427,7 +2444,7 @@ __device__ void fp16_group(const AttnParams& p, char* lds) {
 template <int FMT, int MODE = kSingle>
 __global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16)))
-  char lds[kLdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
+  char lds[kLdsBytes + kFp16LdsBytes + (Traits<FMT>::kRope ? kRopeTableBytes : 0)];
   if (p.nblk == 0) fp16_group<Traits<FMT>::kRope>(p, lds);
   else group_main<FMT, MODE>(p, lds);
 }
